@@ -1,0 +1,375 @@
+"""Pins for the CPU oracle: each check compares it with something other than itself.
+
+* exact rational arithmetic (fractions.Fraction) and IEEE rounding written
+  from the standard's rules (tests/fraction_ref.py);
+* hand-worked scalar cases (tests/golden/handworked_exact_chain.json);
+* algebraic identities (merged == factored, stacked == per-group layers);
+* special cases that reduce to a library routine (torch F.linear in float64);
+* exhaustive indexing of the 4-bit codes.
+
+A plausible slip in the oracle -- a dropped term, a wrong sign, a transposed
+operand, a wrong nibble or block index, a missing or extra rounding, the wrong
+summation order -- fails at least one of these.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import exact_chain as ec
+from oracle import lora_oracle as lo
+from tests.fraction_ref import exact, round_fraction, dot_exact
+import lora_workloads as lw
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "handworked_exact_chain.json")
+
+
+def _hex(v):
+    return float.fromhex(v) if isinstance(v, str) else float(v)
+
+
+def _mat(rows, dtype):
+    if rows is None:
+        return None
+    a = np.array([[_hex(v) for v in r] for r in rows], dtype=np.float64)
+    return lw.to_dtype(a, dtype)
+
+
+def _vec(vals, dtype):
+    if vals is None:
+        return None
+    return lw.to_dtype(np.array([_hex(v) for v in vals], dtype=np.float64), dtype)
+
+
+# ---------------------------------------------------------------- rounding primitives
+
+def _edge_f32_values():
+    rng = np.random.default_rng(11)
+    vals = list((rng.standard_normal(400) * np.exp2(rng.integers(-140, 126, 400))).astype(np.float32))
+    # ties and near-ties at bf16 granularity, subnormals, extremes
+    for base in (1.0, 1.5, 2.0 ** -130, 3.0e38, 2.0 ** -126):
+        b = np.float32(base)
+        u = np.array([b], np.float32).view(np.uint32)[0]
+        for off in (0x7FFF, 0x8000, 0x8001, 0x17FFF, 0x18000, 0x18001, 0xFFFF):
+            vals.append(np.array([u + off], np.uint32).view(np.float32)[0])
+            vals.append(-np.array([u + off], np.uint32).view(np.float32)[0])
+    vals += [np.float32(3.3895314e38), np.float32(np.finfo(np.float32).max), np.float32(1e-45)]
+    return np.array(vals, dtype=np.float32)
+
+
+def test_rn_bf16_matches_exact_rounding():
+    vals = _edge_f32_values()
+    got = ec.rn_bf16(vals.astype(np.float64))
+    assert np.all(np.isfinite(vals))
+    for v, g in zip(vals, got):
+        want = round_fraction(exact(float(v)), "bf16")
+        if float(v) < 0 and want == 0.0:
+            want = -0.0
+        assert g == want or (math.isinf(g) and math.isinf(want) and (g > 0) == (want > 0)), (v, g, want)
+
+
+def test_rn_bf16_signed_zero_and_nan():
+    assert math.copysign(1.0, ec.rn_bf16(np.array([-0.0]))[0]) == -1.0
+    assert np.isnan(ec.rn_bf16(np.array([np.nan]))[0])
+    with pytest.raises(ValueError):
+        ec.rn_bf16(np.array([1.0 + 2.0 ** -40]))  # not an fp32 value
+
+
+def test_rn_f32_matches_exact_rounding():
+    rng = np.random.default_rng(12)
+    vals = rng.standard_normal(300) * np.exp2(rng.integers(-150, 128, 300))
+    vals = np.concatenate([vals, [1 + 2.0 ** -24, 1 + 3 * 2.0 ** -24, 1 + 2.0 ** -24 + 2.0 ** -50,
+                                  2.0 ** -149 * 1.5, 2.0 ** -149 * 2.5, 3.4028235677973366e38]])
+    got = ec.rn_f32(vals)
+    for v, g in zip(vals, got):
+        want = round_fraction(exact(v), "f32")
+        if v < 0 and want == 0.0:
+            want = -0.0
+        assert g == want, (v, g, want)
+
+
+# ---------------------------------------------------------------- E1 ordered GEMM
+
+def test_gemm_ordered_is_correctly_rounded_when_fp64_sum_is_exact():
+    # bf16 inputs with K = 6 and a narrow exponent range: every fp64 partial sum is exact,
+    # so E1 must equal the exact dot product rounded once to fp32.
+    rng = np.random.default_rng(13)
+    P = lw.to_dtype(rng.standard_normal((5, 6)), "bf16")
+    Q = lw.to_dtype(rng.standard_normal((7, 6)), "bf16")
+    got = ec.gemm_ordered(P, Q)
+    Pd, Qd = P.double().numpy(), Q.double().numpy()
+    for i in range(5):
+        for j in range(7):
+            assert got[i, j] == round_fraction(dot_exact(Pd[i], Qd[j]), "f32")
+
+
+def test_golden_linear_chain_and_plain_definition():
+    cases = json.load(open(GOLDEN))["linear"]
+    for c in cases:
+        act, adt = c["act"], c["adapter"]
+        x, W = _mat(c["x"], act), _mat(c["W"], act)
+        b = _vec(c["b"], act)
+        A, B = _mat(c["A"], adt), _mat(c["B"], adt)
+        rs = _hex(c["request_scale"])
+        y = ec.chain_linear(x, W, b, A, B, c["alpha"], c["rank"], c["strength"], rs, act, adt)
+        want = np.array([[_hex(v) for v in r] for r in c["expected"]])
+        assert np.array_equal(y, want), (c["name"], y, want)
+        y64 = lo.lora_linear(x, W, b, A, B, c["alpha"], c["rank"], c["strength"], rs)
+        want64 = np.array([[_hex(v) for v in r] for r in c["exact_fp64"]])
+        if c["name"].startswith("k_ascending"):
+            continue  # the fp64 plain definition itself cancels here; only the chain is pinned
+        assert np.array_equal(y64, want64), (c["name"], y64, want64)
+
+
+def test_golden_dense_patch_chain():
+    for c in json.load(open(GOLDEN))["patch"]:
+        dt = c["dtype"]
+        dst = _vec([c["dst"]], dt)
+        src = _vec([c["src"]], "bf16" if dt == "bf16" else "bf16")
+        got = ec.chain_dense_patch(dst, src, _hex(c["strength"]), c["mode"], dt)
+        assert got[0] == _hex(c["expected"]), (c["name"], got[0].hex(), c["expected"])
+
+
+# ---------------------------------------------------------------- O1 plain definition
+
+def _frac_lora_linear(x, W, b, A, B, s):
+    T, K = x.shape
+    N = W.shape[0]
+    r = A.shape[0] if A is not None else 0
+    out = [[Fraction(0)] * N for _ in range(T)]
+    for m in range(T):
+        t = [dot_exact(x[m], A[q]) for q in range(r)] if A is not None else []
+        for n in range(N):
+            v = dot_exact(x[m], W[n])
+            if b is not None:
+                v += exact(b[n])
+            if A is not None:
+                v += s * sum((t[q] * exact(B[n, q]) for q in range(r)), Fraction(0))
+            out[m][n] = v
+    return out
+
+
+@pytest.mark.parametrize("T,K,N,r,seed", [(3, 4, 2, 3, 0), (2, 3, 4, 1, 1), (4, 2, 3, 4, 2), (1, 4, 4, 2, 3)])
+def test_lora_linear_brute_force_fraction(T, K, N, r, seed):
+    d = lw.small_linear_inputs(T, K, N, r, seed, bias=True, alpha=3.0, strength=0.6, request_scale=1.3)
+    s = lo.combined_scale(d["alpha"], d["rank"], d["strength"], d["request_scale"])
+    xd, Wd, bd, Ad, Bd = (lo.f64(d[k]) for k in ("x", "W", "b", "A", "B"))
+    exact_y = _frac_lora_linear(xd, Wd, bd, Ad, Bd, Fraction(s))
+    y = lo.lora_linear(d["x"], d["W"], d["b"], d["A"], d["B"], d["alpha"], d["rank"], d["strength"],
+                       d["request_scale"])
+    assert y.shape == (T, N)
+    scale = max(abs(float(v)) for row in exact_y for v in row)
+    for m in range(T):
+        for n in range(N):
+            assert abs(y[m, n] - float(exact_y[m][n])) <= 1e-14 * scale
+
+
+def test_combined_scale_is_alpha_over_rank_times_strength_times_request():
+    assert lo.combined_scale(16, 8, 1.0, 1.0) == 2.0
+    assert lo.combined_scale(16, 8, 0.5, 1.0) == 1.0
+    assert lo.combined_scale(64, 64, 1.0, 0.7) == 0.7
+    assert lo.combined_scale(32, 16, 1.0, 1.0) == 2.0  # alpha / rank, not alpha / sqrt(rank)
+
+
+@pytest.mark.parametrize("case", ["s0", "B0", "none", "neg0"])
+def test_inactive_adapter_reduces_to_library_linear(case):
+    d = lw.small_linear_inputs(9, 33, 17, 4, 5, bias=True)
+    A, B, strength = d["A"], d["B"], 1.0
+    if case == "s0":
+        strength = 0.0
+    elif case == "neg0":
+        strength = -0.0
+    elif case == "B0":
+        B = torch.zeros_like(B)
+    else:
+        A = B = None
+    y = lo.lora_linear(d["x"], d["W"], d["b"], A, B, d["alpha"], d["rank"], strength, 1.0)
+    ref = torch.nn.functional.linear(d["x"].double(), d["W"].double(), d["b"].double()).numpy()
+    assert np.array_equal(y, ref)
+    yc = ec.chain_linear(d["x"], d["W"], d["b"], A, B, d["alpha"], d["rank"], strength, 1.0)
+    yb = ec.chain_linear(d["x"], d["W"], d["b"], None, None, d["alpha"], d["rank"], 1.0, 1.0)
+    assert np.array_equal(yc, yb) or case == "B0"
+    if case == "B0":  # zero delta: base + 0 keeps base's value (no exact zeros in base here)
+        assert not np.any(yb == 0)
+        assert np.array_equal(yc, yb)
+
+
+def test_merged_equals_factored():
+    d = lw.small_linear_inputs(40, 72, 56, 8, 7, bias=True, alpha=16, strength=0.8, request_scale=0.7)
+    s = lo.combined_scale(d["alpha"], d["rank"], d["strength"], d["request_scale"])
+    y = lo.lora_linear(d["x"], d["W"], d["b"], d["A"], d["B"], d["alpha"], d["rank"], d["strength"],
+                       d["request_scale"])
+    Wm = lo.merged_weight(d["W"], d["A"], d["B"], s)
+    y_merged = lo.f64(d["x"]) @ Wm.T + lo.f64(d["b"])[None, :]
+    assert np.max(np.abs(y - y_merged)) <= 1e-12 * np.max(np.abs(y))
+    # and the merged weight itself is W + s*B@A elementwise, checked exactly on a few entries
+    Wd, Ad, Bd = lo.f64(d["W"]), lo.f64(d["A"]), lo.f64(d["B"])
+    for n, k in [(0, 0), (55, 71), (13, 40)]:
+        want = exact(Wd[n, k]) + Fraction(s) * dot_exact(Bd[n], Ad[:, k])
+        assert abs(Wm[n, k] - float(want)) <= 1e-15 * max(1.0, abs(float(want)))
+
+
+def test_pure_low_rank_when_base_is_zero():
+    d = lw.small_linear_inputs(3, 5, 4, 2, 9, bias=False, alpha=2.0, strength=1.5)
+    Wz = torch.zeros_like(d["W"])
+    y = lo.lora_linear(d["x"], Wz, None, d["A"], d["B"], d["alpha"], d["rank"], d["strength"], 1.0)
+    s = Fraction(lo.combined_scale(d["alpha"], d["rank"], d["strength"], 1.0))
+    ex = _frac_lora_linear(lo.f64(d["x"]), lo.f64(Wz), None, lo.f64(d["A"]), lo.f64(d["B"]), s)
+    for m in range(3):
+        for n in range(4):
+            assert abs(y[m, n] - float(ex[m][n])) <= 1e-15 * (abs(float(ex[m][n])) + 1e-300)
+
+
+# ---------------------------------------------------------------- stacked
+
+def _stacked_case(seed, bias=True, adt="bf16"):
+    rng = np.random.default_rng(seed)
+    T, K = 11, 24
+    n_cols, ranks, alphas, offs = (7, 5, 9), (3, 2, 4), (6.0, 2.0, 2.0), (0, 9, 14)
+    x = lw.to_dtype(rng.standard_normal((T, K)), "bf16")
+    W = lw.to_dtype(rng.standard_normal((25, K)) / 5, "bf16")  # 2 columns (7, 8) and 23, 24 are base-only
+    b = lw.to_dtype(rng.standard_normal(25) / 7, "bf16") if bias else None
+    groups = []
+    for n, r, a, o in zip(n_cols, ranks, alphas, offs):
+        groups.append(dict(A=lw.to_dtype(rng.standard_normal((r, K)) / 5, adt),
+                           B=lw.to_dtype(rng.standard_normal((n, r)) / 3, adt),
+                           rank=r, alpha=a, col_offset=o, n_cols=n))
+    return x, W, b, groups
+
+
+def test_stacked_equals_per_group_layers():
+    x, W, b, groups = _stacked_case(21)
+    y = lo.lora_linear_stacked(x, W, b, groups, 0.9, 1.1)
+    yc = ec.chain_stacked(x, W, b, groups, 0.9, 1.1)
+    covered = np.zeros(25, bool)
+    for g in groups:
+        o, n = g["col_offset"], g["n_cols"]
+        covered[o:o + n] = True
+        y1 = lo.lora_linear(x, W[o:o + n], b[o:o + n], g["A"], g["B"], g["alpha"], g["rank"], 0.9, 1.1)
+        assert np.array_equal(y[:, o:o + n], y1)
+        c1 = ec.chain_linear(x, W[o:o + n], b[o:o + n], g["A"], g["B"], g["alpha"], g["rank"], 0.9, 1.1)
+        assert np.array_equal(yc[:, o:o + n], c1)
+    base = torch.nn.functional.linear(x.double(), W.double(), b.double()).numpy()
+    assert np.array_equal(y[:, ~covered], base[:, ~covered])
+
+
+# ---------------------------------------------------------------- 4-bit codes
+
+def test_nf4_nibble_order_and_block_index_exhaustive():
+    N, K = 3, 256  # 4 blocks of 64 per row; every code in both nibble positions at block edges
+    codes = np.zeros((N, K // 2), np.uint8)
+    for n in range(N):
+        for j in range(K // 2):
+            lo_c = (j + n) % 16
+            hi_c = (3 * j + 5 * n + 7) % 16
+            codes[n, j] = lo_c | (hi_c << 4)
+    cb = torch.tensor([2.0 ** (c - 8) for c in range(16)], dtype=torch.float32)
+    absmax = torch.tensor([float(i + 1) for i in range(N * K // 64)], dtype=torch.float32)
+    W = lo.nf4_dequant(torch.from_numpy(codes), absmax, cb, K, 64)
+    We = ec.chain_nf4_weight(torch.from_numpy(codes), absmax, cb, K, 64)
+    seen = set()
+    for n in range(N):
+        for k in range(K):
+            byte = int(codes[n, k // 2])
+            code = (byte & 0xF) if k % 2 == 0 else (byte >> 4)
+            blk = (n * K + k) // 64
+            want = 2.0 ** (code - 8) * (blk + 1)
+            assert W[n, k] == want, (n, k)
+            seen.add((code, k % 2))
+            # (blk + 1) * 2^(code - 8) has at most 4 significant bits: exact in bf16
+            assert We[n, k] == want
+    assert len(seen) == 32
+
+
+def test_nf4_weight_rounds_product_to_bf16():
+    codes = torch.tensor([[0x10]], dtype=torch.uint8)  # element 0: code 0, element 1: code 1
+    cb = torch.tensor([1.0 + 2.0 ** -8] + [1.0 + 2.0 ** -7 + 2.0 ** -8] + [0.0] * 14, dtype=torch.float32)
+    absmax = torch.tensor([1.0], dtype=torch.float32)
+    We = ec.chain_nf4_weight(codes, absmax, cb, 2, 2)
+    assert We[0, 0] == 1.0                # tie -> even
+    assert We[0, 1] == 1.0 + 2.0 ** -6    # tie -> even (up)
+
+
+# ---------------------------------------------------------------- dense patch
+
+def test_dense_patch_chain_matches_exact_rounding_random():
+    rng = np.random.default_rng(31)
+    dst = lw.to_dtype(rng.standard_normal(300), "bf16")
+    diff = lw.to_dtype(rng.standard_normal(300) * 1e-3, "bf16")
+    special = torch.tensor([0.0, -0.0, 3.3895e38, -3.3895e38, 1e-40, -1e-40], dtype=torch.bfloat16)
+    dst = torch.cat([dst, special])
+    diff = torch.cat([diff, torch.tensor([-0.0, 0.0, 3.3895e38, 1.0, 1e-40, 1e-41], dtype=torch.bfloat16)])
+    for strength in (0.8, 1.0, -2.5):
+        got = ec.chain_dense_patch(dst, diff, strength, "add", "bf16")
+        s32 = exact(round_fraction(exact(strength), "f32"))
+        for i in range(len(dst)):
+            a, b = float(dst[i]), float(diff[i])
+            prod = round_fraction(exact(b) * s32, "f32")
+            if math.isinf(prod):
+                tot = prod
+            else:
+                tot = round_fraction(exact(a) + exact(prod), "f32") if not math.isinf(a) else a
+            want = tot if math.isinf(tot) else round_fraction(exact(tot), "bf16")
+            g = got[i]
+            if want == 0.0:
+                assert g == 0.0  # sign of exact zeros: IEEE sum rules, checked separately
+            else:
+                assert g == want, (i, a, b, strength, g, want)
+        rep = ec.chain_dense_patch(dst, diff, strength, "replace", "bf16")
+        for i in range(len(dst)):
+            p = round_fraction(exact(float(diff[i])) * s32, "f32")
+            want = p if math.isinf(p) else round_fraction(exact(p), "bf16")
+            assert rep[i] == want or (want == 0.0 and rep[i] == 0.0)
+
+
+def test_dense_patch_plain_definition():
+    dst = torch.tensor([1.0, -2.0, 0.5], dtype=torch.bfloat16)
+    src = torch.tensor([0.25, 0.5, -1.0], dtype=torch.bfloat16)
+    assert np.array_equal(lo.dense_patch(dst, src, 2.0, "add"), [1.5, -1.0, -1.5])
+    assert np.array_equal(lo.dense_patch(dst, src, 0.0, "add"), [1.0, -2.0, 0.5])
+    assert np.array_equal(lo.dense_patch(dst, src, 2.0, "replace"), [0.5, 1.0, -2.0])
+
+
+# ---------------------------------------------------------------- exactness on dyadic inputs
+
+def _representable(q: Fraction, fmt: str) -> bool:
+    return Fraction(round_fraction(q, fmt)) == q
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_dyadic_inputs_every_tier_is_exact(seed):
+    d = lw.dyadic_linear_inputs(6, 40, 9, 3, seed, bias=True)
+    xd, Wd, bd, Ad, Bd = (lo.f64(d[k]) for k in ("x", "W", "b", "A", "B"))
+    alpha, rank, strength, rs = 3.0, 3, 2.0, 0.5  # combined scale 1.0; chain multiplies by 2 then 0.5
+    ex = _frac_lora_linear(xd, Wd, bd, Ad, Bd, Fraction(1))
+    # every intermediate representable: t, d and y in bf16
+    for m in range(6):
+        for q in range(3):
+            assert _representable(dot_exact(xd[m], Ad[q]), "bf16")
+        for n in range(9):
+            assert _representable(ex[m][n], "bf16")
+    y = lo.lora_linear(d["x"], d["W"], d["b"], d["A"], d["B"], alpha, rank, strength, rs)
+    yc = ec.chain_linear(d["x"], d["W"], d["b"], d["A"], d["B"], alpha, rank, strength, rs)
+    for m in range(6):
+        for n in range(9):
+            assert y[m, n] == float(ex[m][n])
+            assert yc[m, n] == float(ex[m][n])
+
+
+# ---------------------------------------------------------------- the accuracy gate is discriminating
+
+def test_chain_error_is_within_gate_and_nonzero():
+    d = lw.small_linear_inputs(48, 256, 80, 16, 41, bias=True, alpha=16, strength=0.8, request_scale=0.7)
+    y64 = lo.lora_linear(d["x"], d["W"], d["b"], d["A"], d["B"], d["alpha"], d["rank"], d["strength"],
+                         d["request_scale"])
+    yc = ec.chain_linear(d["x"], d["W"], d["b"], d["A"], d["B"], d["alpha"], d["rank"], d["strength"],
+                         d["request_scale"])
+    e = lo.rel_rms(yc, y64)
+    assert 1e-4 < e < 4e-3
+    # a single bf16 rounding of the fp64 result is better than the chain
+    e1 = lo.rel_rms(ec.rn_bf16(ec.rn_f32(y64)), y64)
+    assert e1 < e
