@@ -1,0 +1,214 @@
+/*
+ * lora_mi355x.h -- fused LoRA linear for AMD Instinct MI355X (gfx950).
+ *
+ * The layer computes
+ *
+ *     y = x . W^T + b + s . (x . A^T) . B^T,   s = (alpha / rank) . strength . request_scale
+ *
+ * (SGLang PR #43501 "[diffusion] Add the dynamic LoRA delta inside the second
+ * GEMM", Motivation and Modifications; the delta is B @ A as on the FastVideo
+ * lora_patch page). The rank-r update is added into the base GEMM's fp32
+ * accumulator, the bias goes into the epilogue, and the [tokens, out] delta is
+ * never materialized.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are row-major. x [T, K] with row stride ldx (elements), W [N, K]
+ *   (row stride K), bias [N], A [r, K] (row stride K), B [N, r] (row stride r),
+ *   y [T, N] with row stride ldy >= N, so a column view of a wider output is
+ *   y + offset with the wider ldy.
+ * - Every tensor pointer is DEVICE memory owned by the caller, unless a
+ *   parameter says "host". The library never allocates device memory in a
+ *   call; it uses the caller's workspace, sized by lora_linear_workspace_size().
+ * - Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the
+ *   null stream); calls return without synchronizing.
+ * - Status: 0 (LORA_OK) or a positive lora_status. Every argument is validated
+ *   before anything is launched: on a nonzero status nothing has been written.
+ *   A failed launch returns LORA_ERR_HIP; faults inside a kernel surface at the
+ *   caller's next synchronization.
+ * - Scales are plain per-call arguments: nothing is cached between calls (the
+ *   request scale must be honoured per request -- SGLang PR #43501,
+ *   Modifications, "Why not alpha").
+ * - s == +-0, or A == B == NULL, leaves the adapter inactive: y is the base
+ *   output (zero strengths are inactive -- piper-offload README, strengths; no
+ *   adapter means plain X.W -- Unsloth fast-LoRA chapter, section 6).
+ *   A non-finite alpha, strength or request_scale is LORA_ERR_NONFINITE
+ *   (FastVideo DenseLoRAPatch rejects a non-finite strength).
+ * - Calls on distinct streams with distinct output and workspace buffers may
+ *   run concurrently; the library holds no mutable global state.
+ *
+ * Quality tiers (SGLang PR #43501, Modifications):
+ * - LORA_LOSSLESS (default): one fused pass. t~ = RN_adt(s . (x . A^T)) is
+ *   formed in fp32 and rounded once to the adapter dtype, t~ . B^T is added to
+ *   the base GEMM's fp32 accumulator, then y = RN_dt(acc + b).
+ * - LORA_EXACT: the separate-pass chain, bit for bit: every GEMM sums products
+ *   in fp64 with k ascending and rounds once to fp32; base = RN_dt(RN_f32(G +
+ *   b)); t = RN_adt(G(x, A)); d = RN_adt(G(t, B)); d is multiplied by
+ *   alpha/rank, strength and request_scale in turn (each rounded to fp32,
+ *   skipped when exactly 1), rounding to adt after each; y = RN_dt(RN_f32(base
+ *   + d)). Slow by design; kept for bitwise reproducibility.
+ *
+ * Alignment (LORA_ERR_ALIGN): in the lossless tier x, W, A, B, the 4-bit codes
+ * and the workspace must be 16-byte aligned, and K and ldx must be multiples of
+ * 16 bytes' worth of elements (8 for bf16, 4 for fp32); y, ldy and the bias
+ * only need natural element alignment. The exact tier and dense_patch_apply
+ * only need natural element alignment.
+ */
+#ifndef LORA_MI355X_H
+#define LORA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
+
+/* Quality tier; LORA_LOSSLESS is the default (SGLang PR #43501, Modifications). */
+typedef enum { LORA_LOSSLESS = 0, LORA_EXACT = 1 } lora_quality;
+
+/* Dense payloads (FastVideo lora_patch page):
+ * LORA_PATCH_ADD     -- .diff / .diff_b  (DenseLoRAPatch.apply_to)
+ * LORA_PATCH_REPLACE -- .set_weight      (DenseLoRAPatch.replacement_for) */
+typedef enum { LORA_PATCH_ADD = 0, LORA_PATCH_REPLACE = 1 } lora_patch_mode;
+
+typedef enum {
+  LORA_OK = 0,
+  LORA_ERR_NULL_PTR = 1,     /* a required pointer is NULL, or only one of A/B is given      */
+  LORA_ERR_SHAPE = 2,        /* negative/zero size, ld too small, shape mismatch, bad groups */
+  LORA_ERR_DTYPE = 3,        /* unsupported dtype or dtype combination                       */
+  LORA_ERR_NONFINITE = 4,    /* alpha, strength or request_scale is NaN or infinite          */
+  LORA_ERR_ALIGN = 5,        /* pointer or stride misaligned for the lossless kernels        */
+  LORA_ERR_OVERLAP = 6,      /* output overlaps an input or the workspace                    */
+  LORA_ERR_WORKSPACE = 7,    /* workspace NULL or smaller than lora_linear_workspace_size()  */
+  LORA_ERR_UNSUPPORTED = 8,  /* device is not gfx950, or a limit below is exceeded           */
+  LORA_ERR_HIP = 9           /* a HIP runtime call or kernel launch failed                   */
+} lora_status;
+
+/* Limits (LORA_ERR_UNSUPPORTED beyond them). */
+#define LORA_MAX_GROUPS 8
+#define LORA_MAX_RANK 1024
+
+/*
+ * One adapter of a stacked layer (q/k/v or gate/up), covering the output
+ * columns [col_offset, col_offset + n_cols). A [rank, K] and B [n_cols, rank]
+ * are device pointers in the adapter dtype; its combined scale is
+ * (alpha / rank) . strength . request_scale. Groups must not overlap and must
+ * lie inside [0, N_total). Columns outside every group get the base output.
+ */
+typedef struct lora_group {
+  const void* A;
+  const void* B;
+  int32_t rank;
+  int32_t reserved; /* set to 0 */
+  double alpha;
+  int64_t col_offset;
+  int64_t n_cols;
+} lora_group;
+
+/*
+ * lora_linear_fwd -- one LoRA linear layer.
+ *
+ *   x        [T, K] act_dtype, row stride ldx >= K
+ *   W        [N, K] act_dtype
+ *   bias     [N] act_dtype, or NULL
+ *   A, B     [rank, K], [N, rank] adapter_dtype, or both NULL (base only)
+ *   y        [T, N] act_dtype, row stride ldy >= N; must not overlap any input
+ *   act_dtype     LORA_BF16 (adapter LORA_BF16 or LORA_F32), or LORA_F32 (adapter LORA_F32)
+ *   quality       LORA_LOSSLESS or LORA_EXACT
+ *   workspace     device scratch of at least lora_linear_workspace_size(T, &rank, 1, ...)
+ *                 bytes (may be NULL when that size is 0); its contents are not
+ *                 preserved between calls
+ * T == 0 is a valid no-op.
+ */
+int lora_linear_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
+                    const void* W, int64_t N, const void* bias,
+                    const void* A, const void* B, int32_t rank, int32_t adapter_dtype,
+                    double alpha, double strength, double request_scale,
+                    void* y, int64_t ldy, int32_t act_dtype, int32_t quality,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lora_linear_stacked_fwd -- one base GEMM over W [N_total, K] with up to
+ * LORA_MAX_GROUPS adapters, each added to its own column range of y
+ * (SGLang PR #43501, Modifications: stacked q/k/v or gate/up adapters, one
+ * update per group on column views of the output).
+ *
+ *   groups    HOST array of n_groups lora_group (0 <= n_groups <= LORA_MAX_GROUPS);
+ *             the A/B pointers inside are device pointers
+ *   workspace at least lora_linear_workspace_size(T, ranks of the groups, n_groups, ...) bytes
+ * Other arguments as lora_linear_fwd.
+ */
+int lora_linear_stacked_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
+                            const void* W, int64_t N_total, const void* bias,
+                            const lora_group* groups, int32_t n_groups, int32_t adapter_dtype,
+                            double strength, double request_scale,
+                            void* y, int64_t ldy, int32_t act_dtype, int32_t quality,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lora_linear_nf4_fwd -- LoRA linear over a 4-bit codebook base weight,
+ * dequantized inside the GEMM (Unsloth fast-LoRA chapter, section 3,
+ * matmul_lora; 4-bit formats are blockwise -- piper-offload README
+ * quantized-format table; InvokeAI article, NF4 section).
+ *
+ *   codes     uint8 [N, K/2]: row n, byte j holds element (n, 2j) in bits 0-3 and
+ *             element (n, 2j+1) in bits 4-7
+ *   absmax    fp32 [N*K/blocksize]: one scale per block of `blocksize` consecutive
+ *             elements of the row-major [N, K] weight
+ *   codebook  fp32 [16] (device)
+ *   blocksize must be 64; K must be a multiple of 64
+ * The weight element is W[n,k] = RN_bf16(RN_f32(codebook[code] * absmax[(n*K+k)/64]))
+ * in both tiers. Activations, bias and y are bf16; the adapter is bf16 or fp32.
+ */
+int lora_linear_nf4_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
+                        const uint8_t* codes, const float* absmax, const float* codebook,
+                        int32_t blocksize, int64_t N, const void* bias,
+                        const void* A, const void* B, int32_t rank, int32_t adapter_dtype,
+                        double alpha, double strength, double request_scale,
+                        void* y, int64_t ldy, int32_t quality,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dense_patch_apply -- dense payloads of an adapter, applied in place
+ * (FastVideo lora_patch page, DenseLoRAPatch.apply_to / replacement_for):
+ *
+ *   LORA_PATCH_ADD:     dst = RN_dst( RN_f32( dst + RN_f32( src * RN_f32(strength) ) ) )
+ *   LORA_PATCH_REPLACE: dst = RN_dst( RN_f32( src * RN_f32(strength) ) )
+ *
+ * The sum is taken in fp32 whatever the operand dtypes (a bf16 sum would
+ * round away a delta three orders of magnitude below the weight); one
+ * rounding back to dst's dtype; no fused multiply-add.
+ *   dst_shape, src_shape  HOST arrays of dst_ndim / src_ndim sizes; the full shapes
+ *                         must be equal (LORA_ERR_SHAPE otherwise), both tensors contiguous
+ *   strength              finite (LORA_ERR_NONFINITE otherwise)
+ * src must not overlap dst.
+ */
+int dense_patch_apply(void* dst, int32_t dst_dtype, const int64_t* dst_shape, int32_t dst_ndim,
+                      const void* src, int32_t src_dtype, const int64_t* src_shape, int32_t src_ndim,
+                      double strength, int32_t mode, void* stream);
+
+/*
+ * Workspace bytes a call with T tokens needs for adapters of the given ranks
+ * (`ranks` is a HOST array of n_ranks entries: one for lora_linear_fwd and
+ * lora_linear_nf4_fwd, one per group for lora_linear_stacked_fwd). It holds the
+ * rank-wide intermediate [T, sum of ranks rounded up to multiples of 64] in the
+ * adapter dtype. Returns 0 when no rank is positive or T <= 0.
+ */
+size_t lora_linear_workspace_size(int64_t T, const int32_t* ranks, int32_t n_ranks, int32_t adapter_dtype,
+                                  int32_t quality);
+
+/* Static, human-readable text for a status code. */
+const char* lora_status_string(int status);
+
+/* LORA_OK when the current HIP device is a gfx950; LORA_ERR_UNSUPPORTED otherwise. */
+int lora_device_check(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_MI355X_H */

@@ -1,0 +1,284 @@
+// C-ABI of the fused LoRA linear library: argument validation, scale folding
+// and dispatch to the gfx950 kernels. Every check runs before any launch, so a
+// nonzero status means nothing was written.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cfloat>
+#include <cmath>
+#include <cstring>
+
+#include "lora_mi355x.h"
+#include "launch.hpp"
+
+namespace {
+
+using lora::Elt;
+using lora::GroupDev;
+using lora::LinearProblem;
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+  bool empty() const { return lo == hi; }
+};
+
+Span span2d(const void* p, int64_t rows, int64_t ld, int64_t cols, int esize) {
+  Span s;
+  if (p == nullptr || rows <= 0 || cols <= 0) return s;
+  s.lo = reinterpret_cast<uintptr_t>(p);
+  s.hi = s.lo + static_cast<uintptr_t>(((rows - 1) * ld + cols) * esize);
+  return s;
+}
+
+bool overlaps(const Span& a, const Span& b) {
+  return !a.empty() && !b.empty() && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void* p, uintptr_t a) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+bool dtype_ok(int d) { return d == LORA_F32 || d == LORA_BF16; }
+Elt to_elt(int d) { return d == LORA_BF16 ? Elt::BF16 : Elt::F32; }
+int esz(int d) { return d == LORA_BF16 ? 2 : 4; }
+
+bool finite_scale(double v) { return std::isfinite(v); }
+
+// The staging kernels address one tile of rows with 32-bit byte offsets.
+constexpr int64_t kMaxRowBytes = int64_t(1) << 22;
+
+// Adapter description shared by the three linear entry points.
+struct Adapter {
+  const void* A;
+  const void* B;
+  int32_t rank;
+  double alpha;
+  int64_t col_off, n_cols;
+};
+
+int fill_groups(LinearProblem& p, const Adapter* ads, int n, double strength, double request_scale) {
+  p.n_groups = 0;
+  int64_t tcol = 0;
+  for (int i = 0; i < n; ++i) {
+    const Adapter& a = ads[i];
+    if (a.A == nullptr && a.B == nullptr) continue;  // no adapter on these columns
+    const double s = (a.alpha / static_cast<double>(a.rank)) * strength * request_scale;
+    if (s == 0.0) continue;  // a zero combined scale leaves the adapter inactive
+    if (std::fabs(s) > FLT_MAX) return LORA_ERR_NONFINITE;
+    GroupDev& g = p.g[p.n_groups++];
+    g.A = a.A;
+    g.B = a.B;
+    g.col_off = a.col_off;
+    g.n_cols = a.n_cols;
+    g.rank = a.rank;
+    g.r_pad = static_cast<int32_t>(lora::rank_pad(a.rank));
+    g.t_col = static_cast<int32_t>(tcol);
+    g.scale = static_cast<float>(s);
+    g.f[0] = static_cast<float>(a.alpha / static_cast<double>(a.rank));
+    g.f[1] = static_cast<float>(strength);
+    g.f[2] = static_cast<float>(request_scale);
+    tcol += g.r_pad;
+  }
+  p.ldt = tcol;
+  return LORA_OK;
+}
+
+size_t workspace_bytes_for(const LinearProblem& p) {
+  if (p.n_groups == 0 || p.T == 0) return 0;
+  return static_cast<size_t>(p.T) * static_cast<size_t>(p.ldt) * static_cast<size_t>(lora::esize(p.adapter));
+}
+
+// Shared validation + dispatch for lora_linear_fwd / _stacked_fwd / _nf4_fwd.
+int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, const uint8_t* codes,
+               const float* absmax, const float* codebook, bool nf4, int64_t N, const void* bias,
+               const Adapter* ads, int n_ads, int adapter_dtype, double strength, double request_scale,
+               void* y, int64_t ldy, int act_dtype, int quality, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  if (!dtype_ok(act_dtype) || !dtype_ok(adapter_dtype)) return LORA_ERR_DTYPE;
+  if (act_dtype == LORA_F32 && adapter_dtype != LORA_F32) return LORA_ERR_DTYPE;
+  if (quality != LORA_LOSSLESS && quality != LORA_EXACT) return LORA_ERR_UNSUPPORTED;
+  if (T < 0 || K < 1 || N < 1 || ldx < K || ldy < N) return LORA_ERR_SHAPE;
+  if (!finite_scale(strength) || !finite_scale(request_scale)) return LORA_ERR_NONFINITE;
+  if (nf4) {
+    if (codes == nullptr || absmax == nullptr || codebook == nullptr) return LORA_ERR_NULL_PTR;
+    if (K % 64 != 0) return LORA_ERR_SHAPE;
+  } else if (W == nullptr) {
+    return LORA_ERR_NULL_PTR;
+  }
+  if (T > 0 && (x == nullptr || y == nullptr)) return LORA_ERR_NULL_PTR;
+  for (int i = 0; i < n_ads; ++i) {
+    const Adapter& a = ads[i];
+    if ((a.A == nullptr) != (a.B == nullptr)) return LORA_ERR_NULL_PTR;
+    if (!finite_scale(a.alpha)) return LORA_ERR_NONFINITE;
+    if (a.A == nullptr) continue;
+    if (a.rank < 1) return LORA_ERR_SHAPE;
+    if (a.rank > LORA_MAX_RANK) return LORA_ERR_UNSUPPORTED;
+    if (a.n_cols < 1 || a.col_off < 0 || a.col_off + a.n_cols > N) return LORA_ERR_SHAPE;
+  }
+  // stacked groups must be disjoint
+  for (int i = 0; i < n_ads; ++i)
+    for (int j = i + 1; j < n_ads; ++j) {
+      const Adapter &a = ads[i], &b = ads[j];
+      if (a.A == nullptr || b.A == nullptr) continue;
+      if (a.col_off < b.col_off + b.n_cols && b.col_off < a.col_off + a.n_cols) return LORA_ERR_SHAPE;
+    }
+
+  const int ea = esz(act_dtype), el = esz(adapter_dtype);
+  if (ldx * ea > kMaxRowBytes || ldy * ea > kMaxRowBytes || K * 4 > kMaxRowBytes) return LORA_ERR_UNSUPPORTED;
+
+  // alignment
+  if (quality == LORA_LOSSLESS) {
+    const int vec = 16 / ea;
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(y, ea) || !aligned(codes, 16)) return LORA_ERR_ALIGN;
+    if (K % vec != 0 || ldx % vec != 0) return LORA_ERR_ALIGN;
+    for (int i = 0; i < n_ads; ++i)
+      if (!aligned(ads[i].A, 16) || !aligned(ads[i].B, 16)) return LORA_ERR_ALIGN;
+    if (!aligned(workspace, 16)) return LORA_ERR_ALIGN;
+  } else {
+    if (!aligned(x, ea) || !aligned(W, ea) || !aligned(y, ea)) return LORA_ERR_ALIGN;
+    for (int i = 0; i < n_ads; ++i)
+      if (!aligned(ads[i].A, el) || !aligned(ads[i].B, el)) return LORA_ERR_ALIGN;
+    if (!aligned(workspace, 4)) return LORA_ERR_ALIGN;
+  }
+  if (!aligned(bias, ea) || !aligned(absmax, 4) || !aligned(codebook, 4)) return LORA_ERR_ALIGN;
+
+  LinearProblem p;
+  std::memset(&p, 0, sizeof(p));
+  p.x = x; p.ldx = ldx; p.W = W; p.codes = codes; p.absmax = absmax; p.codebook = codebook;
+  p.bias = bias; p.y = y; p.ldy = ldy; p.T = T; p.N = N; p.K = K;
+  p.act = to_elt(act_dtype); p.adapter = to_elt(adapter_dtype); p.nf4 = nf4;
+  const int st = fill_groups(p, ads, n_ads, strength, request_scale);
+  if (st != LORA_OK) return st;
+
+  const size_t need = workspace_bytes_for(p);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LORA_ERR_WORKSPACE;
+  p.work = workspace;
+
+  // the output must not overlap any input or the workspace
+  if (T > 0) {
+    const Span sy = span2d(y, T, ldy, N, ea);
+    const Span sw = nf4 ? span2d(codes, N, K / 2, K / 2, 1) : span2d(W, N, K, K, ea);
+    Span inputs[8] = {span2d(x, T, ldx, K, ea), sw, span2d(bias, 1, N, N, ea),
+                      nf4 ? span2d(absmax, 1, N * K / 64, N * K / 64, 4) : Span{},
+                      span2d(codebook, 1, 16, 16, 4),
+                      need ? Span{reinterpret_cast<uintptr_t>(workspace),
+                                  reinterpret_cast<uintptr_t>(workspace) + need} : Span{},
+                      Span{}, Span{}};
+    for (const Span& s : inputs)
+      if (overlaps(sy, s)) return LORA_ERR_OVERLAP;
+    const Span sws = inputs[5];
+    for (int i = 0; i < n_ads; ++i) {
+      const Adapter& a = ads[i];
+      if (a.A == nullptr) continue;
+      const Span sa = span2d(a.A, a.rank, K, K, el), sb = span2d(a.B, a.n_cols, a.rank, a.rank, el);
+      if (overlaps(sy, sa) || overlaps(sy, sb) || overlaps(sws, sa) || overlaps(sws, sb)) return LORA_ERR_OVERLAP;
+    }
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(sws, inputs[i])) return LORA_ERR_OVERLAP;
+  }
+  if (T == 0) return LORA_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = (quality == LORA_EXACT) ? lora::launch_exact(p, s) : lora::launch_lossless(p, s);
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_linear_fwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, int64_t N, const void* bias,
+                    const void* A, const void* B, int32_t rank, int32_t adapter_dtype, double alpha,
+                    double strength, double request_scale, void* y, int64_t ldy, int32_t act_dtype,
+                    int32_t quality, void* workspace, size_t workspace_bytes, void* stream) {
+  const Adapter a{A, B, rank, alpha, 0, N};
+  return run_linear(x, T, K, ldx, W, nullptr, nullptr, nullptr, false, N, bias, &a, 1, adapter_dtype, strength,
+                    request_scale, y, ldy, act_dtype, quality, workspace, workspace_bytes, stream);
+}
+
+int lora_linear_stacked_fwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, int64_t N_total,
+                            const void* bias, const lora_group* groups, int32_t n_groups, int32_t adapter_dtype,
+                            double strength, double request_scale, void* y, int64_t ldy, int32_t act_dtype,
+                            int32_t quality, void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_groups < 0) return LORA_ERR_SHAPE;
+  if (n_groups > LORA_MAX_GROUPS) return LORA_ERR_UNSUPPORTED;
+  if (n_groups > 0 && groups == nullptr) return LORA_ERR_NULL_PTR;
+  Adapter ads[LORA_MAX_GROUPS];
+  for (int i = 0; i < n_groups; ++i)
+    ads[i] = Adapter{groups[i].A, groups[i].B, groups[i].rank, groups[i].alpha, groups[i].col_offset,
+                     groups[i].n_cols};
+  return run_linear(x, T, K, ldx, W, nullptr, nullptr, nullptr, false, N_total, bias, ads, n_groups,
+                    adapter_dtype, strength, request_scale, y, ldy, act_dtype, quality, workspace,
+                    workspace_bytes, stream);
+}
+
+int lora_linear_nf4_fwd(const void* x, int64_t T, int64_t K, int64_t ldx, const uint8_t* codes,
+                        const float* absmax, const float* codebook, int32_t blocksize, int64_t N, const void* bias,
+                        const void* A, const void* B, int32_t rank, int32_t adapter_dtype, double alpha,
+                        double strength, double request_scale, void* y, int64_t ldy, int32_t quality,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (blocksize != 64) return LORA_ERR_UNSUPPORTED;
+  const Adapter a{A, B, rank, alpha, 0, N};
+  return run_linear(x, T, K, ldx, nullptr, codes, absmax, codebook, true, N, bias, &a, 1, adapter_dtype,
+                    strength, request_scale, y, ldy, LORA_BF16, quality, workspace, workspace_bytes, stream);
+}
+
+int dense_patch_apply(void* dst, int32_t dst_dtype, const int64_t* dst_shape, int32_t dst_ndim, const void* src,
+                      int32_t src_dtype, const int64_t* src_shape, int32_t src_ndim, double strength,
+                      int32_t mode, void* stream) {
+  if (!dtype_ok(dst_dtype) || !dtype_ok(src_dtype)) return LORA_ERR_DTYPE;
+  if (mode != LORA_PATCH_ADD && mode != LORA_PATCH_REPLACE) return LORA_ERR_UNSUPPORTED;
+  if (dst_ndim < 0 || src_ndim < 0) return LORA_ERR_SHAPE;
+  if ((dst_ndim > 0 && dst_shape == nullptr) || (src_ndim > 0 && src_shape == nullptr)) return LORA_ERR_NULL_PTR;
+  if (dst_ndim != src_ndim) return LORA_ERR_SHAPE;
+  int64_t n = 1;
+  for (int i = 0; i < dst_ndim; ++i) {
+    if (dst_shape[i] < 0 || dst_shape[i] != src_shape[i]) return LORA_ERR_SHAPE;
+    n *= dst_shape[i];
+  }
+  if (!std::isfinite(strength)) return LORA_ERR_NONFINITE;
+  if (std::fabs(strength) > FLT_MAX) return LORA_ERR_NONFINITE;
+  if (n > 0 && (dst == nullptr || src == nullptr)) return LORA_ERR_NULL_PTR;
+  if (!aligned(dst, esz(dst_dtype)) || !aligned(src, esz(src_dtype))) return LORA_ERR_ALIGN;
+  if (n > 0 && overlaps(span2d(dst, 1, n, n, esz(dst_dtype)), span2d(src, 1, n, n, esz(src_dtype))))
+    return LORA_ERR_OVERLAP;
+  if (n == 0) return LORA_OK;
+  const hipError_t e = lora::launch_dense_patch(dst, to_elt(dst_dtype), src, to_elt(src_dtype), n,
+                                                static_cast<float>(strength), mode,
+                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+size_t lora_linear_workspace_size(int64_t T, const int32_t* ranks, int32_t n_ranks, int32_t adapter_dtype,
+                                  int32_t quality) {
+  (void)quality;
+  if (T <= 0 || ranks == nullptr || n_ranks <= 0 || !dtype_ok(adapter_dtype)) return 0;
+  int64_t cols = 0;
+  for (int i = 0; i < n_ranks; ++i)
+    if (ranks[i] > 0) cols += lora::rank_pad(ranks[i]);
+  return static_cast<size_t>(T) * static_cast<size_t>(cols) * static_cast<size_t>(esz(adapter_dtype));
+}
+
+const char* lora_status_string(int status) {
+  switch (status) {
+    case LORA_OK: return "ok";
+    case LORA_ERR_NULL_PTR: return "required pointer is NULL (or only one of A/B given)";
+    case LORA_ERR_SHAPE: return "invalid shape, leading dimension or group layout";
+    case LORA_ERR_DTYPE: return "unsupported dtype or dtype combination";
+    case LORA_ERR_NONFINITE: return "alpha, strength or request_scale is not finite";
+    case LORA_ERR_ALIGN: return "pointer or stride misaligned";
+    case LORA_ERR_OVERLAP: return "output overlaps an input or the workspace";
+    case LORA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LORA_ERR_UNSUPPORTED: return "unsupported device, option or size";
+    case LORA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int lora_device_check(void) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LORA_ERR_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LORA_ERR_HIP;
+  return std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? LORA_OK : LORA_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

@@ -1,0 +1,537 @@
+// Lossless tier of the fused LoRA linear on gfx950 (CDNA4).
+//
+// SGLang PR #43501 ("Add the dynamic LoRA delta inside the second GEMM",
+// Modifications): the combined scale (alpha/rank . strength . request scale)
+// multiplies the rank-wide intermediate x.A^T, and the second LoRA product is
+// accumulated straight onto the base output, so the [tokens, out] delta never
+// exists. Here the accumulation happens inside the base GEMM itself:
+//
+//   lora_down_kernel   t~[T, r] = RN_adt( s . x.A^T )      (fp32 accumulate, one rounding)
+//   fused_gemm_kernel  acc = x.W^T  (K loop over `in`)
+//                      acc += t~.B^T (K-extension over the rank, same accumulator)
+//                      y = RN_dt(acc + b)                    (bias in the epilogue)
+//
+// Both kernels are NT GEMMs with K-contiguous operands, which is the native
+// operand layout of the MFMA units: lane l of v_mfma_f32_32x32x16_bf16 takes 8
+// consecutive k of one row of each operand. The MFMA "A" operand carries
+// output columns (rows of W / B / A), the "B" operand carries tokens (rows of
+// x / t~), so each lane ends with 4 consecutive output columns of one token
+// and stores them as one 8-byte (bf16) or 16-byte (fp32) write.
+//
+// Staging: every operand row is staged 128 bytes per K step (64 bf16 or 32
+// fp32) into LDS, with the 16-byte chunk index XOR-swizzled by row so the
+// 16-byte LDS reads of a wave spread over all banks. x and W tiles are copied
+// global->LDS directly by buffer_load ... lds (no VGPR round trip), double
+// buffered; out-of-range rows and K tails read as zero through the buffer
+// resource's range check.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace lora {
+namespace {
+
+constexpr int kRowBytes = 128;  // staged bytes per operand row per K step
+constexpr int kChunks = 8;      // 16-byte chunks per staged row
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kChunks + (chunk ^ ((row >> 1) & 7));
+}
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int NI = WN / 32, NJ = WM / 32;
+  static constexpr int X_BYTES = BM * kRowBytes, W_BYTES = BN * kRowBytes;
+  static constexpr int STAGE_BYTES = X_BYTES + W_BYTES;
+  static constexpr int GROUP_M = 4;  // m-tiles enumerated together (L2 reuse of W)
+};
+
+// Physical workgroup ids are dealt round-robin to the 8 XCDs. Remap so each XCD
+// receives a contiguous run of logical tiles (tiles sharing x rows / W rows then
+// share that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int pid, int G) {
+  const int q = G / 8, rem = G % 8;
+  const int xcd = pid % 8, idx = pid / 8;
+  return (xcd < rem) ? xcd * (q + 1) + idx : rem * (q + 1) + (xcd - rem) * q + idx;
+}
+
+// Copy ROWS x 128 bytes (bytes [kb0, kb0 + 128) of each row) into a swizzled LDS
+// tile with buffer_load_dwordx4 ... lds. Rows >= rows_valid and bytes >= kb_valid
+// are out of the resource's range and arrive as zeros.
+template <int ROWS, int THREADS>
+__device__ __forceinline__ void dma_stage(char* lds_tile, __amdgpu_buffer_rsrc_t rsrc,
+                                          uint32_t ld_bytes, int rows_valid, int kb0, int kb_valid) {
+  constexpr int SLOTS = ROWS * kChunks;
+  static_assert(SLOTS % THREADS == 0, "tile not divisible among threads");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int WAVES = THREADS / 64;
+#pragma unroll
+  for (int it = 0; it < SLOTS / THREADS; ++it) {
+    const int slot0 = (it * WAVES + wave) * 64;  // wave-uniform LDS destination
+    const int s = slot0 + lane;
+    const int row = s >> 3;
+    const int c = (s & 7) ^ ((row >> 1) & 7);
+    const int kb = kb0 + c * 16;
+    const uint32_t voff = (row < rows_valid && kb < kb_valid)
+                              ? static_cast<uint32_t>(row) * ld_bytes + static_cast<uint32_t>(kb)
+                              : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds_tile + slot0 * 16), 16, voff, 0, 0, 0);
+  }
+}
+
+// One 128-byte K step of MFMA work from two swizzled LDS tiles.
+template <class C, typename T>
+struct Mma;
+
+template <class C>
+struct Mma<C, bf16_bits> {
+  __device__ __forceinline__ static void stage(f32x16 (&acc)[C::NI][C::NJ], const char* lw, const char* lx,
+                                               int wn0, int wm0, int lane) {
+    const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 a[C::NI], b[C::NJ];
+#pragma unroll
+      for (int i = 0; i < C::NI; ++i) a[i] = *(const bf16x8*)(lw + swz(wn0 + i * 32 + r, kk * 2 + h) * 16);
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) b[j] = *(const bf16x8*)(lx + swz(wm0 + j * 32 + r, kk * 2 + h) * 16);
+#pragma unroll
+      for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+};
+
+template <class C>
+struct Mma<C, float> {
+  // Lane half h takes logical k = h*16 + s (s = 0..15) of the 32 staged k, the
+  // same for both operands, so the sum over k is the full dot product.
+  __device__ __forceinline__ static void stage(f32x16 (&acc)[C::NI][C::NJ], const char* lw, const char* lx,
+                                               int wn0, int wm0, int lane) {
+    const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      f32x4 a[C::NI], b[C::NJ];
+#pragma unroll
+      for (int i = 0; i < C::NI; ++i) a[i] = *(const f32x4*)(lw + swz(wn0 + i * 32 + r, h * 4 + c4) * 16);
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) b[j] = *(const f32x4*)(lx + swz(wm0 + j * 32 + r, h * 4 + c4) * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+          for (int j = 0; j < C::NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+    }
+  }
+};
+
+// Stage BN rows of the LoRA B matrix (group g) as the W-side operand of one
+// K-extension step: row n of the tile is output column n0 + n; it holds
+// B_g[n0 + n - col_off][q0 .. q0 + 128/e) for columns inside the group and
+// q < rank, zero elsewhere. Goes through VGPRs (B's row stride need not be a
+// multiple of 16 bytes).
+template <int ROWS, int THREADS, typename TL>
+__device__ __forceinline__ void stage_lora_b(char* lds_tile, const GroupDev& g, int64_t n0, int rows_valid,
+                                             int q0) {
+  constexpr int EPC = 16 / sizeof(TL);  // elements per 16-byte chunk
+  constexpr int SLOTS = ROWS * kChunks;
+  const TL* B = static_cast<const TL*>(g.B);
+  const bool vec_ok = ((g.rank * static_cast<int>(sizeof(TL))) % 16) == 0;
+#pragma unroll
+  for (int it = 0; it < SLOTS / THREADS; ++it) {
+    const int s = it * THREADS + threadIdx.x;
+    const int row = s >> 3, c = s & 7;
+    const int64_t n = n0 + row - g.col_off;  // row of B_g
+    const int q = q0 + c * EPC;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < rows_valid && n >= 0 && n < g.n_cols && q < g.rank) {
+      const TL* src = B + n * g.rank + q;
+      if (vec_ok && q + EPC <= g.rank) {
+        v = *reinterpret_cast<const u32x4*>(src);
+      } else {
+        TL tmp[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) tmp[e] = (q + e < g.rank) ? src[e] : TL(0);
+        v = *reinterpret_cast<const u32x4*>(tmp);
+      }
+    }
+    *reinterpret_cast<u32x4*>(lds_tile + swz(row, c) * 16) = v;
+  }
+}
+
+// 4-bit weight: dequantize one 64-element K step of 256 rows into the swizzled
+// bf16 W tile. Thread t owns row t/2 and elements [32*(t&1), 32*(t&1)+32) of the
+// step, i.e. 16 code bytes and the row's absmax for this block.
+struct Nf4Regs {
+  u32x4 codes;
+  float absmax;
+};
+
+__device__ __forceinline__ Nf4Regs nf4_load(const LinearProblem& p, int64_t n0, int rows_valid, int kt) {
+  Nf4Regs r;
+  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+  if (row < rows_valid) {
+    const int64_t n = n0 + row;
+    r.codes = *reinterpret_cast<const u32x4*>(p.codes + n * (p.K / 2) + kt * 32 + half * 16);
+    r.absmax = p.absmax[(n * p.K) / 64 + kt];
+  } else {
+    r.codes = u32x4{0u, 0u, 0u, 0u};
+    r.absmax = 0.f;
+  }
+  return r;
+}
+
+__device__ __forceinline__ void nf4_dequant_store(char* lds_w, const Nf4Regs& r, const float* cb_lds) {
+  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {  // 4 chunks of 8 elements; 4 code bytes per chunk
+    const uint32_t word = r.codes[c];
+    uint32_t packed[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t byte = (word >> (8 * e)) & 0xffu;
+      // element 2j in the low nibble, 2j+1 in the high nibble; the product is
+      // RN_f32 (plain fp32 multiply), then RN_bf16.
+      const float lo = cb_lds[byte & 0xfu] * r.absmax;
+      const float hi = cb_lds[byte >> 4] * r.absmax;
+      packed[e] = pack_bf16x2(lo, hi);
+    }
+    *reinterpret_cast<u32x4*>(lds_w + swz(row, half * 4 + c) * 16) =
+        u32x4{packed[0], packed[1], packed[2], packed[3]};
+  }
+}
+
+template <class C, typename TA>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::NI][C::NJ], const LinearProblem& p, int64_t m0,
+                                         int64_t n0, int wm0, int wn0, int lane) {
+  const int r = lane & 31, h = lane >> 5;
+  const TA* bias = static_cast<const TA*>(p.bias);
+  TA* y = static_cast<TA*>(p.y);
+  // 4 consecutive outputs go out as one 8-byte (bf16) / 16-byte (fp32) store when
+  // every row start keeps that alignment; otherwise element by element.
+  const bool vec_store = (p.ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(p.y) % (4 * sizeof(TA)) == 0);
+#pragma unroll
+  for (int i = 0; i < C::NI; ++i) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int64_t n = n0 + wn0 + i * 32 + gq * 8 + h * 4;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bias != nullptr) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (n + e < p.N) {
+            if constexpr (sizeof(TA) == 2) bv[e] = bf16_to_f32(bias[n + e]);
+            else bv[e] = bias[n + e];
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < C::NJ; ++j) {
+        const int64_t m = m0 + wm0 + j * 32 + r;
+        if (m >= p.T) continue;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[i][j][gq * 4 + e] + bv[e];
+        TA* dst = y + m * p.ldy + n;
+        if (vec_store && n + 3 < p.N) {
+          if constexpr (sizeof(TA) == 2) {
+            uint2 w;
+            w.x = pack_bf16x2(v[0], v[1]);
+            w.y = pack_bf16x2(v[2], v[3]);
+            *reinterpret_cast<uint2*>(dst) = w;
+          } else {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (n + e < p.N) {
+              if constexpr (sizeof(TA) == 2) dst[e] = f32_to_bf16_rne(v[e]);
+              else dst[e] = v[e];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <class C, typename TA, typename TL, bool NF4>
+__global__ __launch_bounds__(C::THREADS) void fused_gemm_kernel(LinearProblem p, int mt, int nt) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE_BYTES];
+  __shared__ float cb_lds[16];
+
+  const int G = mt * nt;
+  const int L = xcd_remap(blockIdx.x, G);
+  const int gsize = C::GROUP_M * nt;
+  const int grp = L / gsize;
+  const int first_m = grp * C::GROUP_M;
+  const int gm = min(C::GROUP_M, mt - first_m);
+  const int within = L - grp * gsize;
+  const int m_idx = first_m + within % gm;
+  const int n_idx = within / gm;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm0 = (wave % C::WAVES_M) * C::WM;
+  const int wn0 = (wave / C::WAVES_M) * C::WN;
+  const int64_t m0 = static_cast<int64_t>(m_idx) * C::BM;
+  const int64_t n0 = static_cast<int64_t>(n_idx) * C::BN;
+  const int rows_m = static_cast<int>(min<int64_t>(C::BM, p.T - m0));
+  const int rows_n = static_cast<int>(min<int64_t>(C::BN, p.N - n0));
+
+  f32x16 acc[C::NI][C::NJ];
+#pragma unroll
+  for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // stage buffer b: x tile at smem + b * STAGE_BYTES, W tile right after it
+  auto bufx = [&](int b) { return smem + b * C::STAGE_BYTES; };
+  auto bufw = [&](int b) { return smem + b * C::STAGE_BYTES + C::X_BYTES; };
+
+  // ---------------- base GEMM: K loop over `in`
+  constexpr int EA = sizeof(TA);
+  const int kb_total = static_cast<int>(p.K * EA);
+  const int nk = (kb_total + kRowBytes - 1) / kRowBytes;
+  const uint32_t ldx_b = static_cast<uint32_t>(p.ldx * EA);
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(static_cast<const char*>(p.x) + m0 * p.ldx * EA, static_cast<uint32_t>(rows_m) * ldx_b);
+
+  if constexpr (!NF4) {
+    const uint32_t ldw_b = static_cast<uint32_t>(p.K * EA);
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc(static_cast<const char*>(p.W) + n0 * p.K * EA, static_cast<uint32_t>(rows_n) * ldw_b);
+    dma_stage<C::BM, C::THREADS>(bufx(0), xr, ldx_b, rows_m, 0, kb_total);
+    dma_stage<C::BN, C::THREADS>(bufw(0), wr, ldw_b, rows_n, 0, kb_total);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmem();
+      __syncthreads();
+      if (kt + 1 < nk) {
+        dma_stage<C::BM, C::THREADS>(bufx((kt + 1) & 1), xr, ldx_b, rows_m, (kt + 1) * kRowBytes, kb_total);
+        dma_stage<C::BN, C::THREADS>(bufw((kt + 1) & 1), wr, ldw_b, rows_n, (kt + 1) * kRowBytes, kb_total);
+      }
+      Mma<C, TA>::stage(acc, bufw(kt & 1), bufx(kt & 1), wn0, wm0, lane);
+    }
+  } else {
+    static_assert(C::BN * 2 == C::THREADS, "4-bit staging maps two threads per weight row");
+    if (tid < 16) cb_lds[tid] = p.codebook[tid];
+    Nf4Regs nr = nf4_load(p, n0, rows_n, 0);
+    dma_stage<C::BM, C::THREADS>(bufx(0), xr, ldx_b, rows_m, 0, kb_total);
+    __syncthreads();
+    nf4_dequant_store(bufw(0), nr, cb_lds);
+    for (int kt = 0; kt < nk; ++kt) {
+      wait_vmem();
+      __syncthreads();
+      if (kt + 1 < nk) {
+        dma_stage<C::BM, C::THREADS>(bufx((kt + 1) & 1), xr, ldx_b, rows_m, (kt + 1) * kRowBytes, kb_total);
+        nr = nf4_load(p, n0, rows_n, kt + 1);
+      }
+      Mma<C, TA>::stage(acc, bufw(kt & 1), bufx(kt & 1), wn0, wm0, lane);
+      if (kt + 1 < nk) nf4_dequant_store(bufw((kt + 1) & 1), nr, cb_lds);
+    }
+  }
+
+  // ---------------- K-extension: acc += t~ . B^T for every group touching this tile
+  constexpr int EL = sizeof(TL);
+  const uint32_t ldt_b = static_cast<uint32_t>(p.ldt * EL);
+  for (int gi = 0; gi < p.n_groups; ++gi) {
+    const GroupDev& g = p.g[gi];
+    if (g.col_off >= n0 + rows_n || g.col_off + g.n_cols <= n0) continue;
+    const __amdgpu_buffer_rsrc_t tr = make_rsrc(
+        static_cast<const char*>(p.work) + (m0 * p.ldt + g.t_col) * EL, static_cast<uint32_t>(rows_m) * ldt_b);
+    const int nst = g.r_pad * EL / kRowBytes;
+    for (int st = 0; st < nst; ++st) {
+      __syncthreads();  // every wave is done reading the previous stage
+      dma_stage<C::BM, C::THREADS>(bufx(0), tr, ldt_b, rows_m, st * kRowBytes, g.r_pad * EL);
+      stage_lora_b<C::BN, C::THREADS, TL>(bufw(0), g, n0, rows_n, st * (kRowBytes / EL));
+      wait_vmem();
+      __syncthreads();
+      Mma<C, TL>::stage(acc, bufw(0), bufx(0), wn0, wm0, lane);
+    }
+  }
+
+  // ---------------- epilogue: + bias (fp32), one rounding, store
+  epilogue<C, TA>(acc, p, m0, n0, wm0, wn0, lane);
+}
+
+// ---------------------------------------------------------------------------
+// t~[m, t_col + q] = RN_adt( s . sum_k x[m,k] A_g[q,k] ), zero for rank <= q < r_pad.
+// Grid: (ceil(T / 256), n_groups, ceil(max r_pad / 128)). 4 waves; wave w owns
+// tokens [64w, 64w + 64) and all (up to 128) rank columns of the block.
+// TX: x element type; CT: compute/adapter type (bf16 MFMA, or fp32 MFMA with x
+// widened exactly to fp32).
+constexpr int kDownBM = 256;
+constexpr int kDownBQ = 128;
+using DownCfg = Cfg<kDownBM, kDownBQ, 64, 128>;  // WAVES_M = 4, WAVES_N = 1
+
+template <typename TX, typename CT>
+__device__ __forceinline__ void down_load_x(u32x4 (&rx)[8], const TX* x, int64_t ldx, int64_t m0, int rows_m,
+                                            int64_t K, int k0) {
+  constexpr int EPC = 16 / sizeof(CT);
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int s = it * 256 + threadIdx.x;
+    const int row = s >> 3, c = s & 7;
+    const int64_t k = k0 + c * EPC;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < rows_m && k < K) {
+      const TX* src = x + (m0 + row) * ldx + k;
+      if constexpr (sizeof(TX) == sizeof(CT)) {
+        v = *reinterpret_cast<const u32x4*>(src);  // K is a multiple of EPC (alignment rule)
+      } else {
+        // bf16 -> fp32 widening of 4 elements (8 bytes)
+        const uint2 w = *reinterpret_cast<const uint2*>(src);
+        v = u32x4{w.x << 16, w.x & 0xffff0000u, w.y << 16, w.y & 0xffff0000u};
+      }
+    }
+    rx[it] = v;
+  }
+}
+
+template <typename CT>
+__device__ __forceinline__ void down_load_a(u32x4 (&ra)[4], const GroupDev& g, int q_base, int64_t K, int k0) {
+  constexpr int EPC = 16 / sizeof(CT);
+  const CT* A = static_cast<const CT*>(g.A);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int s = it * 256 + threadIdx.x;
+    const int row = s >> 3, c = s & 7;
+    const int q = q_base + row;
+    const int64_t k = k0 + c * EPC;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (q < g.rank && k < K) v = *reinterpret_cast<const u32x4*>(A + q * K + k);
+    ra[it] = v;
+  }
+}
+
+template <typename TX, typename CT>
+__global__ __launch_bounds__(256) void lora_down_kernel(LinearProblem p) {
+  __shared__ __attribute__((aligned(1024))) char lx[kDownBM * kRowBytes];
+  __shared__ __attribute__((aligned(1024))) char la[kDownBQ * kRowBytes];
+  using C = DownCfg;
+  const GroupDev& g = p.g[blockIdx.y];
+  const int q_base = blockIdx.z * kDownBQ;
+  if (q_base >= g.r_pad) return;
+  const int nq = min(kDownBQ, g.r_pad - q_base);
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kDownBM;
+  const int rows_m = static_cast<int>(min<int64_t>(kDownBM, p.T - m0));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm0 = wave * 64;
+  const TX* x = static_cast<const TX*>(p.x);
+
+  f32x16 acc[C::NI][C::NJ];
+#pragma unroll
+  for (int i = 0; i < C::NI; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  constexpr int EPS = kRowBytes / sizeof(CT);  // k per stage
+  const int nk = static_cast<int>((p.K + EPS - 1) / EPS);
+  u32x4 rx[8], ra[4];
+  down_load_x<TX, CT>(rx, x, p.ldx, m0, rows_m, p.K, 0);
+  down_load_a<CT>(ra, g, q_base, p.K, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int s = it * 256 + threadIdx.x;
+      *reinterpret_cast<u32x4*>(lx + swz(s >> 3, s & 7) * 16) = rx[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int s = it * 256 + threadIdx.x;
+      *reinterpret_cast<u32x4*>(la + swz(s >> 3, s & 7) * 16) = ra[it];
+    }
+    __syncthreads();
+    if (kt + 1 < nk) {
+      down_load_x<TX, CT>(rx, x, p.ldx, m0, rows_m, p.K, (kt + 1) * EPS);
+      down_load_a<CT>(ra, g, q_base, p.K, (kt + 1) * EPS);
+    }
+    Mma<C, CT>::stage(acc, la, lx, 0, wm0, lane);
+  }
+
+  // D[i = q][j = token]: lane holds q = i*32 + 8*gq + 4*h + e for token j*32 + r.
+  const int r = lane & 31, h = lane >> 5;
+  const float s = g.scale;
+  const bool unit = (s == 1.0f);
+  CT* t = static_cast<CT*>(p.work);
+#pragma unroll
+  for (int j = 0; j < C::NJ; ++j) {
+    const int64_t m = m0 + wm0 + j * 32 + r;
+    if (m >= p.T) continue;
+#pragma unroll
+    for (int i = 0; i < C::NI; ++i) {
+      if (i * 32 >= nq) continue;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int q = q_base + i * 32 + gq * 8 + h * 4;
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = unit ? acc[i][j][gq * 4 + e] : acc[i][j][gq * 4 + e] * s;
+        CT* dst = t + m * p.ldt + g.t_col + q;
+        if constexpr (sizeof(CT) == 2) {
+          uint2 w;
+          w.x = pack_bf16x2(v[0], v[1]);
+          w.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(dst) = w;
+        } else {
+          *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+        }
+      }
+    }
+  }
+}
+
+using MainCfg = Cfg<256, 256, 128, 64>;  // 8 waves: 2 along tokens x 4 along outputs
+
+template <typename TA, typename TL, bool NF4>
+hipError_t launch_fused(const LinearProblem& p, hipStream_t s) {
+  using C = MainCfg;
+  const int mt = static_cast<int>((p.T + C::BM - 1) / C::BM);
+  const int nt = static_cast<int>((p.N + C::BN - 1) / C::BN);
+  hipLaunchKernelGGL((fused_gemm_kernel<C, TA, TL, NF4>), dim3(mt * nt), dim3(C::THREADS), 0, s, p, mt, nt);
+  return hipGetLastError();
+}
+
+template <typename TX, typename CT>
+hipError_t launch_down(const LinearProblem& p, hipStream_t s) {
+  int max_rpad = 0;
+  for (int i = 0; i < p.n_groups; ++i) max_rpad = max_rpad > p.g[i].r_pad ? max_rpad : p.g[i].r_pad;
+  const dim3 grid(static_cast<unsigned>((p.T + kDownBM - 1) / kDownBM), static_cast<unsigned>(p.n_groups),
+                  static_cast<unsigned>((max_rpad + kDownBQ - 1) / kDownBQ));
+  hipLaunchKernelGGL((lora_down_kernel<TX, CT>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lossless(const LinearProblem& p, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  hipError_t e = hipSuccess;
+  const bool act_bf16 = p.act == Elt::BF16, ad_bf16 = p.adapter == Elt::BF16;
+  if (p.n_groups > 0) {
+    if (act_bf16 && ad_bf16) e = launch_down<bf16_bits, bf16_bits>(p, s);
+    else if (act_bf16) e = launch_down<bf16_bits, float>(p, s);
+    else e = launch_down<float, float>(p, s);
+    if (e != hipSuccess) return e;
+  }
+  if (p.nf4) {
+    return ad_bf16 ? launch_fused<bf16_bits, bf16_bits, true>(p, s) : launch_fused<bf16_bits, float, true>(p, s);
+  }
+  if (act_bf16 && ad_bf16) return launch_fused<bf16_bits, bf16_bits, false>(p, s);
+  if (act_bf16) return launch_fused<bf16_bits, float, false>(p, s);
+  return launch_fused<float, float, false>(p, s);
+}
+
+}  // namespace lora

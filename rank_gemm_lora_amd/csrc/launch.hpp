@@ -1,0 +1,55 @@
+// Internal interface between the C-ABI host code (api.cpp) and the kernel
+// launchers (*.hip). Not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lora {
+
+constexpr int kMaxGroups = 8;
+constexpr int kRankPad = 64;  // rank columns of the t~ workspace are padded to this
+
+enum class Elt : int { F32 = 0, BF16 = 1 };
+
+inline int64_t rank_pad(int64_t r) { return (r + kRankPad - 1) / kRankPad * kRankPad; }
+inline int esize(Elt e) { return e == Elt::F32 ? 4 : 2; }
+
+// One adapter group as the kernels see it.
+struct GroupDev {
+  const void* A;     // [rank, K] adapter dtype
+  const void* B;     // [n_cols, rank] adapter dtype
+  int64_t col_off;   // first output column of the group
+  int64_t n_cols;
+  int32_t rank;
+  int32_t t_col;     // first column of this group's block in the t workspace
+  int32_t r_pad;     // padded rank (multiple of kRankPad)
+  float scale;       // lossless: combined scale rounded to fp32
+  float f[3];        // exact tier: alpha/rank, strength, request_scale, each rounded to fp32
+};
+
+struct LinearProblem {
+  const void* x; int64_t ldx;
+  const void* W;                                  // [N, K] act dtype (unused for 4-bit)
+  const uint8_t* codes; const float* absmax; const float* codebook;  // 4-bit weight
+  const void* bias;
+  void* y; int64_t ldy;
+  int64_t T, N, K;
+  Elt act, adapter;
+  bool nf4;
+  int n_groups;
+  GroupDev g[kMaxGroups];
+  void* work;        // t workspace, [T, ldt] in adapter dtype
+  int64_t ldt;       // sum of r_pad over groups
+};
+
+// Lossless tier: t~ = RN_adt(s . x A^T) into the workspace, then the fused GEMM.
+hipError_t launch_lossless(const LinearProblem& p, hipStream_t s);
+// Exact tier: the ordered-fp64 separate-pass chain.
+hipError_t launch_exact(const LinearProblem& p, hipStream_t s);
+// Dense payload over n contiguous elements.
+hipError_t launch_dense_patch(void* dst, Elt dst_t, const void* src, Elt src_t, int64_t n,
+                              float strength32, int mode, hipStream_t s);
+
+}  // namespace lora

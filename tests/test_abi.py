@@ -1,0 +1,170 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every symbol the
+header declares, and rejects each invalid argument with its status code
+before anything is launched (no HIP call is made on these paths)."""
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import rank_gemm_lora_amd as rg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora_mi355x.h")
+
+OK, NULL, SHAPE, DTYPE, NONFIN, ALIGN, OVERLAP, WS, UNSUP, HIP = range(10)
+F32, BF16 = rg.LORA_F32, rg.LORA_BF16
+LOSSLESS, EXACT = rg.LORA_LOSSLESS, rg.LORA_EXACT
+
+# fake, well-separated, 256-byte-aligned device addresses: validation never dereferences them
+X, W, Y, A, B, BIAS, WSP = (0x10_0000_0000 + i * 0x1_0000_0000 for i in range(7))
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return re.findall(r"^(?:int|size_t|const char\*)\s+(\w+)\(", src, flags=re.M)
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_functions())
+    assert {"lora_linear_fwd", "lora_linear_stacked_fwd", "lora_linear_nf4_fwd", "dense_patch_apply",
+            "lora_linear_workspace_size", "lora_status_string", "lora_device_check"} <= names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", rg.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(rg._lib, name)
+
+
+def test_one_hip_runtime_mapped():
+    assert len(rg.hip_runtimes_mapped()) <= 1
+
+
+def lin(**kw):
+    a = dict(x=X, T=64, K=128, ldx=128, W=W, N=96, bias=BIAS, A=A, B=B, rank=8, adt=BF16, alpha=16.0,
+             strength=1.0, rs=1.0, y=Y, ldy=96, act=BF16, q=LOSSLESS, ws=WSP, wsb=1 << 30)
+    a.update(kw)
+    return rg._lib.lora_linear_fwd(a["x"], a["T"], a["K"], a["ldx"], a["W"], a["N"], a["bias"], a["A"], a["B"],
+                                   a["rank"], a["adt"], a["alpha"], a["strength"], a["rs"], a["y"], a["ldy"],
+                                   a["act"], a["q"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), NULL), (dict(y=None), NULL), (dict(W=None), NULL), (dict(B=None), NULL),
+    (dict(A=None), NULL),
+    (dict(T=-1), SHAPE), (dict(K=0), SHAPE), (dict(N=0), SHAPE), (dict(ldx=64), SHAPE), (dict(ldy=95), SHAPE),
+    (dict(rank=0), SHAPE), (dict(rank=5000), UNSUP),
+    (dict(act=F32, adt=BF16), DTYPE), (dict(act=3), DTYPE), (dict(adt=-1), DTYPE), (dict(q=7), UNSUP),
+    (dict(alpha=math.nan), NONFIN), (dict(strength=math.inf), NONFIN), (dict(rs=-math.inf), NONFIN),
+    (dict(alpha=1e300), NONFIN),
+    (dict(x=X + 2), ALIGN), (dict(K=124, ldx=128), ALIGN), (dict(ldx=132), ALIGN), (dict(A=A + 8), ALIGN),
+    (dict(y=Y + 1), ALIGN),
+    (dict(ws=WSP + 4), ALIGN),
+    (dict(y=X + 64), OVERLAP), (dict(y=W), OVERLAP), (dict(y=B - 64), OVERLAP), (dict(ws=Y), OVERLAP),
+    (dict(ws=None), WS), (dict(wsb=64 * 64 * 2 - 1), WS),
+])
+def test_linear_rejects(kw, code):
+    assert lin(**kw) == code
+
+
+def test_linear_valid_noop_and_inactive_need_no_workspace():
+    assert lin(T=0) == OK                       # validated, nothing launched
+    assert lin(T=0, x=None, y=None) == OK
+    assert lin(T=0, A=None, B=None, ws=None, wsb=0) == OK
+    assert lin(T=0, strength=0.0, ws=None, wsb=0) == OK
+    # exact tier needs only element alignment
+    assert lin(T=0, x=X + 2, q=EXACT) == OK
+    assert lin(T=0, x=X + 1, q=EXACT) == ALIGN
+
+
+def test_workspace_size():
+    assert rg.lora_linear_workspace_size(32760, [64], BF16) == 32760 * 64 * 2
+    assert rg.lora_linear_workspace_size(64, [8], F32) == 64 * 64 * 4
+    assert rg.lora_linear_workspace_size(16384, [128, 128, 128], BF16) == 16384 * 384 * 2
+    assert rg.lora_linear_workspace_size(100, [8, 70], BF16) == 100 * (64 + 128) * 2
+    assert rg.lora_linear_workspace_size(0, [8], BF16) == 0
+    assert rg.lora_linear_workspace_size(10, [], BF16) == 0
+
+
+def stacked(groups, n_groups=None, **kw):
+    a = dict(x=X, T=0, K=128, ldx=128, W=W, N=300, bias=None, adt=BF16, strength=1.0, rs=1.0, y=Y, ldy=304,
+             act=BF16, q=LOSSLESS, ws=WSP, wsb=1 << 30)
+    a.update(kw)
+    gs = [rg.LoraGroup(A + i * 0x1000_0000, B + i * 0x1000_0000, r, 0, 1.0, o, n) for i, (r, o, n) in
+          enumerate(groups)]
+    arr = (rg.LoraGroup * max(1, len(gs)))(*gs)
+    return rg._lib.lora_linear_stacked_fwd(a["x"], a["T"], a["K"], a["ldx"], a["W"], a["N"], a["bias"], arr,
+                                           len(gs) if n_groups is None else n_groups, a["adt"], a["strength"],
+                                           a["rs"], a["y"], a["ldy"], a["act"], a["q"], a["ws"], a["wsb"], None)
+
+
+def test_stacked_group_validation():
+    assert stacked([(8, 0, 100), (8, 100, 100), (8, 200, 100)]) == OK
+    assert stacked([(8, 0, 100), (8, 99, 100)]) == SHAPE       # overlapping column ranges
+    assert stacked([(8, 250, 100)]) == SHAPE                   # past N_total
+    assert stacked([(8, -1, 10)]) == SHAPE
+    assert stacked([(8, 0, 0)]) == SHAPE
+    assert stacked([(8, 0, 10)] * 2, n_groups=9) == UNSUP
+    assert stacked([], n_groups=-1) == SHAPE
+    assert stacked([(0, 0, 10)]) == SHAPE
+
+
+def nf4(**kw):
+    a = dict(x=X, T=0, K=128, ldx=128, codes=W, absmax=W + 0x1000_0000, cb=W + 0x2000_0000, bs=64, N=96,
+             bias=None, A=A, B=B, rank=16, adt=BF16, alpha=32.0, y=Y, ldy=96, q=LOSSLESS)
+    a.update(kw)
+    return rg._lib.lora_linear_nf4_fwd(a["x"], a["T"], a["K"], a["ldx"], a["codes"], a["absmax"], a["cb"],
+                                       a["bs"], a["N"], a["bias"], a["A"], a["B"], a["rank"], a["adt"],
+                                       a["alpha"], 1.0, 1.0, a["y"], a["ldy"], a["q"], WSP, 1 << 30, None)
+
+
+def test_nf4_validation():
+    assert nf4() == OK
+    assert nf4(bs=32) == UNSUP
+    assert nf4(K=96, ldx=96) == SHAPE
+    assert nf4(codes=None) == NULL
+    assert nf4(cb=None) == NULL
+    assert nf4(absmax=W + 0x1000_0002) == ALIGN
+
+
+def patch(dshape, sshape, **kw):
+    a = dict(dst=X, ddt=BF16, src=W, sdt=BF16, strength=0.8, mode=rg.LORA_PATCH_ADD)
+    a.update(kw)
+    I64 = rg.ctypes.c_int64
+    ds = (I64 * max(1, len(dshape)))(*dshape)
+    ss = (I64 * max(1, len(sshape)))(*sshape)
+    return rg._lib.dense_patch_apply(a["dst"], a["ddt"], ds, len(dshape), a["src"], a["sdt"], ss, len(sshape),
+                                     a["strength"], a["mode"], None)
+
+
+def test_dense_patch_validation():
+    assert patch([0, 5], [0, 5]) == OK                      # empty: nothing to do
+    assert patch([3, 4], [4, 3]) == SHAPE                   # full-shape compare, not numel
+    assert patch([12], [3, 4]) == SHAPE
+    assert patch([3, 4], [3, 4], strength=math.nan) == NONFIN
+    assert patch([3, 4], [3, 4], mode=9) == UNSUP
+    assert patch([3, 4], [3, 4], ddt=5) == DTYPE
+    assert patch([3, 4], [3, 4], src=X + 8) == OVERLAP
+    assert patch([3, 4], [3, 4], dst=None) == NULL
+    assert patch([3, 4], [3, 4], dst=X + 1) == ALIGN
+
+
+def test_status_strings():
+    for s in range(10):
+        assert rg.lora_status_string(s)
+    assert "unknown" in rg.lora_status_string(99)
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "rank_gemm_lora_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(from|import)\s+oracle\b", text, flags=re.M), f
+                assert "exact_chain" not in text and "lora_oracle" not in text, f

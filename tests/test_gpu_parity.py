@@ -1,0 +1,352 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle, at sizes
+the oracle finishes in seconds that still span several tiles and ragged tails.
+
+Exact tier: bit-identical to the separate-pass chain. Lossless tier: relative
+RMS <= 4e-3 against fp64 (1e-6 for fp32 outputs) and no larger than the chain's
+error; bit-identical to the exact result on dyadic inputs where every rounding
+is the identity. Each GPU step prints its case first.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import lora_workloads as lw
+import rank_gemm_lora_amd as rg
+from oracle import exact_chain as ec
+from oracle import lora_oracle as lo
+from tests.gpu_util import (DEV, LOSSLESS_F32_GATE, assert_bitwise, assert_gate, dev, host64, say)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "handworked_exact_chain.json")
+
+
+def run_linear(d, quality, act="bf16", adapter="bf16", strength=None, request_scale=None, A="A", B="B"):
+    x, W, b = dev(d["x"]), dev(d["W"]), dev(d["b"])
+    Ad = dev(d[A]) if A else None
+    Bd = dev(d[B]) if B else None
+    y = rg.lora_linear(x, W, b, Ad, Bd, d["alpha"], d["strength"] if strength is None else strength,
+                       d["request_scale"] if request_scale is None else request_scale, quality=quality)
+    torch.cuda.synchronize()
+    return y
+
+
+def oracle_pair(d, act="bf16", adapter="bf16", strength=None, request_scale=None):
+    st = d["strength"] if strength is None else strength
+    rs = d["request_scale"] if request_scale is None else request_scale
+    args = (d["x"], d["W"], d["b"], d["A"], d["B"], d["alpha"], d["rank"], st, rs)
+    return lo.lora_linear(*args), ec.chain_linear(*args, act, adapter)
+
+
+def test_device_is_gfx950_and_one_runtime():
+    assert rg.lora_device_check() == 0
+    assert len(rg.hip_runtimes_mapped()) == 1, rg.hip_runtimes_mapped()
+
+
+# ------------------------------------------------------------------ fp32 tiny layer
+
+@pytest.mark.parametrize("variant", ["base", "strength_half", "B_zero"])
+def test_tiny_fp32(variant):
+    s = lw.TINY_FP32
+    d = lw.linear_inputs(s)
+    strength = 0.5 if variant == "strength_half" else 1.0
+    if variant == "B_zero":
+        d["B"] = torch.zeros_like(d["B"])
+    say(f"case tiny_fp32 {variant}")
+    y64, yc = oracle_pair(d, "f32", "f32", strength=strength)
+    y = run_linear(d, "lossless", strength=strength)
+    e = lo.rel_rms(host64(y), y64)
+    say(f"  lossless rel_rms {e:.3e}")
+    assert e <= LOSSLESS_F32_GATE
+    ye = run_linear(d, "exact", strength=strength)
+    assert_bitwise(ye, yc, "tiny fp32 exact")
+    if variant == "B_zero":  # base only, bitwise, in both tiers
+        yb = rg.lora_linear(dev(d["x"]), dev(d["W"]), dev(d["b"]), None, None, d["alpha"], quality="exact")
+        assert torch.equal(ye, yb)
+
+
+def test_tiny_fp32_half_strength_equals_unit_scale():
+    # alpha/rank = 2 and strength 0.5: combined s = 1 (skipped); the chain multiplies
+    # by 2 then 0.5, both exact, so all three outputs agree bit for bit.
+    d = lw.linear_inputs(lw.TINY_FP32)
+    say("case tiny_fp32 half strength == unit")
+    y_half = run_linear(d, "exact", strength=0.5)
+    y_unit = rg.lora_linear(dev(d["x"]), dev(d["W"]), dev(d["b"]), dev(d["A"]), dev(d["B"]), 8.0, 1.0, 1.0,
+                            quality="exact")
+    assert torch.equal(y_half, y_unit)
+    yl_half = run_linear(d, "lossless", strength=0.5)
+    yl_unit = rg.lora_linear(dev(d["x"]), dev(d["W"]), dev(d["b"]), dev(d["A"]), dev(d["B"]), 8.0, 1.0, 1.0)
+    assert torch.equal(yl_half, yl_unit)
+
+
+# ------------------------------------------------------------------ bf16, several tiles, ragged tails
+
+CASES = [
+    # T, K, N, rank, bias, seed   (tiles are 256 x 256 with 64-wide K steps)
+    (300, 200, 520, 24, True, 1),     # ragged T, K, N; rank padded to 64
+    (513, 384, 768, 64, False, 2),    # one-row M tail
+    (64, 136, 96, 5, True, 3),        # rank not a multiple of 8
+    (257, 1536, 300, 32, True, 4),    # long K
+    (40, 64, 1000, 128, True, 5),     # two K-extension steps
+]
+
+
+@pytest.mark.parametrize("T,K,N,r,bias,seed", CASES)
+def test_bf16_linear(T, K, N, r, bias, seed):
+    d = lw.small_linear_inputs(T, K, N, r, seed, bias=bias, alpha=2.0 * r, strength=0.8, request_scale=0.7)
+    say(f"case bf16 T={T} K={K} N={N} r={r} bias={bias}")
+    y64, yc = oracle_pair(d)
+    y = run_linear(d, "lossless")
+    assert_gate(y, y64, yc, what="lossless")
+    ye = run_linear(d, "exact")
+    assert_bitwise(ye, yc, "exact")
+
+
+@pytest.mark.parametrize("T,K,N,r", [(300, 256, 520, 24), (70, 64, 40, 8)])
+def test_bf16_std_spread_variant(T, K, N, r):
+    # second accuracy case: the std reading of N(0, v) (delta ~ 0.1 of base)
+    s = lw.LinearSpec("std", T=T, K=K, N=N, rank=r, alpha=r, strength=1.0, request_scale=0.7, bias=True, seed=9)
+    d = lw.linear_inputs(s, spread="std")
+    say(f"case bf16 std-spread T={T} K={K} N={N} r={r}")
+    y64, yc = oracle_pair(d)
+    assert_gate(run_linear(d, "lossless"), y64, yc, what="lossless std")
+    assert_bitwise(run_linear(d, "exact"), yc, "exact std")
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_dyadic_inputs_lossless_is_exact(seed):
+    T, K, N, r = 290, 192, 300, 16
+    d = lw.dyadic_linear_inputs(T, K, N, r, seed, bias=True, density=0.08)
+    say(f"case dyadic seed={seed}")
+    xd, Wd, bd, Ad, Bd = (lo.f64(d[k]) for k in ("x", "W", "b", "A", "B"))
+    y64 = lo.lora_linear(d["x"], d["W"], d["b"], d["A"], d["B"], 16.0, r, 1.0, 1.0)
+    # every intermediate exactly representable: t in bf16, the result in bf16
+    t = xd @ Ad.T
+    assert np.array_equal(ec.rn_bf16(ec.rn_f32(t)), t)
+    assert np.array_equal(ec.rn_bf16(ec.rn_f32(y64)), y64)
+    y = rg.lora_linear(dev(d["x"]), dev(d["W"]), dev(d["b"]), dev(d["A"]), dev(d["B"]), 16.0, 1.0, 1.0)
+    torch.cuda.synchronize()
+    assert_bitwise(y, y64, "lossless dyadic")
+    ye = rg.lora_linear(dev(d["x"]), dev(d["W"]), dev(d["b"]), dev(d["A"]), dev(d["B"]), 16.0, 1.0, 1.0,
+                        quality="exact")
+    torch.cuda.synchronize()
+    assert_bitwise(ye, y64, "exact dyadic")
+
+
+def test_inactive_adapter_is_base_only_bitwise():
+    d = lw.small_linear_inputs(300, 200, 520, 24, 7, bias=True, alpha=24.0)
+    x, W, b, A, B = (dev(d[k]) for k in ("x", "W", "b", "A", "B"))
+    say("case inactive adapter")
+    for q in ("lossless", "exact"):
+        y_none = rg.lora_linear(x, W, b, None, None, 24.0, quality=q)
+        y_s0 = rg.lora_linear(x, W, b, A, B, 24.0, 0.0, 1.0, quality=q)
+        y_neg0 = rg.lora_linear(x, W, b, A, B, 24.0, -0.0, 1.0, quality=q)
+        y_B0 = rg.lora_linear(x, W, b, A, torch.zeros_like(B), 24.0, 1.0, 1.0, quality=q)
+        torch.cuda.synchronize()
+        assert torch.equal(y_none, y_s0) and torch.equal(y_none, y_neg0)
+        assert not bool((y_none == 0).any())
+        assert torch.equal(y_none, y_B0)
+    base_chain = ec.chain_linear(d["x"], d["W"], d["b"], None, None, 24.0, 24, 1.0, 1.0)
+    assert_bitwise(rg.lora_linear(x, W, b, None, None, 24.0, quality="exact"), base_chain, "base exact")
+
+
+def test_request_scale_is_read_per_call():
+    d = lw.small_linear_inputs(300, 128, 260, 16, 8, bias=True, alpha=16.0)
+    say("case request scale per call")
+    outs = []
+    for rs in (0.7, 0.3, 0.7):
+        y = run_linear(d, "lossless", request_scale=rs)
+        y64, yc = oracle_pair(d, request_scale=rs)
+        assert_gate(y, y64, yc, what=f"rs={rs}")
+        outs.append(y.clone())
+    assert not torch.equal(outs[0], outs[1])
+    assert torch.equal(outs[0], outs[2])
+
+
+def test_default_quality_is_lossless_and_deterministic():
+    d = lw.small_linear_inputs(300, 200, 520, 24, 11, bias=True, alpha=48.0, strength=0.8, request_scale=0.7)
+    say("case default quality + determinism")
+    x, W, b, A, B = (dev(d[k]) for k in ("x", "W", "b", "A", "B"))
+    y_default = rg.lora_linear(x, W, b, A, B, 48.0, 0.8, 0.7)
+    y_lossless = rg.lora_linear(x, W, b, A, B, 48.0, 0.8, 0.7, quality="lossless")
+    y_again = rg.lora_linear(x, W, b, A, B, 48.0, 0.8, 0.7)
+    torch.cuda.synchronize()
+    assert torch.equal(y_default, y_lossless) and torch.equal(y_default, y_again)
+
+
+def test_column_view_output_with_wider_ldy():
+    d = lw.small_linear_inputs(130, 128, 200, 16, 12, bias=True, alpha=16.0, strength=0.9)
+    say("case column view")
+    x, W, b, A, B = (dev(d[k]) for k in ("x", "W", "b", "A", "B"))
+    for q in ("lossless", "exact"):
+        wide = torch.full((130, 328), 7.0, dtype=torch.bfloat16, device=DEV)
+        view = wide[:, 64:264]
+        rg.lora_linear(x, W, b, A, B, 16.0, 0.9, 1.0, out=view, quality=q)
+        ref = rg.lora_linear(x, W, b, A, B, 16.0, 0.9, 1.0, quality=q)
+        torch.cuda.synchronize()
+        assert torch.equal(view, ref)
+        assert bool((wide[:, :64] == 7.0).all()) and bool((wide[:, 264:] == 7.0).all())
+
+
+# ------------------------------------------------------------------ goldens through the exact tier
+
+def _hex(v):
+    return float.fromhex(v) if isinstance(v, str) else float(v)
+
+
+def test_handworked_goldens_exact_tier():
+    cases = json.load(open(GOLDEN))["linear"]
+    for c in cases:
+        act, adt = c["act"], c["adapter"]
+        say(f"case golden {c['name']}")
+        mat = lambda rows, dt: None if rows is None else lw.to_dtype(
+            np.array([[_hex(v) for v in r] for r in rows]), dt)
+        x, W, A, B = mat(c["x"], act), mat(c["W"], act), mat(c["A"], adt), mat(c["B"], adt)
+        b = None if c["b"] is None else lw.to_dtype(np.array([_hex(v) for v in c["b"]]), act)
+        y = rg.lora_linear(dev(x), dev(W), dev(b), dev(A), dev(B), c["alpha"], c["strength"],
+                           _hex(c["request_scale"]), quality="exact")
+        torch.cuda.synchronize()
+        want = np.array([[_hex(v) for v in r] for r in c["expected"]])
+        assert_bitwise(y, want, c["name"])
+
+
+# ------------------------------------------------------------------ fp32 adapter on bf16 activations
+
+@pytest.mark.parametrize("T,K,N,r", [(300, 200, 520, 24), (257, 512, 300, 64)])
+def test_fp32_adapter_on_bf16(T, K, N, r):
+    d = lw.small_linear_inputs(T, K, N, r, 21, adapter="f32", bias=True, alpha=2.0 * r, strength=0.8,
+                               request_scale=0.7)
+    say(f"case fp32 adapter T={T} K={K} N={N} r={r}")
+    y64, yc = oracle_pair(d, "bf16", "f32")
+    assert_gate(run_linear(d, "lossless"), y64, yc, what="lossless f32-adapter")
+    assert_bitwise(run_linear(d, "exact"), yc, "exact f32-adapter")
+
+
+# ------------------------------------------------------------------ stacked groups
+
+def _stacked_inputs(seed, adapter="bf16", bias=True):
+    rng = np.random.default_rng(seed)
+    T, K, Nt = 300, 256, 700
+    specs = [(24, 48.0, 0, 200), (16, 8.0, 248, 300), (64, 64.0, 560, 140)]  # rank, alpha, offset, n_cols
+    x = lw.to_dtype(rng.standard_normal((T, K)), "bf16")
+    W = lw.to_dtype(rng.standard_normal((Nt, K)) / np.sqrt(K), "bf16")
+    b = lw.to_dtype(rng.standard_normal(Nt) * np.sqrt(0.02), "bf16") if bias else None
+    groups = [dict(A=lw.to_dtype(rng.standard_normal((r, K)) / np.sqrt(K), adapter),
+                   B=lw.to_dtype(rng.standard_normal((n, r)) * np.sqrt(0.02), adapter),
+                   rank=r, alpha=a, col_offset=o, n_cols=n) for r, a, o, n in specs]
+    return x, W, b, groups
+
+
+@pytest.mark.parametrize("adapter", ["bf16", "f32"])
+def test_stacked_groups(adapter):
+    x, W, b, groups = _stacked_inputs(31, adapter)
+    say(f"case stacked adapter={adapter}")
+    y64 = lo.lora_linear_stacked(x, W, b, groups, 0.9, 0.8)
+    yc = ec.chain_stacked(x, W, b, groups, 0.9, 0.8, "bf16", adapter)
+    gg = [dict(g, A=dev(g["A"]), B=dev(g["B"])) for g in groups]
+    y = rg.lora_linear_stacked(dev(x), dev(W), dev(b), gg, 0.9, 0.8)
+    torch.cuda.synchronize()
+    assert_gate(y, y64, yc, what="stacked lossless")
+    ye = rg.lora_linear_stacked(dev(x), dev(W), dev(b), gg, 0.9, 0.8, quality="exact")
+    torch.cuda.synchronize()
+    assert_bitwise(ye, yc, "stacked exact")
+    # stacked == one call per group into column views of the same output
+    for q, ys in (("lossless", y), ("exact", ye)):
+        sep = rg.lora_linear(dev(x), dev(W), dev(b), None, None, 1.0, quality=q)
+        for g in gg:
+            o, n = g["col_offset"], g["n_cols"]
+            rg.lora_linear(dev(x), dev(W)[o:o + n], dev(b)[o:o + n], g["A"], g["B"], g["alpha"], 0.9, 0.8,
+                           out=sep[:, o:o + n], quality=q)
+        torch.cuda.synchronize()
+        assert torch.equal(sep, ys), q
+
+
+# ------------------------------------------------------------------ 4-bit base weight
+
+def _nf4_small(T=130, K=256, N=300, r=16, seed=41, bias=True, adapter="bf16"):
+    rng = np.random.default_rng(seed)
+    x = lw.to_dtype(rng.standard_normal((T, K)), "bf16")
+    codes = torch.from_numpy(rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8))
+    absmax = torch.from_numpy(np.abs(rng.standard_normal(N * K // 64)) * np.sqrt(0.05)).float()
+    A = lw.to_dtype(rng.standard_normal((r, K)) / np.sqrt(K), adapter)
+    B = lw.to_dtype(rng.standard_normal((N, r)) * np.sqrt(0.02), adapter)
+    b = lw.to_dtype(rng.standard_normal(N) * np.sqrt(0.02), "bf16") if bias else None
+    return dict(x=x, codes=codes, absmax=absmax, codebook=lw.nf4_style_codebook(), A=A, B=B, b=b, rank=r,
+                alpha=32.0, N=N)
+
+
+@pytest.mark.parametrize("adapter", ["bf16", "f32"])
+def test_nf4_linear(adapter):
+    d = _nf4_small(adapter=adapter)
+    say(f"case nf4 adapter={adapter}")
+    y64 = lo.lora_linear_nf4(d["x"], d["codes"], d["absmax"], d["codebook"], 64, d["b"], d["A"], d["B"],
+                             d["alpha"], d["rank"], 1.0, 0.9)
+    yc = ec.chain_nf4(d["x"], d["codes"], d["absmax"], d["codebook"], 64, d["b"], d["A"], d["B"], d["alpha"],
+                      d["rank"], 1.0, 0.9) if adapter == "bf16" else None
+    args = (dev(d["x"]), dev(d["codes"]), dev(d["absmax"]), dev(d["codebook"]), d["N"], dev(d["b"]),
+            dev(d["A"]), dev(d["B"]), d["alpha"], 1.0, 0.9)
+    y = rg.lora_linear_nf4(*args)
+    torch.cuda.synchronize()
+    if adapter == "f32":
+        W = ec.chain_nf4_weight(d["codes"], d["absmax"], d["codebook"], 256)
+        yc = ec.chain_linear(d["x"], W, d["b"], d["A"], d["B"], d["alpha"], d["rank"], 1.0, 0.9, "bf16", "f32")
+    assert_gate(y, y64, yc, what="nf4 lossless")
+    ye = rg.lora_linear_nf4(*args, quality="exact")
+    torch.cuda.synchronize()
+    assert_bitwise(ye, yc, "nf4 exact")
+
+
+def test_nf4_one_hot_returns_dequantized_columns():
+    d = _nf4_small(T=256, K=256, N=300, bias=False)
+    say("case nf4 one-hot")
+    x = torch.zeros((256, 256), dtype=torch.bfloat16)
+    x[torch.arange(256), torch.arange(256)] = 1.0  # row m selects k = m
+    Wq = ec.chain_nf4_weight(d["codes"], d["absmax"], d["codebook"], 256)  # [N, K]
+    for q in ("lossless", "exact"):
+        y = rg.lora_linear_nf4(dev(x), dev(d["codes"]), dev(d["absmax"]), dev(d["codebook"]), 300, None, None,
+                               None, 32.0, quality=q)
+        torch.cuda.synchronize()
+        assert_bitwise(y, Wq.T.copy(), f"one-hot {q}")
+
+
+# ------------------------------------------------------------------ dense patches
+
+@pytest.mark.parametrize("shape,dt_dst,dt_src,mode", [
+    ((1031, 77), "bf16", "bf16", "add"), ((3072 + 5,), "bf16", "bf16", "add"), ((513, 64), "f32", "bf16", "add"),
+    ((300, 40), "bf16", "f32", "add"), ((333,), "f32", "f32", "replace"), ((1031, 77), "bf16", "bf16", "replace"),
+])
+def test_dense_patch(shape, dt_dst, dt_src, mode):
+    rng = np.random.default_rng(51)
+    n = int(np.prod(shape))
+    dst = lw.to_dtype(rng.standard_normal(n) * 0.02, dt_dst).reshape(shape)
+    src = lw.to_dtype(rng.standard_normal(n) * 2e-5, dt_src).reshape(shape)
+    say(f"case dense patch {shape} {dt_dst}<-{dt_src} {mode}")
+    want = ec.chain_dense_patch(dst, src, 0.8, mode, dt_dst)
+    g = dev(dst)
+    rg.dense_patch(g, dev(src), 0.8, mode)
+    torch.cuda.synchronize()
+    assert_bitwise(g, want.reshape(shape), "patch")
+
+
+def test_dense_patch_unaligned_and_goldens():
+    rng = np.random.default_rng(52)
+    base = lw.to_dtype(rng.standard_normal(1001) * 0.02, "bf16")
+    diff = lw.to_dtype(rng.standard_normal(1001) * 2e-5, "bf16")
+    say("case dense patch unaligned")
+    g = dev(base)
+    gs = dev(diff)
+    rg.dense_patch(g[1:], gs[:1000], 0.8)  # dst starts 2 bytes into its allocation
+    torch.cuda.synchronize()
+    want = ec.chain_dense_patch(base[1:], diff[:1000], 0.8, "add", "bf16")
+    assert_bitwise(g[1:], want, "unaligned patch")
+    for c in json.load(open(GOLDEN))["patch"]:
+        say(f"case golden {c['name']}")
+        dst = lw.to_dtype(np.array([_hex(c["dst"])] * 19), c["dtype"])
+        src = lw.to_dtype(np.array([_hex(c["src"])] * 19), "bf16")
+        gd = dev(dst)
+        rg.dense_patch(gd, dev(src), _hex(c["strength"]), c["mode"])
+        torch.cuda.synchronize()
+        assert bool((host64(gd) == _hex(c["expected"])).all()), c["name"]
