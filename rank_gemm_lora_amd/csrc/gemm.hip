@@ -493,6 +493,498 @@ __global__ __launch_bounds__(256) void lora_down_kernel(LinearProblem p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined kernel for the hot configuration (bf16 activations and adapters,
+// dense weight, rank a multiple of 8).
+//
+// K advances RB bytes of every operand row per stage through a ring of S LDS
+// stages filled by buffer_load ... lds; up to S - 1 stages of loads are in
+// flight while one is consumed. A stage holds RB / 32 MFMA steps of 16 k whose
+// fragments alternate between two register sets; the barrier that publishes
+// the next stage sits inside the last step, so LDS latency and the barrier
+// hide behind MFMA work. The LoRA K-extension (t~ rows against B rows of every
+// group meeting the tile) is simply more stages of the same ring.
+namespace pipe {
+
+template <int BM_, int BN_, int WM_, int WN_, int RB_, int S_>
+struct PCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RB = RB_, S = S_;
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int NI = WN / 32, NJ = WM / 32;
+  static constexpr int CPR = RB / 16;      // 16-byte chunks per staged row
+  static constexpr int RPL = 256 / RB;     // staged rows per 256-byte line of the 64 LDS banks
+  static constexpr int KK = RB / 32;       // 16-k MFMA steps per stage
+  static constexpr int X_BYTES = BM * RB, STAGE_BYTES = (BM + BN) * RB;
+  static constexpr int LPS = (BM + BN) * CPR / THREADS;  // buffer loads per thread per stage
+  static constexpr int GROUP_M = 4;
+  static_assert(KK % 2 == 0, "fragment sets alternate across stages");
+  static_assert((BM * CPR / 64) % WAVES == 0 && (BN * CPR / 64) % WAVES == 0, "uneven load split");
+  static_assert(S * STAGE_BYTES <= 160 * 1024, "LDS");
+  static_assert((S - 2) * LPS <= 63, "vmcnt range");
+};
+
+// Chunk index XORed with (row / RPL) % CPR: the 16-byte reads of 16 consecutive
+// rows at one chunk (one quarter of a wave's ds_read_b128) hit distinct banks.
+template <class P>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * P::CPR + (chunk ^ ((row / P::RPL) % P::CPR));
+}
+
+// Tile rows [row_lo, row_hi) come from source row (row + shift), bytes
+// [kb0, kb0 + RB) of it; other rows and bytes >= kb_valid read as zero.
+template <class P, int ROWS>
+__device__ __forceinline__ void dma(char* lds, __amdgpu_buffer_rsrc_t rsrc, uint32_t ld_bytes, int row_lo,
+                                    int row_hi, int shift, int kb0, int kb_valid) {
+  constexpr int INSTR = ROWS * P::CPR / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int it = 0; it < INSTR / P::WAVES; ++it) {
+    const int slot0 = (it * P::WAVES + wave) * 64;  // wave-uniform LDS destination
+    const int sl = slot0 + lane;
+    const int row = sl / P::CPR;
+    const int c = (sl % P::CPR) ^ ((row / P::RPL) % P::CPR);
+    const int kb = kb0 + c * 16;
+    const uint32_t voff = (row >= row_lo && row < row_hi && kb < kb_valid)
+                              ? static_cast<uint32_t>(row + shift) * ld_bytes + static_cast<uint32_t>(kb)
+                              : 0x80000000u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + slot0 * 16), 16, voff, 0, 0, 0);
+  }
+}
+
+template <class P>
+struct Frags {
+  bf16x8 a[P::NI], b[P::NJ];
+};
+
+template <class P>
+__device__ __forceinline__ void load_frags(Frags<P>& f, const char* stage, int kk, int wn0, int wm0, int lane) {
+  const int r = lane & 31, h = lane >> 5;
+  const char* lx = stage;
+  const char* lw = stage + P::X_BYTES;
+#pragma unroll
+  for (int i = 0; i < P::NI; ++i) f.a[i] = *(const bf16x8*)(lw + swz<P>(wn0 + i * 32 + r, kk * 2 + h) * 16);
+#pragma unroll
+  for (int j = 0; j < P::NJ; ++j) f.b[j] = *(const bf16x8*)(lx + swz<P>(wm0 + j * 32 + r, kk * 2 + h) * 16);
+}
+
+template <class P>
+__device__ __forceinline__ void mfma_frags(f32x16 (&acc)[P::NI][P::NJ], const Frags<P>& f) {
+#pragma unroll
+  for (int i = 0; i < P::NI; ++i)
+#pragma unroll
+    for (int j = 0; j < P::NJ; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Scheduling hint for a block "NI + NJ fragment reads + NI * NJ MFMAs": the reads
+// go out two at a time behind the first MFMAs and complete while the rest run.
+template <class P>
+__device__ __forceinline__ void interleave_reads_with_mfma() {
+  constexpr int R = P::NI + P::NJ, M = P::NI * P::NJ;
+#pragma unroll
+  for (int i = 0; i < R / 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // 2 DS reads
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, M - R / 2, 0);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] bits 3:0, expcnt bits 6:4,
+// lgkmcnt bits 11:8, vmcnt[5:4] bits 15:14); counters not named stay at their
+// maximum, i.e. are not waited for. Using the builtin (not inline asm) lets the
+// compiler's own wait insertion see these waits.
+constexpr int waitcnt_vm(int n) { return (n & 0xf) | ((n >> 4) << 14) | 0x70 | 0xf00; }
+constexpr int kWaitLgkm0 = 0xc07f;
+
+// Wait until at most `n` stages of this thread's buffer loads are outstanding.
+template <int LPS>
+__device__ __forceinline__ void wait_stages(int n) {
+  if (n >= 4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * LPS > 63 ? 63 : 4 * LPS));
+  else if (n == 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * LPS > 63 ? 63 : 3 * LPS));
+  else if (n == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPS));
+  else if (n == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPS));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads (those
+// would also wait for the loads of later stages). LDS reads of this wave are
+// complete before it arrives.
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Per-lane byte offsets of one operand tile's rows for the buffer_load ... lds
+// copies (k offset 0); rows outside [row_lo, row_hi) get an offset past the
+// resource range. The k offset of a stage travels in the scalar soffset.
+template <class P, int ROWS>
+struct TileOffsets {
+  static constexpr int N = ROWS * P::CPR / 64 / P::WAVES;
+  uint32_t v[N];
+  __device__ __forceinline__ void init(uint32_t ld_bytes, int row_lo, int row_hi, int shift) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int sl = (it * P::WAVES + wave) * 64 + lane;
+      const int row = sl / P::CPR;
+      const int c = (sl % P::CPR) ^ ((row / P::RPL) % P::CPR);
+      v[it] = (row >= row_lo && row < row_hi) ? static_cast<uint32_t>(row + shift) * ld_bytes + c * 16
+                                              : 0x80000000u;
+    }
+  }
+  // Copy the stage at byte offset kb0 into lds. With a K tail, chunks at or past
+  // kb_valid are redirected out of range as well.
+  __device__ __forceinline__ void load(char* lds, __amdgpu_buffer_rsrc_t rsrc, int kb0, bool tail, int kb_valid) const {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+    for (int it = 0; it < N; ++it) {
+      const int slot0 = (it * P::WAVES + wave) * 64;
+      uint32_t voff = v[it];
+      if (tail) {
+        const int sl = slot0 + lane;
+        const int row = sl / P::CPR;
+        const int c = (sl % P::CPR) ^ ((row / P::RPL) % P::CPR);
+        if (kb0 + c * 16 >= kb_valid) voff = 0x80000000u;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + slot0 * 16), 16, voff, kb0, 0, 0);
+    }
+  }
+};
+
+template <class P>
+__global__ __launch_bounds__(P::THREADS) void gemm_pipe_kernel(LinearProblem p, int mt, int nt) {
+  __shared__ __attribute__((aligned(1024))) char smem[P::S * P::STAGE_BYTES];
+
+  const int G = mt * nt;
+  const int L = xcd_remap(blockIdx.x, G);
+  const int gsize = P::GROUP_M * nt;
+  const int grp = L / gsize;
+  const int first_m = grp * P::GROUP_M;
+  const int gm = min(P::GROUP_M, mt - first_m);
+  const int within = L - grp * gsize;
+  const int m_idx = first_m + within % gm;
+  const int n_idx = within / gm;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm0 = (wave % P::WAVES_M) * P::WM;
+  const int wn0 = (wave / P::WAVES_M) * P::WN;
+  const int64_t m0 = static_cast<int64_t>(m_idx) * P::BM;
+  const int64_t n0 = static_cast<int64_t>(n_idx) * P::BN;
+  const int rows_m = static_cast<int>(min<int64_t>(P::BM, p.T - m0));
+  const int rows_n = static_cast<int>(min<int64_t>(P::BN, p.N - n0));
+
+  // main stages
+  const int kb_total = static_cast<int>(p.K * 2);
+  const int nk = (kb_total + P::RB - 1) / P::RB;
+  const bool k_tail = (kb_total % P::RB) != 0;
+  const uint32_t ldx_b = static_cast<uint32_t>(p.ldx * 2), ldw_b = static_cast<uint32_t>(p.K * 2);
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(static_cast<const char*>(p.x) + m0 * p.ldx * 2, static_cast<uint32_t>(rows_m) * ldx_b);
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(static_cast<const char*>(p.W) + n0 * p.K * 2, static_cast<uint32_t>(rows_n) * ldw_b);
+  TileOffsets<P, P::BM> ox;
+  TileOffsets<P, P::BN> ow;
+  ox.init(ldx_b, 0, rows_m, 0);
+  ow.init(ldw_b, 0, rows_n, 0);
+  // K-extension stages: 2 * r_pad / RB per group whose columns meet the tile
+  int n_ext = 0;
+  for (int gi = 0; gi < p.n_groups; ++gi) {
+    const GroupDev& g = p.g[gi];
+    if (g.col_off < n0 + rows_n && g.col_off + g.n_cols > n0) n_ext += g.r_pad * 2 / P::RB;
+  }
+  const int NS = nk + n_ext;
+  const uint32_t ldt_b = static_cast<uint32_t>(p.ldt * 2);
+
+  auto issue_main = [&](int s) {
+    char* bx = smem + (s % P::S) * P::STAGE_BYTES;
+    const bool tail = k_tail && s == nk - 1;
+    ox.load(bx, xr, s * P::RB, tail, kb_total);
+    ow.load(bx + P::X_BYTES, wr, s * P::RB, tail, kb_total);
+  };
+  auto issue_ext = [&](int s) {
+    char* bx = smem + (s % P::S) * P::STAGE_BYTES;
+    int e = s - nk;
+    for (int gi = 0; gi < p.n_groups; ++gi) {
+      const GroupDev& g = p.g[gi];
+      if (!(g.col_off < n0 + rows_n && g.col_off + g.n_cols > n0)) continue;
+      const int ns = g.r_pad * 2 / P::RB;
+      if (e >= ns) {
+        e -= ns;
+        continue;
+      }
+      const __amdgpu_buffer_rsrc_t tr = make_rsrc(static_cast<const char*>(p.work) + (m0 * p.ldt + g.t_col) * 2,
+                                                  static_cast<uint32_t>(rows_m) * ldt_b);
+      dma<P, P::BM>(bx, tr, ldt_b, 0, rows_m, 0, e * P::RB, g.r_pad * 2);
+      const uint32_t ldb_b = static_cast<uint32_t>(g.rank * 2);
+      const __amdgpu_buffer_rsrc_t br = make_rsrc(g.B, static_cast<uint32_t>(g.n_cols) * ldb_b);
+      const int lo = static_cast<int>(max<int64_t>(0, g.col_off - n0));
+      const int hi = static_cast<int>(min<int64_t>(rows_n, g.col_off + g.n_cols - n0));
+      dma<P, P::BN>(bx + P::X_BYTES, br, ldb_b, lo, hi, static_cast<int>(n0 - g.col_off), e * P::RB, g.rank * 2);
+      return;
+    }
+  };
+  auto issue = [&](int s) {
+    if (s < nk) issue_main(s);
+    else issue_ext(s);
+  };
+
+  f32x16 acc[P::NI][P::NJ];
+#pragma unroll
+  for (int i = 0; i < P::NI; ++i)
+#pragma unroll
+    for (int j = 0; j < P::NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // prologue: the first S stages in flight, wait for stage 0
+  for (int s = 0; s < P::S && s < NS; ++s) issue(s);
+  wait_stages<P::LPS>(min(NS, P::S) - 1);
+  stage_barrier();
+  Frags<P> fr[2];
+  load_frags<P>(fr[0], smem, 0, wn0, wm0, lane);
+
+  // one stage of MFMA work; in its last 16-k step the next stage is published by
+  // a barrier and (steady state) stage j + S is issued into the freed buffer
+  auto run_stage = [&](int j, bool steady) {
+    const char* st = smem + (j % P::S) * P::STAGE_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < P::KK; ++kk) {
+      if (kk + 1 < P::KK) {
+        load_frags<P>(fr[(kk + 1) & 1], st, kk + 1, wn0, wm0, lane);
+      } else {
+        if (steady) {
+          wait_stages<P::LPS>(P::S - 2);
+        } else {
+          wait_stages<P::LPS>(min(NS - j - 2, P::S - 2));
+        }
+        stage_barrier();  // stage j + 1 visible; every wave is done reading stage j
+        if (steady) {
+          if (j + P::S < nk) issue_main(j + P::S);
+          else issue_ext(j + P::S);
+        }
+        load_frags<P>(fr[(kk + 1) & 1], smem + ((j + 1) % P::S) * P::STAGE_BYTES, 0, wn0, wm0, lane);
+      }
+      mfma_frags<P>(acc, fr[kk & 1]);
+      interleave_reads_with_mfma<P>();
+    }
+  };
+  int j = 0;
+  for (; j + P::S < NS; ++j) run_stage(j, true);
+  for (; j + 1 < NS; ++j) run_stage(j, false);
+  {
+    const char* st = smem + ((NS - 1) % P::S) * P::STAGE_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < P::KK; ++kk) {
+      if (kk + 1 < P::KK) load_frags<P>(fr[(kk + 1) & 1], st, kk + 1, wn0, wm0, lane);
+      mfma_frags<P>(acc, fr[kk & 1]);
+    }
+  }
+
+  // epilogue: + bias (fp32), one rounding, store
+  epilogue<Cfg<P::BM, P::BN, P::WM, P::WN>, bf16_bits>(acc, p, m0, n0, wm0, wn0, lane);
+}
+
+// ---------------------------------------------------------------------------
+// Register-staged variant: 256 x 256 x 64 tile, 4 waves of 128 x 128, two LDS
+// stages and two register staging sets. Global loads (buffer_load_dwordx4 into
+// VGPRs) run two stages ahead of the LDS write, so about two stages (128 KB per
+// CU) are in flight while one stage is multiplied; the LDS write of stage j + 1
+// happens in the middle of stage j's MFMA work.
+namespace vs {
+using P = PCfg<256, 256, 128, 128, 128, 2>;
+constexpr int LPS = P::LPS;  // 16 loads of 16 bytes per thread per stage
+
+struct Src {
+  __amdgpu_buffer_rsrc_t xr, wr;
+  uint32_t ldx, ldw;
+  int x_hi, w_lo, w_hi, w_shift, kb0, x_kbv, w_kbv;
+};
+
+__device__ __forceinline__ void gload(u32x4 (&v)[LPS], const Src& s) {
+#pragma unroll
+  for (int it = 0; it < LPS; ++it) {
+    const int chunk = it * P::THREADS + threadIdx.x;
+    const int row = chunk / P::CPR, c = chunk % P::CPR;
+    const int kb = s.kb0 + c * 16;
+    if (it < P::BM * P::CPR / P::THREADS) {
+      const uint32_t voff = (row < s.x_hi && kb < s.x_kbv) ? static_cast<uint32_t>(row) * s.ldx + kb : 0x80000000u;
+      v[it] = __builtin_amdgcn_raw_buffer_load_b128(s.xr, voff, 0, 0);
+    } else {
+      const int r = row - P::BM;
+      const uint32_t voff = (r >= s.w_lo && r < s.w_hi && kb < s.w_kbv)
+                                ? static_cast<uint32_t>(r + s.w_shift) * s.ldw + kb
+                                : 0x80000000u;
+      v[it] = __builtin_amdgcn_raw_buffer_load_b128(s.wr, voff, 0, 0);
+    }
+  }
+}
+
+__device__ __forceinline__ void lwrite(const u32x4 (&v)[LPS], char* buf) {
+#pragma unroll
+  for (int it = 0; it < LPS; ++it) {
+    const int chunk = it * P::THREADS + threadIdx.x;
+    const int row = chunk / P::CPR, c = chunk % P::CPR;
+    *reinterpret_cast<u32x4*>(buf + swz<P>(row, c) * 16) = v[it];  // x rows then W rows: one swizzled space
+  }
+}
+
+__global__ __launch_bounds__(P::THREADS) void gemm_vs_kernel(LinearProblem p, int mt, int nt) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * P::STAGE_BYTES];
+
+  const int G = mt * nt;
+  const int L = xcd_remap(blockIdx.x, G);
+  const int gsize = P::GROUP_M * nt;
+  const int grp = L / gsize;
+  const int first_m = grp * P::GROUP_M;
+  const int gm = min(P::GROUP_M, mt - first_m);
+  const int within = L - grp * gsize;
+  const int m_idx = first_m + within % gm;
+  const int n_idx = within / gm;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm0 = (wave % P::WAVES_M) * P::WM;
+  const int wn0 = (wave / P::WAVES_M) * P::WN;
+  const int64_t m0 = static_cast<int64_t>(m_idx) * P::BM;
+  const int64_t n0 = static_cast<int64_t>(n_idx) * P::BN;
+  const int rows_m = static_cast<int>(min<int64_t>(P::BM, p.T - m0));
+  const int rows_n = static_cast<int>(min<int64_t>(P::BN, p.N - n0));
+
+  const int kb_total = static_cast<int>(p.K * 2);
+  const int nk = (kb_total + P::RB - 1) / P::RB;
+  const uint32_t ldx_b = static_cast<uint32_t>(p.ldx * 2), ldw_b = static_cast<uint32_t>(p.K * 2);
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(static_cast<const char*>(p.x) + m0 * p.ldx * 2, static_cast<uint32_t>(rows_m) * ldx_b);
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(static_cast<const char*>(p.W) + n0 * p.K * 2, static_cast<uint32_t>(rows_n) * ldw_b);
+  int n_ext = 0;
+  for (int gi = 0; gi < p.n_groups; ++gi) {
+    const GroupDev& g = p.g[gi];
+    if (g.col_off < n0 + rows_n && g.col_off + g.n_cols > n0) n_ext += g.r_pad * 2 / P::RB;
+  }
+  const int NS = nk + n_ext;
+  const uint32_t ldt_b = static_cast<uint32_t>(p.ldt * 2);
+
+  auto source = [&](int st) {
+    Src s;
+    if (st < nk) {
+      s = Src{xr, wr, ldx_b, ldw_b, rows_m, 0, rows_n, 0, st * P::RB, kb_total, kb_total};
+      return s;
+    }
+    int e = st - nk;
+    for (int gi = 0; gi < p.n_groups; ++gi) {
+      const GroupDev& g = p.g[gi];
+      if (!(g.col_off < n0 + rows_n && g.col_off + g.n_cols > n0)) continue;
+      const int ns = g.r_pad * 2 / P::RB;
+      if (e >= ns) {
+        e -= ns;
+        continue;
+      }
+      const uint32_t ldb_b = static_cast<uint32_t>(g.rank * 2);
+      s = Src{make_rsrc(static_cast<const char*>(p.work) + (m0 * p.ldt + g.t_col) * 2,
+                        static_cast<uint32_t>(rows_m) * ldt_b),
+              make_rsrc(g.B, static_cast<uint32_t>(g.n_cols) * ldb_b), ldt_b, ldb_b, rows_m,
+              static_cast<int>(max<int64_t>(0, g.col_off - n0)),
+              static_cast<int>(min<int64_t>(rows_n, g.col_off + g.n_cols - n0)), static_cast<int>(n0 - g.col_off),
+              e * P::RB, g.r_pad * 2, g.rank * 2};
+      return s;
+    }
+    return s;
+  };
+
+  f32x16 acc[P::NI][P::NJ];
+#pragma unroll
+  for (int i = 0; i < P::NI; ++i)
+#pragma unroll
+    for (int j = 0; j < P::NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  u32x4 va[LPS], vb[LPS];  // staging sets: even stages in va, odd stages in vb
+  Frags<P> fr[2];
+  char* b0 = smem;
+  char* b1 = smem + P::STAGE_BYTES;
+
+  gload(va, source(0));
+  if (NS > 1) gload(vb, source(1));
+  lwrite(va, b0);
+  if (NS > 2) gload(va, source(2));
+  stage_barrier();
+  load_frags<P>(fr[0], b0, 0, wn0, wm0, lane);
+
+  // One stage: 4 MFMA steps of 16 k on buffer `cur`; in step 1 the next stage is
+  // written from its staging set to `nxt` and the set is refilled with stage j + 3;
+  // the barrier before step 3 publishes `nxt`.
+  auto stage = [&](int j, char* cur, char* nxt, u32x4 (&vnext)[LPS], bool full) {
+    load_frags<P>(fr[1], cur, 1, wn0, wm0, lane);
+    mfma_frags<P>(acc, fr[0]);
+    load_frags<P>(fr[0], cur, 2, wn0, wm0, lane);
+    if (full || j + 1 < NS) lwrite(vnext, nxt);
+    if (full || j + 3 < NS) gload(vnext, source(j + 3));
+    mfma_frags<P>(acc, fr[1]);
+    load_frags<P>(fr[1], cur, 3, wn0, wm0, lane);
+    mfma_frags<P>(acc, fr[0]);
+    if (full || j + 1 < NS) {
+      stage_barrier();
+      load_frags<P>(fr[0], nxt, 0, wn0, wm0, lane);
+    }
+    mfma_frags<P>(acc, fr[1]);
+  };
+
+  int j = 0;
+  for (; j + 4 < NS; j += 2) {
+    stage(j, b0, b1, vb, true);
+    stage(j + 1, b1, b0, va, true);
+  }
+  for (; j < NS; ++j) {
+    if (j & 1) stage(j, b1, b0, va, false);
+    else stage(j, b0, b1, vb, false);
+  }
+
+  epilogue<Cfg<P::BM, P::BN, P::WM, P::WN>, bf16_bits>(acc, p, m0, n0, wm0, wn0, lane);
+}
+
+hipError_t launch(const LinearProblem& p, hipStream_t s) {
+  const int mt = static_cast<int>((p.T + P::BM - 1) / P::BM);
+  const int nt = static_cast<int>((p.N + P::BN - 1) / P::BN);
+  hipLaunchKernelGGL(gemm_vs_kernel, dim3(mt * nt), dim3(P::THREADS), 0, s, p, mt, nt);
+  return hipGetLastError();
+}
+}  // namespace vs
+
+#ifndef LORA_PIPE_CFG
+#define LORA_PIPE_CFG 8
+#endif
+#if LORA_PIPE_CFG == 1
+using HotCfg = PCfg<256, 256, 128, 128, 64, 4>;
+#elif LORA_PIPE_CFG == 2
+using HotCfg = PCfg<256, 256, 128, 128, 128, 2>;
+#elif LORA_PIPE_CFG == 3
+using HotCfg = PCfg<256, 128, 128, 64, 128, 3>;
+#elif LORA_PIPE_CFG == 4
+using HotCfg = PCfg<128, 256, 64, 128, 128, 3>;
+#elif LORA_PIPE_CFG == 5
+using HotCfg = PCfg<256, 256, 128, 64, 64, 4>;
+#elif LORA_PIPE_CFG == 6
+using HotCfg = PCfg<256, 128, 128, 64, 64, 6>;
+#elif LORA_PIPE_CFG == 7
+using HotCfg = PCfg<256, 256, 128, 64, 128, 2>;
+#elif LORA_PIPE_CFG == 8
+using HotCfg = PCfg<256, 256, 64, 128, 64, 4>;
+#endif
+
+hipError_t launch(const LinearProblem& p, hipStream_t s) {
+  using P = HotCfg;
+  const int mt = static_cast<int>((p.T + P::BM - 1) / P::BM);
+  const int nt = static_cast<int>((p.N + P::BN - 1) / P::BN);
+  hipLaunchKernelGGL(gemm_pipe_kernel<P>, dim3(mt * nt), dim3(P::THREADS), 0, s, p, mt, nt);
+  return hipGetLastError();
+}
+
+}  // namespace pipe
+
 using MainCfg = Cfg<256, 256, 128, 64>;  // 8 waves: 2 along tokens x 4 along outputs
 
 template <typename TA, typename TL, bool NF4>
@@ -529,7 +1021,15 @@ hipError_t launch_lossless(const LinearProblem& p, hipStream_t s) {
   if (p.nf4) {
     return ad_bf16 ? launch_fused<bf16_bits, bf16_bits, true>(p, s) : launch_fused<bf16_bits, float, true>(p, s);
   }
-  if (act_bf16 && ad_bf16) return launch_fused<bf16_bits, bf16_bits, false>(p, s);
+  if (act_bf16 && ad_bf16) {
+    bool ranks_ok = true;
+    for (int i = 0; i < p.n_groups; ++i) ranks_ok = ranks_ok && (p.g[i].rank % 8 == 0);
+#ifdef LORA_USE_VS
+    if (ranks_ok) return pipe::vs::launch(p, s);
+#endif
+    if (ranks_ok) return pipe::launch(p, s);
+    return launch_fused<bf16_bits, bf16_bits, false>(p, s);
+  }
   if (act_bf16) return launch_fused<bf16_bits, float, false>(p, s);
   return launch_fused<float, float, false>(p, s);
 }
