@@ -1,0 +1,239 @@
+"""Benchmark of the fused LoRA linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload: the synthetic video-DiT FFN pair at 32760 tokens, rank 64 -- up
+projection 1536 -> 8960 (no bias), then down projection 8960 -> 1536 (bias in
+the epilogue), alpha 64, strength 1.0, request scale 0.7, bf16, lossless tier.
+One step = both layers over one batch, inputs resident in HBM. Prints one JSON
+line: fused TFLOP/s (algorithmic FLOPs: 2 T (K N + K r + r N) per layer), the
+overhead over the base GEMM alone (min of this library's base-only path and
+torch's F.linear), the roofline of the dominant kernel, and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "fused LoRA-linear TFLOP/s + % overhead vs base GEMM (tokens=32760, r=64)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_gemm_ffn_pair.json")
+KERNEL_SOURCES = ["rank_gemm_lora_amd/csrc/gemm.hip", "rank_gemm_lora_amd/csrc/common.hpp",
+                  "rank_gemm_lora_amd/csrc/launch.hpp"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def layer_flops(T, K, N, r):
+    return 2.0 * T * (K * N + K * r + r * N)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates HBM byte counters) and exit")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="only run the timed fused steps (for counter collection) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build runs the layer on a single MI355X "
+              "(token-parallel sharding needs no collective; see the design notes). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    if args.copy_probe:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_each_way": src.numel() * 2, "launches": 3}), flush=True)
+        return
+
+    import lora_workloads as lw
+    import rank_gemm_lora_amd as rg
+    t0 = time.time()
+    up_h, down_h = lw.ffn_pair_inputs()
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    layers = []
+    for spec, h in ((lw.FFN_UP, up_h), (lw.FFN_DOWN, down_h)):
+        d = {k: (v.to(dev) if hasattr(v, "to") else v) for k, v in h.items()}
+        T, K, N, r = spec.T, spec.K, spec.N, spec.rank
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, [r], rg.LORA_BF16)), dtype=torch.uint8, device=dev)
+        layers.append(dict(spec=spec, d=d, y=y, ws=ws, T=T, K=K, N=N, r=r))
+    del up_h, down_h
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def call(L, lora=True):
+        d = L["d"]
+        rg.lora_linear_fwd(d["x"].data_ptr(), L["T"], L["K"], L["K"], d["W"].data_ptr(), L["N"],
+                           None if d["b"] is None else d["b"].data_ptr(),
+                           d["A"].data_ptr() if lora else None, d["B"].data_ptr() if lora else None,
+                           L["r"], rg.LORA_BF16, d["alpha"], d["strength"], d["request_scale"],
+                           L["y"].data_ptr(), L["N"], rg.LORA_BF16, rg.LORA_LOSSLESS,
+                           L["ws"].data_ptr(), L["ws"].numel(), sp)
+
+    def step():
+        for L in layers:
+            call(L)
+
+    # ---------------- timed region: K steps, events around every layer call
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * len(layers) + 1)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    i = 0
+    evs[0].record(stream)
+    for _ in range(args.steps):
+        for L in layers:
+            call(L)
+            i += 1
+            evs[i].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    if args.layer_only:
+        print(json.dumps({"ms_per_step": ms_total / args.steps}), flush=True)
+        return
+    ms_per_step = ms_total / args.steps
+    per_layer_ms = [0.0] * len(layers)
+    for s in range(args.steps):
+        for li in range(len(layers)):
+            k = s * len(layers) + li
+            per_layer_ms[li] += evs[k].elapsed_time(evs[k + 1]) / args.steps
+
+    flops = [layer_flops(L["T"], L["K"], L["N"], L["r"]) for L in layers]
+    step_flops = sum(flops)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    # ---------------- base GEMM alone: own base-only path and torch F.linear (hipBLASLt)
+    def time_fn(fn, iters=10, warm=3):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(iters):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / iters
+
+    base = []
+    for L in layers:
+        d = L["d"]
+        t_own = time_fn(lambda: call(L, lora=False))
+        t_torch = time_fn(lambda: torch.nn.functional.linear(d["x"], d["W"], d["b"]))
+        base.append(dict(own_ms=t_own, torch_ms=t_torch, min_ms=min(t_own, t_torch)))
+    base_ms = sum(b["min_ms"] for b in base)
+    overhead = ms_per_step / base_ms - 1.0
+
+    # ---------------- roofline of the dominant kernel (the fused layer kernel)
+    dom_ms = sum(per_layer_ms)
+    achieved = step_flops / (dom_ms * 1e-3) / 1e12
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_hash") == kernel_hash():
+            traffic = tr.get("bytes_per_step")
+    except FileNotFoundError:
+        pass
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "fused LoRA linear layer call (rank-wide producer + fused GEMM), FFN up + down",
+                "per_launch_ms": [round(x, 4) for x in per_layer_ms]}
+
+    # ---------------- CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(layers, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "ffn_pair_tokens32760_rank64", "tokens": 32760,
+                   "layers": [{"in": L["K"], "out": L["N"], "rank": L["r"], "bias": L["d"]["b"] is not None}
+                              for L in layers],
+                   "alpha": 64.0, "strength": 1.0, "request_scale": 0.7, "quality": "lossless"},
+        "overhead_vs_base": round(overhead, 4),
+        "base_ms": round(base_ms, 4),
+        "base_detail": [{k: round(v, 4) for k, v in b.items()} for b in base],
+        "pct_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(layers, target_s):
+    """The fp64 oracle (as it stands) on the first rows of both layers' inputs."""
+    import numpy as np
+    from oracle import lora_oracle as lo
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"),
+                    default=len(os.sched_getaffinity(0)))
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    host = []
+    for L in layers:
+        d = L["d"]
+        host.append({k: (d[k].cpu() if d[k] is not None else None) for k in ("x", "W", "b", "A", "B")})
+
+    def run(rows):
+        t = time.perf_counter()
+        fl = 0.0
+        for L, h in zip(layers, host):
+            lo.lora_linear(h["x"][:rows], h["W"], h["b"], h["A"], h["B"], L["d"]["alpha"], L["r"],
+                           L["d"]["strength"], L["d"]["request_scale"])
+            fl += layer_flops(rows, L["K"], L["N"], L["r"])
+        return time.perf_counter() - t, fl
+
+    rows = 256
+    dt, fl = run(rows)
+    while dt < target_s / 2 and rows < layers[0]["T"]:
+        rows = min(layers[0]["T"], int(rows * max(2.0, min(8.0, target_s / max(dt, 1e-3) / 2))))
+        dt, fl = run(rows)
+    return {"value": float(f"{fl / dt / 1e12:.4g}"), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {rows} of 32760 tokens of both FFN layers, numpy float64, {dt:.1f}s",
+            "cpu": platform.processor() or platform.machine()}
+
+
+if __name__ == "__main__":
+    main()
