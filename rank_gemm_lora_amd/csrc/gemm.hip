@@ -787,172 +787,6 @@ __global__ __launch_bounds__(P::THREADS) void gemm_pipe_kernel(LinearProblem p, 
   epilogue<Cfg<P::BM, P::BN, P::WM, P::WN>, bf16_bits>(acc, p, m0, n0, wm0, wn0, lane);
 }
 
-// ---------------------------------------------------------------------------
-// Register-staged variant: 256 x 256 x 64 tile, 4 waves of 128 x 128, two LDS
-// stages and two register staging sets. Global loads (buffer_load_dwordx4 into
-// VGPRs) run two stages ahead of the LDS write, so about two stages (128 KB per
-// CU) are in flight while one stage is multiplied; the LDS write of stage j + 1
-// happens in the middle of stage j's MFMA work.
-namespace vs {
-using P = PCfg<256, 256, 128, 128, 128, 2>;
-constexpr int LPS = P::LPS;  // 16 loads of 16 bytes per thread per stage
-
-struct Src {
-  __amdgpu_buffer_rsrc_t xr, wr;
-  uint32_t ldx, ldw;
-  int x_hi, w_lo, w_hi, w_shift, kb0, x_kbv, w_kbv;
-};
-
-__device__ __forceinline__ void gload(u32x4 (&v)[LPS], const Src& s) {
-#pragma unroll
-  for (int it = 0; it < LPS; ++it) {
-    const int chunk = it * P::THREADS + threadIdx.x;
-    const int row = chunk / P::CPR, c = chunk % P::CPR;
-    const int kb = s.kb0 + c * 16;
-    if (it < P::BM * P::CPR / P::THREADS) {
-      const uint32_t voff = (row < s.x_hi && kb < s.x_kbv) ? static_cast<uint32_t>(row) * s.ldx + kb : 0x80000000u;
-      v[it] = __builtin_amdgcn_raw_buffer_load_b128(s.xr, voff, 0, 0);
-    } else {
-      const int r = row - P::BM;
-      const uint32_t voff = (r >= s.w_lo && r < s.w_hi && kb < s.w_kbv)
-                                ? static_cast<uint32_t>(r + s.w_shift) * s.ldw + kb
-                                : 0x80000000u;
-      v[it] = __builtin_amdgcn_raw_buffer_load_b128(s.wr, voff, 0, 0);
-    }
-  }
-}
-
-__device__ __forceinline__ void lwrite(const u32x4 (&v)[LPS], char* buf) {
-#pragma unroll
-  for (int it = 0; it < LPS; ++it) {
-    const int chunk = it * P::THREADS + threadIdx.x;
-    const int row = chunk / P::CPR, c = chunk % P::CPR;
-    *reinterpret_cast<u32x4*>(buf + swz<P>(row, c) * 16) = v[it];  // x rows then W rows: one swizzled space
-  }
-}
-
-__global__ __launch_bounds__(P::THREADS) void gemm_vs_kernel(LinearProblem p, int mt, int nt) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * P::STAGE_BYTES];
-
-  const int G = mt * nt;
-  const int L = xcd_remap(blockIdx.x, G);
-  const int gsize = P::GROUP_M * nt;
-  const int grp = L / gsize;
-  const int first_m = grp * P::GROUP_M;
-  const int gm = min(P::GROUP_M, mt - first_m);
-  const int within = L - grp * gsize;
-  const int m_idx = first_m + within % gm;
-  const int n_idx = within / gm;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm0 = (wave % P::WAVES_M) * P::WM;
-  const int wn0 = (wave / P::WAVES_M) * P::WN;
-  const int64_t m0 = static_cast<int64_t>(m_idx) * P::BM;
-  const int64_t n0 = static_cast<int64_t>(n_idx) * P::BN;
-  const int rows_m = static_cast<int>(min<int64_t>(P::BM, p.T - m0));
-  const int rows_n = static_cast<int>(min<int64_t>(P::BN, p.N - n0));
-
-  const int kb_total = static_cast<int>(p.K * 2);
-  const int nk = (kb_total + P::RB - 1) / P::RB;
-  const uint32_t ldx_b = static_cast<uint32_t>(p.ldx * 2), ldw_b = static_cast<uint32_t>(p.K * 2);
-  const __amdgpu_buffer_rsrc_t xr =
-      make_rsrc(static_cast<const char*>(p.x) + m0 * p.ldx * 2, static_cast<uint32_t>(rows_m) * ldx_b);
-  const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(static_cast<const char*>(p.W) + n0 * p.K * 2, static_cast<uint32_t>(rows_n) * ldw_b);
-  int n_ext = 0;
-  for (int gi = 0; gi < p.n_groups; ++gi) {
-    const GroupDev& g = p.g[gi];
-    if (g.col_off < n0 + rows_n && g.col_off + g.n_cols > n0) n_ext += g.r_pad * 2 / P::RB;
-  }
-  const int NS = nk + n_ext;
-  const uint32_t ldt_b = static_cast<uint32_t>(p.ldt * 2);
-
-  auto source = [&](int st) {
-    Src s;
-    if (st < nk) {
-      s = Src{xr, wr, ldx_b, ldw_b, rows_m, 0, rows_n, 0, st * P::RB, kb_total, kb_total};
-      return s;
-    }
-    int e = st - nk;
-    for (int gi = 0; gi < p.n_groups; ++gi) {
-      const GroupDev& g = p.g[gi];
-      if (!(g.col_off < n0 + rows_n && g.col_off + g.n_cols > n0)) continue;
-      const int ns = g.r_pad * 2 / P::RB;
-      if (e >= ns) {
-        e -= ns;
-        continue;
-      }
-      const uint32_t ldb_b = static_cast<uint32_t>(g.rank * 2);
-      s = Src{make_rsrc(static_cast<const char*>(p.work) + (m0 * p.ldt + g.t_col) * 2,
-                        static_cast<uint32_t>(rows_m) * ldt_b),
-              make_rsrc(g.B, static_cast<uint32_t>(g.n_cols) * ldb_b), ldt_b, ldb_b, rows_m,
-              static_cast<int>(max<int64_t>(0, g.col_off - n0)),
-              static_cast<int>(min<int64_t>(rows_n, g.col_off + g.n_cols - n0)), static_cast<int>(n0 - g.col_off),
-              e * P::RB, g.r_pad * 2, g.rank * 2};
-      return s;
-    }
-    return s;
-  };
-
-  f32x16 acc[P::NI][P::NJ];
-#pragma unroll
-  for (int i = 0; i < P::NI; ++i)
-#pragma unroll
-    for (int j = 0; j < P::NJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  u32x4 va[LPS], vb[LPS];  // staging sets: even stages in va, odd stages in vb
-  Frags<P> fr[2];
-  char* b0 = smem;
-  char* b1 = smem + P::STAGE_BYTES;
-
-  gload(va, source(0));
-  if (NS > 1) gload(vb, source(1));
-  lwrite(va, b0);
-  if (NS > 2) gload(va, source(2));
-  stage_barrier();
-  load_frags<P>(fr[0], b0, 0, wn0, wm0, lane);
-
-  // One stage: 4 MFMA steps of 16 k on buffer `cur`; in step 1 the next stage is
-  // written from its staging set to `nxt` and the set is refilled with stage j + 3;
-  // the barrier before step 3 publishes `nxt`.
-  auto stage = [&](int j, char* cur, char* nxt, u32x4 (&vnext)[LPS], bool full) {
-    load_frags<P>(fr[1], cur, 1, wn0, wm0, lane);
-    mfma_frags<P>(acc, fr[0]);
-    load_frags<P>(fr[0], cur, 2, wn0, wm0, lane);
-    if (full || j + 1 < NS) lwrite(vnext, nxt);
-    if (full || j + 3 < NS) gload(vnext, source(j + 3));
-    mfma_frags<P>(acc, fr[1]);
-    load_frags<P>(fr[1], cur, 3, wn0, wm0, lane);
-    mfma_frags<P>(acc, fr[0]);
-    if (full || j + 1 < NS) {
-      stage_barrier();
-      load_frags<P>(fr[0], nxt, 0, wn0, wm0, lane);
-    }
-    mfma_frags<P>(acc, fr[1]);
-  };
-
-  int j = 0;
-  for (; j + 4 < NS; j += 2) {
-    stage(j, b0, b1, vb, true);
-    stage(j + 1, b1, b0, va, true);
-  }
-  for (; j < NS; ++j) {
-    if (j & 1) stage(j, b1, b0, va, false);
-    else stage(j, b0, b1, vb, false);
-  }
-
-  epilogue<Cfg<P::BM, P::BN, P::WM, P::WN>, bf16_bits>(acc, p, m0, n0, wm0, wn0, lane);
-}
-
-hipError_t launch(const LinearProblem& p, hipStream_t s) {
-  const int mt = static_cast<int>((p.T + P::BM - 1) / P::BM);
-  const int nt = static_cast<int>((p.N + P::BN - 1) / P::BN);
-  hipLaunchKernelGGL(gemm_vs_kernel, dim3(mt * nt), dim3(P::THREADS), 0, s, p, mt, nt);
-  return hipGetLastError();
-}
-}  // namespace vs
 
 #ifndef LORA_PIPE_CFG
 #define LORA_PIPE_CFG 8
@@ -983,6 +817,139 @@ hipError_t launch(const LinearProblem& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// Rank-wide producer for the hot path: t~[m, t_col + q] = RN_bf16(s . sum_k x[m,k] A_g[q,k])
+// for 128-token blocks and 128 adapter rows per workgroup, streamed with the
+// same LDS ring (128-byte stages, 3 deep). Rows past the rank read as zero, so
+// the padded columns of t~ come out as zeros. HBM-bound: it reads x once per
+// 128-row chunk of each group.
+namespace down {
+// 128 tokens per workgroup, 4 waves along tokens; adapter rows per task: 64 (5-deep
+// ring, ~64 KB of x in flight per CU) when every group's padded rank is 64, else 128.
+using DP64 = PCfg<128, 64, 32, 64, 128, 5>;
+using DP128 = PCfg<128, 128, 32, 128, 128, 4>;
+
+// One pipelined K loop over NS stages for config P; issue(s) fills ring slot s % S.
+template <class P, class Issue>
+__device__ __forceinline__ void pipe_loop(f32x16 (&acc)[P::NI][P::NJ], char* smem, int NS, Issue&& issue,
+                                          int wn0, int wm0, int lane) {
+#pragma unroll
+  for (int i = 0; i < P::NI; ++i)
+#pragma unroll
+    for (int j = 0; j < P::NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  for (int s = 0; s < P::S && s < NS; ++s) issue(s);
+  wait_stages<P::LPS>(min(NS, P::S) - 1);
+  stage_barrier();
+  Frags<P> fr[2];
+  load_frags<P>(fr[0], smem, 0, wn0, wm0, lane);
+  auto run_stage = [&](int j, bool steady) {
+    const char* st = smem + (j % P::S) * P::STAGE_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < P::KK; ++kk) {
+      if (kk + 1 < P::KK) {
+        load_frags<P>(fr[(kk + 1) & 1], st, kk + 1, wn0, wm0, lane);
+      } else {
+        if (steady) wait_stages<P::LPS>(P::S - 2);
+        else wait_stages<P::LPS>(min(NS - j - 2, P::S - 2));
+        stage_barrier();
+        if (steady) issue(j + P::S);
+        load_frags<P>(fr[(kk + 1) & 1], smem + ((j + 1) % P::S) * P::STAGE_BYTES, 0, wn0, wm0, lane);
+      }
+      mfma_frags<P>(acc, fr[kk & 1]);
+      interleave_reads_with_mfma<P>();
+    }
+  };
+  int j = 0;
+  for (; j + P::S < NS; ++j) run_stage(j, true);
+  for (; j + 1 < NS; ++j) run_stage(j, false);
+  const char* st = smem + ((NS - 1) % P::S) * P::STAGE_BYTES;
+#pragma unroll
+  for (int kk = 0; kk < P::KK; ++kk) {
+    if (kk + 1 < P::KK) load_frags<P>(fr[(kk + 1) & 1], st, kk + 1, wn0, wm0, lane);
+    mfma_frags<P>(acc, fr[kk & 1]);
+  }
+}
+
+// grid: (ceil(T / BM), total chunks of BN adapter rows over all groups)
+template <class DP>
+__global__ __launch_bounds__(DP::THREADS) void down_kernel(LinearProblem p) {
+  using P = DP;
+  __shared__ __attribute__((aligned(1024))) char smem[P::S * P::STAGE_BYTES];
+  int c = static_cast<int>(blockIdx.y), gi = 0;
+  while (gi + 1 < p.n_groups && c >= (p.g[gi].r_pad + P::BN - 1) / P::BN) {
+    c -= (p.g[gi].r_pad + P::BN - 1) / P::BN;
+    ++gi;
+  }
+  const GroupDev& g = p.g[gi];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm0 = (wave % P::WAVES_M) * P::WM, wn0 = (wave / P::WAVES_M) * P::WN;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * P::BM;
+  const int rows_m = static_cast<int>(min<int64_t>(P::BM, p.T - m0));
+  const int q0 = c * P::BN;
+  const int rows_q = min(P::BN, g.rank - q0);
+  const int kb_total = static_cast<int>(p.K * 2);
+  const int nk = (kb_total + P::RB - 1) / P::RB;
+  const bool k_tail = (kb_total % P::RB) != 0;
+  const uint32_t ldx_b = static_cast<uint32_t>(p.ldx * 2), lda_b = static_cast<uint32_t>(p.K * 2);
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(static_cast<const char*>(p.x) + m0 * p.ldx * 2, static_cast<uint32_t>(rows_m) * ldx_b);
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(static_cast<const char*>(g.A) + static_cast<int64_t>(q0) * p.K * 2,
+                                              static_cast<uint32_t>(max(rows_q, 0)) * lda_b);
+  TileOffsets<P, P::BM> ox;
+  TileOffsets<P, P::BN> oa;
+  ox.init(ldx_b, 0, rows_m, 0);
+  oa.init(lda_b, 0, rows_q, 0);
+  auto issue = [&](int s) {
+    char* bx = smem + (s % P::S) * P::STAGE_BYTES;
+    const bool tail = k_tail && s == nk - 1;
+    ox.load(bx, xr, s * P::RB, tail, kb_total);
+    oa.load(bx + P::X_BYTES, ar, s * P::RB, tail, kb_total);
+  };
+  f32x16 acc[P::NI][P::NJ];
+  pipe_loop<P>(acc, smem, nk, issue, wn0, wm0, lane);
+
+  // D[i = adapter row][j = token]: lane holds rows q0 + wn0 + 32 i + 8 gq + 4 h + e of token wm0 + r
+  const int r = lane & 31, h = lane >> 5;
+  const int64_t m = m0 + wm0 + r;
+  if (m >= p.T) return;
+  const float sc = g.scale;
+  const bool unit = sc == 1.0f;
+  bf16_bits* t = static_cast<bf16_bits*>(p.work);
+#pragma unroll
+  for (int i = 0; i < P::NI; ++i) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int q = q0 + wn0 + i * 32 + gq * 8 + h * 4;
+      if (q >= g.r_pad) continue;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = unit ? acc[i][0][gq * 4 + e] : acc[i][0][gq * 4 + e] * sc;
+      uint2 w;
+      w.x = pack_bf16x2(v[0], v[1]);
+      w.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(t + m * p.ldt + g.t_col + q) = w;
+    }
+  }
+}
+
+template <class DP>
+hipError_t launch_cfg(const LinearProblem& p, hipStream_t s) {
+  int chunks = 0;
+  for (int i = 0; i < p.n_groups; ++i) chunks += (p.g[i].r_pad + DP::BN - 1) / DP::BN;
+  const dim3 grid(static_cast<unsigned>((p.T + DP::BM - 1) / DP::BM), static_cast<unsigned>(chunks));
+  hipLaunchKernelGGL(down_kernel<DP>, grid, dim3(DP::THREADS), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch(const LinearProblem& p, hipStream_t s) {
+  bool narrow = true;
+  for (int i = 0; i < p.n_groups; ++i) narrow = narrow && p.g[i].r_pad <= DP64::BN;
+  return narrow ? launch_cfg<DP64>(p, s) : launch_cfg<DP128>(p, s);
+}
+}  // namespace down
 }  // namespace pipe
 
 using MainCfg = Cfg<256, 256, 128, 64>;  // 8 waves: 2 along tokens x 4 along outputs
@@ -1010,9 +977,20 @@ hipError_t launch_down(const LinearProblem& p, hipStream_t s) {
 
 hipError_t launch_lossless(const LinearProblem& p, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
-  hipError_t e = hipSuccess;
   const bool act_bf16 = p.act == Elt::BF16, ad_bf16 = p.adapter == Elt::BF16;
+  bool ranks_ok = true;
+  for (int i = 0; i < p.n_groups; ++i) ranks_ok = ranks_ok && (p.g[i].rank % 8 == 0);
+  // hot path: streaming rank-wide producer, then the pipelined fused GEMM
+  if (act_bf16 && ad_bf16 && !p.nf4 && ranks_ok) {
+    if (p.n_groups > 0) {
+      const hipError_t e = pipe::down::launch(p, s);
+      if (e != hipSuccess) return e;
+    }
+    return pipe::launch(p, s);
+  }
+  // other dtypes / 4-bit weight / ragged ranks: producer kernel, then the fused GEMM
   if (p.n_groups > 0) {
+    hipError_t e;
     if (act_bf16 && ad_bf16) e = launch_down<bf16_bits, bf16_bits>(p, s);
     else if (act_bf16) e = launch_down<bf16_bits, float>(p, s);
     else e = launch_down<float, float>(p, s);
@@ -1021,15 +999,7 @@ hipError_t launch_lossless(const LinearProblem& p, hipStream_t s) {
   if (p.nf4) {
     return ad_bf16 ? launch_fused<bf16_bits, bf16_bits, true>(p, s) : launch_fused<bf16_bits, float, true>(p, s);
   }
-  if (act_bf16 && ad_bf16) {
-    bool ranks_ok = true;
-    for (int i = 0; i < p.n_groups; ++i) ranks_ok = ranks_ok && (p.g[i].rank % 8 == 0);
-#ifdef LORA_USE_VS
-    if (ranks_ok) return pipe::vs::launch(p, s);
-#endif
-    if (ranks_ok) return pipe::launch(p, s);
-    return launch_fused<bf16_bits, bf16_bits, false>(p, s);
-  }
+  if (act_bf16 && ad_bf16) return launch_fused<bf16_bits, bf16_bits, false>(p, s);
   if (act_bf16) return launch_fused<bf16_bits, float, false>(p, s);
   return launch_fused<float, float, false>(p, s);
 }
