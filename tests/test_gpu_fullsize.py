@@ -1,0 +1,113 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py
+uses (same entry points, lossless default), on rows the CPU oracle can afford:
+the first rows, the rows of the ragged last 256-token tile and random rows in
+between. Lossless: relative RMS <= 4e-3 against fp64 and no larger than the
+separate-pass chain's error on the same rows. Exact tier: bit-identical to the
+chain on the same rows. Dense patches: bit-identical over the whole tensor.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lora_workloads as lw
+import rank_gemm_lora_amd as rg
+from oracle import exact_chain as ec
+from oracle import lora_oracle as lo
+from tests.gpu_util import assert_bitwise, assert_gate, dev, host64, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _linear_case(d, name, act="bf16", adapter="bf16"):
+    T = d["x"].shape[0]
+    rows = sample_rows(T, n_each=32, seed=1)
+    say(f"case full-size {name}: T={T} K={d['x'].shape[1]} N={d['W'].shape[0]} r={d['rank']} rows={len(rows)}")
+    args = (dev(d["x"]), dev(d["W"]), dev(d["b"]), dev(d["A"]), dev(d["B"]), d["alpha"], d["strength"],
+            d["request_scale"])
+    y = rg.lora_linear(*args)
+    torch.cuda.synchronize()
+    xs = d["x"][rows]
+    oargs = (xs, d["W"], d["b"], d["A"], d["B"], d["alpha"], d["rank"], d["strength"], d["request_scale"])
+    y64 = lo.lora_linear(*oargs)
+    yc = ec.chain_linear(*oargs, act, adapter)
+    assert_gate(y[torch.from_numpy(rows).to(y.device)], y64, yc, what=f"{name} lossless (sampled rows)")
+    ye = rg.lora_linear(*args, quality="exact")
+    torch.cuda.synchronize()
+    assert_bitwise(ye[torch.from_numpy(rows).to(ye.device)], yc, f"{name} exact (sampled rows)")
+    assert not bool(torch.isnan(y).any())
+
+
+def test_attention_projection_full():
+    _linear_case(lw.linear_inputs(lw.ATTN_PROJ), "attn_proj")
+
+
+def test_ffn_pair_full():
+    up, down = lw.ffn_pair_inputs()
+    _linear_case(up, "ffn_up")
+    _linear_case(down, "ffn_down")
+
+
+@pytest.mark.parametrize("adapter", ["bf16", "f32"])
+def test_qkv_stacked_full(adapter):
+    spec = lw.QKV_STACKED if adapter == "bf16" else lw.StackedSpec(
+        **{**lw.QKV_STACKED.__dict__, "name": "qkv_stacked_f32", "adapter": "f32"})
+    d = lw.stacked_inputs(spec)
+    T = spec.T
+    rows = sample_rows(T, n_each=24, seed=2)
+    say(f"case full-size qkv stacked adapter={adapter} rows={len(rows)}")
+    gg = [dict(g, A=dev(g["A"]), B=dev(g["B"])) for g in d["groups"]]
+    y = rg.lora_linear_stacked(dev(d["x"]), dev(d["W"]), dev(d["b"]), gg, d["strength"], d["request_scale"])
+    torch.cuda.synchronize()
+    xs = d["x"][rows]
+    y64 = lo.lora_linear_stacked(xs, d["W"], d["b"], d["groups"], d["strength"], d["request_scale"])
+    yc = ec.chain_stacked(xs, d["W"], d["b"], d["groups"], d["strength"], d["request_scale"], "bf16", adapter)
+    idx = torch.from_numpy(rows).to(y.device)
+    assert_gate(y[idx], y64, yc, what=f"stacked {adapter} lossless (sampled rows)")
+    ye = rg.lora_linear_stacked(dev(d["x"]), dev(d["W"]), dev(d["b"]), gg, d["strength"], d["request_scale"],
+                                quality="exact")
+    torch.cuda.synchronize()
+    assert_bitwise(ye[idx], yc, f"stacked {adapter} exact (sampled rows)")
+
+
+def test_nf4_layer_full():
+    s = lw.NF4_LAYER
+    d = lw.nf4_inputs(s)
+    rows = sample_rows(s.T, n_each=24, seed=3)
+    say(f"case full-size nf4 T={s.T} K={s.K} N={s.N} r={s.rank} rows={len(rows)}")
+    args = (dev(d["x"]), dev(d["codes"]), dev(d["absmax"]), dev(d["codebook"]), s.N, dev(d["b"]), dev(d["A"]),
+            dev(d["B"]), d["alpha"], d["strength"], d["request_scale"])
+    y = rg.lora_linear_nf4(*args)
+    torch.cuda.synchronize()
+    xs = d["x"][rows]
+    W = ec.chain_nf4_weight(d["codes"], d["absmax"], d["codebook"], s.K, 64)
+    y64 = lo.lora_linear(xs, W, d["b"], d["A"], d["B"], d["alpha"], d["rank"], d["strength"], d["request_scale"])
+    yc = ec.chain_linear(xs, W, d["b"], d["A"], d["B"], d["alpha"], d["rank"], d["strength"], d["request_scale"])
+    # the fp64 reference of the 4-bit layer uses the exact codebook x absmax product
+    y64_exact_w = lo.lora_linear_nf4(xs, d["codes"], d["absmax"], d["codebook"], 64, d["b"], d["A"], d["B"],
+                                     d["alpha"], d["rank"], d["strength"], d["request_scale"])
+    idx = torch.from_numpy(rows).to(y.device)
+    assert_gate(y[idx], y64, yc, what="nf4 lossless vs bf16-weight fp64 (sampled rows)")
+    assert_gate(y[idx], y64_exact_w, None, what="nf4 lossless vs exact-weight fp64 (sampled rows)")
+    ye = rg.lora_linear_nf4(*args, quality="exact")
+    torch.cuda.synchronize()
+    assert_bitwise(ye[idx], yc, "nf4 exact (sampled rows)")
+
+
+@pytest.mark.parametrize("spec", [lw.PATCH_WEIGHT, lw.PATCH_NORM], ids=["weight_14336x4096", "rmsnorm_3072"])
+def test_dense_patch_full(spec):
+    d = lw.patch_inputs(spec)
+    say(f"case full-size dense patch {spec.shape}")
+    want = ec.chain_dense_patch(d["dst"], d["diff"], spec.strength, "add", "bf16")
+    g = dev(d["dst"])
+    rg.dense_patch(g, dev(d["diff"]), spec.strength, "add")
+    torch.cuda.synchronize()
+    assert_bitwise(g, want.reshape(spec.shape), "dense patch add")
+    # the page's point: the delta survives because the sum is taken in fp32
+    changed = float((host64(g) != lo.f64(d["dst"])).mean())
+    say(f"  fraction of elements changed by the patch: {changed:.3f}")
+    assert changed > 0.01
+    want_r = ec.chain_dense_patch(d["dst"], d["diff"], spec.strength, "replace", "bf16")
+    g2 = dev(d["dst"])
+    rg.dense_patch(g2, dev(d["diff"]), spec.strength, "replace")
+    torch.cuda.synchronize()
+    assert_bitwise(g2, want_r.reshape(spec.shape), "dense patch replace")
