@@ -38,7 +38,7 @@ _QUALITY = {"lossless": LORA_LOSSLESS, "exact": LORA_EXACT}
 _MODE = {"add": LORA_PATCH_ADD, "replace": LORA_PATCH_REPLACE}
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m rank_gemm_lora_amd._build` "
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python rank_gemm_lora_amd/_build.py` "
                       "(or __graft_entry__.build()); there is no fallback path")
 _lib = ctypes.CDLL(LIB_PATH)
 

@@ -1,6 +1,6 @@
 """Build liblora_mi355x.so in place with hipcc for gfx950.
 
-    python -m rank_gemm_lora_amd._build [-v]
+    python rank_gemm_lora_amd/_build.py [-v]
 
 Every kernel is compiled for gfx950 only. Files whose arithmetic must follow
 an exact rounding sequence (the exact tier, the dense patch) are compiled with
