@@ -988,10 +988,38 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow_kernel(LinearProblem p, 
       break;
     }
   }
-  const int ns0 = gs0 < p.n_groups ? p.g[gs0].r_pad * 2 / P::RB : 0;
-  const int ns1 = gs1 < p.n_groups ? p.g[gs1].r_pad * 2 / P::RB : 0;
-  const int NS = nk + ns0 + ns1;
+  // The fields the copies need, read once: a kernel-argument load inside a
+  // stage would make the wave wait for all of its outstanding LDS reads.
+  struct ExtGroup {
+    const char* B;
+    int tcb, tpb, rkb, n_cols, lo, hi, sh, ns;
+  };
+  auto ext_group = [&](int gi) {
+    ExtGroup e{nullptr, 0, 0, 0, 0, 0, 0, 0, 0};
+    if (gi < p.n_groups) {
+      const GroupDev& g = p.g[gi];
+      e.B = static_cast<const char*>(g.B);
+      e.tcb = g.t_col * 2;
+      e.tpb = g.r_pad * 2;
+      e.rkb = g.rank * 2;
+      e.n_cols = static_cast<int>(g.n_cols);
+      e.lo = static_cast<int>(max<int64_t>(0, g.col_off - n0));
+      e.hi = static_cast<int>(min<int64_t>(rows_n, g.col_off + g.n_cols - n0));
+      e.sh = static_cast<int>(n0 - g.col_off);
+      e.ns = g.r_pad * 2 / P::RB;
+    }
+    return e;
+  };
+  const ExtGroup eg0 = ext_group(gs0), eg1 = ext_group(gs1);
+  // Stage order: the K-extension stages first (the first group's, then the
+  // second's), then the main stages; stage s >= NE is main stage s - NE. Their
+  // copies then sit in the prologue, where a wait is exposed anyway, instead
+  // of in stages that would have to use the slower generic copy path.
+  const int NE = eg0.ns + eg1.ns;
+  const int NS = NE + nk;
   const int NU = 2 * NS;
+  const __amdgpu_buffer_rsrc_t tr =
+      make_rsrc(static_cast<const char*>(p.work) + m0 * p.ldt * 2, static_cast<uint32_t>(rows_m) * ldt_b);
 
   auto slot = [&](int u) { return smem + (u % P::SLOTS) * P::SLOT_BYTES; };
   // Load l of unit u, any unit (nothing for u >= NU); per-lane offsets are
@@ -1001,24 +1029,21 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow_kernel(LinearProblem p, 
     char* dst = slot(u);
     const int s = u >> 1;
     const bool is_w = (u & 1) != 0;
-    if (s < nk) {
-      if (is_w) dma_one<P, P::BN>(l, dst, wr, ldw_b, 0, rows_n, 0, s * P::RB, kb_total);
-      else dma_one<P, P::BM>(l, dst, xr, ldx_b, 0, rows_m, 0, s * P::RB, kb_total);
+    if (s >= NE) {
+      const int kb = (s - NE) * P::RB;
+      if (is_w) dma_one<P, P::BN>(l, dst, wr, ldw_b, 0, rows_n, 0, kb, kb_total);
+      else dma_one<P, P::BM>(l, dst, xr, ldx_b, 0, rows_m, 0, kb, kb_total);
       return;
     }
-    const int e = s - nk;
-    const GroupDev& g = p.g[e >= ns0 ? gs1 : gs0];
-    const int ee = e >= ns0 ? e - ns0 : e;
+    const bool second = s >= eg0.ns;
+    const ExtGroup& g = second ? eg1 : eg0;
+    const int e = second ? s - eg0.ns : s;
     if (!is_w) {
-      const __amdgpu_buffer_rsrc_t tr = make_rsrc(static_cast<const char*>(p.work) + (m0 * p.ldt + g.t_col) * 2,
-                                                  static_cast<uint32_t>(rows_m) * ldt_b);
-      dma_one<P, P::BM>(l, dst, tr, ldt_b, 0, rows_m, 0, ee * P::RB, g.r_pad * 2);
+      // t~ rows of the group: columns [tcb, tcb + tpb) of the tile's t~ rows
+      dma_one<P, P::BM>(l, dst, tr, ldt_b, 0, rows_m, 0, g.tcb + e * P::RB, g.tcb + g.tpb);
     } else {
-      const uint32_t ldb = static_cast<uint32_t>(g.rank * 2);
-      const __amdgpu_buffer_rsrc_t br = make_rsrc(g.B, static_cast<uint32_t>(g.n_cols) * ldb);
-      dma_one<P, P::BN>(l, dst, br, ldb, static_cast<int>(max<int64_t>(0, g.col_off - n0)),
-                        static_cast<int>(min<int64_t>(rows_n, g.col_off + g.n_cols - n0)),
-                        static_cast<int>(n0 - g.col_off), ee * P::RB, g.rank * 2);
+      const __amdgpu_buffer_rsrc_t br = make_rsrc(g.B, static_cast<uint32_t>(g.n_cols) * static_cast<uint32_t>(g.rkb));
+      dma_one<P, P::BN>(l, dst, br, static_cast<uint32_t>(g.rkb), g.lo, g.hi, g.sh, e * P::RB, g.rkb);
     }
   };
 
@@ -1031,7 +1056,7 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow_kernel(LinearProblem p, 
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   // prologue: x and W of stage 0, x of stage 1, first half of W of stage 1
-  if (nk >= 3) {
+  if (NE == 0 && nk >= 3) {
 #pragma unroll
     for (int l = 0; l < NL; ++l) ox.load_one(l, smem, xr, 0);
 #pragma unroll
@@ -1067,7 +1092,8 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow_kernel(LinearProblem p, 
 #pragma unroll
   for (int q = 0; q < 8; ++q) read_frag(fr[0], q, slot(0), slot(1), 0);
 
-  // stage t whose copy loads all belong to main, tail-free units
+  // stage t whose copy loads all belong to main, tail-free units (stages t + 1
+  // and t + 2 are main stages t + 1 - NE and t + 2 - NE)
   auto stage = [&](int t, int a) {
     const int b1 = a == 4 ? 0 : a + 1;           // W of stage t
     const int a2 = a >= 3 ? a - 3 : a + 2;       // x of stage t + 1
@@ -1095,24 +1121,17 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow_kernel(LinearProblem p, 
       }
       if ((bb & 3) == 2) {
         const int d = bb >> 2;  // 0..15
-        if (d < 4) ow.load_one(NL / 2 + d, smem + b2 * P::SLOT_BYTES, wr, (t + 1) * P::RB);
-        else if (d < 12) ox.load_one(d - 4, smem + a3 * P::SLOT_BYTES, xr, (t + 2) * P::RB);
-        else ow.load_one(d - 12, smem + a * P::SLOT_BYTES, wr, (t + 2) * P::RB);
+        if (d < 4) ow.load_one(NL / 2 + d, smem + b2 * P::SLOT_BYTES, wr, (t + 1 - NE) * P::RB);
+        else if (d < 12) ox.load_one(d - 4, smem + a3 * P::SLOT_BYTES, xr, (t + 2 - NE) * P::RB);
+        else ow.load_one(d - 12, smem + a * P::SLOT_BYTES, wr, (t + 2 - NE) * P::RB);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  const int t_fast = nk - 2 - (k_tail ? 1 : 0);
-  int a = 0;  // slot of x of stage t
-  int t = 0;
-  for (; t < t_fast && t + 1 < NS; ++t) {
-    stage(t, a);
-    a = a >= 3 ? a - 3 : a + 2;
-  }
-  // remaining stages (last main stages, K-extension): same copy assignment as
-  // the fast stages, issued in bulk, with compiler-scheduled MFMA steps
-  for (; t + 1 < NS; ++t) {
+  // The generic stage: same copy assignment as a fast stage, issued in bulk,
+  // with compiler-scheduled MFMA steps (first K-extension stages, last main stages).
+  auto generic_stage = [&](int t, int a) {
     const int b1 = a == 4 ? 0 : a + 1;
     const int a2 = a >= 3 ? a - 3 : a + 2;
     const int b2 = a2 == 4 ? 0 : a2 + 1;
@@ -1133,7 +1152,25 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow_kernel(LinearProblem p, 
       }
       mfma_frags<P>(acc, fr[kk & 1]);
     }
-    a = a2;
+  };
+
+  // fast stages: t >= NE - 1 (stage t + 1 is main stage t + 1 - NE) and main
+  // stage t + 2 - NE is neither past the last nor the K-tail stage
+  const int t_first = NE > 0 ? NE - 1 : 0;
+  const int t_end = NE + nk - 2 - (k_tail ? 1 : 0);
+  int a = 0;  // slot of x of stage t
+  int t = 0;
+  for (; t < t_first && t + 1 < NS; ++t) {
+    generic_stage(t, a);
+    a = a >= 3 ? a - 3 : a + 2;
+  }
+  for (; t < t_end && t + 1 < NS; ++t) {
+    stage(t, a);
+    a = a >= 3 ? a - 3 : a + 2;
+  }
+  for (; t + 1 < NS; ++t) {
+    generic_stage(t, a);
+    a = a >= 3 ? a - 3 : a + 2;
   }
   {  // last stage: no refill, no barrier
     const char* xs = smem + a * P::SLOT_BYTES;
