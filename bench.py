@@ -55,7 +55,13 @@ def main():
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters) and exit")
     ap.add_argument("--layer-only", action="store_true",
                     help="only run the timed fused steps (for counter collection) and exit")
+    ap.add_argument("--write-traffic", metavar="DIR",
+                    help="turn the four counter runs in DIR (f/, w/: FETCH_SIZE / WRITE_SIZE of --layer-only; "
+                         "cf/, cw/: the same of --copy-probe) into the traffic file and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(args.write_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build runs the layer on a single MI355X "
               "(token-parallel sharding needs no collective; see the design notes). Use --gpus 1.",
@@ -94,24 +100,30 @@ def main():
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
 
-    def call(L, lora=True):
+    def call(L, lora=True, phase=0):
         d = L["d"]
-        rg.lora_linear_fwd(d["x"].data_ptr(), L["T"], L["K"], L["K"], d["W"].data_ptr(), L["N"],
-                           None if d["b"] is None else d["b"].data_ptr(),
-                           d["A"].data_ptr() if lora else None, d["B"].data_ptr() if lora else None,
-                           L["r"], rg.LORA_BF16, d["alpha"], d["strength"], d["request_scale"],
-                           L["y"].data_ptr(), L["N"], rg.LORA_BF16, rg.LORA_LOSSLESS,
-                           L["ws"].data_ptr(), L["ws"].numel(), sp)
+        args = (d["x"].data_ptr(), L["T"], L["K"], L["K"], d["W"].data_ptr(), L["N"],
+                None if d["b"] is None else d["b"].data_ptr(),
+                d["A"].data_ptr() if lora else None, d["B"].data_ptr() if lora else None,
+                L["r"], rg.LORA_BF16, d["alpha"], d["strength"], d["request_scale"],
+                L["y"].data_ptr(), L["N"], rg.LORA_BF16, rg.LORA_LOSSLESS,
+                L["ws"].data_ptr(), L["ws"].numel(), sp)
+        if phase == 0:
+            rg.lora_linear_fwd(*args)
+        else:
+            rg.lora_linear_fwd_phase(phase, *args)
 
     def step():
         for L in layers:
             call(L)
 
-    # ---------------- timed region: K steps, events around every layer call
+    # ---------------- timed region: K steps; every layer call is its two kernels
+    # (phase 1: rank-wide producer, phase 2: fused GEMM), with an event after each
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * len(layers) + 1)]
+    n_ev = args.steps * len(layers) * 2 + 1
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -120,21 +132,29 @@ def main():
     evs[0].record(stream)
     for _ in range(args.steps):
         for L in layers:
-            call(L)
-            i += 1
-            evs[i].record(stream)
+            for ph in (1, 2):
+                call(L, phase=ph)
+                i += 1
+                evs[i].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
-    if args.layer_only:
-        print(json.dumps({"ms_per_step": ms_total / args.steps}), flush=True)
-        return
     ms_per_step = ms_total / args.steps
-    per_layer_ms = [0.0] * len(layers)
-    for s in range(args.steps):
+    prod_ms = [0.0] * len(layers)   # per launch, averaged over the steps
+    gemm_ms = [0.0] * len(layers)
+    for s_ in range(args.steps):
         for li in range(len(layers)):
-            k = s * len(layers) + li
-            per_layer_ms[li] += evs[k].elapsed_time(evs[k + 1]) / args.steps
+            k = (s_ * len(layers) + li) * 2
+            prod_ms[li] += evs[k].elapsed_time(evs[k + 1]) / args.steps
+            gemm_ms[li] += evs[k + 1].elapsed_time(evs[k + 2]) / args.steps
+    if args.layer_only:
+        # the same per-launch means a kernel trace of this process reports for the timed launches
+        print(json.dumps({"ms_per_step": round(ms_per_step, 4), "timed_steps": args.steps,
+                          "warmup_steps": args.warmup,
+                          "gemm_ms_per_launch": [round(x, 4) for x in gemm_ms],
+                          "producer_ms_per_launch": [round(x, 4) for x in prod_ms]}), flush=True)
+        return
+    per_layer_ms = [p_ + g_ for p_, g_ in zip(prod_ms, gemm_ms)]
 
     flops = [layer_flops(L["T"], L["K"], L["N"], L["r"]) for L in layers]
     step_flops = sum(flops)
@@ -162,21 +182,28 @@ def main():
     base_ms = sum(b["min_ms"] for b in base)
     overhead = ms_per_step / base_ms - 1.0
 
-    # ---------------- roofline of the dominant kernel (the fused layer kernel)
-    dom_ms = sum(per_layer_ms)
-    achieved = step_flops / (dom_ms * 1e-3) / 1e12
+    # ---------------- roofline of the dominant kernel: the fused GEMM (phase 2)
+    # algorithmic FLOPs per launch 2 T (K N + r N); the producer (phase 1) is HBM-bound:
+    # algorithmic bytes per launch = x once (T K 2) + A (r K 2) + t~ written (T r_pad 2)
+    gemm_flops = [2.0 * L["T"] * (L["K"] * L["N"] + L["r"] * L["N"]) for L in layers]
+    achieved = sum(gemm_flops) / (sum(gemm_ms) * 1e-3) / 1e12
+    prod_bytes = [2.0 * (L["T"] * L["K"] + L["r"] * L["K"] + L["T"] * ((L["r"] + 63) // 64 * 64)) for L in layers]
+    prod_gbs = sum(prod_bytes) / (sum(prod_ms) * 1e-3) / 1e9
     traffic = None
     try:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if tr.get("kernel_hash") == kernel_hash():
-            traffic = tr.get("bytes_per_step")
+            traffic = tr.get("bytes_per_launch")
     except FileNotFoundError:
         pass
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "fused LoRA linear layer call (rank-wide producer + fused GEMM), FFN up + down",
-                "per_launch_ms": [round(x, 4) for x in per_layer_ms]}
+                "kernel": "fused LoRA GEMM (gemm_flow_kernel), FFN up + down launches",
+                "per_launch_ms": [round(x, 4) for x in gemm_ms],
+                "producer": {"bound": "hbm", "achieved": round(prod_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(prod_gbs / PEAK_HBM_GBS, 4),
+                             "per_launch_ms": [round(x, 4) for x in prod_ms]}}
 
     # ---------------- CPU oracle on a bounded sample of the same workload
     cpu = None
@@ -198,6 +225,63 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    print(json.dumps(out), flush=True)
+
+
+def _counter_means(csv_path, counter):
+    """Mean counter value (KiB) per dispatch, keyed by (kernel kind, grid size)."""
+    import csv
+    import statistics
+    vals = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            n = r["Kernel_Name"]
+            kind = ("gemm" if "gemm_flow_kernel" in n else "producer" if "down_kernel" in n
+                    else "copy" if "copyBuffer" in n else None)
+            if kind is None:
+                continue
+            vals.setdefault((kind, int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+    return {k: statistics.mean(v) for k, v in vals.items()}
+
+
+def write_traffic(d):
+    """HBM-side bytes per launch of the fused GEMM from FETCH_SIZE / WRITE_SIZE, each
+    scaled by what the same counter reads for a plain 1 GiB device copy."""
+    import glob
+    import lora_workloads as lw
+
+    def one(sub, counter):
+        paths = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
+        assert paths, f"no counter_collection.csv under {os.path.join(d, sub)}"
+        return _counter_means(paths[0], counter)
+    f, w = one("f", "FETCH_SIZE"), one("w", "WRITE_SIZE")
+    cf, cw = one("cf", "FETCH_SIZE"), one("cw", "WRITE_SIZE")
+    kib = (1 << 30) / 1024
+    fs = kib / max(v for (k, _), v in cf.items() if k == "copy")
+    ws = kib / max(v for (k, _), v in cw.items() if k == "copy")
+    launches = []
+    for spec in (lw.FFN_UP, lw.FFN_DOWN):
+        tiles = -(-spec.T // 256) * -(-spec.N // 256)
+        key = ("gemm", tiles * 256)
+        fb, wb = f[key] * 1024 * fs, w[key] * 1024 * ws
+        alg = 2.0 * (spec.T * spec.K + spec.N * spec.K + spec.T * 64 + spec.N * spec.rank + spec.T * spec.N) \
+            + (2.0 * spec.N if spec.bias else 0.0)
+        launches.append({"layer": f"{spec.K}->{spec.N}", "FETCH_SIZE_KiB": round(f[key]), "WRITE_SIZE_KiB": round(w[key]),
+                         "fetch_bytes": round(fb), "write_bytes": round(wb), "algorithmic_bytes": round(alg)})
+    out = {"kernel_hash": kernel_hash(), "fetch_scale": fs, "write_scale": ws,
+           "bytes_per_launch": round(sum(L["fetch_bytes"] + L["write_bytes"] for L in launches) / len(launches)),
+           "algorithmic_bytes_per_launch": round(sum(L["algorithmic_bytes"] for L in launches) / len(launches)),
+           "per_launch": launches,
+           "commands": [
+               "rocprofv3 --pmc FETCH_SIZE -d <dir>/f -o f --output-format csv -- python3 bench.py --layer-only --steps 2 --warmup 1",
+               "rocprofv3 --pmc WRITE_SIZE -d <dir>/w -o w --output-format csv -- python3 bench.py --layer-only --steps 2 --warmup 1",
+               "rocprofv3 --pmc FETCH_SIZE -d <dir>/cf -o cf --output-format csv -- python3 bench.py --copy-probe",
+               "rocprofv3 --pmc WRITE_SIZE -d <dir>/cw -o cw --output-format csv -- python3 bench.py --copy-probe",
+               "python3 bench.py --write-traffic <dir>"]}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
     print(json.dumps(out), flush=True)
 
 

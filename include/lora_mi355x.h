@@ -132,6 +132,28 @@ int lora_linear_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * lora_linear_fwd_phase -- one half of the lossless lora_linear_fwd, for
+ * callers that schedule or time the two kernels of the path separately
+ * (SGLang PR #43501, Modifications: the scale is applied to the rank-wide
+ * intermediate, then the second LoRA product lands on the base output).
+ *
+ *   phase 1  writes the rank-wide intermediate RN_adt(s . x A^T) into the workspace
+ *            (nothing when the adapter is inactive: s == 0 or A == B == NULL)
+ *   phase 2  runs the fused GEMM y = RN(x W^T + t~ B^T + bias) reading that
+ *            intermediate; the workspace must still hold what a phase-1 call with
+ *            the same x, A, ranks and scales wrote (the library cannot check this)
+ * Phase 1 then phase 2 on one stream gives exactly the output of lora_linear_fwd.
+ * Arguments, validation and status codes as lora_linear_fwd; phase not 1 or 2, or
+ * quality other than LORA_LOSSLESS, returns LORA_ERR_UNSUPPORTED.
+ */
+int lora_linear_fwd_phase(int32_t phase, const void* x, int64_t T, int64_t K, int64_t ldx,
+                          const void* W, int64_t N, const void* bias,
+                          const void* A, const void* B, int32_t rank, int32_t adapter_dtype,
+                          double alpha, double strength, double request_scale,
+                          void* y, int64_t ldy, int32_t act_dtype, int32_t quality,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * lora_linear_stacked_fwd -- one base GEMM over W [N_total, K] with up to
  * LORA_MAX_GROUPS adapters, each added to its own column range of y
  * (SGLang PR #43501, Modifications: stacked q/k/v or gate/up adapters, one

@@ -24,7 +24,8 @@ import torch  # loads the HIP runtime this library binds to (one runtime per pro
 __all__ = [
     "LIB_PATH", "LoraError", "LORA_F32", "LORA_BF16", "LORA_LOSSLESS", "LORA_EXACT",
     "LORA_PATCH_ADD", "LORA_PATCH_REPLACE", "lora_linear_fwd", "lora_linear_stacked_fwd",
-    "lora_linear_nf4_fwd", "dense_patch_apply", "lora_linear_workspace_size", "lora_status_string",
+    "lora_linear_nf4_fwd", "dense_patch_apply", "lora_linear_fwd_phase", "lora_linear_workspace_size",
+    "lora_status_string",
     "lora_device_check", "lora_linear", "lora_linear_stacked", "lora_linear_nf4", "dense_patch",
     "LoraGroup", "hip_runtimes_mapped",
 ]
@@ -54,6 +55,9 @@ class LoraGroup(ctypes.Structure):
 _lib.lora_linear_fwd.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _f64, _f64, _f64,
                                  _p, _i64, _i32, _i32, _p, _sz, _p]
 _lib.lora_linear_fwd.restype = ctypes.c_int
+_lib.lora_linear_fwd_phase.argtypes = [_i32, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _f64, _f64,
+                                       _f64, _p, _i64, _i32, _i32, _p, _sz, _p]
+_lib.lora_linear_fwd_phase.restype = ctypes.c_int
 _lib.lora_linear_stacked_fwd.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, ctypes.POINTER(LoraGroup), _i32,
                                          _i32, _f64, _f64, _p, _i64, _i32, _i32, _p, _sz, _p]
 _lib.lora_linear_stacked_fwd.restype = ctypes.c_int
@@ -90,6 +94,13 @@ def lora_linear_fwd(x, T, K, ldx, W, N, bias, A, B, rank, adapter_dtype, alpha, 
     return _check(_lib.lora_linear_fwd(x, T, K, ldx, W, N, bias, A, B, rank, adapter_dtype, alpha, strength,
                                        request_scale, y, ldy, act_dtype, quality, workspace, workspace_bytes,
                                        stream), "lora_linear_fwd")
+
+
+def lora_linear_fwd_phase(phase, x, T, K, ldx, W, N, bias, A, B, rank, adapter_dtype, alpha, strength,
+                          request_scale, y, ldy, act_dtype, quality, workspace, workspace_bytes, stream):
+    return _check(_lib.lora_linear_fwd_phase(phase, x, T, K, ldx, W, N, bias, A, B, rank, adapter_dtype, alpha,
+                                             strength, request_scale, y, ldy, act_dtype, quality, workspace,
+                                             workspace_bytes, stream), "lora_linear_fwd_phase")
 
 
 def lora_linear_stacked_fwd(x, T, K, ldx, W, N_total, bias, groups, n_groups, adapter_dtype, strength,

@@ -91,7 +91,7 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
                const float* absmax, const float* codebook, bool nf4, int64_t N, const void* bias,
                const Adapter* ads, int n_ads, int adapter_dtype, double strength, double request_scale,
                void* y, int64_t ldy, int act_dtype, int quality, void* workspace, size_t workspace_bytes,
-               void* stream) {
+               void* stream, int phase = 0) {
   if (!dtype_ok(act_dtype) || !dtype_ok(adapter_dtype)) return LORA_ERR_DTYPE;
   if (act_dtype == LORA_F32 && adapter_dtype != LORA_F32) return LORA_ERR_DTYPE;
   if (quality != LORA_LOSSLESS && quality != LORA_EXACT) return LORA_ERR_UNSUPPORTED;
@@ -177,7 +177,7 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
   if (T == 0) return LORA_OK;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = (quality == LORA_EXACT) ? lora::launch_exact(p, s) : lora::launch_lossless(p, s);
+  const hipError_t e = (quality == LORA_EXACT) ? lora::launch_exact(p, s) : lora::launch_lossless(p, s, phase);
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
@@ -192,6 +192,17 @@ int lora_linear_fwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void
   const Adapter a{A, B, rank, alpha, 0, N};
   return run_linear(x, T, K, ldx, W, nullptr, nullptr, nullptr, false, N, bias, &a, 1, adapter_dtype, strength,
                     request_scale, y, ldy, act_dtype, quality, workspace, workspace_bytes, stream);
+}
+
+int lora_linear_fwd_phase(int32_t phase, const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, int64_t N,
+                          const void* bias, const void* A, const void* B, int32_t rank, int32_t adapter_dtype,
+                          double alpha, double strength, double request_scale, void* y, int64_t ldy,
+                          int32_t act_dtype, int32_t quality, void* workspace, size_t workspace_bytes, void* stream) {
+  if (phase != 1 && phase != 2) return LORA_ERR_UNSUPPORTED;
+  if (quality != LORA_LOSSLESS) return LORA_ERR_UNSUPPORTED;
+  const Adapter a{A, B, rank, alpha, 0, N};
+  return run_linear(x, T, K, ldx, W, nullptr, nullptr, nullptr, false, N, bias, &a, 1, adapter_dtype, strength,
+                    request_scale, y, ldy, act_dtype, quality, workspace, workspace_bytes, stream, phase);
 }
 
 int lora_linear_stacked_fwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, int64_t N_total,

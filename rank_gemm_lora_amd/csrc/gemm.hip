@@ -1380,27 +1380,28 @@ hipError_t launch_down(const LinearProblem& p, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_lossless(const LinearProblem& p, hipStream_t s) {
+hipError_t launch_lossless(const LinearProblem& p, hipStream_t s, int phase) {
   if (p.T == 0) return hipSuccess;
   const bool act_bf16 = p.act == Elt::BF16, ad_bf16 = p.adapter == Elt::BF16;
   bool ranks_ok = true;
   for (int i = 0; i < p.n_groups; ++i) ranks_ok = ranks_ok && (p.g[i].rank % 8 == 0);
   // hot path: streaming rank-wide producer, then the pipelined fused GEMM
   if (act_bf16 && ad_bf16 && !p.nf4 && ranks_ok) {
-    if (p.n_groups > 0) {
+    if (p.n_groups > 0 && phase != 2) {
       const hipError_t e = pipe::down::launch(p, s);
       if (e != hipSuccess) return e;
     }
-    return pipe::launch(p, s);
+    return phase == 1 ? hipSuccess : pipe::launch(p, s);
   }
   // other dtypes / 4-bit weight / ragged ranks: producer kernel, then the fused GEMM
-  if (p.n_groups > 0) {
+  if (p.n_groups > 0 && phase != 2) {
     hipError_t e;
     if (act_bf16 && ad_bf16) e = launch_down<bf16_bits, bf16_bits>(p, s);
     else if (act_bf16) e = launch_down<bf16_bits, float>(p, s);
     else e = launch_down<float, float>(p, s);
     if (e != hipSuccess) return e;
   }
+  if (phase == 1) return hipSuccess;
   if (p.nf4) {
     return ad_bf16 ? launch_fused<bf16_bits, bf16_bits, true>(p, s) : launch_fused<bf16_bits, float, true>(p, s);
   }

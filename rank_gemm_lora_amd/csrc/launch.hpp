@@ -45,7 +45,9 @@ struct LinearProblem {
 };
 
 // Lossless tier: t~ = RN_adt(s . x A^T) into the workspace, then the fused GEMM.
-hipError_t launch_lossless(const LinearProblem& p, hipStream_t s);
+// phase 0 runs both, 1 only the rank-wide producer, 2 only the fused GEMM
+// (which reads the t~ a phase-1 call left in the workspace).
+hipError_t launch_lossless(const LinearProblem& p, hipStream_t s, int phase = 0);
 // Exact tier: the ordered-fp64 separate-pass chain.
 hipError_t launch_exact(const LinearProblem& p, hipStream_t s);
 // Dense payload over n contiguous elements.

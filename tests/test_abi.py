@@ -82,6 +82,27 @@ def test_linear_valid_noop_and_inactive_need_no_workspace():
     assert lin(T=0, x=X + 1, q=EXACT) == ALIGN
 
 
+def phase(ph, **kw):
+    a = dict(x=X, T=64, K=128, ldx=128, W=W, N=96, bias=BIAS, A=A, B=B, rank=8, adt=BF16, alpha=16.0,
+             strength=1.0, rs=1.0, y=Y, ldy=96, act=BF16, q=LOSSLESS, ws=WSP, wsb=1 << 30)
+    a.update(kw)
+    return rg._lib.lora_linear_fwd_phase(ph, a["x"], a["T"], a["K"], a["ldx"], a["W"], a["N"], a["bias"], a["A"],
+                                         a["B"], a["rank"], a["adt"], a["alpha"], a["strength"], a["rs"], a["y"],
+                                         a["ldy"], a["act"], a["q"], a["ws"], a["wsb"], None)
+
+
+def test_phase_entry_point_validation():
+    assert phase(0) == UNSUP and phase(3) == UNSUP and phase(-1) == UNSUP
+    assert phase(1, q=EXACT) == UNSUP and phase(2, q=EXACT) == UNSUP
+    for ph in (1, 2):                      # the same validation as lora_linear_fwd, before any launch
+        assert phase(ph, T=0) == OK
+        assert phase(ph, x=None) == NULL
+        assert phase(ph, ldy=95) == SHAPE
+        assert phase(ph, ws=None) == WS
+        assert phase(ph, y=W) == OVERLAP
+        assert phase(ph, strength=math.nan) == NONFIN
+
+
 def test_workspace_size():
     assert rg.lora_linear_workspace_size(32760, [64], BF16) == 32760 * 64 * 2
     assert rg.lora_linear_workspace_size(64, [8], F32) == 64 * 64 * 4

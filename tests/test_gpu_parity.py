@@ -177,6 +177,33 @@ def test_default_quality_is_lossless_and_deterministic():
     assert torch.equal(y_default, y_lossless) and torch.equal(y_default, y_again)
 
 
+@pytest.mark.parametrize("T,K,N,r,adapter", [(300, 200, 520, 24, "bf16"), (513, 384, 768, 64, "bf16"),
+                                              (257, 512, 300, 64, "f32"), (64, 136, 96, 5, "bf16")])
+def test_phases_compose_to_the_fused_call(T, K, N, r, adapter):
+    """Phase 1 (rank-wide producer) then phase 2 (fused GEMM) equal lora_linear_fwd bit for bit."""
+    d = lw.small_linear_inputs(T, K, N, r, 21, bias=True, alpha=2.0 * r, strength=0.8, request_scale=0.7)
+    say(f"case phases T={T} K={K} N={N} r={r} adapter={adapter}")
+    x, W, b = dev(d["x"]), dev(d["W"]), dev(d["b"])
+    adt = rg.LORA_F32 if adapter == "f32" else rg.LORA_BF16
+    tdt = torch.float32 if adapter == "f32" else torch.bfloat16
+    A, B = dev(d["A"]).to(tdt).contiguous(), dev(d["B"]).to(tdt).contiguous()
+    ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, [r], adt)), dtype=torch.uint8, device=DEV)
+    y_one = torch.empty((T, N), dtype=torch.bfloat16, device=DEV)
+    y_two = torch.full((T, N), 3.0, dtype=torch.bfloat16, device=DEV)
+    sp = torch.cuda.current_stream().cuda_stream
+    args = (x.data_ptr(), T, K, K, W.data_ptr(), N, b.data_ptr(), A.data_ptr(), B.data_ptr(), r, adt,
+            d["alpha"], 0.8, 0.7)
+    tail = (rg.LORA_BF16, rg.LORA_LOSSLESS, ws.data_ptr(), ws.numel(), sp)
+    rg.lora_linear_fwd(*args, y_one.data_ptr(), N, *tail)
+    ws.zero_()
+    rg.lora_linear_fwd_phase(1, *args, y_two.data_ptr(), N, *tail)
+    torch.cuda.synchronize()
+    assert bool((y_two == 3.0).all())      # phase 1 writes only the workspace
+    rg.lora_linear_fwd_phase(2, *args, y_two.data_ptr(), N, *tail)
+    torch.cuda.synchronize()
+    assert torch.equal(y_one, y_two)
+
+
 def test_column_view_output_with_wider_ldy():
     d = lw.small_linear_inputs(130, 128, 200, 16, 12, bias=True, alpha=16.0, strength=0.9)
     say("case column view")
