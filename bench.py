@@ -199,7 +199,7 @@ def main():
         pass
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "fused LoRA GEMM (gemm_flow_kernel), FFN up + down launches",
+                "kernel": "fused LoRA GEMM (gemm_flow16_kernel), FFN up + down launches",
                 "per_launch_ms": [round(x, 4) for x in gemm_ms],
                 "producer": {"bound": "hbm", "achieved": round(prod_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(prod_gbs / PEAK_HBM_GBS, 4),
@@ -238,7 +238,7 @@ def _counter_means(csv_path, counter):
             if r["Counter_Name"] != counter:
                 continue
             n = r["Kernel_Name"]
-            kind = ("gemm" if "gemm_flow_kernel" in n else "producer" if "down_kernel" in n
+            kind = ("gemm" if "gemm_flow16_kernel" in n else "producer" if "down_kernel" in n
                     else "copy" if "copyBuffer" in n else None)
             if kind is None:
                 continue

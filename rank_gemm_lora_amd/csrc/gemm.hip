@@ -1194,9 +1194,406 @@ hipError_t launch_flow(const LinearProblem& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// The hot kernel on v_mfma_f32_16x16x32_bf16. Same tile (256 x 256, 4 waves of
+// 128 x 128), ring and copies as above; each wave holds 8 x 8 blocks of 16 x 16
+// (4 accumulators per lane each) and a 64-k stage is two 32-k steps of 64 MFMAs.
+// Under a sustained MFMA load this instruction runs at a clearly higher clock
+// than the 32 x 32 x 16 one for the same work per cycle (measured on MI355X:
+// about 2.05 against 1.77 GHz with LDS operand reads), which is where the
+// kernel's throughput is decided once the copies are hidden.
+template <int BM_, int BN_, int WM_, int WN_, int RB_, int SLOTS_>
+struct QCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RB = RB_, SLOTS = SLOTS_;
+  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, WAVES = WAVES_M * WAVES_N;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int NI = WN / 16, NJ = WM / 16;   // 16 x 16 blocks per wave
+  static constexpr int CPR = RB / 16, RPL = 256 / RB;
+  static constexpr int KK = RB / 64;                  // 32-k MFMA steps per stage
+  static constexpr int SLOT_BYTES = BM * RB;
+  static constexpr int GROUP_M = 4;
+  static_assert(BM == BN && RB == 128 && KK == 2, "x and W units share one slot size; two k-steps per stage");
+  static_assert((BM * CPR / 64) % WAVES == 0, "uneven load split");
+  static_assert(SLOTS == 5 && SLOTS * SLOT_BYTES <= 160 * 1024, "LDS");
+};
+
+template <class P>
+struct Frags16 {
+  bf16x8 a[P::NI], b[P::NJ];
+};
+
+// Operand fragments of 32-k step kk: lane (r = lane % 16, q = lane / 16) holds
+// k = 8q .. 8q + 7 of row r of each 16-row block, i.e. 16-byte chunk 4 kk + q.
+// With 128-byte rows the swizzle term (row / 2) % 8 is the same for every
+// 16-row block, so block i sits at a fixed 2048-byte offset from the lane's
+// block-0 address, and k-step 1 is k-step 0's address with byte bit 6 flipped.
+struct FragOffsets {
+  uint32_t x, w;  // byte offsets of this lane's k-step-0 chunk in block 0 of an x / W slot
+};
+
+template <class P>
+__device__ __forceinline__ FragOffsets frag_offsets(int wn0, int wm0, int lane) {
+  const int r = lane & 15, q = lane >> 4;
+  const int c = q ^ ((r >> 1) & 7);
+  return FragOffsets{static_cast<uint32_t>(((wm0 + r) * P::CPR + c) * 16),
+                     static_cast<uint32_t>(((wn0 + r) * P::CPR + c) * 16)};
+}
+
+template <class P>
+__device__ __forceinline__ void ring_frags16(Frags16<P>& f, const char* xs, const char* ws, int kk,
+                                             FragOffsets o) {
+  const uint32_t flip = kk ? 64u : 0u;
+#pragma unroll
+  for (int i = 0; i < P::NI; ++i) f.a[i] = *(const bf16x8*)(ws + (o.w ^ flip) + i * 2048);
+#pragma unroll
+  for (int j = 0; j < P::NJ; ++j) f.b[j] = *(const bf16x8*)(xs + (o.x ^ flip) + j * 2048);
+}
+
+template <class P>
+__device__ __forceinline__ void mfma_frags16(f32x4 (&acc)[P::NI][P::NJ], const Frags16<P>& f) {
+#pragma unroll
+  for (int i = 0; i < P::NI; ++i)
+#pragma unroll
+    for (int j = 0; j < P::NJ; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+}
+
+// Epilogue of the 16 x 16 layout: lane (r, q) of block (i, j) holds outputs
+// i*16 + 4q .. +3 of token j*16 + r. Bias in fp32, one rounding, staged in the
+// wave's 32 KB of LDS as token rows (16-byte chunks XOR-swizzled by row), then
+// written as whole 256-byte output rows, as in the 32 x 32 epilogue.
+template <class P>
+__device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[P::NI][P::NJ], const LinearProblem& p,
+                                               int64_t m0, int64_t n0, int wm0, int wn0, int lane, int wave,
+                                               char* smem) {
+  static_assert(P::WM == 128 && P::WN == 128, "staging written for 128 x 128 wave blocks");
+  const int r = lane & 15, q = lane >> 4;
+  char* st = smem + wave * (128 * 256);
+  const bf16_bits* bias = static_cast<const bf16_bits*>(p.bias);
+#pragma unroll
+  for (int i = 0; i < P::NI; ++i) {
+    const int cl = i * 16 + q * 4;  // first of 4 columns, local to the wave block
+    const int64_t n = n0 + wn0 + cl;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias != nullptr) {
+      if (n + 3 < p.N) {
+        const uint2 w = *reinterpret_cast<const uint2*>(bias + n);  // 8-byte aligned: n is a multiple of 4
+        bv[0] = __uint_as_float(w.x << 16); bv[1] = __uint_as_float(w.x & 0xffff0000u);
+        bv[2] = __uint_as_float(w.y << 16); bv[3] = __uint_as_float(w.y & 0xffff0000u);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.N) bv[e] = bf16_to_f32(bias[n + e]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < P::NJ; ++j) {
+      const int row = j * 16 + r;
+      uint2 w;
+      w.x = pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]);
+      w.y = pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]);
+      const int chunk = (cl >> 3) ^ (row & 15);
+      *reinterpret_cast<uint2*>(st + row * 256 + chunk * 16 + (q & 1) * 8) = w;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keeps accumulator reads from being hoisted (register pressure)
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's staging is complete (only this wave reads it)
+  const int c = lane & 15, rr = lane >> 4;
+  const int64_t n = n0 + wn0 + c * 8;
+  bf16_bits* y = static_cast<bf16_bits*>(p.y);
+  const bool aligned16 = (reinterpret_cast<uintptr_t>(p.y) % 16 == 0) && (p.ldy % 8 == 0);
+#pragma unroll 8
+  for (int it = 0; it < 32; ++it) {
+    const int row = it * 4 + rr;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * 256 + ((c ^ (row & 15)) * 16));
+    const int64_t m = m0 + wm0 + row;
+    if (m < p.T) {
+      bf16_bits* dst = y + m * p.ldy + n;
+      if (aligned16 && n + 7 < p.N) {
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (n + e < p.N) dst[e] = static_cast<bf16_bits>(v[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+}
+
+// Stage t of the 16 x 16 kernel is 128 MFMA bundles (k-step kk = bundle / 64).
+// Copies, one every eighth bundle: the 8 loads of x of stage t + 2 in the
+// first half (its slot was released by the previous stage's barrier), the 8 of
+// W of stage t + 2 in the second (into the slot of x of stage t, released by
+// this stage's barrier at the first bundle of k-step 1). The barrier waits for
+// everything but the x loads of this stage. Fragment reads: k-step 1 of this
+// stage one every fourth bundle of k-step 0, k-step 0 of stage t + 1 one every
+// fourth bundle after the barrier.
+template <class P>
+__global__ __launch_bounds__(P::THREADS) void gemm_flow16_kernel(LinearProblem p, int mt, int nt) {
+  static_assert(P::NI == 8 && P::NJ == 8 && P::WAVES == 4, "schedule written for 4 waves of 8 x 8 blocks");
+  __shared__ __attribute__((aligned(1024))) char smem[P::SLOTS * P::SLOT_BYTES];
+  constexpr int NL = TileOffsets<P, P::BM>::N;  // copy loads per wave per unit
+  static_assert(NL == 8, "copy schedule assumes 8 loads per unit");
+
+  const int G = mt * nt;
+  const int L = xcd_remap(blockIdx.x, G);
+  const int gsize = P::GROUP_M * nt;
+  const int grp = L / gsize;
+  const int first_m = grp * P::GROUP_M;
+  const int gm = min(P::GROUP_M, mt - first_m);
+  const int within = L - grp * gsize;
+  const int m_idx = first_m + within % gm;
+  const int n_idx = within / gm;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm0 = (wave % P::WAVES_M) * P::WM;
+  const int wn0 = (wave / P::WAVES_M) * P::WN;
+  const int64_t m0 = static_cast<int64_t>(m_idx) * P::BM;
+  const int64_t n0 = static_cast<int64_t>(n_idx) * P::BN;
+  const int rows_m = static_cast<int>(min<int64_t>(P::BM, p.T - m0));
+  const int rows_n = static_cast<int>(min<int64_t>(P::BN, p.N - n0));
+
+  const int kb_total = static_cast<int>(p.K * 2);
+  const int nk = (kb_total + P::RB - 1) / P::RB;
+  const bool k_tail = (kb_total % P::RB) != 0;
+  const uint32_t ldx_b = static_cast<uint32_t>(p.ldx * 2), ldw_b = static_cast<uint32_t>(p.K * 2);
+  const __amdgpu_buffer_rsrc_t xr =
+      make_rsrc(static_cast<const char*>(p.x) + m0 * p.ldx * 2, static_cast<uint32_t>(rows_m) * ldx_b);
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(static_cast<const char*>(p.W) + n0 * p.K * 2, static_cast<uint32_t>(rows_n) * ldw_b);
+  TileOffsets<P, P::BM> ox;
+  TileOffsets<P, P::BN> ow;
+  ox.init(ldx_b, 0, rows_m, 0);
+  ow.init(ldw_b, 0, rows_n, 0);
+
+  // K-extension plan of this tile: the (at most two) groups whose columns meet it.
+  const uint32_t ldt_b = static_cast<uint32_t>(p.ldt * 2);
+  int gs0 = p.n_groups, gs1 = p.n_groups;
+  for (int gi = 0; gi < p.n_groups; ++gi) {
+    if (!(p.g[gi].col_off < n0 + rows_n && p.g[gi].col_off + p.g[gi].n_cols > n0)) continue;
+    if (gs0 == p.n_groups) {
+      gs0 = gi;
+    } else {
+      gs1 = gi;
+      break;
+    }
+  }
+  struct ExtGroup {
+    const char* B;
+    int tcb, tpb, rkb, n_cols, lo, hi, sh, ns;
+  };
+  auto ext_group = [&](int gi) {
+    ExtGroup e{nullptr, 0, 0, 0, 0, 0, 0, 0, 0};
+    if (gi < p.n_groups) {
+      const GroupDev& g = p.g[gi];
+      e.B = static_cast<const char*>(g.B);
+      e.tcb = g.t_col * 2;
+      e.tpb = g.r_pad * 2;
+      e.rkb = g.rank * 2;
+      e.n_cols = static_cast<int>(g.n_cols);
+      e.lo = static_cast<int>(max<int64_t>(0, g.col_off - n0));
+      e.hi = static_cast<int>(min<int64_t>(rows_n, g.col_off + g.n_cols - n0));
+      e.sh = static_cast<int>(n0 - g.col_off);
+      e.ns = g.r_pad * 2 / P::RB;
+    }
+    return e;
+  };
+  const ExtGroup eg0 = ext_group(gs0), eg1 = ext_group(gs1);
+  // Stage order: the K-extension stages first, then the main stages (s >= NE is main stage s - NE).
+  const int NE = eg0.ns + eg1.ns;
+  const int NS = NE + nk;
+  const int NU = 2 * NS;
+  const __amdgpu_buffer_rsrc_t tr =
+      make_rsrc(static_cast<const char*>(p.work) + m0 * p.ldt * 2, static_cast<uint32_t>(rows_m) * ldt_b);
+
+  auto slot = [&](int u) { return smem + (u % P::SLOTS) * P::SLOT_BYTES; };
+  auto issue_load = [&](int u, int l) {
+    if (u >= NU) return;
+    char* dst = slot(u);
+    const int s = u >> 1;
+    const bool is_w = (u & 1) != 0;
+    if (s >= NE) {
+      const int kb = (s - NE) * P::RB;
+      if (is_w) dma_one<P, P::BN>(l, dst, wr, ldw_b, 0, rows_n, 0, kb, kb_total);
+      else dma_one<P, P::BM>(l, dst, xr, ldx_b, 0, rows_m, 0, kb, kb_total);
+      return;
+    }
+    const bool second = s >= eg0.ns;
+    const ExtGroup& g = second ? eg1 : eg0;
+    const int e = second ? s - eg0.ns : s;
+    if (!is_w) {
+      dma_one<P, P::BM>(l, dst, tr, ldt_b, 0, rows_m, 0, g.tcb + e * P::RB, g.tcb + g.tpb);
+    } else {
+      const __amdgpu_buffer_rsrc_t br = make_rsrc(g.B, static_cast<uint32_t>(g.n_cols) * static_cast<uint32_t>(g.rkb));
+      dma_one<P, P::BN>(l, dst, br, static_cast<uint32_t>(g.rkb), g.lo, g.hi, g.sh, e * P::RB, g.rkb);
+    }
+  };
+
+  f32x4 acc[P::NI][P::NJ];
+#pragma unroll
+  for (int i = 0; i < P::NI; ++i)
+#pragma unroll
+    for (int j = 0; j < P::NJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
+
+  // prologue: x and W of stages 0 and 1 (units 0 .. 3)
+  if (NE == 0 && nk - (k_tail ? 1 : 0) >= 2) {
+#pragma unroll
+    for (int l = 0; l < NL; ++l) ox.load_one(l, smem, xr, 0);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) ow.load_one(l, smem + P::SLOT_BYTES, wr, 0);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) ox.load_one(l, smem + 2 * P::SLOT_BYTES, xr, P::RB);
+#pragma unroll
+    for (int l = 0; l < NL; ++l) ow.load_one(l, smem + 3 * P::SLOT_BYTES, wr, P::RB);
+  } else {
+    for (int u = 0; u < 4; ++u)
+      for (int l = 0; l < NL; ++l) issue_load(u, l);
+  }
+  if (NU > 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NL));  // stage 0 landed; stage 1 may be in flight
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  stage_barrier();
+  const FragOffsets fo = frag_offsets<P>(wn0, wm0, lane);
+  Frags16<P> fr[2];
+  // fragment q of a k-step, in order of first use: a0, b0 .. b7, a1 .. a7
+  auto read_frag = [&](Frags16<P>& f, int q, const char* xs, const char* ws, int kk) {
+    const uint32_t flip = kk ? 64u : 0u;
+    if (q == 0 || q > P::NJ) {
+      const int ia = q == 0 ? 0 : q - P::NJ;
+      f.a[ia] = *(const bf16x8*)(ws + (fo.w ^ flip) + ia * 2048);
+    } else {
+      f.b[q - 1] = *(const bf16x8*)(xs + (fo.x ^ flip) + (q - 1) * 2048);
+    }
+  };
+#pragma unroll
+  for (int q = 0; q < 16; ++q) read_frag(fr[0], q, slot(0), slot(1), 0);
+
+  // stage t whose copies all belong to main stage t + 2 - NE, which is neither
+  // past the last nor the K-tail stage
+  auto stage = [&](int t, int a) {
+    const int b1 = a == 4 ? 0 : a + 1;           // W of stage t
+    const int a2 = a >= 3 ? a - 3 : a + 2;       // x of stage t + 1
+    const int b2 = a2 == 4 ? 0 : a2 + 1;         // W of stage t + 1
+    const int a3 = b2 == 4 ? 0 : b2 + 1;         // x of stage t + 2
+    const char* xs = smem + a * P::SLOT_BYTES;
+    const char* ws = smem + b1 * P::SLOT_BYTES;
+    const char* xs2 = smem + a2 * P::SLOT_BYTES;
+    const char* ws2 = smem + b2 * P::SLOT_BYTES;
+    const int kb2 = (t + 2 - NE) * P::RB;
+    char* const xdst = smem + a3 * P::SLOT_BYTES;
+    char* const wdst = smem + a * P::SLOT_BYTES;
+    // (two loops of 64 bundles: one loop of 128 is past the compiler's full-unroll limit)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < 64; ++m) {  // k-step 0
+      acc[m >> 3][m & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0].a[m >> 3], fr[0].b[m & 7], acc[m >> 3][m & 7], 0, 0, 0);
+      if ((m & 3) == 0) read_frag(fr[1], m >> 2, xs, ws, 1);
+      if ((m & 7) == 4) ox.load_one(m >> 3, xdst, xr, kb2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int m = 0; m < 64; ++m) {  // k-step 1
+      acc[m >> 3][m & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[1].a[m >> 3], fr[1].b[m & 7], acc[m >> 3][m & 7], 0, 0, 0);
+      if (m == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));  // x of stage t + 2 may still be in flight
+        stage_barrier();  // stage t + 1 landed and visible; every wave is done reading stage t
+      } else if ((m & 3) == 1) {
+        read_frag(fr[0], m >> 2, xs2, ws2, 0);
+      }
+      if ((m & 7) == 4) ow.load_one(m >> 3, wdst, wr, kb2);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // The generic stage: same copies as a fast stage, issued in bulk, with
+  // compiler-scheduled MFMA steps (stages whose copies are K-extension units).
+  auto generic_stage = [&](int t, int a) {
+    const int b1 = a == 4 ? 0 : a + 1;
+    const int a2 = a >= 3 ? a - 3 : a + 2;
+    const int b2 = a2 == 4 ? 0 : a2 + 1;
+    const char* xs = smem + a * P::SLOT_BYTES;
+    const char* ws = smem + b1 * P::SLOT_BYTES;
+    for (int l = 0; l < NL; ++l) issue_load(2 * t + 4, l);
+    ring_frags16<P>(fr[1], xs, ws, 1, fo);
+    mfma_frags16<P>(acc, fr[0]);
+    if (2 * t + 4 < NU) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    stage_barrier();  // stage t + 1 landed and visible; every wave is done reading stage t
+    for (int l = 0; l < NL; ++l) issue_load(2 * t + 5, l);
+    ring_frags16<P>(fr[0], smem + a2 * P::SLOT_BYTES, smem + b2 * P::SLOT_BYTES, 0, fo);
+    mfma_frags16<P>(acc, fr[1]);
+  };
+
+  // The last stages: their copies (if any) are whole main units, one of them
+  // possibly the K-tail stage, so they go through the precomputed offsets.
+  auto main_unit = [&](int u) {
+    if (u >= NU) return;
+    const int kb = ((u >> 1) - NE) * P::RB;
+    const bool tl = k_tail && (u >> 1) == NS - 1;
+    if (u & 1) ow.load(slot(u), wr, kb, tl, kb_total);
+    else ox.load(slot(u), xr, kb, tl, kb_total);
+  };
+  auto tail_stage = [&](int t, int a) {
+    const int b1 = a == 4 ? 0 : a + 1;
+    const int a2 = a >= 3 ? a - 3 : a + 2;
+    const int b2 = a2 == 4 ? 0 : a2 + 1;
+    const char* xs = smem + a * P::SLOT_BYTES;
+    const char* ws = smem + b1 * P::SLOT_BYTES;
+    main_unit(2 * t + 4);
+    ring_frags16<P>(fr[1], xs, ws, 1, fo);
+    mfma_frags16<P>(acc, fr[0]);
+    if (2 * t + 4 < NU) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    stage_barrier();  // stage t + 1 landed and visible; every wave is done reading stage t
+    main_unit(2 * t + 5);
+    ring_frags16<P>(fr[0], smem + a2 * P::SLOT_BYTES, smem + b2 * P::SLOT_BYTES, 0, fo);
+    mfma_frags16<P>(acc, fr[1]);
+  };
+
+  // stages t < t_first copy K-extension units (generic path); stages from
+  // t_end on copy the last main units or nothing
+  const int t_first = NE > 2 ? NE - 2 : 0;
+  const int t_end = NE + nk - 2 - (k_tail ? 1 : 0);
+  int a = 0;  // slot of x of stage t
+  int t = 0;
+  for (; t < t_first && t + 1 < NS; ++t) {
+    generic_stage(t, a);
+    a = a >= 3 ? a - 3 : a + 2;
+  }
+  for (; t < t_end && t + 1 < NS; ++t) {
+    stage(t, a);
+    a = a >= 3 ? a - 3 : a + 2;
+  }
+  for (; t + 1 < NS; ++t) {
+    tail_stage(t, a);
+    a = a >= 3 ? a - 3 : a + 2;
+  }
+  {  // last stage: no refill, no barrier
+    const char* xs = smem + a * P::SLOT_BYTES;
+    const char* ws = smem + (a == 4 ? 0 : a + 1) * P::SLOT_BYTES;
+    ring_frags16<P>(fr[1], xs, ws, 1, fo);
+    mfma_frags16<P>(acc, fr[0]);
+    mfma_frags16<P>(acc, fr[1]);
+  }
+
+  __syncthreads();  // every wave is done reading the ring; LDS becomes the staging area
+  epilogue_lds16<P>(acc, p, m0, n0, wm0, wn0, lane, wave, smem);
+}
+
+template <class P>
+hipError_t launch_flow16(const LinearProblem& p, hipStream_t s) {
+  const int mt = static_cast<int>((p.T + P::BM - 1) / P::BM);
+  const int nt = static_cast<int>((p.N + P::BN - 1) / P::BN);
+  hipLaunchKernelGGL(gemm_flow16_kernel<P>, dim3(mt * nt), dim3(P::THREADS), 0, s, p, mt, nt);
+  return hipGetLastError();
+}
+
 // General pipelined kernel (used when more than two adapter groups meet one tile).
 using HotCfg = PCfg<256, 256, 64, 128, 64, 4>;
 using FlowCfg = RCfg<256, 256, 128, 128, 128, 5>;
+using Flow16Cfg = QCfg<256, 256, 128, 128, 128, 5>;
 
 // Largest number of adapter groups whose columns meet one BN-wide output tile.
 int max_groups_per_tile(const LinearProblem& p, int bn) {
@@ -1214,7 +1611,7 @@ int max_groups_per_tile(const LinearProblem& p, int bn) {
 }
 
 hipError_t launch(const LinearProblem& p, hipStream_t s) {
-  if (max_groups_per_tile(p, FlowCfg::BN) <= 2) return launch_flow<FlowCfg>(p, s);
+  if (max_groups_per_tile(p, Flow16Cfg::BN) <= 2) return launch_flow16<Flow16Cfg>(p, s);
   using P = HotCfg;
   const int mt = static_cast<int>((p.T + P::BM - 1) / P::BM);
   const int nt = static_cast<int>((p.N + P::BN - 1) / P::BN);
