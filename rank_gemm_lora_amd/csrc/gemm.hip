@@ -1259,23 +1259,21 @@ __device__ __forceinline__ void mfma_frags16(f32x4 (&acc)[P::NI][P::NJ], const F
 }
 
 // Epilogue of the 16 x 16 layout: lane (r, q) of block (i, j) holds outputs
-// i*16 + 4q .. +3 of token j*16 + r. Bias in fp32, one rounding, staged in the
-// wave's 32 KB of LDS as token rows (16-byte chunks XOR-swizzled by row), then
-// written as whole 256-byte output rows, as in the 32 x 32 epilogue.
-template <class P>
-__device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[P::NI][P::NJ], const LinearProblem& p,
-                                               int64_t m0, int64_t n0, int wm0, int wn0, int lane, int wave,
-                                               char* smem) {
-  static_assert(P::WM == 128 && P::WN == 128, "staging written for 128 x 128 wave blocks");
+// i*16 + 4q .. +3 of token j*16 + r. Bias in fp32 (no add without a bias), one
+// rounding, staged in the wave's 32 KB of LDS as token rows (16-byte chunks
+// XOR-swizzled by row), then written as whole 256-byte output rows, as in the
+// 32 x 32 epilogue.
+template <class P, bool BIAS>
+__device__ __forceinline__ void stage_out16(const f32x4 (&acc)[P::NI][P::NJ], const LinearProblem& p, int64_t n0,
+                                            int wn0, int lane, char* st) {
   const int r = lane & 15, q = lane >> 4;
-  char* st = smem + wave * (128 * 256);
   const bf16_bits* bias = static_cast<const bf16_bits*>(p.bias);
 #pragma unroll
   for (int i = 0; i < P::NI; ++i) {
     const int cl = i * 16 + q * 4;  // first of 4 columns, local to the wave block
-    const int64_t n = n0 + wn0 + cl;
     float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (bias != nullptr) {
+    if (BIAS) {
+      const int64_t n = n0 + wn0 + cl;
       if (n + 3 < p.N) {
         const uint2 w = *reinterpret_cast<const uint2*>(bias + n);  // 8-byte aligned: n is a multiple of 4
         bv[0] = __uint_as_float(w.x << 16); bv[1] = __uint_as_float(w.x & 0xffff0000u);
@@ -1290,23 +1288,55 @@ __device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[P::NI][P::NJ],
     for (int j = 0; j < P::NJ; ++j) {
       const int row = j * 16 + r;
       uint2 w;
-      w.x = pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]);
-      w.y = pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]);
+      if (BIAS) {
+        w.x = pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]);
+        w.y = pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]);
+      } else {
+        w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+      }
       const int chunk = (cl >> 3) ^ (row & 15);
       *reinterpret_cast<uint2*>(st + row * 256 + chunk * 16 + (q & 1) * 8) = w;
     }
     __builtin_amdgcn_sched_barrier(0);  // keeps accumulator reads from being hoisted (register pressure)
   }
+}
+
+template <class P>
+__device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[P::NI][P::NJ], const LinearProblem& p,
+                                               int64_t m0, int64_t n0, int wm0, int wn0, int lane, int wave,
+                                               char* smem) {
+  static_assert(P::WM == 128 && P::WN == 128, "staging written for 128 x 128 wave blocks");
+  char* st = smem + wave * (128 * 256);
+  if (p.bias != nullptr) stage_out16<P, true>(acc, p, n0, wn0, lane, st);
+  else stage_out16<P, false>(acc, p, n0, wn0, lane, st);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's staging is complete (only this wave reads it)
   const int c = lane & 15, rr = lane >> 4;
+  const int64_t mb = m0 + wm0;  // first token of the wave block
   const int64_t n = n0 + wn0 + c * 8;
   bf16_bits* y = static_cast<bf16_bits*>(p.y);
   const bool aligned16 = (reinterpret_cast<uintptr_t>(p.y) % 16 == 0) && (p.ldy % 8 == 0);
+  if (aligned16 && n0 + wn0 + 128 <= p.N) {
+    // all 128 columns exist: buffer stores over the block's valid rows; a row past
+    // T has its offset (in the per-lane offset, which the range check covers)
+    // beyond the range and is dropped
+    const int64_t rows = min<int64_t>(128, p.T - mb);
+    if (rows <= 0) return;
+    const uint32_t ldb = static_cast<uint32_t>(p.ldy * 2);
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y + mb * p.ldy + n0 + wn0, static_cast<uint32_t>(rows) * ldb);
+#pragma unroll 8
+    for (int it = 0; it < 32; ++it) {
+      const int row = it * 4 + rr;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * 256 + ((c ^ (row & 15)) * 16));
+      __builtin_amdgcn_raw_buffer_store_b128(v, yr, static_cast<uint32_t>(row) * ldb + static_cast<uint32_t>(c) * 16, 0, 0);
+    }
+    return;
+  }
 #pragma unroll 8
   for (int it = 0; it < 32; ++it) {
     const int row = it * 4 + rr;
     const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * 256 + ((c ^ (row & 15)) * 16));
-    const int64_t m = m0 + wm0 + row;
+    const int64_t m = mb + row;
     if (m < p.T) {
       bf16_bits* dst = y + m * p.ldy + n;
       if (aligned16 && n + 7 < p.N) {
@@ -1318,6 +1348,28 @@ __device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[P::NI][P::NJ],
       }
     }
   }
+}
+
+// K-extension plan of one adapter group for one output tile: where its t~
+// columns and B rows are, which tile rows its B rows cover, and how many
+// 64-k stages its padded rank takes.
+struct ExtPlan {
+  const char* B;
+  int tcb, tpb, rkb, n_cols, lo, hi, sh, ns;
+};
+
+// Copies of K-extension stage e of group g through precomputed per-lane
+// offsets: t~ rows (every padded column exists) into xdst, B rows (chunks past
+// the rank read as zero) into wdst.
+template <class P>
+__device__ __forceinline__ void ext_stage_loads(const ExtPlan& g, int e, const TileOffsets<P, P::BM>& ot,
+                                                __amdgpu_buffer_rsrc_t tr, char* xdst, char* wdst) {
+#pragma unroll
+  for (int l = 0; l < TileOffsets<P, P::BM>::N; ++l) ot.load_one(l, xdst, tr, g.tcb + e * P::RB);
+  TileOffsets<P, P::BN> ob;
+  ob.init(static_cast<uint32_t>(g.rkb), g.lo, g.hi, g.sh);
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(g.B, static_cast<uint32_t>(g.n_cols) * static_cast<uint32_t>(g.rkb));
+  ob.load(wdst, br, e * P::RB, (e + 1) * P::RB > g.rkb, g.rkb);
 }
 
 // Stage t of the 16 x 16 kernel is 128 MFMA bundles (k-step kk = bundle / 64).
@@ -1378,12 +1430,8 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow16_kernel(LinearProblem p
       break;
     }
   }
-  struct ExtGroup {
-    const char* B;
-    int tcb, tpb, rkb, n_cols, lo, hi, sh, ns;
-  };
   auto ext_group = [&](int gi) {
-    ExtGroup e{nullptr, 0, 0, 0, 0, 0, 0, 0, 0};
+    ExtPlan e{nullptr, 0, 0, 0, 0, 0, 0, 0, 0};
     if (gi < p.n_groups) {
       const GroupDev& g = p.g[gi];
       e.B = static_cast<const char*>(g.B);
@@ -1398,7 +1446,7 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow16_kernel(LinearProblem p
     }
     return e;
   };
-  const ExtGroup eg0 = ext_group(gs0), eg1 = ext_group(gs1);
+  const ExtPlan eg0 = ext_group(gs0), eg1 = ext_group(gs1);
   // Stage order: the K-extension stages first, then the main stages (s >= NE is main stage s - NE).
   const int NE = eg0.ns + eg1.ns;
   const int NS = NE + nk;
@@ -1419,7 +1467,7 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow16_kernel(LinearProblem p
       return;
     }
     const bool second = s >= eg0.ns;
-    const ExtGroup& g = second ? eg1 : eg0;
+    const ExtPlan& g = second ? eg1 : eg0;
     const int e = second ? s - eg0.ns : s;
     if (!is_w) {
       dma_one<P, P::BM>(l, dst, tr, ldt_b, 0, rows_m, 0, g.tcb + e * P::RB, g.tcb + g.tpb);
@@ -1437,7 +1485,9 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow16_kernel(LinearProblem p
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
 
-  // prologue: x and W of stages 0 and 1 (units 0 .. 3)
+  // prologue: units 0 .. 3 (stages 0 and 1). Up to two K-extension stages (ranks
+  // up to 128) use precomputed per-lane offsets like the main stages; more
+  // extension stages take the generic path.
   if (NE == 0 && nk - (k_tail ? 1 : 0) >= 2) {
 #pragma unroll
     for (int l = 0; l < NL; ++l) ox.load_one(l, smem, xr, 0);
@@ -1447,6 +1497,19 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow16_kernel(LinearProblem p
     for (int l = 0; l < NL; ++l) ox.load_one(l, smem + 2 * P::SLOT_BYTES, xr, P::RB);
 #pragma unroll
     for (int l = 0; l < NL; ++l) ow.load_one(l, smem + 3 * P::SLOT_BYTES, wr, P::RB);
+  } else if (NE == 1 || NE == 2) {
+    TileOffsets<P, P::BM> ot;
+    ot.init(ldt_b, 0, rows_m, 0);
+    ext_stage_loads<P>(eg0, 0, ot, tr, smem, smem + P::SLOT_BYTES);
+    if (NE == 1) {  // main stage 0 (it is the K-tail stage when K < 64)
+      const bool tail0 = k_tail && nk == 1;
+      ox.load(smem + 2 * P::SLOT_BYTES, xr, 0, tail0, kb_total);
+      ow.load(smem + 3 * P::SLOT_BYTES, wr, 0, tail0, kb_total);
+    } else if (eg0.ns == 2) {
+      ext_stage_loads<P>(eg0, 1, ot, tr, smem + 2 * P::SLOT_BYTES, smem + 3 * P::SLOT_BYTES);
+    } else {
+      ext_stage_loads<P>(eg1, 0, ot, tr, smem + 2 * P::SLOT_BYTES, smem + 3 * P::SLOT_BYTES);
+    }
   } else {
     for (int u = 0; u < 4; ++u)
       for (int l = 0; l < NL; ++l) issue_load(u, l);
