@@ -14,6 +14,7 @@ timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -47,9 +48,11 @@ def layer_flops(T, K, N, r):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the per-config measurements of the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters) and exit")
@@ -213,13 +216,20 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(layers, args.cpu_seconds)
 
+    # ---------------- every other workload: fused time, base time, roofline, oracle beside it
+    layer_cfg = [{"in": L["K"], "out": L["N"], "rank": L["r"], "bias": L["d"]["b"] is not None} for L in layers]
+    configs = None
+    if not args.headline_only:
+        del layers, L, d
+        torch.cuda.empty_cache()
+        configs = config_sweep(torch, dev, stream, with_oracle=not args.no_cpu_baseline)
+
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "ffn_pair_tokens32760_rank64", "tokens": 32760,
-                   "layers": [{"in": L["K"], "out": L["N"], "rank": L["r"], "bias": L["d"]["b"] is not None}
-                              for L in layers],
+                   "layers": layer_cfg,
                    "alpha": 64.0, "strength": 1.0, "request_scale": 0.7, "quality": "lossless"},
         "overhead_vs_base": round(overhead, 4),
         "base_ms": round(base_ms, 4),
@@ -227,8 +237,201 @@ def main():
         "pct_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "configs": configs,
     }
     print(json.dumps(out), flush=True)
+
+
+def _launch_stats(torch, stream, fn, n=100, warm=10):
+    """Median, p10 and p90 (ms) of n launches of fn, each between its own pair of events."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"median": round(t[n // 2], 5), "p10": round(t[n // 10], 5), "p90": round(t[(9 * n) // 10], 5)}
+
+
+def _gemm_entry(flops, ms, base_own, base_torch, bytes_alg):
+    """TFLOP/s, share of the bf16 MFMA peak and overhead over the faster base path."""
+    tf = flops / (ms["median"] * 1e-3) / 1e12
+    base = min(b for b in (base_own, base_torch) if b is not None)
+    return {"tflops": round(tf, 1), "pct_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "ms": ms, "base_ms": {"own": base_own, "torch": base_torch},
+            "overhead_vs_base": round(ms["median"] / base - 1.0, 4), "bound": "mfma",
+            "algorithmic_flop": flops, "algorithmic_bytes": bytes_alg}
+
+
+def config_sweep(torch, dev, stream, with_oracle=True):
+    """The other workloads of the method at their full sizes, each timed over 100 launches
+    (median, p10, p90): attention projection, stacked q/k/v (bf16 and fp32 adapters), the
+    4-bit layer, the dense patches and the tiny fp32 layer. FLOPs count what the method
+    computes (2 T (K N + K r + r N) per adapter layer), bytes each tensor once."""
+    import lora_workloads as lw
+    import rank_gemm_lora_amd as rg
+    F = torch.nn.functional
+    out = {}
+
+    def d2(t):
+        return None if t is None else t.to(dev)
+
+    def linear_case(spec, tag):
+        h = lw.linear_inputs(spec)
+        x, W, b, A, B = (d2(h[k]) for k in ("x", "W", "b", "A", "B"))
+        T, K, N, r = spec.T, spec.K, spec.N, spec.rank
+        y = torch.empty((T, N), dtype=x.dtype, device=dev)
+        adt = rg.LORA_F32 if spec.adapter == "f32" else rg.LORA_BF16
+        ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, [r], adt)), dtype=torch.uint8, device=dev)
+        fused = _launch_stats(torch, stream, lambda: rg.lora_linear(x, W, b, A, B, spec.alpha, spec.strength,
+                                                                     spec.request_scale, out=y, workspace=ws))
+        own = _launch_stats(torch, stream, lambda: rg.lora_linear(x, W, b, None, None, spec.alpha, out=y,
+                                                                   workspace=ws))["median"]
+        tor = _launch_stats(torch, stream, lambda: F.linear(x, W, b))["median"]
+        esz = x.element_size()
+        byt = esz * (T * K + N * K + T * N + (N if b is not None else 0)) + A.element_size() * r * (K + N)
+        e = _gemm_entry(2.0 * T * (K * N + K * r + r * N), fused, own, tor, byt)
+        e["workload"] = f"{tag}: T={T} K={K} N={N} r={r} {spec.act}/{spec.adapter}"
+        if with_oracle:
+            e["cpu_oracle"] = _oracle_time(lambda: _oracle_linear(h, spec), e["algorithmic_flop"])
+        return e
+
+    out["attn_proj"] = linear_case(lw.ATTN_PROJ, "attention projection")
+    torch.cuda.empty_cache()
+
+    for adapter in ("bf16", "f32"):
+        spec = lw.QKV_STACKED if adapter == "bf16" else dataclasses.replace(lw.QKV_STACKED, adapter="f32",
+                                                                           name="qkv_stacked_f32")
+        h = lw.stacked_inputs(spec)
+        x, W, b = d2(h["x"]), d2(h["W"]), d2(h["b"])
+        groups = [dict(g, A=d2(g["A"]), B=d2(g["B"])) for g in h["groups"]]
+        T, K = spec.T, spec.K
+        Nt = sum(spec.n_cols)
+        y = torch.empty((T, Nt), dtype=x.dtype, device=dev)
+        adt = rg.LORA_F32 if adapter == "f32" else rg.LORA_BF16
+        ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, list(spec.ranks), adt)), dtype=torch.uint8,
+                         device=dev)
+        fused = _launch_stats(torch, stream, lambda: rg.lora_linear_stacked(x, W, b, groups, spec.strength,
+                                                                             spec.request_scale, out=y, workspace=ws))
+        own = _launch_stats(torch, stream, lambda: rg.lora_linear(x, W, b, None, None, 1.0, out=y,
+                                                                   workspace=ws))["median"]
+        tor = _launch_stats(torch, stream, lambda: F.linear(x, W, b))["median"]
+        fl = 2.0 * T * (K * Nt + sum(r * (K + n) for r, n in zip(spec.ranks, spec.n_cols)))
+        esz = 4 if adapter == "f32" else 2
+        byt = 2 * (T * K + Nt * K + T * Nt) + esz * sum(r * (K + n) for r, n in zip(spec.ranks, spec.n_cols))
+        e = _gemm_entry(fl, fused, own, tor, byt)
+        e["workload"] = f"stacked q/k/v: T={T} K={K} N=3x3072 r=3x128 bf16/{adapter}"
+        if adapter == "f32":
+            e["note"] = "the adapter part runs on fp32 MFMA (157 TFLOP/s peak)"
+        if with_oracle:
+            e["cpu_oracle"] = _oracle_time(lambda: _oracle_stacked(h, spec), fl)
+        out["qkv_stacked_" + adapter] = e
+        del x, W, b, groups, y, ws, h
+        torch.cuda.empty_cache()
+
+    spec = lw.NF4_LAYER
+    h = lw.nf4_inputs(spec)
+    x, codes, absmax, cb, A, B, b = (d2(h[k]) for k in ("x", "codes", "absmax", "codebook", "A", "B", "b"))
+    T, K, N, r = spec.T, spec.K, spec.N, spec.rank
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, [r], rg.LORA_BF16)), dtype=torch.uint8, device=dev)
+    fused = _launch_stats(torch, stream, lambda: rg.lora_linear_nf4(x, codes, absmax, cb, N, b, A, B, spec.alpha,
+                                                                     out=y, workspace=ws))
+    own = _launch_stats(torch, stream, lambda: rg.lora_linear_nf4(x, codes, absmax, cb, N, b, None, None,
+                                                                   spec.alpha, out=y, workspace=ws))["median"]
+    # hipBLASLt on the same GEMM with the weight already dequantized to bf16 (plain torch ops)
+    c = codes.to(torch.int64)
+    idx = torch.stack((c & 15, c >> 4), dim=-1).reshape(N, K)
+    W_deq = (cb[idx] * absmax.repeat_interleave(spec.blocksize).reshape(N, K)).to(torch.bfloat16)
+    del c, idx
+    tor = _launch_stats(torch, stream, lambda: F.linear(x, W_deq, b))["median"]
+    byt = 2 * (T * K + T * N) + N * K // 2 + 4 * (N * K // spec.blocksize) + 2 * r * (K + N)
+    e = _gemm_entry(2.0 * T * (K * N + K * r + r * N), fused, own, None, byt)
+    e["workload"] = f"4-bit weight: T={T} K={K} N={N} r={r}, codebook + fp32 absmax per 64"
+    e["bf16_hipblaslt_ms"] = tor
+    e["note"] = ("overhead against the 4-bit base path (torch has no 4-bit GEMM); bf16_hipblaslt_ms: "
+                 "hipBLASLt on the same GEMM with the weight dequantized to bf16 beforehand, for context")
+    if with_oracle:
+        e["cpu_oracle"] = _oracle_time(lambda: _oracle_nf4(h, spec), e["algorithmic_flop"])
+    out["nf4_layer"] = e
+    del x, codes, absmax, cb, A, B, b, y, ws, W_deq
+    torch.cuda.empty_cache()
+
+    for spec in (lw.PATCH_WEIGHT, lw.PATCH_NORM):
+        h = lw.patch_inputs(spec)
+        dst, diff = d2(h["dst"]), d2(h["diff"])
+        n = dst.numel()
+        for mode in ("add", "replace"):
+            ms = _launch_stats(torch, stream, lambda: rg.dense_patch(dst, diff, spec.strength, mode))
+            byt = (3 if mode == "add" else 2) * n * 2
+            gbs = byt / (ms["median"] * 1e-3) / 1e9
+            e = {"workload": f"dense patch {mode}: shape={list(spec.shape)} bf16", "ms": ms,
+                 "bound": "hbm" if n > 1 << 20 else "launch latency", "achieved_gbs": round(gbs, 1),
+                 "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": byt}
+            if with_oracle and mode == "add":
+                e["cpu_oracle"] = _oracle_time(lambda: _oracle_patch(h, spec), None, byt)
+            out[f"{spec.name}_{mode}"] = e
+        del dst, diff, h
+        torch.cuda.empty_cache()
+
+    spec = lw.TINY_FP32
+    h = lw.linear_inputs(spec)
+    x, W, b, A, B = (d2(h[k]) for k in ("x", "W", "b", "A", "B"))
+    y = torch.empty((spec.T, spec.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, rg.lora_linear_workspace_size(spec.T, [spec.rank], rg.LORA_F32)), dtype=torch.uint8,
+                     device=dev)
+    ms = _launch_stats(torch, stream, lambda: rg.lora_linear(x, W, b, A, B, spec.alpha, out=y, workspace=ws))
+    out["tiny_fp32"] = {"workload": "tiny fp32: T=64 K=128 N=96 r=8", "ms": ms, "bound": "launch latency",
+                        "note": "back-to-back calls from Python: the figure is mostly the host's time per call"}
+    return out
+
+
+def _oracle_time(fn, flops, nbytes=None):
+    """Wall time of one oracle call on the host (numpy float64, threaded BLAS)."""
+    t = time.perf_counter()
+    fn()
+    dt = time.perf_counter() - t
+    r = {"seconds": round(dt, 3), "threads": _blas_threads()}
+    if flops:
+        r["tflops"] = round(flops / dt / 1e12, 4)
+    if nbytes:
+        r["gbs"] = round(nbytes / dt / 1e9, 2)
+    return r
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"),
+                   default=len(os.sched_getaffinity(0)))
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def _oracle_linear(h, spec):
+    from oracle import lora_oracle as lo
+    return lo.lora_linear(h["x"], h["W"], h["b"], h["A"], h["B"], spec.alpha, spec.rank, spec.strength,
+                          spec.request_scale)
+
+
+def _oracle_stacked(h, spec):
+    from oracle import lora_oracle as lo
+    return lo.lora_linear_stacked(h["x"], h["W"], h["b"], h["groups"], spec.strength, spec.request_scale)
+
+
+def _oracle_nf4(h, spec):
+    from oracle import lora_oracle as lo
+    return lo.lora_linear_nf4(h["x"], h["codes"], h["absmax"], h["codebook"], spec.blocksize, h["b"], h["A"],
+                              h["B"], spec.alpha, spec.rank, spec.strength, spec.request_scale)
+
+
+def _oracle_patch(h, spec):
+    from oracle import lora_oracle as lo
+    return lo.dense_patch(h["dst"], h["diff"], spec.strength, "add")
 
 
 def _counter_means(csv_path, counter):

@@ -218,6 +218,47 @@ def test_column_view_output_with_wider_ldy():
         assert bool((wide[:, :64] == 7.0).all()) and bool((wide[:, 264:] == 7.0).all())
 
 
+# ------------------------------------------------------------------ more tiles than compute units
+# Launches of several waves of output tiles (one adapter over all columns, or
+# none), against launches small enough for one wave, bitwise, and against the
+# oracle. Ragged T and N, K tails, 1, 2 and 4 K-extension stages.
+
+@pytest.mark.parametrize("T,K,N,r,bias", [(2600, 200, 13000, 24, True), (2600, 512, 6000, 100, False),
+                                          (1100, 256, 16000, 200, True), (2600, 320, 6000, 0, True)])
+def test_more_tiles_than_compute_units(T, K, N, r, bias):
+    rank = max(r, 1)
+    d = lw.small_linear_inputs(T, K, N, rank, 40 + r, bias=bias, alpha=2.0 * rank, strength=0.9,
+                               request_scale=0.7)
+    say(f"case many tiles T={T} K={K} N={N} r={r} bias={bias}")
+    x, W, b = dev(d["x"]), dev(d["W"]), dev(d["b"])
+    A, B = (dev(d["A"]), dev(d["B"])) if r else (None, None)
+    y = rg.lora_linear(x, W, b, A, B, d["alpha"], 0.9, 0.7)
+    torch.cuda.synchronize()
+    rows = min(T, 256 * (256 // -(-N // 256)))  # whole tile rows of a launch with at most 256 tiles
+    y_few = rg.lora_linear(x[:rows].contiguous(), W, b, A, B, d["alpha"], 0.9, 0.7)
+    torch.cuda.synchronize()
+    assert torch.equal(y[:rows], y_few), "a launch of several tile waves and one of a single wave differ"
+    if r:
+        y64, yc = oracle_pair(d, strength=0.9, request_scale=0.7)
+    else:
+        y64 = lo.lora_linear(d["x"], d["W"], d["b"], None, None, d["alpha"], rank, 0.9, 0.7)
+        yc = None
+    assert_gate(y, y64, yc, what="many tiles")
+
+
+def test_many_tiles_unaligned_column_view():
+    d = lw.small_linear_inputs(2600, 192, 6000, 64, 47, bias=True, alpha=64.0)
+    say("case many tiles, unaligned column view")
+    x, W, b, A, B = (dev(d[k]) for k in ("x", "W", "b", "A", "B"))
+    wide = torch.full((2600, 6011), 5.0, dtype=torch.bfloat16, device=DEV)
+    view = wide[:, 3:6003]
+    rg.lora_linear(x, W, b, A, B, 64.0, out=view)
+    ref = rg.lora_linear(x, W, b, A, B, 64.0)
+    torch.cuda.synchronize()
+    assert torch.equal(view, ref)
+    assert bool((wide[:, :3] == 5.0).all()) and bool((wide[:, 6003:] == 5.0).all())
+
+
 # ------------------------------------------------------------------ goldens through the exact tier
 
 def _hex(v):
