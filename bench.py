@@ -97,7 +97,7 @@ def main():
         d = {k: (v.to(dev) if hasattr(v, "to") else v) for k, v in h.items()}
         T, K, N, r = spec.T, spec.K, spec.N, spec.rank
         y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, [r], rg.LORA_BF16)), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, K, N, [r], rg.LORA_BF16)), dtype=torch.uint8, device=dev)
         layers.append(dict(spec=spec, d=d, y=y, ws=ws, T=T, K=K, N=N, r=r))
     del up_h, down_h
     stream = torch.cuda.current_stream()
@@ -286,7 +286,7 @@ def config_sweep(torch, dev, stream, with_oracle=True):
         T, K, N, r = spec.T, spec.K, spec.N, spec.rank
         y = torch.empty((T, N), dtype=x.dtype, device=dev)
         adt = rg.LORA_F32 if spec.adapter == "f32" else rg.LORA_BF16
-        ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, [r], adt)), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, K, N, [r], adt)), dtype=torch.uint8, device=dev)
         fused = _launch_stats(torch, stream, lambda: rg.lora_linear(x, W, b, A, B, spec.alpha, spec.strength,
                                                                      spec.request_scale, out=y, workspace=ws))
         own = _launch_stats(torch, stream, lambda: rg.lora_linear(x, W, b, None, None, spec.alpha, out=y,
@@ -313,7 +313,7 @@ def config_sweep(torch, dev, stream, with_oracle=True):
         Nt = sum(spec.n_cols)
         y = torch.empty((T, Nt), dtype=x.dtype, device=dev)
         adt = rg.LORA_F32 if adapter == "f32" else rg.LORA_BF16
-        ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, list(spec.ranks), adt)), dtype=torch.uint8,
+        ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, K, Nt, list(spec.ranks), adt)), dtype=torch.uint8,
                          device=dev)
         fused = _launch_stats(torch, stream, lambda: rg.lora_linear_stacked(x, W, b, groups, spec.strength,
                                                                              spec.request_scale, out=y, workspace=ws))
@@ -338,7 +338,7 @@ def config_sweep(torch, dev, stream, with_oracle=True):
     x, codes, absmax, cb, A, B, b = (d2(h[k]) for k in ("x", "codes", "absmax", "codebook", "A", "B", "b"))
     T, K, N, r = spec.T, spec.K, spec.N, spec.rank
     y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, [r], rg.LORA_BF16)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, K, N, [r], rg.LORA_BF16)), dtype=torch.uint8, device=dev)
     fused = _launch_stats(torch, stream, lambda: rg.lora_linear_nf4(x, codes, absmax, cb, N, b, A, B, spec.alpha,
                                                                      out=y, workspace=ws))
     own = _launch_stats(torch, stream, lambda: rg.lora_linear_nf4(x, codes, absmax, cb, N, b, None, None,
@@ -382,7 +382,7 @@ def config_sweep(torch, dev, stream, with_oracle=True):
     h = lw.linear_inputs(spec)
     x, W, b, A, B = (d2(h[k]) for k in ("x", "W", "b", "A", "B"))
     y = torch.empty((spec.T, spec.N), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(1, rg.lora_linear_workspace_size(spec.T, [spec.rank], rg.LORA_F32)), dtype=torch.uint8,
+    ws = torch.empty(max(1, rg.lora_linear_workspace_size(spec.T, spec.K, spec.N, [spec.rank], rg.LORA_F32)), dtype=torch.uint8,
                      device=dev)
     ms = _launch_stats(torch, stream, lambda: rg.lora_linear(x, W, b, A, B, spec.alpha, out=y, workspace=ws))
     out["tiny_fp32"] = {"workload": "tiny fp32: T=64 K=128 N=96 r=8", "ms": ms, "bound": "launch latency",

@@ -119,7 +119,7 @@ typedef struct lora_group {
  *   y        [T, N] act_dtype, row stride ldy >= N; must not overlap any input
  *   act_dtype     LORA_BF16 (adapter LORA_BF16 or LORA_F32), or LORA_F32 (adapter LORA_F32)
  *   quality       LORA_LOSSLESS or LORA_EXACT
- *   workspace     device scratch of at least lora_linear_workspace_size(T, &rank, 1, ...)
+ *   workspace     device scratch of at least lora_linear_workspace_size(T, K, N, &rank, 1, ...)
  *                 bytes (may be NULL when that size is 0); its contents are not
  *                 preserved between calls
  * T == 0 is a valid no-op.
@@ -161,7 +161,8 @@ int lora_linear_fwd_phase(int32_t phase, const void* x, int64_t T, int64_t K, in
  *
  *   groups    HOST array of n_groups lora_group (0 <= n_groups <= LORA_MAX_GROUPS);
  *             the A/B pointers inside are device pointers
- *   workspace at least lora_linear_workspace_size(T, ranks of the groups, n_groups, ...) bytes
+ *   workspace at least lora_linear_workspace_size(T, K, N_total, ranks of the groups, n_groups, ...)
+ *             bytes
  * Other arguments as lora_linear_fwd.
  */
 int lora_linear_stacked_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
@@ -214,14 +215,19 @@ int dense_patch_apply(void* dst, int32_t dst_dtype, const int64_t* dst_shape, in
                       double strength, int32_t mode, void* stream);
 
 /*
- * Workspace bytes a call with T tokens needs for adapters of the given ranks
- * (`ranks` is a HOST array of n_ranks entries: one for lora_linear_fwd and
- * lora_linear_nf4_fwd, one per group for lora_linear_stacked_fwd). It holds the
- * rank-wide intermediate [T, sum of ranks rounded up to multiples of 64] in the
- * adapter dtype. Returns 0 when no rank is positive or T <= 0.
+ * Workspace bytes a call with T tokens, K inputs and N outputs needs for
+ * adapters of the given ranks (`ranks` is a HOST array of n_ranks entries: one
+ * for lora_linear_fwd and lora_linear_nf4_fwd, one per group for
+ * lora_linear_stacked_fwd). It holds the rank-wide intermediate
+ * [T, R] in the adapter dtype, R = the sum of the ranks rounded up to
+ * multiples of 64. A lossless call with an fp32 adapter on bf16 activations
+ * runs the adapter products on bf16 MFMA over an exact hi + lo split of each
+ * fp32 value, so its workspace holds the intermediate as [T, 3 R] bf16 plus
+ * the split copies of A ([2 R, K]) and B (at most [N, 3 R]), each region
+ * 256-byte aligned. Returns 0 when no rank is positive or T, K or N <= 0.
  */
-size_t lora_linear_workspace_size(int64_t T, const int32_t* ranks, int32_t n_ranks, int32_t adapter_dtype,
-                                  int32_t quality);
+size_t lora_linear_workspace_size(int64_t T, int64_t K, int64_t N, const int32_t* ranks, int32_t n_ranks,
+                                  int32_t adapter_dtype, int32_t quality);
 
 /* Static, human-readable text for a status code. */
 const char* lora_status_string(int status);

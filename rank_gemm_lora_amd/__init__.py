@@ -67,7 +67,7 @@ _lib.lora_linear_nf4_fwd.restype = ctypes.c_int
 _lib.dense_patch_apply.argtypes = [_p, _i32, ctypes.POINTER(_i64), _i32, _p, _i32, ctypes.POINTER(_i64), _i32,
                                    _f64, _i32, _p]
 _lib.dense_patch_apply.restype = ctypes.c_int
-_lib.lora_linear_workspace_size.argtypes = [_i64, ctypes.POINTER(_i32), _i32, _i32, _i32]
+_lib.lora_linear_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_i32), _i32, _i32, _i32]
 _lib.lora_linear_workspace_size.restype = _sz
 _lib.lora_status_string.argtypes = [ctypes.c_int]
 _lib.lora_status_string.restype = ctypes.c_char_p
@@ -125,9 +125,9 @@ def dense_patch_apply(dst, dst_dtype, dst_shape, src, src_dtype, src_shape, stre
                                          strength, mode, stream), "dense_patch_apply")
 
 
-def lora_linear_workspace_size(T, ranks, adapter_dtype, quality=LORA_LOSSLESS) -> int:
+def lora_linear_workspace_size(T, K, N, ranks, adapter_dtype, quality=LORA_LOSSLESS) -> int:
     arr = (_i32 * max(1, len(ranks)))(*ranks)
-    return int(_lib.lora_linear_workspace_size(T, arr, len(ranks), adapter_dtype, quality))
+    return int(_lib.lora_linear_workspace_size(T, K, N, arr, len(ranks), adapter_dtype, quality))
 
 
 def lora_status_string(status: int) -> str:
@@ -173,8 +173,8 @@ def _row_major(t: torch.Tensor, name: str):
     return t.stride(0)
 
 
-def _workspace(T, ranks, adapter_dtype, quality, workspace, device):
-    need = lora_linear_workspace_size(T, list(ranks), adapter_dtype, quality)
+def _workspace(T, K, N, ranks, adapter_dtype, quality, workspace, device):
+    need = lora_linear_workspace_size(T, K, N, list(ranks), adapter_dtype, quality)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     return workspace, need
@@ -192,7 +192,7 @@ def lora_linear(x, W, b, A, B, alpha, strength=1.0, request_scale=1.0, out=None,
     rank = 0 if A is None else A.shape[0]
     adt = _dt(A) if A is not None else _dt(x)
     q = _QUALITY[quality]
-    ws, need = _workspace(T, [rank] if rank else [], adt, q, workspace, x.device)
+    ws, need = _workspace(T, K, N, [rank] if rank else [], adt, q, workspace, x.device)
     lora_linear_fwd(x.data_ptr(), T, K, ldx, W.data_ptr(), N, _ptr(b), _ptr(A), _ptr(B), rank, adt,
                     float(alpha), float(strength), float(request_scale), out.data_ptr(), ldy, _dt(x), q,
                     ws.data_ptr(), ws.numel(), _stream(stream))
@@ -212,7 +212,7 @@ def lora_linear_stacked(x, W, b, groups, strength=1.0, request_scale=1.0, out=No
     cg = [LoraGroup(_ptr(g["A"]), _ptr(g["B"]), 0 if g["A"] is None else g["A"].shape[0], 0, float(g["alpha"]),
                     int(g["col_offset"]), int(g["n_cols"])) for g in groups]
     q = _QUALITY[quality]
-    ws, need = _workspace(T, [g.rank for g in cg if g.rank > 0], adt, q, workspace, x.device)
+    ws, need = _workspace(T, K, N, [g.rank for g in cg if g.rank > 0], adt, q, workspace, x.device)
     lora_linear_stacked_fwd(x.data_ptr(), T, K, ldx, W.data_ptr(), N, _ptr(b), cg, len(cg), adt, float(strength),
                             float(request_scale), out.data_ptr(), ldy, _dt(x), q, ws.data_ptr(), ws.numel(),
                             _stream(stream))
@@ -229,7 +229,7 @@ def lora_linear_nf4(x, codes, absmax, codebook, N, b, A, B, alpha, strength=1.0,
     rank = 0 if A is None else A.shape[0]
     adt = _dt(A) if A is not None else LORA_BF16
     q = _QUALITY[quality]
-    ws, need = _workspace(T, [rank] if rank else [], adt, q, workspace, x.device)
+    ws, need = _workspace(T, K, N, [rank] if rank else [], adt, q, workspace, x.device)
     lora_linear_nf4_fwd(x.data_ptr(), T, K, ldx, codes.data_ptr(), absmax.data_ptr(), codebook.data_ptr(),
                         blocksize, N, _ptr(b), _ptr(A), _ptr(B), rank, adt, float(alpha), float(strength),
                         float(request_scale), out.data_ptr(), ldy, q, ws.data_ptr(), ws.numel(),

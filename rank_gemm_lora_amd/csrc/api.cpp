@@ -81,9 +81,35 @@ int fill_groups(LinearProblem& p, const Adapter* ads, int n, double strength, do
   return LORA_OK;
 }
 
-size_t workspace_bytes_for(const LinearProblem& p) {
+constexpr size_t kWsAlign = 256;
+size_t round_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+// Workspace layout of a call. Usually t~ [T, sum r_pad] in the adapter dtype.
+// Lossless fp32 adapters on bf16 activations: t~ [T, 3 sum r_pad] bf16, then the
+// split copies A2 of every group ([2 r_pad, K] bf16), then B2 ([n_cols, 3 r_pad]
+// bf16); assign_split() points the groups at them.
+size_t workspace_bytes_for(const LinearProblem& p, bool lossless) {
   if (p.n_groups == 0 || p.T == 0) return 0;
+  if (lossless && lora::split_fp32_adapter(p.act, p.adapter, p.nf4)) {
+    size_t bytes = round_up(static_cast<size_t>(p.T) * static_cast<size_t>(3 * p.ldt) * 2);
+    for (int i = 0; i < p.n_groups; ++i) bytes += round_up(static_cast<size_t>(2 * p.g[i].r_pad) * p.K * 2);
+    for (int i = 0; i < p.n_groups; ++i) bytes += round_up(static_cast<size_t>(p.g[i].n_cols) * 3 * p.g[i].r_pad * 2);
+    return bytes;
+  }
   return static_cast<size_t>(p.T) * static_cast<size_t>(p.ldt) * static_cast<size_t>(lora::esize(p.adapter));
+}
+
+void assign_split(LinearProblem& p) {
+  char* w = static_cast<char*>(p.work);
+  size_t off = round_up(static_cast<size_t>(p.T) * static_cast<size_t>(3 * p.ldt) * 2);
+  for (int i = 0; i < p.n_groups; ++i) {
+    p.g[i].A2 = w + off;
+    off += round_up(static_cast<size_t>(2 * p.g[i].r_pad) * p.K * 2);
+  }
+  for (int i = 0; i < p.n_groups; ++i) {
+    p.g[i].B2 = w + off;
+    off += round_up(static_cast<size_t>(p.g[i].n_cols) * 3 * p.g[i].r_pad * 2);
+  }
 }
 
 // Shared validation + dispatch for lora_linear_fwd / _stacked_fwd / _nf4_fwd.
@@ -148,9 +174,11 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
   const int st = fill_groups(p, ads, n_ads, strength, request_scale);
   if (st != LORA_OK) return st;
 
-  const size_t need = workspace_bytes_for(p);
+  const bool lossless = quality == LORA_LOSSLESS;
+  const size_t need = workspace_bytes_for(p, lossless);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LORA_ERR_WORKSPACE;
   p.work = workspace;
+  if (need > 0 && lossless && lora::split_fp32_adapter(p.act, p.adapter, p.nf4)) assign_split(p);
 
   // the output must not overlap any input or the workspace
   if (T > 0) {
@@ -258,13 +286,28 @@ int dense_patch_apply(void* dst, int32_t dst_dtype, const int64_t* dst_shape, in
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
-size_t lora_linear_workspace_size(int64_t T, const int32_t* ranks, int32_t n_ranks, int32_t adapter_dtype,
-                                  int32_t quality) {
-  (void)quality;
-  if (T <= 0 || ranks == nullptr || n_ranks <= 0 || !dtype_ok(adapter_dtype)) return 0;
+size_t lora_linear_workspace_size(int64_t T, int64_t K, int64_t N, const int32_t* ranks, int32_t n_ranks,
+                                  int32_t adapter_dtype, int32_t quality) {
+  if (T <= 0 || K <= 0 || N <= 0 || ranks == nullptr || n_ranks <= 0 || !dtype_ok(adapter_dtype)) return 0;
   int64_t cols = 0;
+  int n = 0;
   for (int i = 0; i < n_ranks; ++i)
-    if (ranks[i] > 0) cols += lora::rank_pad(ranks[i]);
+    if (ranks[i] > 0) {
+      cols += lora::rank_pad(ranks[i]);
+      ++n;
+    }
+  if (cols == 0) return 0;
+  if (quality == LORA_LOSSLESS && adapter_dtype == LORA_F32) {
+    // the bf16-activation layout (the larger of the two an fp32 adapter can need);
+    // every group's n_cols is at most N
+    size_t bytes = round_up(static_cast<size_t>(T) * static_cast<size_t>(3 * cols) * 2);
+    for (int i = 0; i < n_ranks; ++i) {
+      if (ranks[i] <= 0) continue;
+      const size_t rp = static_cast<size_t>(lora::rank_pad(ranks[i]));
+      bytes += round_up(2 * rp * static_cast<size_t>(K) * 2) + round_up(static_cast<size_t>(N) * 3 * rp * 2);
+    }
+    return bytes;
+  }
   return static_cast<size_t>(T) * static_cast<size_t>(cols) * static_cast<size_t>(esz(adapter_dtype));
 }
 

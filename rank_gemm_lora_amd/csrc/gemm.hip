@@ -1779,14 +1779,20 @@ __device__ __forceinline__ void pipe_loop(f32x16 (&acc)[P::NI][P::NJ], char* sme
   }
 }
 
+// Rows of A a group's producer tasks cover: its padded rank, or with SPLIT
+// (fp32 adapter on bf16 activations) the 2 r_pad interleaved hi / lo rows of
+// its bf16 split copy.
+template <bool SPLIT>
+__device__ __forceinline__ int producer_rows(const GroupDev& g) { return SPLIT ? 2 * g.r_pad : g.r_pad; }
+
 // grid: (ceil(T / BM), total chunks of BN adapter rows over all groups)
-template <class DP>
+template <class DP, bool SPLIT>
 __global__ __launch_bounds__(DP::THREADS) void down_kernel(LinearProblem p) {
   using P = DP;
   __shared__ __attribute__((aligned(1024))) char smem[P::S * P::STAGE_BYTES];
   int c = static_cast<int>(blockIdx.y), gi = 0;
-  while (gi + 1 < p.n_groups && c >= (p.g[gi].r_pad + P::BN - 1) / P::BN) {
-    c -= (p.g[gi].r_pad + P::BN - 1) / P::BN;
+  while (gi + 1 < p.n_groups && c >= (producer_rows<SPLIT>(p.g[gi]) + P::BN - 1) / P::BN) {
+    c -= (producer_rows<SPLIT>(p.g[gi]) + P::BN - 1) / P::BN;
     ++gi;
   }
   const GroupDev& g = p.g[gi];
@@ -1795,14 +1801,15 @@ __global__ __launch_bounds__(DP::THREADS) void down_kernel(LinearProblem p) {
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * P::BM;
   const int rows_m = static_cast<int>(min<int64_t>(P::BM, p.T - m0));
   const int q0 = c * P::BN;
-  const int rows_q = min(P::BN, g.rank - q0);
+  const int rows_q = min(P::BN, (SPLIT ? 2 * g.r_pad : g.rank) - q0);
   const int kb_total = static_cast<int>(p.K * 2);
   const int nk = (kb_total + P::RB - 1) / P::RB;
   const bool k_tail = (kb_total % P::RB) != 0;
   const uint32_t ldx_b = static_cast<uint32_t>(p.ldx * 2), lda_b = static_cast<uint32_t>(p.K * 2);
   const __amdgpu_buffer_rsrc_t xr =
       make_rsrc(static_cast<const char*>(p.x) + m0 * p.ldx * 2, static_cast<uint32_t>(rows_m) * ldx_b);
-  const __amdgpu_buffer_rsrc_t ar = make_rsrc(static_cast<const char*>(g.A) + static_cast<int64_t>(q0) * p.K * 2,
+  const char* a_src = static_cast<const char*>(SPLIT ? g.A2 : g.A);
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(a_src + static_cast<int64_t>(q0) * p.K * 2,
                                               static_cast<uint32_t>(max(rows_q, 0)) * lda_b);
   TileOffsets<P, P::BM> ox;
   TileOffsets<P, P::BN> oa;
@@ -1824,6 +1831,33 @@ __global__ __launch_bounds__(DP::THREADS) void down_kernel(LinearProblem p) {
   const float sc = g.scale;
   const bool unit = sc == 1.0f;
   bf16_bits* t = static_cast<bf16_bits*>(p.work);
+  if (SPLIT) {
+    // rows 2q, 2q + 1 hold x.hi(A[q]) and x.lo(A[q]): t = their fp32 sum, t~ = RN_f32(s t),
+    // written as hi(t~) | hi(t~) | lo(t~) into the group's three r_pad-wide blocks
+    bf16_bits* row = t + m * (3 * p.ldt) + 3 * g.t_col;
+#pragma unroll
+    for (int i = 0; i < P::NI; ++i) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int q = (q0 + wn0 + i * 32 + gq * 8 + h * 4) / 2;  // first of this lane's 2 ranks
+        if (q >= g.r_pad) continue;
+        bf16_bits hi[2], lo[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float tv = acc[i][0][gq * 4 + 2 * e] + acc[i][0][gq * 4 + 2 * e + 1];
+          const float ts = unit ? tv : tv * sc;
+          hi[e] = f32_to_bf16_rne(ts);
+          lo[e] = f32_to_bf16_rne(ts - bf16_to_f32(hi[e]));
+        }
+        const uint32_t whi = static_cast<uint32_t>(hi[0]) | (static_cast<uint32_t>(hi[1]) << 16);
+        const uint32_t wlo = static_cast<uint32_t>(lo[0]) | (static_cast<uint32_t>(lo[1]) << 16);
+        *reinterpret_cast<uint32_t*>(row + q) = whi;
+        *reinterpret_cast<uint32_t*>(row + g.r_pad + q) = whi;
+        *reinterpret_cast<uint32_t*>(row + 2 * g.r_pad + q) = wlo;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < P::NI; ++i) {
 #pragma unroll
@@ -1841,20 +1875,23 @@ __global__ __launch_bounds__(DP::THREADS) void down_kernel(LinearProblem p) {
   }
 }
 
-template <class DP>
+template <class DP, bool SPLIT>
 hipError_t launch_cfg(const LinearProblem& p, hipStream_t s) {
   int chunks = 0;
-  for (int i = 0; i < p.n_groups; ++i) chunks += (p.g[i].r_pad + DP::BN - 1) / DP::BN;
+  for (int i = 0; i < p.n_groups; ++i) chunks += ((SPLIT ? 2 * p.g[i].r_pad : p.g[i].r_pad) + DP::BN - 1) / DP::BN;
   const dim3 grid(static_cast<unsigned>((p.T + DP::BM - 1) / DP::BM), static_cast<unsigned>(chunks));
-  hipLaunchKernelGGL(down_kernel<DP>, grid, dim3(DP::THREADS), 0, s, p);
+  hipLaunchKernelGGL((down_kernel<DP, SPLIT>), grid, dim3(DP::THREADS), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch(const LinearProblem& p, hipStream_t s) {
   bool narrow = true;
   for (int i = 0; i < p.n_groups; ++i) narrow = narrow && p.g[i].r_pad <= DP64::BN;
-  return narrow ? launch_cfg<DP64>(p, s) : launch_cfg<DP128>(p, s);
+  return narrow ? launch_cfg<DP64, false>(p, s) : launch_cfg<DP128, false>(p, s);
 }
+
+// fp32 adapter on bf16 activations: t~ as hi | hi | lo from the split copies of A
+hipError_t launch_split(const LinearProblem& p, hipStream_t s) { return launch_cfg<DP128, true>(p, s); }
 }  // namespace down
 }  // namespace pipe
 
@@ -1881,9 +1918,80 @@ hipError_t launch_down(const LinearProblem& p, hipStream_t s) {
 
 }  // namespace
 
+// Split copies of an fp32 adapter (layout in GroupDev): hi(v) = RN_bf16(v) and
+// lo(v) = RN_bf16(v - hi(v)), where v - hi(v) is exact in fp32, so hi + lo
+// carries v to about 16 significant bits.
+__global__ __launch_bounds__(256) void split_a_kernel(const float* __restrict__ A, int rank, int r_pad, int64_t K,
+                                                      bf16_bits* __restrict__ A2) {
+  const int64_t n = 2 * static_cast<int64_t>(r_pad) * K;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t row = i / K, k = i - row * K;
+    const int q = static_cast<int>(row >> 1);
+    const float v = q < rank ? A[q * K + k] : 0.f;
+    const bf16_bits hi = f32_to_bf16_rne(v);
+    A2[i] = (row & 1) ? f32_to_bf16_rne(v - bf16_to_f32(hi)) : hi;
+  }
+}
+
+__global__ __launch_bounds__(256) void split_b_kernel(const float* __restrict__ B, int rank, int r_pad,
+                                                      int64_t n_cols, bf16_bits* __restrict__ B2) {
+  const int w = 3 * r_pad;
+  const int64_t n = n_cols * w;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t row = i / w;
+    const int c = static_cast<int>(i - row * w);
+    const int seg = c / r_pad, q = c - seg * r_pad;
+    const float v = q < rank ? B[row * rank + q] : 0.f;
+    const bf16_bits hi = f32_to_bf16_rne(v);
+    B2[i] = seg == 1 ? f32_to_bf16_rne(v - bf16_to_f32(hi)) : hi;
+  }
+}
+
+// The split path's phase 1: split copies of every group, then the producer.
+hipError_t split_producer(const LinearProblem& p, hipStream_t s) {
+  for (int i = 0; i < p.n_groups; ++i) {
+    const GroupDev& g = p.g[i];
+    const int64_t na = 2 * static_cast<int64_t>(g.r_pad) * p.K, nb = g.n_cols * 3 * g.r_pad;
+    const unsigned ga = static_cast<unsigned>((na + 255) / 256 < 4096 ? (na + 255) / 256 : 4096);
+    const unsigned gb = static_cast<unsigned>((nb + 255) / 256 < 4096 ? (nb + 255) / 256 : 4096);
+    hipLaunchKernelGGL(split_a_kernel, dim3(ga), dim3(256),
+                       0, s, static_cast<const float*>(g.A), g.rank, g.r_pad, p.K, static_cast<bf16_bits*>(g.A2));
+    hipLaunchKernelGGL(split_b_kernel, dim3(gb), dim3(256),
+                       0, s, static_cast<const float*>(g.B), g.rank, g.r_pad, g.n_cols,
+                       static_cast<bf16_bits*>(g.B2));
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return pipe::down::launch_split(p, s);
+}
+
+// The split path's phase 2: the hot GEMM over bf16 groups of rank 3 r_pad
+// (t_hi | t_hi | t_lo against hi(B) | lo(B) | hi(B)).
+hipError_t split_gemm(const LinearProblem& p, hipStream_t s) {
+  LinearProblem q = p;
+  q.adapter = Elt::BF16;
+  q.ldt = 3 * p.ldt;
+  for (int i = 0; i < q.n_groups; ++i) {
+    GroupDev& g = q.g[i];
+    g.B = g.B2;
+    g.rank = 3 * g.r_pad;
+    g.r_pad = 3 * g.r_pad;
+    g.t_col = 3 * g.t_col;
+  }
+  return pipe::launch(q, s);
+}
+
 hipError_t launch_lossless(const LinearProblem& p, hipStream_t s, int phase) {
   if (p.T == 0) return hipSuccess;
   const bool act_bf16 = p.act == Elt::BF16, ad_bf16 = p.adapter == Elt::BF16;
+  // fp32 adapter on bf16 activations: the adapter products on bf16 MFMA over the hi / lo split
+  if (split_fp32_adapter(p.act, p.adapter, p.nf4)) {
+    if (p.n_groups > 0 && phase != 2) {
+      const hipError_t e = split_producer(p, s);
+      if (e != hipSuccess) return e;
+    }
+    return phase == 1 ? hipSuccess : split_gemm(p, s);
+  }
   bool ranks_ok = true;
   for (int i = 0; i < p.n_groups; ++i) ranks_ok = ranks_ok && (p.g[i].rank % 8 == 0);
   // hot path: streaming rank-wide producer, then the pipelined fused GEMM
@@ -1906,8 +2014,7 @@ hipError_t launch_lossless(const LinearProblem& p, hipStream_t s, int phase) {
   if (p.nf4) {
     return ad_bf16 ? launch_fused<bf16_bits, bf16_bits, true>(p, s) : launch_fused<bf16_bits, float, true>(p, s);
   }
-  if (act_bf16 && ad_bf16) return launch_fused<bf16_bits, bf16_bits, false>(p, s);
-  if (act_bf16) return launch_fused<bf16_bits, float, false>(p, s);
+  if (act_bf16) return launch_fused<bf16_bits, bf16_bits, false>(p, s);  // (an fp32 adapter took the split path)
   return launch_fused<float, float, false>(p, s);
 }
 

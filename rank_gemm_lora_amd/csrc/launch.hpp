@@ -27,7 +27,20 @@ struct GroupDev {
   int32_t r_pad;     // padded rank (multiple of kRankPad)
   float scale;       // lossless: combined scale rounded to fp32
   float f[3];        // exact tier: alpha/rank, strength, request_scale, each rounded to fp32
+  // Lossless tier, fp32 adapter on bf16 activations: bf16 split copies in the
+  // workspace. A2 [2 r_pad, K]: row 2q = hi(A[q]), row 2q + 1 = lo(A[q]);
+  // B2 [n_cols, 3 r_pad]: hi(B) | lo(B) | hi(B), each block r_pad wide
+  // (hi(v) = RN_bf16(v), lo(v) = RN_bf16(v - hi(v)); padding zero).
+  void* A2;
+  void* B2;
 };
+
+// Lossless fp32 adapter on bf16 activations: the products run on bf16 MFMA
+// over the hi/lo split (the t~ block of a group is then t_hi | t_hi | t_lo,
+// 3 r_pad columns). Workspace bytes of that layout.
+inline bool split_fp32_adapter(Elt act, Elt adapter, bool nf4) {
+  return act == Elt::BF16 && adapter == Elt::F32 && !nf4;
+}
 
 struct LinearProblem {
   const void* x; int64_t ldx;

@@ -104,12 +104,20 @@ def test_phase_entry_point_validation():
 
 
 def test_workspace_size():
-    assert rg.lora_linear_workspace_size(32760, [64], BF16) == 32760 * 64 * 2
-    assert rg.lora_linear_workspace_size(64, [8], F32) == 64 * 64 * 4
-    assert rg.lora_linear_workspace_size(16384, [128, 128, 128], BF16) == 16384 * 384 * 2
-    assert rg.lora_linear_workspace_size(100, [8, 70], BF16) == 100 * (64 + 128) * 2
-    assert rg.lora_linear_workspace_size(0, [8], BF16) == 0
-    assert rg.lora_linear_workspace_size(10, [], BF16) == 0
+    ws = rg.lora_linear_workspace_size
+    assert ws(32760, 1536, 8960, [64], BF16) == 32760 * 64 * 2
+    assert ws(16384, 3072, 9216, [128, 128, 128], BF16) == 16384 * 384 * 2
+    assert ws(100, 64, 96, [8, 70], BF16) == 100 * (64 + 128) * 2
+    assert ws(64, 128, 96, [8], F32, EXACT) == 64 * 64 * 4
+    # lossless fp32 adapter: t~ [T, 3R] bf16, A split [2 r_pad, K] and B split [N, 3 r_pad] bf16 per
+    # group, each region rounded up to 256 bytes
+    r256 = lambda v: -(-v // 256) * 256
+    assert ws(64, 128, 96, [8], F32) == r256(64 * 192 * 2) + r256(2 * 64 * 128 * 2) + r256(96 * 192 * 2)
+    assert ws(100, 200, 300, [8, 70], F32) == (r256(100 * 3 * 192 * 2) + r256(2 * 64 * 200 * 2) + r256(300 * 192 * 2)
+                                               + r256(2 * 128 * 200 * 2) + r256(300 * 384 * 2))
+    assert ws(0, 128, 96, [8], BF16) == 0
+    assert ws(10, 128, 96, [], BF16) == 0
+    assert ws(10, 0, 96, [8], BF16) == 0
 
 
 def stacked(groups, n_groups=None, **kw):

@@ -187,7 +187,7 @@ def test_phases_compose_to_the_fused_call(T, K, N, r, adapter):
     adt = rg.LORA_F32 if adapter == "f32" else rg.LORA_BF16
     tdt = torch.float32 if adapter == "f32" else torch.bfloat16
     A, B = dev(d["A"]).to(tdt).contiguous(), dev(d["B"]).to(tdt).contiguous()
-    ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, [r], adt)), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, K, N, [r], adt)), dtype=torch.uint8, device=DEV)
     y_one = torch.empty((T, N), dtype=torch.bfloat16, device=DEV)
     y_two = torch.full((T, N), 3.0, dtype=torch.bfloat16, device=DEV)
     sp = torch.cuda.current_stream().cuda_stream
