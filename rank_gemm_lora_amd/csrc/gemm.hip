@@ -1440,7 +1440,9 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow16_kernel(LinearProblem p
   const int m_idx = first_m + within % gm;
   const int n_idx = within / gm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (the wave index through readfirstlane: the compiler then knows it, and all
+  // that derives from it -- wave block origin, output resource -- is wave-uniform)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave % P::WAVES_M) * P::WM;
   const int wn0 = (wave / P::WAVES_M) * P::WN;
   const int64_t m0 = static_cast<int64_t>(m_idx) * P::BM;
