@@ -846,37 +846,6 @@ __global__ __launch_bounds__(P::THREADS) void gemm_pipe_kernel(LinearProblem p, 
 
 
 // ---------------------------------------------------------------------------
-// Configuration of the hot kernel: the x part and the W part of a K stage are
-// separate "units" of a ring of SLOTS equal LDS slots (unit 2s = x rows of stage
-// s, unit 2s + 1 = W rows, slot = unit % SLOTS). With RB = 128 every staged row
-// is a whole 128-byte line.
-template <int BM_, int BN_, int WM_, int WN_, int RB_, int SLOTS_>
-struct RCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RB = RB_, SLOTS = SLOTS_;
-  static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, WAVES = WAVES_M * WAVES_N;
-  static constexpr int THREADS = 64 * WAVES;
-  static constexpr int NI = WN / 32, NJ = WM / 32;
-  static constexpr int CPR = RB / 16, RPL = 256 / RB, KK = RB / 32;
-  static constexpr int SLOT_BYTES = BM * RB;
-  static constexpr int LPU = BM * CPR / 64 / WAVES;  // buffer loads per thread per unit
-  static constexpr int GROUP_M = 4;
-  static_assert(BM == BN, "x and W units share one slot size");
-  static_assert(KK % 2 == 0, "fragment sets alternate across stages");
-  static_assert((BM * CPR / 64) % WAVES == 0, "uneven load split");
-  static_assert(SLOTS >= 4 && SLOTS * SLOT_BYTES <= 160 * 1024, "LDS");
-  static_assert((SLOTS - 2) * LPU <= 63, "vmcnt range");
-};
-
-template <class P>
-__device__ __forceinline__ void ring_frags(Frags<P>& f, const char* xs, const char* ws, int kk, int wn0, int wm0,
-                                           int lane) {
-  const int r = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < P::NI; ++i) f.a[i] = *(const bf16x8*)(ws + swz<P>(wn0 + i * 32 + r, kk * 2 + h) * 16);
-#pragma unroll
-  for (int j = 0; j < P::NJ; ++j) f.b[j] = *(const bf16x8*)(xs + swz<P>(wm0 + j * 32 + r, kk * 2 + h) * 16);
-}
-
 // One copy instruction `it` of a staged tile whose rows come from source row
 // (row + shift) for rows in [row_lo, row_hi), bytes [kb0, kb_valid); other
 // lanes read as zero (K-extension units: t~ rows and LoRA B rows).
@@ -896,345 +865,11 @@ __device__ __forceinline__ void dma_one(int it, char* lds, __amdgpu_buffer_rsrc_
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + slot0 * 16), 16, voff, 0, 0, 0);
 }
 
-// Epilogue through LDS: each wave adds the bias in fp32, rounds its 128 x 128
-// block to bf16 once and writes it to its own 32 KB of LDS as rows of tokens
-// (16-byte chunks XOR-swizzled by row), then every store instruction writes
-// four whole 256-byte output rows (16 bytes per lane), so the L2 sees full
-// 128-byte lines instead of 16-byte pieces. Outputs that are not 16-byte
-// aligned (odd column views) are written element by element.
-template <class P>
-__device__ __forceinline__ void epilogue_lds(const f32x16 (&acc)[P::NI][P::NJ], const LinearProblem& p, int64_t m0,
-                                             int64_t n0, int wm0, int wn0, int lane, int wave, char* smem) {
-  static_assert(P::WM == 128 && P::WN == 128, "staging written for 128 x 128 wave blocks");
-  const int r = lane & 31, h = lane >> 5;
-  char* st = smem + wave * (128 * 256);
-  const bf16_bits* bias = static_cast<const bf16_bits*>(p.bias);
-#pragma unroll
-  for (int i = 0; i < P::NI; ++i) {
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int cl = i * 32 + gq * 8 + h * 4;  // first of 4 columns, local to the wave block
-      const int64_t n = n0 + wn0 + cl;
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bias != nullptr) {
-        if (n + 3 < p.N) {
-          const uint2 w = *reinterpret_cast<const uint2*>(bias + n);  // 8-byte aligned: n is a multiple of 4
-          bv[0] = __uint_as_float(w.x << 16); bv[1] = __uint_as_float(w.x & 0xffff0000u);
-          bv[2] = __uint_as_float(w.y << 16); bv[3] = __uint_as_float(w.y & 0xffff0000u);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < p.N) bv[e] = bf16_to_f32(bias[n + e]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < P::NJ; ++j) {
-        const int row = j * 32 + r;
-        uint2 w;
-        w.x = pack_bf16x2(acc[i][j][gq * 4 + 0] + bv[0], acc[i][j][gq * 4 + 1] + bv[1]);
-        w.y = pack_bf16x2(acc[i][j][gq * 4 + 2] + bv[2], acc[i][j][gq * 4 + 3] + bv[3]);
-        const int chunk = (cl >> 3) ^ (row & 15);
-        *reinterpret_cast<uint2*>(st + row * 256 + chunk * 16 + h * 8) = w;
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keeps accumulator reads from being hoisted (register pressure)
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this wave's staging is complete (only this wave reads it)
-  const int c = lane & 15, rr = lane >> 4;
-  const int64_t n = n0 + wn0 + c * 8;
-  bf16_bits* y = static_cast<bf16_bits*>(p.y);
-  const bool aligned16 = (reinterpret_cast<uintptr_t>(p.y) % 16 == 0) && (p.ldy % 8 == 0);
-#pragma unroll 8
-  for (int it = 0; it < 32; ++it) {
-    const int row = it * 4 + rr;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * 256 + ((c ^ (row & 15)) * 16));
-    const int64_t m = m0 + wm0 + row;
-    if (m < p.T) {
-      bf16_bits* dst = y + m * p.ldy + n;
-      if (aligned16 && n + 7 < p.N) {
-        *reinterpret_cast<u32x4*>(dst) = v;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (n + e < p.N) dst[e] = static_cast<bf16_bits>(v[e >> 1] >> (16 * (e & 1)));
-      }
-    }
-  }
-}
-
-// Hot kernel: 256 x 256 tile, 4 waves of 128 x 128, 64-k stages of 128-byte
-// rows in a five-slot LDS ring (unit 2t = x rows of stage t, 2t + 1 = W rows;
-// slot = unit mod 5). Every stage is 64 MFMA bundles. Fragment reads go one to
-// every other bundle, copy loads one to every fourth, so neither the LDS nor
-// the address path (about 64 B/clk of LDS-DMA per CU) is ever flooded. The
-// barrier that ends the reads of stage t sits after the first MFMA of its last
-// k-step. Copy schedule of stage t (bundle b): b = 2..14 finish W of stage
-// t + 1, b = 18..46 load x of stage t + 2, and b = 50..62 (after the barrier,
-// into the slot x of stage t just released) start W of stage t + 2.
-// K-extension stages follow the main stages; at most two adapter groups may
-// meet one tile (the host checks this and otherwise uses the general kernel).
-template <class P>
-__global__ __launch_bounds__(P::THREADS) void gemm_flow_kernel(LinearProblem p, int mt, int nt) {
-  static_assert(P::SLOTS == 5 && P::RB == 128 && P::NI == 4 && P::NJ == 4 && P::WAVES == 4,
-                "schedule written for 4 waves of 128 x 128 and a five-slot ring of 128-byte rows");
-  __shared__ __attribute__((aligned(1024))) char smem[P::SLOTS * P::SLOT_BYTES];
-  constexpr int NL = TileOffsets<P, P::BM>::N;  // copy loads per wave per unit
-  static_assert(NL == 8, "copy schedule assumes 8 loads per unit");
-
-  const int G = mt * nt;
-  const int L = xcd_remap(blockIdx.x, G);
-  const int gsize = P::GROUP_M * nt;
-  const int grp = L / gsize;
-  const int first_m = grp * P::GROUP_M;
-  const int gm = min(P::GROUP_M, mt - first_m);
-  const int within = L - grp * gsize;
-  const int m_idx = first_m + within % gm;
-  const int n_idx = within / gm;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm0 = (wave % P::WAVES_M) * P::WM;
-  const int wn0 = (wave / P::WAVES_M) * P::WN;
-  const int64_t m0 = static_cast<int64_t>(m_idx) * P::BM;
-  const int64_t n0 = static_cast<int64_t>(n_idx) * P::BN;
-  const int rows_m = static_cast<int>(min<int64_t>(P::BM, p.T - m0));
-  const int rows_n = static_cast<int>(min<int64_t>(P::BN, p.N - n0));
-
-  const int kb_total = static_cast<int>(p.K * 2);
-  const int nk = (kb_total + P::RB - 1) / P::RB;
-  const bool k_tail = (kb_total % P::RB) != 0;
-  const uint32_t ldx_b = static_cast<uint32_t>(p.ldx * 2), ldw_b = static_cast<uint32_t>(p.K * 2);
-  const __amdgpu_buffer_rsrc_t xr =
-      make_rsrc(static_cast<const char*>(p.x) + m0 * p.ldx * 2, static_cast<uint32_t>(rows_m) * ldx_b);
-  const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(static_cast<const char*>(p.W) + n0 * p.K * 2, static_cast<uint32_t>(rows_n) * ldw_b);
-  TileOffsets<P, P::BM> ox;
-  TileOffsets<P, P::BN> ow;
-  ox.init(ldx_b, 0, rows_m, 0);
-  ow.init(ldw_b, 0, rows_n, 0);
-
-  // K-extension plan of this tile: the (at most two) groups whose columns meet
-  // it. t~ rows of every group come through one descriptor over the tile's t~
-  // rows; the B rows of each group through their own.
-  const uint32_t ldt_b = static_cast<uint32_t>(p.ldt * 2);
-  int gs0 = p.n_groups, gs1 = p.n_groups;
-  for (int gi = 0; gi < p.n_groups; ++gi) {
-    if (!(p.g[gi].col_off < n0 + rows_n && p.g[gi].col_off + p.g[gi].n_cols > n0)) continue;
-    if (gs0 == p.n_groups) {
-      gs0 = gi;
-    } else {
-      gs1 = gi;
-      break;
-    }
-  }
-  // The fields the copies need, read once: a kernel-argument load inside a
-  // stage would make the wave wait for all of its outstanding LDS reads.
-  struct ExtGroup {
-    const char* B;
-    int tcb, tpb, rkb, n_cols, lo, hi, sh, ns;
-  };
-  auto ext_group = [&](int gi) {
-    ExtGroup e{nullptr, 0, 0, 0, 0, 0, 0, 0, 0};
-    if (gi < p.n_groups) {
-      const GroupDev& g = p.g[gi];
-      e.B = static_cast<const char*>(g.B);
-      e.tcb = g.t_col * 2;
-      e.tpb = g.r_pad * 2;
-      e.rkb = g.rank * 2;
-      e.n_cols = static_cast<int>(g.n_cols);
-      e.lo = static_cast<int>(max<int64_t>(0, g.col_off - n0));
-      e.hi = static_cast<int>(min<int64_t>(rows_n, g.col_off + g.n_cols - n0));
-      e.sh = static_cast<int>(n0 - g.col_off);
-      e.ns = g.r_pad * 2 / P::RB;
-    }
-    return e;
-  };
-  const ExtGroup eg0 = ext_group(gs0), eg1 = ext_group(gs1);
-  // Stage order: the K-extension stages first (the first group's, then the
-  // second's), then the main stages; stage s >= NE is main stage s - NE. Their
-  // copies then sit in the prologue, where a wait is exposed anyway, instead
-  // of in stages that would have to use the slower generic copy path.
-  const int NE = eg0.ns + eg1.ns;
-  const int NS = NE + nk;
-  const int NU = 2 * NS;
-  const __amdgpu_buffer_rsrc_t tr =
-      make_rsrc(static_cast<const char*>(p.work) + m0 * p.ldt * 2, static_cast<uint32_t>(rows_m) * ldt_b);
-
-  auto slot = [&](int u) { return smem + (u % P::SLOTS) * P::SLOT_BYTES; };
-  // Load l of unit u, any unit (nothing for u >= NU); per-lane offsets are
-  // computed here, so the index l need not be a compile-time constant.
-  auto issue_load = [&](int u, int l) {
-    if (u >= NU) return;
-    char* dst = slot(u);
-    const int s = u >> 1;
-    const bool is_w = (u & 1) != 0;
-    if (s >= NE) {
-      const int kb = (s - NE) * P::RB;
-      if (is_w) dma_one<P, P::BN>(l, dst, wr, ldw_b, 0, rows_n, 0, kb, kb_total);
-      else dma_one<P, P::BM>(l, dst, xr, ldx_b, 0, rows_m, 0, kb, kb_total);
-      return;
-    }
-    const bool second = s >= eg0.ns;
-    const ExtGroup& g = second ? eg1 : eg0;
-    const int e = second ? s - eg0.ns : s;
-    if (!is_w) {
-      // t~ rows of the group: columns [tcb, tcb + tpb) of the tile's t~ rows
-      dma_one<P, P::BM>(l, dst, tr, ldt_b, 0, rows_m, 0, g.tcb + e * P::RB, g.tcb + g.tpb);
-    } else {
-      const __amdgpu_buffer_rsrc_t br = make_rsrc(g.B, static_cast<uint32_t>(g.n_cols) * static_cast<uint32_t>(g.rkb));
-      dma_one<P, P::BN>(l, dst, br, static_cast<uint32_t>(g.rkb), g.lo, g.hi, g.sh, e * P::RB, g.rkb);
-    }
-  };
-
-  f32x16 acc[P::NI][P::NJ];
-#pragma unroll
-  for (int i = 0; i < P::NI; ++i)
-#pragma unroll
-    for (int j = 0; j < P::NJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  // prologue: x and W of stage 0, x of stage 1, first half of W of stage 1
-  if (NE == 0 && nk >= 3) {
-#pragma unroll
-    for (int l = 0; l < NL; ++l) ox.load_one(l, smem, xr, 0);
-#pragma unroll
-    for (int l = 0; l < NL; ++l) ow.load_one(l, smem + P::SLOT_BYTES, wr, 0);
-#pragma unroll
-    for (int l = 0; l < NL; ++l) ox.load_one(l, smem + 2 * P::SLOT_BYTES, xr, P::RB);
-#pragma unroll
-    for (int l = 0; l < NL / 2; ++l) ow.load_one(l, smem + 3 * P::SLOT_BYTES, wr, P::RB);
-  } else {
-    for (int l = 0; l < NL; ++l) issue_load(0, l);
-    for (int l = 0; l < NL; ++l) issue_load(1, l);
-    for (int l = 0; l < NL; ++l) issue_load(2, l);
-    for (int l = 0; l < NL / 2; ++l) issue_load(3, l);
-  }
-  {
-    const int after = (2 < NU ? NL : 0) + (3 < NU ? NL / 2 : 0);  // loads issued after stage 0's
-    if (after >= NL + NL / 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL + NL / 2));
-    else if (after >= NL) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  }
-  stage_barrier();
-  const int r = lane & 31, h = lane >> 5;
-  Frags<P> fr[2];
-  // fragment q of k-step kk, in order of first use: a0, b0 .. b3, a1 .. a3
-  auto read_frag = [&](Frags<P>& f, int q, const char* xs, const char* ws, int kk) {
-    if (q == 0 || q > P::NJ) {
-      const int ia = q == 0 ? 0 : q - P::NJ;
-      f.a[ia] = *(const bf16x8*)(ws + swz<P>(wn0 + ia * 32 + r, kk * 2 + h) * 16);
-    } else {
-      f.b[q - 1] = *(const bf16x8*)(xs + swz<P>(wm0 + (q - 1) * 32 + r, kk * 2 + h) * 16);
-    }
-  };
-#pragma unroll
-  for (int q = 0; q < 8; ++q) read_frag(fr[0], q, slot(0), slot(1), 0);
-
-  // stage t whose copy loads all belong to main, tail-free units (stages t + 1
-  // and t + 2 are main stages t + 1 - NE and t + 2 - NE)
-  auto stage = [&](int t, int a) {
-    const int b1 = a == 4 ? 0 : a + 1;           // W of stage t
-    const int a2 = a >= 3 ? a - 3 : a + 2;       // x of stage t + 1
-    const int b2 = a2 == 4 ? 0 : a2 + 1;         // W of stage t + 1
-    const int a3 = a2 >= 3 ? a2 - 3 : a2 + 2;    // x of stage t + 2
-    const char* xs = smem + a * P::SLOT_BYTES;
-    const char* ws = smem + b1 * P::SLOT_BYTES;
-    const char* xs2 = smem + a2 * P::SLOT_BYTES;
-    const char* ws2 = smem + b2 * P::SLOT_BYTES;
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int bb = 0; bb < 64; ++bb) {
-      const int kk = bb >> 4, m = bb & 15;
-      const Frags<P>& cf = fr[kk & 1];
-      Frags<P>& nf = fr[(kk + 1) & 1];
-      acc[m >> 2][m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf.a[m >> 2], cf.b[m & 3], acc[m >> 2][m & 3], 0, 0, 0);
-      if (kk < 3) {
-        if ((m & 1) == 0) read_frag(nf, m >> 1, xs, ws, kk + 1);
-      } else if (m == 0) {
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));  // x of stage t + 2 may still be in flight
-        stage_barrier();  // stage t + 1 landed and visible; every wave is done reading stage t
-      } else if (m & 1) {
-        read_frag(nf, m >> 1, xs2, ws2, 0);
-      }
-      if ((bb & 3) == 2) {
-        const int d = bb >> 2;  // 0..15
-        if (d < 4) ow.load_one(NL / 2 + d, smem + b2 * P::SLOT_BYTES, wr, (t + 1 - NE) * P::RB);
-        else if (d < 12) ox.load_one(d - 4, smem + a3 * P::SLOT_BYTES, xr, (t + 2 - NE) * P::RB);
-        else ow.load_one(d - 12, smem + a * P::SLOT_BYTES, wr, (t + 2 - NE) * P::RB);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-
-  // The generic stage: same copy assignment as a fast stage, issued in bulk,
-  // with compiler-scheduled MFMA steps (first K-extension stages, last main stages).
-  auto generic_stage = [&](int t, int a) {
-    const int b1 = a == 4 ? 0 : a + 1;
-    const int a2 = a >= 3 ? a - 3 : a + 2;
-    const int b2 = a2 == 4 ? 0 : a2 + 1;
-    const char* xs = smem + a * P::SLOT_BYTES;
-    const char* ws = smem + b1 * P::SLOT_BYTES;
-    for (int l = NL / 2; l < NL; ++l) issue_load(2 * t + 3, l);
-    for (int l = 0; l < NL; ++l) issue_load(2 * t + 4, l);
-#pragma unroll
-    for (int kk = 0; kk < P::KK; ++kk) {
-      if (kk + 1 < P::KK) {
-        ring_frags<P>(fr[(kk + 1) & 1], xs, ws, kk + 1, wn0, wm0, lane);
-      } else {
-        if (2 * t + 4 < NU) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-        stage_barrier();  // stage t + 1 landed and visible; every wave is done reading stage t
-        for (int l = 0; l < NL / 2; ++l) issue_load(2 * t + 5, l);
-        ring_frags<P>(fr[(kk + 1) & 1], smem + a2 * P::SLOT_BYTES, smem + b2 * P::SLOT_BYTES, 0, wn0, wm0, lane);
-      }
-      mfma_frags<P>(acc, fr[kk & 1]);
-    }
-  };
-
-  // fast stages: t >= NE - 1 (stage t + 1 is main stage t + 1 - NE) and main
-  // stage t + 2 - NE is neither past the last nor the K-tail stage
-  const int t_first = NE > 0 ? NE - 1 : 0;
-  const int t_end = NE + nk - 2 - (k_tail ? 1 : 0);
-  int a = 0;  // slot of x of stage t
-  int t = 0;
-  for (; t < t_first && t + 1 < NS; ++t) {
-    generic_stage(t, a);
-    a = a >= 3 ? a - 3 : a + 2;
-  }
-  for (; t < t_end && t + 1 < NS; ++t) {
-    stage(t, a);
-    a = a >= 3 ? a - 3 : a + 2;
-  }
-  for (; t + 1 < NS; ++t) {
-    generic_stage(t, a);
-    a = a >= 3 ? a - 3 : a + 2;
-  }
-  {  // last stage: no refill, no barrier
-    const char* xs = smem + a * P::SLOT_BYTES;
-    const char* ws = smem + (a == 4 ? 0 : a + 1) * P::SLOT_BYTES;
-#pragma unroll
-    for (int kk = 0; kk < P::KK; ++kk) {
-      if (kk + 1 < P::KK) ring_frags<P>(fr[(kk + 1) & 1], xs, ws, kk + 1, wn0, wm0, lane);
-      mfma_frags<P>(acc, fr[kk & 1]);
-    }
-  }
-
-  __syncthreads();  // every wave is done reading the ring; LDS becomes the staging area
-  epilogue_lds<P>(acc, p, m0, n0, wm0, wn0, lane, wave, smem);
-}
-
-template <class P>
-hipError_t launch_flow(const LinearProblem& p, hipStream_t s) {
-  const int mt = static_cast<int>((p.T + P::BM - 1) / P::BM);
-  const int nt = static_cast<int>((p.N + P::BN - 1) / P::BN);
-  hipLaunchKernelGGL(gemm_flow_kernel<P>, dim3(mt * nt), dim3(P::THREADS), 0, s, p, mt, nt);
-  return hipGetLastError();
-}
-
 // ---------------------------------------------------------------------------
-// The hot kernel on v_mfma_f32_16x16x32_bf16. Same tile (256 x 256, 4 waves of
-// 128 x 128), ring and copies as above; each wave holds 8 x 8 blocks of 16 x 16
+// The hot kernel on v_mfma_f32_16x16x32_bf16: 256 x 256 tile, 4 waves of
+// 128 x 128; the x part and the W part of a 64-k stage are separate units of a
+// ring of five 32 KB LDS slots (unit 2s = x rows of stage s, 2s + 1 = W rows,
+// slot = unit mod 5), 128-byte rows; each wave holds 8 x 8 blocks of 16 x 16
 // (4 accumulators per lane each) and a 64-k stage is two 32-k steps of 64 MFMAs.
 // Under a sustained MFMA load this instruction runs at a clearly higher clock
 // than the 32 x 32 x 16 one for the same work per cycle (measured on MI355X:
@@ -1701,7 +1336,6 @@ hipError_t launch_flow16(const LinearProblem& p, hipStream_t s) {
 
 // General pipelined kernel (used when more than two adapter groups meet one tile).
 using HotCfg = PCfg<256, 256, 64, 128, 64, 4>;
-using FlowCfg = RCfg<256, 256, 128, 128, 128, 5>;
 using Flow16Cfg = QCfg<256, 256, 128, 128, 128, 5>;
 
 // Largest number of adapter groups whose columns meet one BN-wide output tile.
