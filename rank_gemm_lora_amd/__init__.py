@@ -25,6 +25,7 @@ __all__ = [
     "LIB_PATH", "LoraError", "LORA_F32", "LORA_BF16", "LORA_LOSSLESS", "LORA_EXACT",
     "LORA_PATCH_ADD", "LORA_PATCH_REPLACE", "lora_linear_fwd", "lora_linear_stacked_fwd",
     "lora_linear_nf4_fwd", "dense_patch_apply", "lora_linear_fwd_phase", "lora_linear_workspace_size",
+    "lora_linear_nf4_workspace_size",
     "lora_status_string",
     "lora_device_check", "lora_linear", "lora_linear_stacked", "lora_linear_nf4", "dense_patch",
     "LoraGroup", "hip_runtimes_mapped",
@@ -69,6 +70,8 @@ _lib.dense_patch_apply.argtypes = [_p, _i32, ctypes.POINTER(_i64), _i32, _p, _i3
 _lib.dense_patch_apply.restype = ctypes.c_int
 _lib.lora_linear_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_i32), _i32, _i32, _i32]
 _lib.lora_linear_workspace_size.restype = _sz
+_lib.lora_linear_nf4_workspace_size.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32]
+_lib.lora_linear_nf4_workspace_size.restype = _sz
 _lib.lora_status_string.argtypes = [ctypes.c_int]
 _lib.lora_status_string.restype = ctypes.c_char_p
 _lib.lora_device_check.argtypes = []
@@ -128,6 +131,10 @@ def dense_patch_apply(dst, dst_dtype, dst_shape, src, src_dtype, src_shape, stre
 def lora_linear_workspace_size(T, K, N, ranks, adapter_dtype, quality=LORA_LOSSLESS) -> int:
     arr = (_i32 * max(1, len(ranks)))(*ranks)
     return int(_lib.lora_linear_workspace_size(T, K, N, arr, len(ranks), adapter_dtype, quality))
+
+
+def lora_linear_nf4_workspace_size(T, K, N, rank, adapter_dtype, quality=LORA_LOSSLESS) -> int:
+    return int(_lib.lora_linear_nf4_workspace_size(T, K, N, rank, adapter_dtype, quality))
 
 
 def lora_status_string(status: int) -> str:
@@ -229,7 +236,8 @@ def lora_linear_nf4(x, codes, absmax, codebook, N, b, A, B, alpha, strength=1.0,
     rank = 0 if A is None else A.shape[0]
     adt = _dt(A) if A is not None else LORA_BF16
     q = _QUALITY[quality]
-    ws, need = _workspace(T, K, N, [rank] if rank else [], adt, q, workspace, x.device)
+    need = lora_linear_nf4_workspace_size(T, K, N, rank, adt, q)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     lora_linear_nf4_fwd(x.data_ptr(), T, K, ldx, codes.data_ptr(), absmax.data_ptr(), codebook.data_ptr(),
                         blocksize, N, _ptr(b), _ptr(A), _ptr(B), rank, adt, float(alpha), float(strength),
                         float(request_scale), out.data_ptr(), ldy, q, ws.data_ptr(), ws.numel(),

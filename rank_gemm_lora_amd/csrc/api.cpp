@@ -87,16 +87,27 @@ size_t round_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 // Workspace layout of a call. Usually t~ [T, sum r_pad] in the adapter dtype.
 // Lossless fp32 adapters on bf16 activations: t~ [T, 3 sum r_pad] bf16, then the
 // split copies A2 of every group ([2 r_pad, K] bf16), then B2 ([n_cols, 3 r_pad]
-// bf16); assign_split() points the groups at them.
-size_t workspace_bytes_for(const LinearProblem& p, bool lossless) {
+// bf16); assign_split() points the groups at them. A lossless 4-bit weight with
+// T >= kNf4PanelMinT adds its bf16 panel [N, K] after all of that (256-byte
+// aligned); the GEMM then sees a bf16 weight, so an fp32 adapter takes the
+// split layout.
+size_t adapter_bytes_for(const LinearProblem& p, bool lossless, bool gemm_nf4) {
   if (p.n_groups == 0 || p.T == 0) return 0;
-  if (lossless && lora::split_fp32_adapter(p.act, p.adapter, p.nf4)) {
+  if (lossless && lora::split_fp32_adapter(p.act, p.adapter, gemm_nf4)) {
     size_t bytes = round_up(static_cast<size_t>(p.T) * static_cast<size_t>(3 * p.ldt) * 2);
     for (int i = 0; i < p.n_groups; ++i) bytes += round_up(static_cast<size_t>(2 * p.g[i].r_pad) * p.K * 2);
     for (int i = 0; i < p.n_groups; ++i) bytes += round_up(static_cast<size_t>(p.g[i].n_cols) * 3 * p.g[i].r_pad * 2);
     return bytes;
   }
   return static_cast<size_t>(p.T) * static_cast<size_t>(p.ldt) * static_cast<size_t>(lora::esize(p.adapter));
+}
+
+size_t panel_bytes(int64_t N, int64_t K) { return static_cast<size_t>(N) * static_cast<size_t>(K) * 2; }
+
+size_t workspace_bytes_for(const LinearProblem& p, bool lossless) {
+  const bool panel = lora::nf4_uses_panel(p.nf4, lossless, p.T);
+  const size_t ad = adapter_bytes_for(p, lossless, p.nf4 && !panel);
+  return panel ? round_up(ad) + panel_bytes(p.N, p.K) : ad;
 }
 
 void assign_split(LinearProblem& p) {
@@ -175,10 +186,12 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
   if (st != LORA_OK) return st;
 
   const bool lossless = quality == LORA_LOSSLESS;
+  const bool use_panel = lora::nf4_uses_panel(nf4, lossless, T);
   const size_t need = workspace_bytes_for(p, lossless);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LORA_ERR_WORKSPACE;
   p.work = workspace;
-  if (need > 0 && lossless && lora::split_fp32_adapter(p.act, p.adapter, p.nf4)) assign_split(p);
+  if (p.n_groups > 0 && lossless && lora::split_fp32_adapter(p.act, p.adapter, nf4 && !use_panel)) assign_split(p);
+  if (use_panel) p.panel = static_cast<char*>(workspace) + round_up(adapter_bytes_for(p, lossless, false));
 
   // the output must not overlap any input or the workspace
   if (T > 0) {
@@ -309,6 +322,14 @@ size_t lora_linear_workspace_size(int64_t T, int64_t K, int64_t N, const int32_t
     return bytes;
   }
   return static_cast<size_t>(T) * static_cast<size_t>(cols) * static_cast<size_t>(esz(adapter_dtype));
+}
+
+size_t lora_linear_nf4_workspace_size(int64_t T, int64_t K, int64_t N, int32_t rank, int32_t adapter_dtype,
+                                      int32_t quality) {
+  if (T <= 0 || K <= 0 || N <= 0 || !dtype_ok(adapter_dtype)) return 0;
+  const size_t ad = rank > 0 ? lora_linear_workspace_size(T, K, N, &rank, 1, adapter_dtype, quality) : 0;
+  if (!lora::nf4_uses_panel(true, quality == LORA_LOSSLESS, T)) return ad;
+  return round_up(ad) + panel_bytes(N, K);
 }
 
 const char* lora_status_string(int status) {

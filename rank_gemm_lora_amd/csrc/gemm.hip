@@ -1590,6 +1590,52 @@ __global__ __launch_bounds__(256) void split_b_kernel(const float* __restrict__ 
   }
 }
 
+// 4-bit weight, many tokens: the whole weight dequantized once into the bf16
+// panel [N, K] (the same element value as inside the GEMM: RN_bf16 of the fp32
+// product codebook[code] * absmax). Lane t of a wave writes the 16 output bytes
+// at t * 16 + j * 1024 of the wave's 4 KB (2048 elements) for j = 0 .. 3, so
+// every load and store instruction of the wave covers one contiguous range:
+// 8 elements = one code dword, one absmax. Both nibbles of a code byte come from
+// a 256-entry LDS table of codebook pairs in one 8-byte read.
+constexpr int kPanelWaveElems = 2048;
+
+__global__ __launch_bounds__(256) void nf4_panel_kernel(const uint8_t* __restrict__ codes,
+                                                        const float* __restrict__ absmax,
+                                                        const float* __restrict__ codebook, int64_t n_elems,
+                                                        bf16_bits* __restrict__ panel) {
+  __shared__ f32x2 pair[256];
+  pair[threadIdx.x] = f32x2{codebook[threadIdx.x & 15], codebook[threadIdx.x >> 4]};
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t wave0 = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int64_t wstride = static_cast<int64_t>(gridDim.x) * 4;
+  for (int64_t wv = wave0; wv * kPanelWaveElems < n_elems; wv += wstride) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t e0 = wv * kPanelWaveElems + j * 512 + lane * 8;  // first of this lane's 8 elements
+      if (e0 >= n_elems) continue;  // n_elems is a multiple of 64: 8 elements are all in or all out
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + e0 / 2);
+      const float a = absmax[e0 >> 6];
+      u32x4 o;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {  // byte b holds elements e0 + 2b (bits 0-3) and e0 + 2b + 1 (bits 4-7)
+        const f32x2 v = pair[(w >> (8 * b)) & 0xffu];
+        o[b] = pack_bf16x2(v[0] * a, v[1] * a);
+      }
+      *reinterpret_cast<u32x4*>(panel + e0) = o;
+    }
+  }
+}
+
+hipError_t launch_nf4_panel(const LinearProblem& p, hipStream_t s) {
+  const int64_t n = p.N * p.K;
+  const int64_t waves = (n + kPanelWaveElems - 1) / kPanelWaveElems;
+  const int64_t blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL(nf4_panel_kernel, dim3(static_cast<unsigned>(blocks < 8192 ? blocks : 8192)), dim3(256), 0, s,
+                     p.codes, p.absmax, p.codebook, n, static_cast<bf16_bits*>(p.panel));
+  return hipGetLastError();
+}
+
 // The split path's phase 1: split copies of every group, then the producer.
 hipError_t split_producer(const LinearProblem& p, hipStream_t s) {
   for (int i = 0; i < p.n_groups; ++i) {
@@ -1626,6 +1672,21 @@ hipError_t split_gemm(const LinearProblem& p, hipStream_t s) {
 
 hipError_t launch_lossless(const LinearProblem& p, hipStream_t s, int phase) {
   if (p.T == 0) return hipSuccess;
+  if (p.nf4 && p.panel != nullptr) {
+    // the weight dequantized once into the panel, then the bf16 path over it
+    if (phase != 2) {
+      const hipError_t e = launch_nf4_panel(p, s);
+      if (e != hipSuccess) return e;
+    }
+    LinearProblem q = p;
+    q.nf4 = false;
+    q.W = p.panel;
+    q.codes = nullptr;
+    q.absmax = nullptr;
+    q.codebook = nullptr;
+    q.panel = nullptr;
+    return launch_lossless(q, s, phase);
+  }
   const bool act_bf16 = p.act == Elt::BF16, ad_bf16 = p.adapter == Elt::BF16;
   // fp32 adapter on bf16 activations: the adapter products on bf16 MFMA over the hi / lo split
   if (split_fp32_adapter(p.act, p.adapter, p.nf4)) {

@@ -35,6 +35,14 @@ struct GroupDev {
   void* B2;
 };
 
+// Lossless 4-bit weight with at least this many tokens: the weight is
+// dequantized once per call into a bf16 panel [N, K] in the workspace and the
+// bf16 GEMM runs on it. Below it, every output tile dequantizes its own weight
+// stages in registers inside the GEMM (the panel's write and re-read would cost
+// more than the repeated dequantization saves).
+constexpr int64_t kNf4PanelMinT = 512;
+inline bool nf4_uses_panel(bool nf4, bool lossless, int64_t T) { return nf4 && lossless && T >= kNf4PanelMinT; }
+
 // Lossless fp32 adapter on bf16 activations: the products run on bf16 MFMA
 // over the hi/lo split (the t~ block of a group is then t_hi | t_hi | t_lo,
 // 3 r_pad columns). Workspace bytes of that layout.
@@ -46,6 +54,7 @@ struct LinearProblem {
   const void* x; int64_t ldx;
   const void* W;                                  // [N, K] act dtype (unused for 4-bit)
   const uint8_t* codes; const float* absmax; const float* codebook;  // 4-bit weight
+  void* panel;       // 4-bit weight, lossless, T >= kNf4PanelMinT: bf16 [N, K] dequantized copy in the workspace
   const void* bias;
   void* y; int64_t ldy;
   int64_t T, N, K;

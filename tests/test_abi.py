@@ -152,6 +152,19 @@ def nf4(**kw):
                                        a["alpha"], 1.0, 1.0, a["y"], a["ldy"], a["q"], WSP, 1 << 30, None)
 
 
+def test_nf4_workspace_query():
+    q = rg.lora_linear_nf4_workspace_size
+    assert q(130, 256, 300, 16, BF16) == rg.lora_linear_workspace_size(130, 256, 300, [16], BF16)
+    assert q(130, 256, 300, 0, BF16) == 0                              # no adapter, in-GEMM dequantization
+    assert q(511, 256, 300, 16, BF16, EXACT) == rg.lora_linear_workspace_size(511, 256, 300, [16], BF16, EXACT)
+    # from 512 tokens (lossless) a bf16 panel of the weight follows the adapter's share, 256-byte aligned
+    ad = rg.lora_linear_workspace_size(600, 256, 300, [16], BF16)
+    assert q(600, 256, 300, 16, BF16) == (ad + 255) // 256 * 256 + 300 * 256 * 2
+    assert q(600, 256, 300, 0, BF16) == 300 * 256 * 2
+    assert q(600, 256, 300, 16, BF16, EXACT) == rg.lora_linear_workspace_size(600, 256, 300, [16], BF16, EXACT)
+    assert q(0, 256, 300, 16, BF16) == 0
+
+
 def test_nf4_validation():
     assert nf4() == OK
     assert nf4(bs=32) == UNSUP

@@ -346,10 +346,14 @@ def _nf4_small(T=130, K=256, N=300, r=16, seed=41, bias=True, adapter="bf16"):
                 alpha=32.0, N=N)
 
 
+# T = 130: each output tile dequantizes its weight stages inside the GEMM;
+# T = 600 (>= 512 tokens): the weight is dequantized once into a bf16 panel in
+# the workspace, then the bf16 GEMM runs over it (three m-tiles, ragged tail).
+@pytest.mark.parametrize("T", [130, 600])
 @pytest.mark.parametrize("adapter", ["bf16", "f32"])
-def test_nf4_linear(adapter):
-    d = _nf4_small(adapter=adapter)
-    say(f"case nf4 adapter={adapter}")
+def test_nf4_linear(adapter, T):
+    d = _nf4_small(T=T, adapter=adapter)
+    say(f"case nf4 adapter={adapter} T={T}")
     y64 = lo.lora_linear_nf4(d["x"], d["codes"], d["absmax"], d["codebook"], 64, d["b"], d["A"], d["B"],
                              d["alpha"], d["rank"], 1.0, 0.9)
     yc = ec.chain_nf4(d["x"], d["codes"], d["absmax"], d["codebook"], 64, d["b"], d["A"], d["B"], d["alpha"],
@@ -367,17 +371,19 @@ def test_nf4_linear(adapter):
     assert_bitwise(ye, yc, "nf4 exact")
 
 
-def test_nf4_one_hot_returns_dequantized_columns():
-    d = _nf4_small(T=256, K=256, N=300, bias=False)
-    say("case nf4 one-hot")
-    x = torch.zeros((256, 256), dtype=torch.bfloat16)
-    x[torch.arange(256), torch.arange(256)] = 1.0  # row m selects k = m
+@pytest.mark.parametrize("T", [256, 512])
+def test_nf4_one_hot_returns_dequantized_columns(T):
+    d = _nf4_small(T=T, K=256, N=300, bias=False)
+    say(f"case nf4 one-hot T={T}")
+    x = torch.zeros((T, 256), dtype=torch.bfloat16)
+    x[torch.arange(T), torch.arange(T) % 256] = 1.0  # row m selects k = m mod 256
     Wq = ec.chain_nf4_weight(d["codes"], d["absmax"], d["codebook"], 256)  # [N, K]
+    want = Wq.T[np.arange(T) % 256].copy()
     for q in ("lossless", "exact"):
         y = rg.lora_linear_nf4(dev(x), dev(d["codes"]), dev(d["absmax"]), dev(d["codebook"]), 300, None, None,
                                None, 32.0, quality=q)
         torch.cuda.synchronize()
-        assert_bitwise(y, Wq.T.copy(), f"one-hot {q}")
+        assert_bitwise(y, want, f"one-hot {q}")
 
 
 # ------------------------------------------------------------------ dense patches
