@@ -224,13 +224,17 @@ int dense_patch_apply(void* dst, int32_t dst_dtype, const int64_t* dst_shape, in
  * Workspace bytes a call with T tokens, K inputs and N outputs needs for
  * adapters of the given ranks (`ranks` is a HOST array of n_ranks entries: one
  * for lora_linear_fwd and lora_linear_nf4_fwd, one per group for
- * lora_linear_stacked_fwd). It holds the rank-wide intermediate
- * [T, R] in the adapter dtype, R = the sum of the ranks rounded up to
- * multiples of 64. A lossless call with an fp32 adapter on bf16 activations
- * runs the adapter products on bf16 MFMA over an exact hi + lo split of each
- * fp32 value, so its workspace holds the intermediate as [T, 3 R] bf16 plus
- * the split copies of A ([2 R, K]) and B (at most [N, 3 R]), each region
- * 256-byte aligned. Returns 0 when no rank is positive or T, K or N <= 0.
+ * lora_linear_stacked_fwd; n_ranks may be 0 for a call without adapters). It
+ * holds the rank-wide intermediate [T, R] in the adapter dtype, R = the sum of
+ * the ranks rounded up to multiples of 64. A lossless call with an fp32
+ * adapter on bf16 activations runs the adapter products on bf16 MFMA over an
+ * exact hi + lo split of each fp32 value, so its workspace holds the
+ * intermediate as [T, 3 R] bf16 plus the split copies of A ([2 R, K]) and B (at
+ * most [N, 3 R]), each region 256-byte aligned. A lossless call with at most 64
+ * tokens on bf16 activations splits K into S chunks and needs S fp32 partial
+ * sums of the outputs and of x.A^T instead ([S, T, round_up(N, 64) + R] fp32);
+ * for T <= 64 the larger of the layouts is returned. Returns 0 when T, K or
+ * N <= 0, or when no rank is positive and T > 64.
  */
 size_t lora_linear_workspace_size(int64_t T, int64_t K, int64_t N, const int32_t* ranks, int32_t n_ranks,
                                   int32_t adapter_dtype, int32_t quality);

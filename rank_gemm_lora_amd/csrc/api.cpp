@@ -105,6 +105,7 @@ size_t adapter_bytes_for(const LinearProblem& p, bool lossless, bool gemm_nf4) {
 size_t panel_bytes(int64_t N, int64_t K) { return static_cast<size_t>(N) * static_cast<size_t>(K) * 2; }
 
 size_t workspace_bytes_for(const LinearProblem& p, bool lossless) {
+  if (lora::skinny_path(p.act, lossless, p.T, p.ldt)) return lora::skinny_bytes(p.T, p.K, p.N, p.ldt);
   const bool panel = lora::nf4_uses_panel(p.nf4, lossless, p.T);
   const size_t ad = adapter_bytes_for(p, lossless, p.nf4 && !panel);
   return panel ? round_up(ad) + panel_bytes(p.N, p.K) : ad;
@@ -186,12 +187,17 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
   if (st != LORA_OK) return st;
 
   const bool lossless = quality == LORA_LOSSLESS;
-  const bool use_panel = lora::nf4_uses_panel(nf4, lossless, T);
+  const bool use_skinny = lora::skinny_path(p.act, lossless, T, p.ldt);
+  const bool use_panel = !use_skinny && lora::nf4_uses_panel(nf4, lossless, T);
   const size_t need = workspace_bytes_for(p, lossless);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LORA_ERR_WORKSPACE;
   p.work = workspace;
-  if (p.n_groups > 0 && lossless && lora::split_fp32_adapter(p.act, p.adapter, nf4 && !use_panel)) assign_split(p);
-  if (use_panel) p.panel = static_cast<char*>(workspace) + round_up(adapter_bytes_for(p, lossless, false));
+  if (use_skinny) {
+    p.skinny = static_cast<float*>(workspace);
+  } else {
+    if (p.n_groups > 0 && lossless && lora::split_fp32_adapter(p.act, p.adapter, nf4 && !use_panel)) assign_split(p);
+    if (use_panel) p.panel = static_cast<char*>(workspace) + round_up(adapter_bytes_for(p, lossless, false));
+  }
 
   // the output must not overlap any input or the workspace
   if (T > 0) {
@@ -301,7 +307,8 @@ int dense_patch_apply(void* dst, int32_t dst_dtype, const int64_t* dst_shape, in
 
 size_t lora_linear_workspace_size(int64_t T, int64_t K, int64_t N, const int32_t* ranks, int32_t n_ranks,
                                   int32_t adapter_dtype, int32_t quality) {
-  if (T <= 0 || K <= 0 || N <= 0 || ranks == nullptr || n_ranks <= 0 || !dtype_ok(adapter_dtype)) return 0;
+  if (T <= 0 || K <= 0 || N <= 0 || n_ranks < 0 || (n_ranks > 0 && ranks == nullptr) || !dtype_ok(adapter_dtype))
+    return 0;
   int64_t cols = 0;
   int n = 0;
   for (int i = 0; i < n_ranks; ++i)
@@ -309,7 +316,11 @@ size_t lora_linear_workspace_size(int64_t T, int64_t K, int64_t N, const int32_t
       cols += lora::rank_pad(ranks[i]);
       ++n;
     }
-  if (cols == 0) return 0;
+  // few tokens (lossless, bf16 activations): fp32 partial sums instead of the
+  // intermediate; the activation dtype is not an argument, so the larger of the two
+  const size_t skinny = (quality == LORA_LOSSLESS && T <= lora::kSkinnyMaxT && cols <= lora::kSkinnyMaxLdt)
+                            ? lora::skinny_bytes(T, K, N, cols) : 0;
+  if (cols == 0) return skinny;
   if (quality == LORA_LOSSLESS && adapter_dtype == LORA_F32) {
     // the bf16-activation layout (the larger of the two an fp32 adapter can need);
     // every group's n_cols is at most N
@@ -319,14 +330,16 @@ size_t lora_linear_workspace_size(int64_t T, int64_t K, int64_t N, const int32_t
       const size_t rp = static_cast<size_t>(lora::rank_pad(ranks[i]));
       bytes += round_up(2 * rp * static_cast<size_t>(K) * 2) + round_up(static_cast<size_t>(N) * 3 * rp * 2);
     }
-    return bytes;
+    return std::max(bytes, skinny);
   }
-  return static_cast<size_t>(T) * static_cast<size_t>(cols) * static_cast<size_t>(esz(adapter_dtype));
+  return std::max(static_cast<size_t>(T) * static_cast<size_t>(cols) * static_cast<size_t>(esz(adapter_dtype)), skinny);
 }
 
 size_t lora_linear_nf4_workspace_size(int64_t T, int64_t K, int64_t N, int32_t rank, int32_t adapter_dtype,
                                       int32_t quality) {
   if (T <= 0 || K <= 0 || N <= 0 || !dtype_ok(adapter_dtype)) return 0;
+  if (quality == LORA_LOSSLESS && T <= lora::kSkinnyMaxT)  // activations are bf16: the skinny path
+    return lora::skinny_bytes(T, K, N, rank > 0 ? lora::rank_pad(rank) : 0);
   const size_t ad = rank > 0 ? lora_linear_workspace_size(T, K, N, &rank, 1, adapter_dtype, quality) : 0;
   if (!lora::nf4_uses_panel(true, quality == LORA_LOSSLESS, T)) return ad;
   return round_up(ad) + panel_bytes(N, K);

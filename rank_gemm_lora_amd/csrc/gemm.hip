@@ -1559,6 +1559,327 @@ hipError_t launch_down(const LinearProblem& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Few tokens (skinny_path): row block b of 64 rows, 4 waves of 16; blocks
+// b < nbw are weight rows, the rest the padded A rows of the groups in order
+// (block b - nbw starts at column 64 (b - nbw) of the rank-wide layout). Grid y
+// is the K chunk (a multiple of 128). Fragments go from global memory straight
+// to registers through range-checked buffer loads (rows past the end, tokens
+// past T and k past the chunk read as zeros), one 128-k group ahead of the
+// MFMAs. Within a group lane (r, q) takes the 32 consecutive k at 32 q and
+// feeds them to v_mfma_f32_16x16x32_bf16 as 4 steps of 8 (step s: k = 32 q +
+// 8 s + 0..7) for row r (the "A" operand) and for token 16 tb + r (the "B"
+// operand) alike, so each step sums 32 distinct k and the 4 steps cover the
+// group: the same dot product, with each lane's weight bytes contiguous (16
+// code bytes of a 4-bit row, 64 bytes of a bf16 row, 128 of an fp32 A row).
+// After the chunk a lane holds the partial sums of rows 4q .. 4q + 3 of token
+// 16 tb + r. A 4-bit weight is looked up as byte pairs in an LDS table,
+// multiplied by its block's absmax in fp32 and rounded to bf16; an fp32 A row
+// is split exactly into hi = RN_bf16(v) and lo = RN_bf16(v - hi), both through
+// the MFMA into the same fp32 sum.
+__device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
+
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past every range: the load returns zeros
+enum { kRowsBf16 = 0, kRowsNf4 = 1, kRowsF32 = 2 };
+
+template <int KIND, int TB>
+struct SkGroup {
+  static constexpr int NW = KIND == kRowsBf16 ? 4 : (KIND == kRowsNf4 ? 1 : 8);  // 16-byte pieces of the row
+  u32x4 w[NW];
+  float am;          // 4-bit: the block's absmax
+  u32x4 x[TB][4];    // token fragments of the 4 steps
+};
+
+struct SkSrc {
+  __amdgpu_buffer_rsrc_t w, am, x;  // rows of this wave (from its first row), absmax likewise, all tokens
+  uint32_t w_row_b, ldx_b;          // row strides in bytes
+  int64_t K;
+};
+
+template <int KIND, int TB>
+__device__ __forceinline__ void sk_load(SkGroup<KIND, TB>& f, const SkSrc& src, int r, int q, int64_t kg,
+                                        int64_t k_hi) {
+  const int64_t kl = kg + 32 * q;  // the lane's first k of the group
+  const uint32_t row = static_cast<uint32_t>(r) * src.w_row_b;
+  if constexpr (KIND == kRowsNf4) {
+    // K and the chunk ends are multiples of 64: the lane's 32 elements are all in
+    // or all out, and sit inside one 64-element block
+    const bool in = kl < k_hi;
+    f.w[0] = __builtin_amdgcn_raw_buffer_load_b128(src.w, in ? row + static_cast<uint32_t>(kl / 2) : kOutOfRange, 0, 0);
+    const uint32_t blk = static_cast<uint32_t>((static_cast<int64_t>(r) * src.K + kl) / 64);
+    f.am = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(src.am, in ? blk * 4 : kOutOfRange, 0, 0));
+  } else {
+    constexpr int EB = KIND == kRowsF32 ? 4 : 2;  // element bytes; K is a multiple of 8 (whole pieces)
+#pragma unroll
+    for (int i = 0; i < SkGroup<KIND, TB>::NW; ++i) {
+      const int64_t ke = kl + i * (16 / EB);
+      f.w[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          src.w, ke < k_hi ? row + static_cast<uint32_t>(ke * EB) : kOutOfRange, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int64_t ke = kl + 8 * st;
+      const uint32_t off = static_cast<uint32_t>(tb * 16 + r) * src.ldx_b + static_cast<uint32_t>(ke * 2);
+      f.x[tb][st] = __builtin_amdgcn_raw_buffer_load_b128(src.x, ke < k_hi ? off : kOutOfRange, 0, 0);
+    }
+}
+
+template <int KIND, int TB>
+__device__ __forceinline__ void sk_mma(f32x4 (&acc)[TB], const SkGroup<KIND, TB>& f, const f32x2* pair) {
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    if constexpr (KIND == kRowsF32) {
+      const u32x4 v0 = f.w[2 * st], v1 = f.w[2 * st + 1];
+      const float v[8] = {__uint_as_float(v0[0]), __uint_as_float(v0[1]), __uint_as_float(v0[2]),
+                          __uint_as_float(v0[3]), __uint_as_float(v1[0]), __uint_as_float(v1[1]),
+                          __uint_as_float(v1[2]), __uint_as_float(v1[3])};
+      u32x4 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16_bits h0 = f32_to_bf16_rne(v[2 * e]), h1 = f32_to_bf16_rne(v[2 * e + 1]);
+        const bf16_bits l0 = f32_to_bf16_rne(v[2 * e] - bf16_to_f32(h0));
+        const bf16_bits l1 = f32_to_bf16_rne(v[2 * e + 1] - bf16_to_f32(h1));
+        hi[e] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+        lo[e] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+      }
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) {
+        const bf16x8 xf = __builtin_bit_cast(bf16x8, f.x[tb][st]);
+        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, hi), xf, acc[tb], 0, 0, 0);
+        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, lo), xf, acc[tb], 0, 0, 0);
+      }
+    } else {
+      bf16x8 a;
+      if constexpr (KIND == kRowsNf4) {
+        const uint32_t w = f.w[0][st];  // 4 code bytes: elements 8 st .. 8 st + 7 of the lane's 32
+        u32x4 o;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {  // byte bb: element 2 bb in bits 0-3, 2 bb + 1 in bits 4-7
+          const f32x2 v = pair[(w >> (8 * bb)) & 0xffu];
+          o[bb] = pack_bf16x2(v[0] * f.am, v[1] * f.am);
+        }
+        a = __builtin_bit_cast(bf16x8, o);
+      } else {
+        a = __builtin_bit_cast(bf16x8, f.w[st]);
+      }
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+        acc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, f.x[tb][st]), acc[tb], 0, 0, 0);
+    }
+  }
+}
+
+// The chunk [k_lo, k_hi) of this wave's 16 rows, one group of loads ahead.
+template <int KIND, int TB>
+__device__ __forceinline__ void sk_chunk(f32x4 (&acc)[TB], const SkSrc& src, int r, int q, int64_t k_lo,
+                                         int64_t k_hi, const f32x2* pair) {
+  SkGroup<KIND, TB> cur;
+  sk_load<KIND, TB>(cur, src, r, q, k_lo, k_hi);
+  int64_t kg = k_lo;
+  for (; kg + 128 < k_hi; kg += 128) {
+    SkGroup<KIND, TB> nxt;
+    sk_load<KIND, TB>(nxt, src, r, q, kg + 128, k_hi);
+    sk_mma<KIND, TB>(acc, cur, pair);
+    cur = nxt;
+  }
+  sk_mma<KIND, TB>(acc, cur, pair);
+}
+
+template <bool NF4, bool AF32, int TB>
+__global__ __launch_bounds__(256) void skinny_kernel(LinearProblem p, int nbw, int64_t kchunk, int64_t npad) {
+  __shared__ f32x2 pair[256];
+  if constexpr (NF4) {
+    pair[threadIdx.x] = f32x2{p.codebook[threadIdx.x & 15], p.codebook[threadIdx.x >> 4]};
+    __syncthreads();
+  }
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, q = lane >> 4;
+  const int split = blockIdx.y;
+  const int64_t k_lo = split * kchunk;
+  const int64_t k_hi = min<int64_t>(p.K, k_lo + kchunk);
+  f32x4 acc[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  SkSrc src;
+  src.K = p.K;
+  src.ldx_b = static_cast<uint32_t>(p.ldx * 2);
+  src.x = make_rsrc(p.x, static_cast<uint32_t>(p.T) * src.ldx_b);
+  const int b = blockIdx.x;
+  if (b < nbw) {
+    const int64_t n0 = static_cast<int64_t>(b) * kSkinnyRows + wave * 16;
+    // (wave-uniform by construction; readfirstlane keeps the buffer descriptors in scalar registers)
+    const int64_t rows = __builtin_amdgcn_readfirstlane(static_cast<int>(max<int64_t>(0, min<int64_t>(16, p.N - n0))));
+    if constexpr (NF4) {
+      src.w_row_b = static_cast<uint32_t>(p.K / 2);
+      src.w = make_rsrc(p.codes + n0 * (p.K / 2), static_cast<uint32_t>(rows) * src.w_row_b);
+      src.am = make_rsrc(p.absmax + n0 * (p.K / 64), static_cast<uint32_t>(rows * (p.K / 64) * 4));
+      sk_chunk<kRowsNf4, TB>(acc, src, r, q, k_lo, k_hi, pair);
+    } else {
+      src.w_row_b = static_cast<uint32_t>(p.K * 2);
+      src.w = make_rsrc(static_cast<const bf16_bits*>(p.W) + n0 * p.K, static_cast<uint32_t>(rows) * src.w_row_b);
+      sk_chunk<kRowsBf16, TB>(acc, src, r, q, k_lo, k_hi, pair);
+    }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int64_t t = tb * 16 + r;
+      if (t < p.T) *reinterpret_cast<f32x4*>(p.skinny + (split * p.T + t) * npad + n0 + 4 * q) = acc[tb];
+    }
+    return;
+  }
+  // adapter rows: x . A_g^T into the rank-wide partial sums
+  const int rb = (b - nbw) * kSkinnyRows;
+  int gi = 0;
+  while (gi + 1 < p.n_groups && rb >= p.g[gi + 1].t_col) ++gi;
+  const GroupDev& g = p.g[gi];
+  const int q0 = rb - g.t_col + wave * 16;  // first A row of this wave
+  const int64_t rows = __builtin_amdgcn_readfirstlane(max(0, min(16, g.rank - q0)));
+  if constexpr (AF32) {
+    src.w_row_b = static_cast<uint32_t>(p.K * 4);
+    src.w = make_rsrc(static_cast<const float*>(g.A) + static_cast<int64_t>(q0) * p.K,
+                      static_cast<uint32_t>(rows) * src.w_row_b);
+    sk_chunk<kRowsF32, TB>(acc, src, r, q, k_lo, k_hi, pair);
+  } else {
+    src.w_row_b = static_cast<uint32_t>(p.K * 2);
+    src.w = make_rsrc(static_cast<const bf16_bits*>(g.A) + static_cast<int64_t>(q0) * p.K,
+                      static_cast<uint32_t>(rows) * src.w_row_b);
+    sk_chunk<kRowsBf16, TB>(acc, src, r, q, k_lo, k_hi, pair);
+  }
+  float* pt = p.skinny + static_cast<int64_t>(gridDim.y) * p.T * npad;
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    const int64_t t = tb * 16 + r;
+    if (t < p.T) *reinterpret_cast<f32x4*>(pt + (split * p.T + t) * p.ldt + g.t_col + q0 + 4 * q) = acc[tb];
+  }
+}
+
+// Second kernel of the skinny path: grid (ceil(N / 256), ceil(T / 4)). The
+// block first forms t~ = RN_adt(s . t) of its 4 tokens in LDS (t = the K
+// chunks' partial sums added in chunk order), then each thread takes one output
+// column: acc = the weight partial sums in chunk order, += t~ . B_g^T in fp32
+// (rank index ascending) for the group covering the column, + bias, one
+// rounding. Token rows past T repeat the last token (valid memory) and are
+// never stored; all partial sums of a thread are loaded before they are added.
+constexpr int kFinishTokens = 4;
+constexpr int kMaxChunks = 8;  // skinny_plan never makes more
+
+template <bool AF32>
+__global__ __launch_bounds__(256) void skinny_finish_kernel(LinearProblem p, int S, int64_t npad) {
+  extern __shared__ float tt[];  // [kFinishTokens, ldt]
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kFinishTokens;
+  const int ldt = static_cast<int>(p.ldt);
+  const float* pt = p.skinny + static_cast<int64_t>(S) * p.T * npad;
+  for (int c = threadIdx.x; c < kFinishTokens * ldt; c += 256) {
+    const int j = c / ldt, col = c - j * ldt;
+    const int64_t t = min<int64_t>(t0 + j, p.T - 1);
+    float v[kMaxChunks];
+#pragma unroll
+    for (int s = 0; s < kMaxChunks; ++s) v[s] = s < S ? pt[(s * p.T + t) * ldt + col] : 0.f;
+    float sum = 0.f;
+#pragma unroll
+    for (int s = 0; s < kMaxChunks; ++s)
+      if (s < S) sum += v[s];
+    int gi = 0;
+    while (gi + 1 < p.n_groups && col >= p.g[gi + 1].t_col) ++gi;
+    const float sc = p.g[gi].scale;
+    if (sc != 1.0f) sum *= sc;
+    tt[c] = AF32 ? sum : bf16_to_f32(f32_to_bf16_rne(sum));
+  }
+  __syncthreads();
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (n >= p.N) return;
+  float acc[kFinishTokens];
+  {
+    float v[kFinishTokens][kMaxChunks];
+#pragma unroll
+    for (int i = 0; i < kFinishTokens; ++i) {
+      const int64_t t = min<int64_t>(t0 + i, p.T - 1);
+#pragma unroll
+      for (int s = 0; s < kMaxChunks; ++s) v[i][s] = s < S ? p.skinny[(s * p.T + t) * npad + n] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kFinishTokens; ++i) {
+      acc[i] = 0.f;
+#pragma unroll
+      for (int s = 0; s < kMaxChunks; ++s)
+        if (s < S) acc[i] += v[i][s];
+    }
+  }
+  for (int gi = 0; gi < p.n_groups; ++gi) {
+    const GroupDev& g = p.g[gi];
+    if (n < g.col_off || n >= g.col_off + g.n_cols) continue;
+    const int64_t row = (n - g.col_off) * g.rank;
+    const float* tg = tt + g.t_col;
+    int qq = 0;
+    // the row of B in 16-byte pieces when its start keeps that alignment (B itself is 16-byte aligned)
+    constexpr int PE = AF32 ? 4 : 8;  // elements per piece
+    if (g.rank % PE == 0) {
+      for (; qq < g.rank; qq += PE) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const char*>(g.B) + (row + qq) * (AF32 ? 4 : 2));
+        float bv[PE];
+#pragma unroll
+        for (int e = 0; e < PE; ++e)
+          bv[e] = AF32 ? __uint_as_float(w[e]) : __uint_as_float(e & 1 ? w[e >> 1] & 0xffff0000u : w[e >> 1] << 16);
+#pragma unroll
+        for (int e = 0; e < PE; ++e)
+#pragma unroll
+          for (int i = 0; i < kFinishTokens; ++i) acc[i] = fmaf(tg[i * ldt + qq + e], bv[e], acc[i]);
+      }
+    }
+    for (; qq < g.rank; ++qq) {
+      const float bv = AF32 ? static_cast<const float*>(g.B)[row + qq]
+                            : bf16_to_f32(static_cast<const bf16_bits*>(g.B)[row + qq]);
+#pragma unroll
+      for (int i = 0; i < kFinishTokens; ++i) acc[i] = fmaf(tg[i * ldt + qq], bv, acc[i]);
+    }
+  }
+  const bool has_bias = p.bias != nullptr;
+  const float bias = has_bias ? bf16_to_f32(static_cast<const bf16_bits*>(p.bias)[n]) : 0.f;
+#pragma unroll
+  for (int i = 0; i < kFinishTokens; ++i) {
+    if (t0 + i < p.T)
+      static_cast<bf16_bits*>(p.y)[(t0 + i) * p.ldy + n] = f32_to_bf16_rne(has_bias ? acc[i] + bias : acc[i]);
+  }
+}
+
+template <bool NF4, bool AF32>
+hipError_t launch_skinny_tb(const LinearProblem& p, hipStream_t s, dim3 grid, int nbw, int64_t kchunk,
+                            int64_t npad) {
+  switch ((p.T + 15) / 16) {
+    case 1: hipLaunchKernelGGL((skinny_kernel<NF4, AF32, 1>), grid, dim3(256), 0, s, p, nbw, kchunk, npad); break;
+    case 2: hipLaunchKernelGGL((skinny_kernel<NF4, AF32, 2>), grid, dim3(256), 0, s, p, nbw, kchunk, npad); break;
+    case 3: hipLaunchKernelGGL((skinny_kernel<NF4, AF32, 3>), grid, dim3(256), 0, s, p, nbw, kchunk, npad); break;
+    default: hipLaunchKernelGGL((skinny_kernel<NF4, AF32, 4>), grid, dim3(256), 0, s, p, nbw, kchunk, npad); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny(const LinearProblem& p, hipStream_t s) {
+  int S;
+  int64_t kchunk;
+  skinny_plan(p.K, &S, &kchunk);
+  const int nbw = static_cast<int>((p.N + kSkinnyRows - 1) / kSkinnyRows);
+  const int nba = static_cast<int>(p.ldt / kSkinnyRows);
+  const int64_t npad = skinny_npad(p.N);
+  const bool af32 = p.n_groups > 0 && p.adapter == Elt::F32;
+  const dim3 grid(static_cast<unsigned>(nbw + nba), static_cast<unsigned>(S));
+  hipError_t e;
+  if (p.nf4) e = af32 ? launch_skinny_tb<true, true>(p, s, grid, nbw, kchunk, npad)
+                      : launch_skinny_tb<true, false>(p, s, grid, nbw, kchunk, npad);
+  else e = af32 ? launch_skinny_tb<false, true>(p, s, grid, nbw, kchunk, npad)
+                : launch_skinny_tb<false, false>(p, s, grid, nbw, kchunk, npad);
+  if (e != hipSuccess) return e;
+  // t~ of a block's tokens in LDS: 4 x ldt fp32, ldt <= 8 x 1024 (at most 128 KB)
+  const dim3 fgrid(static_cast<unsigned>((p.N + 255) / 256),
+                   static_cast<unsigned>((p.T + kFinishTokens - 1) / kFinishTokens));
+  const size_t shmem = static_cast<size_t>(kFinishTokens) * static_cast<size_t>(p.ldt) * 4;
+  if (af32) hipLaunchKernelGGL(skinny_finish_kernel<true>, fgrid, dim3(256), shmem, s, p, S, npad);
+  else hipLaunchKernelGGL(skinny_finish_kernel<false>, fgrid, dim3(256), shmem, s, p, S, npad);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // Split copies of an fp32 adapter (layout in GroupDev): hi(v) = RN_bf16(v) and
@@ -1672,6 +1993,8 @@ hipError_t split_gemm(const LinearProblem& p, hipStream_t s) {
 
 hipError_t launch_lossless(const LinearProblem& p, hipStream_t s, int phase) {
   if (p.T == 0) return hipSuccess;
+  // few tokens: the rank-wide product runs inside the same launches (phase 1 has nothing to do)
+  if (p.skinny != nullptr) return phase == 1 ? hipSuccess : launch_skinny(p, s);
   if (p.nf4 && p.panel != nullptr) {
     // the weight dequantized once into the panel, then the bf16 path over it
     if (phase != 2) {

@@ -35,13 +35,41 @@ struct GroupDev {
   void* B2;
 };
 
-// Lossless 4-bit weight with at least this many tokens: the weight is
-// dequantized once per call into a bf16 panel [N, K] in the workspace and the
-// bf16 GEMM runs on it. Below it, every output tile dequantizes its own weight
-// stages in registers inside the GEMM (the panel's write and re-read would cost
-// more than the repeated dequantization saves).
-constexpr int64_t kNf4PanelMinT = 512;
-inline bool nf4_uses_panel(bool nf4, bool lossless, int64_t T) { return nf4 && lossless && T >= kNf4PanelMinT; }
+// Few tokens (lossless, bf16 activations, T <= kSkinnyMaxT): the weight read is
+// the whole cost. Each wave multiplies 16 weight rows (or adapter A rows) over
+// one K chunk by all the tokens, straight from global memory (a 4-bit weight is
+// dequantized in registers); the K chunks write fp32 partial sums [S, T, .] to
+// the workspace and a second kernel adds them in chunk order, forms the
+// rank-wide intermediate, adds the rank-r update and the bias, and rounds once.
+constexpr int64_t kSkinnyMaxT = 64;
+constexpr int kSkinnyRows = 64;      // weight rows per workgroup (4 waves of 16)
+constexpr int64_t kSkinnyMaxLdt = 4096;  // sum of the padded ranks (the finishing block holds 4 x ldt fp32 in LDS)
+inline bool skinny_path(Elt act, bool lossless, int64_t T, int64_t ldt) {
+  return lossless && act == Elt::BF16 && T > 0 && T <= kSkinnyMaxT && ldt <= kSkinnyMaxLdt;
+}
+// K chunk (a multiple of 128 elements) and number of chunks S <= 8: about 8 chunks,
+// fixed by K alone, so the summation order of an output does not depend on N or
+// on the adapters (a stacked call equals one call per group, bit for bit).
+inline void skinny_plan(int64_t K, int* S, int64_t* kchunk) {
+  int64_t c = (K + 7) / 8;
+  c = (c + 127) / 128 * 128;
+  *kchunk = c;
+  *S = static_cast<int>((K + c - 1) / c);
+}
+inline int64_t skinny_npad(int64_t N) { return (N + kSkinnyRows - 1) / kSkinnyRows * kSkinnyRows; }
+// fp32 partial sums of the outputs [S, T, npad] followed by those of x.A^T [S, T, ldt].
+inline size_t skinny_bytes(int64_t T, int64_t K, int64_t N, int64_t ldt) {
+  int S;
+  int64_t c;
+  skinny_plan(K, &S, &c);
+  return static_cast<size_t>(S) * static_cast<size_t>(T) * static_cast<size_t>(skinny_npad(N) + ldt) * 4;
+}
+
+// Lossless 4-bit weight beyond the skinny range: the weight is dequantized once
+// per call into a bf16 panel [N, K] in the workspace and the bf16 GEMM runs on
+// it (dequantizing inside the GEMM would repeat the work once per 256-token
+// output tile; measured slower at every token count above the skinny range).
+inline bool nf4_uses_panel(bool nf4, bool lossless, int64_t T) { return nf4 && lossless && T > kSkinnyMaxT; }
 
 // Lossless fp32 adapter on bf16 activations: the products run on bf16 MFMA
 // over the hi/lo split (the t~ block of a group is then t_hi | t_hi | t_lo,
@@ -54,7 +82,8 @@ struct LinearProblem {
   const void* x; int64_t ldx;
   const void* W;                                  // [N, K] act dtype (unused for 4-bit)
   const uint8_t* codes; const float* absmax; const float* codebook;  // 4-bit weight
-  void* panel;       // 4-bit weight, lossless, T >= kNf4PanelMinT: bf16 [N, K] dequantized copy in the workspace
+  void* panel;       // 4-bit weight, lossless, T > kSkinnyMaxT: bf16 [N, K] dequantized copy in the workspace
+  float* skinny;     // skinny path: fp32 partial sums in the workspace (null otherwise)
   const void* bias;
   void* y; int64_t ldy;
   int64_t T, N, K;

@@ -112,12 +112,32 @@ def test_workspace_size():
     # lossless fp32 adapter: t~ [T, 3R] bf16, A split [2 r_pad, K] and B split [N, 3 r_pad] bf16 per
     # group, each region rounded up to 256 bytes
     r256 = lambda v: -(-v // 256) * 256
-    assert ws(64, 128, 96, [8], F32) == r256(64 * 192 * 2) + r256(2 * 64 * 128 * 2) + r256(96 * 192 * 2)
+    assert ws(65, 128, 96, [8], F32) == r256(65 * 192 * 2) + r256(2 * 64 * 128 * 2) + r256(96 * 192 * 2)
     assert ws(100, 200, 300, [8, 70], F32) == (r256(100 * 3 * 192 * 2) + r256(2 * 64 * 200 * 2) + r256(300 * 192 * 2)
                                                + r256(2 * 128 * 200 * 2) + r256(300 * 384 * 2))
     assert ws(0, 128, 96, [8], BF16) == 0
-    assert ws(10, 128, 96, [], BF16) == 0
+    assert ws(65, 128, 96, [], BF16) == 0
     assert ws(10, 0, 96, [8], BF16) == 0
+
+
+@pytest.mark.parametrize("T,K,N,ranks", [(1, 4096, 14336, [16]), (16, 1536, 8960, [64]), (64, 8960, 1536, [64]),
+                                         (10, 128, 96, []), (33, 3072, 9216, [128, 128, 128]), (64, 64, 96, [8])])
+def test_workspace_size_few_tokens(T, K, N, ranks):
+    """T <= 64 (lossless): S fp32 partial sums [S, T, round_up(N, 64) + R], 1 <= S <= ceil(K / 64),
+    or the intermediate's layout when that is larger (the activation dtype is not an argument)."""
+    R = sum(-(-r // 64) * 64 for r in ranks)
+    row = T * (-(-N // 64) * 64 + R) * 4
+    for adt in (BF16, F32):
+        got = rg.lora_linear_workspace_size(T, K, N, ranks, adt)
+        plain = T * R * (2 if adt == BF16 else 4)
+        if adt == F32 and ranks:
+            r256 = lambda v: -(-v // 256) * 256
+            plain = r256(T * 3 * R * 2) + sum(r256(2 * (-(-r // 64) * 64) * K * 2) + r256(N * 3 * (-(-r // 64) * 64) * 2)
+                                              for r in ranks)
+        assert got >= plain
+        if got != plain or got % row == 0:
+            assert got % row == 0 and 1 <= got // row <= -(-K // 64), (got, row)
+    assert rg.lora_linear_workspace_size(T, K, N, ranks, BF16, EXACT) == T * R * 2
 
 
 def stacked(groups, n_groups=None, **kw):
@@ -154,10 +174,13 @@ def nf4(**kw):
 
 def test_nf4_workspace_query():
     q = rg.lora_linear_nf4_workspace_size
-    assert q(130, 256, 300, 16, BF16) == rg.lora_linear_workspace_size(130, 256, 300, [16], BF16)
-    assert q(130, 256, 300, 0, BF16) == 0                              # no adapter, in-GEMM dequantization
-    assert q(511, 256, 300, 16, BF16, EXACT) == rg.lora_linear_workspace_size(511, 256, 300, [16], BF16, EXACT)
-    # from 512 tokens (lossless) a bf16 panel of the weight follows the adapter's share, 256-byte aligned
+    # up to 64 tokens (lossless): the skinny partial sums, the weight dequantized in registers
+    assert q(64, 256, 300, 16, BF16) == rg.lora_linear_workspace_size(64, 256, 300, [16], BF16)
+    assert q(64, 256, 300, 0, BF16) == rg.lora_linear_workspace_size(64, 256, 300, [], BF16) > 0
+    assert q(64, 256, 300, 16, BF16, EXACT) == rg.lora_linear_workspace_size(64, 256, 300, [16], BF16, EXACT)
+    # from 65 tokens (lossless) a bf16 panel of the weight follows the adapter's share, 256-byte aligned
+    ad = rg.lora_linear_workspace_size(65, 256, 300, [16], BF16)
+    assert q(65, 256, 300, 16, BF16) == (ad + 255) // 256 * 256 + 300 * 256 * 2
     ad = rg.lora_linear_workspace_size(600, 256, 300, [16], BF16)
     assert q(600, 256, 300, 16, BF16) == (ad + 255) // 256 * 256 + 300 * 256 * 2
     assert q(600, 256, 300, 0, BF16) == 300 * 256 * 2

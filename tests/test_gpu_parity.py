@@ -116,11 +116,11 @@ def test_bf16_std_spread_variant(T, K, N, r):
     assert_bitwise(run_linear(d, "exact"), yc, "exact std")
 
 
-@pytest.mark.parametrize("seed", [0, 1])
-def test_dyadic_inputs_lossless_is_exact(seed):
-    T, K, N, r = 290, 192, 300, 16
+@pytest.mark.parametrize("T,seed", [(290, 0), (290, 1), (50, 2), (1, 3)])
+def test_dyadic_inputs_lossless_is_exact(T, seed):
+    K, N, r = 192, 300, 16
     d = lw.dyadic_linear_inputs(T, K, N, r, seed, bias=True, density=0.08)
-    say(f"case dyadic seed={seed}")
+    say(f"case dyadic T={T} seed={seed}")
     xd, Wd, bd, Ad, Bd = (lo.f64(d[k]) for k in ("x", "W", "b", "A", "B"))
     y64 = lo.lora_linear(d["x"], d["W"], d["b"], d["A"], d["B"], 16.0, r, 1.0, 1.0)
     # every intermediate exactly representable: t in bf16, the result in bf16
@@ -136,10 +136,11 @@ def test_dyadic_inputs_lossless_is_exact(seed):
     assert_bitwise(ye, y64, "exact dyadic")
 
 
-def test_inactive_adapter_is_base_only_bitwise():
-    d = lw.small_linear_inputs(300, 200, 520, 24, 7, bias=True, alpha=24.0)
+@pytest.mark.parametrize("T", [300, 33])
+def test_inactive_adapter_is_base_only_bitwise(T):
+    d = lw.small_linear_inputs(T, 200, 520, 24, 7, bias=True, alpha=24.0)
     x, W, b, A, B = (dev(d[k]) for k in ("x", "W", "b", "A", "B"))
-    say("case inactive adapter")
+    say(f"case inactive adapter T={T}")
     for q in ("lossless", "exact"):
         y_none = rg.lora_linear(x, W, b, None, None, 24.0, quality=q)
         y_s0 = rg.lora_linear(x, W, b, A, B, 24.0, 0.0, 1.0, quality=q)
@@ -293,11 +294,36 @@ def test_fp32_adapter_on_bf16(T, K, N, r):
     assert_bitwise(run_linear(d, "exact"), yc, "exact f32-adapter")
 
 
+# ------------------------------------------------------------------ few tokens (T <= 64)
+# The weight read is the whole cost: K is split into chunks whose fp32 partial
+# sums a second kernel adds. Ragged K (not a multiple of 64), ragged N, ranks
+# that are not multiples of 8, tokens from 1 to 64.
+
+@pytest.mark.parametrize("T,K,N,r,bias", [(1, 328, 300, 16, True), (7, 1536, 300, 70, False),
+                                          (16, 328, 1000, 8, True), (33, 64, 96, 128, True),
+                                          (64, 2056, 520, 24, False)])
+def test_few_tokens_linear(T, K, N, r, bias):
+    d = lw.small_linear_inputs(T, K, N, r, 60 + T, bias=bias, alpha=2.0 * r, strength=0.8, request_scale=0.7)
+    say(f"case few tokens T={T} K={K} N={N} r={r} bias={bias}")
+    y64, yc = oracle_pair(d)
+    assert_gate(run_linear(d, "lossless"), y64, yc, what="few-token lossless")
+    assert_bitwise(run_linear(d, "exact"), yc, "few-token exact")
+
+
+@pytest.mark.parametrize("T,K,N,r", [(40, 256, 520, 24), (3, 512, 300, 64)])
+def test_few_tokens_fp32_adapter(T, K, N, r):
+    d = lw.small_linear_inputs(T, K, N, r, 70 + T, adapter="f32", bias=True, alpha=2.0 * r, strength=0.8,
+                               request_scale=0.7)
+    say(f"case few tokens fp32 adapter T={T} K={K} N={N} r={r}")
+    y64, yc = oracle_pair(d, "bf16", "f32")
+    assert_gate(run_linear(d, "lossless"), y64, yc, what="few-token lossless f32-adapter")
+
+
 # ------------------------------------------------------------------ stacked groups
 
-def _stacked_inputs(seed, adapter="bf16", bias=True):
+def _stacked_inputs(seed, adapter="bf16", bias=True, T=300):
     rng = np.random.default_rng(seed)
-    T, K, Nt = 300, 256, 700
+    K, Nt = 256, 700
     specs = [(24, 48.0, 0, 200), (16, 8.0, 248, 300), (64, 64.0, 560, 140)]  # rank, alpha, offset, n_cols
     x = lw.to_dtype(rng.standard_normal((T, K)), "bf16")
     W = lw.to_dtype(rng.standard_normal((Nt, K)) / np.sqrt(K), "bf16")
@@ -308,10 +334,11 @@ def _stacked_inputs(seed, adapter="bf16", bias=True):
     return x, W, b, groups
 
 
+@pytest.mark.parametrize("T", [300, 20])
 @pytest.mark.parametrize("adapter", ["bf16", "f32"])
-def test_stacked_groups(adapter):
-    x, W, b, groups = _stacked_inputs(31, adapter)
-    say(f"case stacked adapter={adapter}")
+def test_stacked_groups(adapter, T):
+    x, W, b, groups = _stacked_inputs(31, adapter, T=T)
+    say(f"case stacked adapter={adapter} T={T}")
     y64 = lo.lora_linear_stacked(x, W, b, groups, 0.9, 0.8)
     yc = ec.chain_stacked(x, W, b, groups, 0.9, 0.8, "bf16", adapter)
     gg = [dict(g, A=dev(g["A"]), B=dev(g["B"])) for g in groups]
@@ -346,10 +373,10 @@ def _nf4_small(T=130, K=256, N=300, r=16, seed=41, bias=True, adapter="bf16"):
                 alpha=32.0, N=N)
 
 
-# T = 130: each output tile dequantizes its weight stages inside the GEMM;
-# T = 600 (>= 512 tokens): the weight is dequantized once into a bf16 panel in
-# the workspace, then the bf16 GEMM runs over it (three m-tiles, ragged tail).
-@pytest.mark.parametrize("T", [130, 600])
+# T <= 64: the few-token kernel dequantizes weight fragments in registers;
+# T = 130 and 600: the weight is dequantized once into a bf16 panel in the
+# workspace, then the bf16 GEMM runs over it (ragged tails).
+@pytest.mark.parametrize("T", [1, 64, 130, 600])
 @pytest.mark.parametrize("adapter", ["bf16", "f32"])
 def test_nf4_linear(adapter, T):
     d = _nf4_small(T=T, adapter=adapter)
@@ -371,7 +398,7 @@ def test_nf4_linear(adapter, T):
     assert_bitwise(ye, yc, "nf4 exact")
 
 
-@pytest.mark.parametrize("T", [256, 512])
+@pytest.mark.parametrize("T", [64, 256])
 def test_nf4_one_hot_returns_dequantized_columns(T):
     d = _nf4_small(T=T, K=256, N=300, bias=False)
     say(f"case nf4 one-hot T={T}")
