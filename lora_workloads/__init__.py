@@ -31,7 +31,8 @@ import torch
 __all__ = [
     "LinearSpec", "StackedSpec", "Nf4Spec", "PatchSpec",
     "TINY_FP32", "ATTN_PROJ", "FFN_UP", "FFN_DOWN", "QKV_STACKED", "NF4_LAYER",
-    "PATCH_WEIGHT", "PATCH_NORM",
+    "PATCH_WEIGHT", "PATCH_NORM", "ZIMAGE_ATTN", "ZIMAGE_FFN_UP", "ZIMAGE_FFN_DOWN", "H3_FFN_UP",
+    "H3_FFN_DOWN", "FEW_FFN_UP", "FEW_FFN_DOWN", "NF4_VECTOR",
     "linear_inputs", "ffn_pair_inputs", "stacked_inputs", "nf4_inputs", "patch_inputs",
     "nf4_style_codebook", "dyadic_linear_inputs", "to_dtype",
 ]
@@ -144,6 +145,28 @@ QKV_STACKED = StackedSpec("qkv_stacked", T=16384, K=3072, n_cols=(3072, 3072, 30
                           request_scale=1.0, bias=False, seed=4)
 NF4_LAYER = Nf4Spec("nf4_layer", T=8192, K=4096, N=14336, rank=16, alpha=32.0, strength=1.0,
                     request_scale=1.0, bias=False, seed=5)
+# The other token regimes of the pages' per-forward cost table (the table gives
+# ranks and token counts, not layer dims: the 1536 / 8960 layers above are
+# reused). Z-Image-Turbo at 1024^2: rank 32, 4352 tokens; MiniMax-H3 with
+# Ulysses 2: rank 64, 18871 tokens per rank; and few tokens (the single-vector
+# 4-bit case, a 64-token FFN pair).
+ZIMAGE_ATTN = LinearSpec("zimage_attn", T=4352, K=1536, N=1536, rank=32, alpha=32.0, strength=0.8,
+                         request_scale=1.0, bias=True, seed=8)
+ZIMAGE_FFN_UP = LinearSpec("zimage_ffn_up", T=4352, K=1536, N=8960, rank=32, alpha=32.0, strength=1.0,
+                           request_scale=0.7, bias=False, seed=9)
+ZIMAGE_FFN_DOWN = LinearSpec("zimage_ffn_down", T=4352, K=8960, N=1536, rank=32, alpha=32.0, strength=1.0,
+                             request_scale=0.7, bias=True, seed=9)
+H3_FFN_UP = LinearSpec("h3_ffn_up", T=18871, K=1536, N=8960, rank=64, alpha=64.0, strength=1.0,
+                       request_scale=0.7, bias=False, seed=10)
+H3_FFN_DOWN = LinearSpec("h3_ffn_down", T=18871, K=8960, N=1536, rank=64, alpha=64.0, strength=1.0,
+                         request_scale=0.7, bias=True, seed=10)
+FEW_FFN_UP = LinearSpec("few_ffn_up", T=64, K=1536, N=8960, rank=64, alpha=64.0, strength=1.0,
+                        request_scale=0.7, bias=False, seed=11)
+FEW_FFN_DOWN = LinearSpec("few_ffn_down", T=64, K=8960, N=1536, rank=64, alpha=64.0, strength=1.0,
+                          request_scale=0.7, bias=True, seed=11)
+NF4_VECTOR = Nf4Spec("nf4_vector", T=1, K=4096, N=14336, rank=16, alpha=32.0, strength=1.0,
+                     request_scale=1.0, bias=False, seed=12)
+
 PATCH_WEIGHT = PatchSpec("patch_weight", shape=(14336, 4096), strength=0.8, seed=6,
                          base_mean=0.0, base_var=1.0 / 4096, diff_var=(1e-3) ** 2 / 4096)
 PATCH_NORM = PatchSpec("patch_norm", shape=(3072,), strength=0.8, seed=7,

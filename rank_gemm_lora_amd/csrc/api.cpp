@@ -91,6 +91,12 @@ size_t round_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 // T >= kNf4PanelMinT adds its bf16 panel [N, K] after all of that (256-byte
 // aligned); the GEMM then sees a bf16 weight, so an fp32 adapter takes the
 // split layout.
+// The lossless bf16 producer splits K (fp32 partial sums after t~, 256-byte aligned).
+bool producer_split(const LinearProblem& p, bool lossless) {
+  return lossless && p.act == Elt::BF16 && p.adapter == Elt::BF16 && p.n_groups > 0 &&
+         lora::producer_partial_bytes(p.T, p.K, p.ldt) > 0;
+}
+
 size_t adapter_bytes_for(const LinearProblem& p, bool lossless, bool gemm_nf4) {
   if (p.n_groups == 0 || p.T == 0) return 0;
   if (lossless && lora::split_fp32_adapter(p.act, p.adapter, gemm_nf4)) {
@@ -99,7 +105,9 @@ size_t adapter_bytes_for(const LinearProblem& p, bool lossless, bool gemm_nf4) {
     for (int i = 0; i < p.n_groups; ++i) bytes += round_up(static_cast<size_t>(p.g[i].n_cols) * 3 * p.g[i].r_pad * 2);
     return bytes;
   }
-  return static_cast<size_t>(p.T) * static_cast<size_t>(p.ldt) * static_cast<size_t>(lora::esize(p.adapter));
+  size_t bytes = static_cast<size_t>(p.T) * static_cast<size_t>(p.ldt) * static_cast<size_t>(lora::esize(p.adapter));
+  if (producer_split(p, lossless)) bytes = round_up(bytes) + lora::producer_partial_bytes(p.T, p.K, p.ldt);
+  return bytes;
 }
 
 size_t panel_bytes(int64_t N, int64_t K) { return static_cast<size_t>(N) * static_cast<size_t>(K) * 2; }
@@ -196,6 +204,9 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
     p.skinny = static_cast<float*>(workspace);
   } else {
     if (p.n_groups > 0 && lossless && lora::split_fp32_adapter(p.act, p.adapter, nf4 && !use_panel)) assign_split(p);
+    if (producer_split(p, lossless))
+      p.tpart = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                         round_up(static_cast<size_t>(T) * static_cast<size_t>(p.ldt) * 2));
     if (use_panel) p.panel = static_cast<char*>(workspace) + round_up(adapter_bytes_for(p, lossless, false));
   }
 
@@ -332,7 +343,12 @@ size_t lora_linear_workspace_size(int64_t T, int64_t K, int64_t N, const int32_t
     }
     return std::max(bytes, skinny);
   }
-  return std::max(static_cast<size_t>(T) * static_cast<size_t>(cols) * static_cast<size_t>(esz(adapter_dtype)), skinny);
+  size_t bytes = static_cast<size_t>(T) * static_cast<size_t>(cols) * static_cast<size_t>(esz(adapter_dtype));
+  if (quality == LORA_LOSSLESS && adapter_dtype == LORA_BF16) {  // the producer's K-split partial sums
+    const size_t part = lora::producer_partial_bytes(T, K, cols);
+    if (part > 0) bytes = round_up(bytes) + part;
+  }
+  return std::max(bytes, skinny);
 }
 
 size_t lora_linear_nf4_workspace_size(int64_t T, int64_t K, int64_t N, int32_t rank, int32_t adapter_dtype,

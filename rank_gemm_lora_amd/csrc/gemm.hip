@@ -166,48 +166,6 @@ __device__ __forceinline__ void stage_lora_b(char* lds_tile, const GroupDev& g, 
   }
 }
 
-// 4-bit weight: dequantize one 64-element K step of 256 rows into the swizzled
-// bf16 W tile. Thread t owns row t/2 and elements [32*(t&1), 32*(t&1)+32) of the
-// step, i.e. 16 code bytes and the row's absmax for this block.
-struct Nf4Regs {
-  u32x4 codes;
-  float absmax;
-};
-
-__device__ __forceinline__ Nf4Regs nf4_load(const LinearProblem& p, int64_t n0, int rows_valid, int kt) {
-  Nf4Regs r;
-  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-  if (row < rows_valid) {
-    const int64_t n = n0 + row;
-    r.codes = *reinterpret_cast<const u32x4*>(p.codes + n * (p.K / 2) + kt * 32 + half * 16);
-    r.absmax = p.absmax[(n * p.K) / 64 + kt];
-  } else {
-    r.codes = u32x4{0u, 0u, 0u, 0u};
-    r.absmax = 0.f;
-  }
-  return r;
-}
-
-__device__ __forceinline__ void nf4_dequant_store(char* lds_w, const Nf4Regs& r, const float* cb_lds) {
-  const int row = threadIdx.x >> 1, half = threadIdx.x & 1;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {  // 4 chunks of 8 elements; 4 code bytes per chunk
-    const uint32_t word = r.codes[c];
-    uint32_t packed[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t byte = (word >> (8 * e)) & 0xffu;
-      // element 2j in the low nibble, 2j+1 in the high nibble; the product is
-      // RN_f32 (plain fp32 multiply), then RN_bf16.
-      const float lo = cb_lds[byte & 0xfu] * r.absmax;
-      const float hi = cb_lds[byte >> 4] * r.absmax;
-      packed[e] = pack_bf16x2(lo, hi);
-    }
-    *reinterpret_cast<u32x4*>(lds_w + swz(row, half * 4 + c) * 16) =
-        u32x4{packed[0], packed[1], packed[2], packed[3]};
-  }
-}
-
 template <class C, typename TA>
 __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::NI][C::NJ], const LinearProblem& p, int64_t m0,
                                          int64_t n0, int wm0, int wn0, int lane) {
@@ -263,10 +221,9 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::NI][C::NJ], cons
   }
 }
 
-template <class C, typename TA, typename TL, bool NF4>
+template <class C, typename TA, typename TL>
 __global__ __launch_bounds__(C::THREADS) void fused_gemm_kernel(LinearProblem p, int mt, int nt) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE_BYTES];
-  __shared__ float cb_lds[16];
 
   const int G = mt * nt;
   const int L = xcd_remap(blockIdx.x, G);
@@ -306,38 +263,19 @@ __global__ __launch_bounds__(C::THREADS) void fused_gemm_kernel(LinearProblem p,
   const __amdgpu_buffer_rsrc_t xr =
       make_rsrc(static_cast<const char*>(p.x) + m0 * p.ldx * EA, static_cast<uint32_t>(rows_m) * ldx_b);
 
-  if constexpr (!NF4) {
-    const uint32_t ldw_b = static_cast<uint32_t>(p.K * EA);
-    const __amdgpu_buffer_rsrc_t wr =
-        make_rsrc(static_cast<const char*>(p.W) + n0 * p.K * EA, static_cast<uint32_t>(rows_n) * ldw_b);
-    dma_stage<C::BM, C::THREADS>(bufx(0), xr, ldx_b, rows_m, 0, kb_total);
-    dma_stage<C::BN, C::THREADS>(bufw(0), wr, ldw_b, rows_n, 0, kb_total);
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_vmem();
-      __syncthreads();
-      if (kt + 1 < nk) {
-        dma_stage<C::BM, C::THREADS>(bufx((kt + 1) & 1), xr, ldx_b, rows_m, (kt + 1) * kRowBytes, kb_total);
-        dma_stage<C::BN, C::THREADS>(bufw((kt + 1) & 1), wr, ldw_b, rows_n, (kt + 1) * kRowBytes, kb_total);
-      }
-      Mma<C, TA>::stage(acc, bufw(kt & 1), bufx(kt & 1), wn0, wm0, lane);
-    }
-  } else {
-    static_assert(C::BN * 2 == C::THREADS, "4-bit staging maps two threads per weight row");
-    if (tid < 16) cb_lds[tid] = p.codebook[tid];
-    Nf4Regs nr = nf4_load(p, n0, rows_n, 0);
-    dma_stage<C::BM, C::THREADS>(bufx(0), xr, ldx_b, rows_m, 0, kb_total);
+  const uint32_t ldw_b = static_cast<uint32_t>(p.K * EA);
+  const __amdgpu_buffer_rsrc_t wr =
+      make_rsrc(static_cast<const char*>(p.W) + n0 * p.K * EA, static_cast<uint32_t>(rows_n) * ldw_b);
+  dma_stage<C::BM, C::THREADS>(bufx(0), xr, ldx_b, rows_m, 0, kb_total);
+  dma_stage<C::BN, C::THREADS>(bufw(0), wr, ldw_b, rows_n, 0, kb_total);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vmem();
     __syncthreads();
-    nf4_dequant_store(bufw(0), nr, cb_lds);
-    for (int kt = 0; kt < nk; ++kt) {
-      wait_vmem();
-      __syncthreads();
-      if (kt + 1 < nk) {
-        dma_stage<C::BM, C::THREADS>(bufx((kt + 1) & 1), xr, ldx_b, rows_m, (kt + 1) * kRowBytes, kb_total);
-        nr = nf4_load(p, n0, rows_n, kt + 1);
-      }
-      Mma<C, TA>::stage(acc, bufw(kt & 1), bufx(kt & 1), wn0, wm0, lane);
-      if (kt + 1 < nk) nf4_dequant_store(bufw((kt + 1) & 1), nr, cb_lds);
+    if (kt + 1 < nk) {
+      dma_stage<C::BM, C::THREADS>(bufx((kt + 1) & 1), xr, ldx_b, rows_m, (kt + 1) * kRowBytes, kb_total);
+      dma_stage<C::BN, C::THREADS>(bufw((kt + 1) & 1), wr, ldw_b, rows_n, (kt + 1) * kRowBytes, kb_total);
     }
+    Mma<C, TA>::stage(acc, bufw(kt & 1), bufx(kt & 1), wn0, wm0, lane);
   }
 
   // ---------------- K-extension: acc += t~ . B^T for every group touching this tile
@@ -1429,8 +1367,11 @@ template <bool SPLIT>
 __device__ __forceinline__ int producer_rows(const GroupDev& g) { return SPLIT ? 2 * g.r_pad : g.r_pad; }
 
 // grid: (ceil(T / BM), total chunks of BN adapter rows over all groups)
+// grid z: K splits of ks stages each (gridDim.z > 1 only without SPLIT): each
+// writes its fp32 partial sums of x.A^T to p.tpart [z, T, ldt] and
+// down_finish_kernel adds them.
 template <class DP, bool SPLIT>
-__global__ __launch_bounds__(DP::THREADS) void down_kernel(LinearProblem p) {
+__global__ __launch_bounds__(DP::THREADS) void down_kernel(LinearProblem p, int ks) {
   using P = DP;
   __shared__ __attribute__((aligned(1024))) char smem[P::S * P::STAGE_BYTES];
   int c = static_cast<int>(blockIdx.y), gi = 0;
@@ -1458,19 +1399,34 @@ __global__ __launch_bounds__(DP::THREADS) void down_kernel(LinearProblem p) {
   TileOffsets<P, P::BN> oa;
   ox.init(ldx_b, 0, rows_m, 0);
   oa.init(lda_b, 0, rows_q, 0);
+  const int s_lo = static_cast<int>(blockIdx.z) * ks;  // this split's stages [s_lo, s_lo + ns)
+  const int ns = min(nk, s_lo + ks) - s_lo;
   auto issue = [&](int s) {
     char* bx = smem + (s % P::S) * P::STAGE_BYTES;
-    const bool tail = k_tail && s == nk - 1;
-    ox.load(bx, xr, s * P::RB, tail, kb_total);
-    oa.load(bx + P::X_BYTES, ar, s * P::RB, tail, kb_total);
+    const bool tail = k_tail && s_lo + s == nk - 1;
+    ox.load(bx, xr, (s_lo + s) * P::RB, tail, kb_total);
+    oa.load(bx + P::X_BYTES, ar, (s_lo + s) * P::RB, tail, kb_total);
   };
   f32x16 acc[P::NI][P::NJ];
-  pipe_loop<P>(acc, smem, nk, issue, wn0, wm0, lane);
+  pipe_loop<P>(acc, smem, ns, issue, wn0, wm0, lane);
 
   // D[i = adapter row][j = token]: lane holds rows q0 + wn0 + 32 i + 8 gq + 4 h + e of token wm0 + r
   const int r = lane & 31, h = lane >> 5;
   const int64_t m = m0 + wm0 + r;
   if (m >= p.T) return;
+  if (!SPLIT && gridDim.z > 1) {  // partial sums of this K split, unscaled
+    float* part = p.tpart + (static_cast<int64_t>(blockIdx.z) * p.T + m) * p.ldt + g.t_col;
+#pragma unroll
+    for (int i = 0; i < P::NI; ++i)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int q = q0 + wn0 + i * 32 + gq * 8 + h * 4;
+        if (q >= g.r_pad) continue;
+        *reinterpret_cast<f32x4*>(part + q) =
+            f32x4{acc[i][0][gq * 4], acc[i][0][gq * 4 + 1], acc[i][0][gq * 4 + 2], acc[i][0][gq * 4 + 3]};
+      }
+    return;
+  }
   const float sc = g.scale;
   const bool unit = sc == 1.0f;
   bf16_bits* t = static_cast<bf16_bits*>(p.work);
@@ -1518,12 +1474,43 @@ __global__ __launch_bounds__(DP::THREADS) void down_kernel(LinearProblem p) {
   }
 }
 
+// t~ = RN_bf16(s . sum of the K splits' partial sums, in split order): 4 columns per thread.
+__global__ __launch_bounds__(256) void down_finish_kernel(LinearProblem p, int S) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (i >= p.T * p.ldt) return;
+  const int64_t m = i / p.ldt;
+  const int col = static_cast<int>(i - m * p.ldt);
+  f32x4 v[kMaxProducerSplits];
+#pragma unroll
+  for (int z = 0; z < kMaxProducerSplits; ++z)
+    if (z < S) v[z] = *reinterpret_cast<const f32x4*>(p.tpart + (z * p.T + m) * p.ldt + col);
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int z = 0; z < kMaxProducerSplits; ++z)
+    if (z < S) sum += v[z];
+  int gi = 0;
+  while (gi + 1 < p.n_groups && col >= p.g[gi + 1].t_col) ++gi;
+  const float sc = p.g[gi].scale;
+  if (sc != 1.0f) sum *= sc;
+  uint2 w;
+  w.x = pack_bf16x2(sum[0], sum[1]);
+  w.y = pack_bf16x2(sum[2], sum[3]);
+  *reinterpret_cast<uint2*>(static_cast<bf16_bits*>(p.work) + i) = w;
+}
+
 template <class DP, bool SPLIT>
 hipError_t launch_cfg(const LinearProblem& p, hipStream_t s) {
   int chunks = 0;
   for (int i = 0; i < p.n_groups; ++i) chunks += ((SPLIT ? 2 * p.g[i].r_pad : p.g[i].r_pad) + DP::BN - 1) / DP::BN;
-  const dim3 grid(static_cast<unsigned>((p.T + DP::BM - 1) / DP::BM), static_cast<unsigned>(chunks));
-  hipLaunchKernelGGL((down_kernel<DP, SPLIT>), grid, dim3(DP::THREADS), 0, s, p);
+  int S = 1, ks = (static_cast<int>(p.K * 2) + DP::RB - 1) / DP::RB;
+  if (!SPLIT && p.tpart != nullptr) producer_plan(p.T, p.K, &S, &ks);
+  const dim3 grid(static_cast<unsigned>((p.T + DP::BM - 1) / DP::BM), static_cast<unsigned>(chunks),
+                  static_cast<unsigned>(S));
+  hipLaunchKernelGGL((down_kernel<DP, SPLIT>), grid, dim3(DP::THREADS), 0, s, p, ks);
+  if (S > 1) {
+    const int64_t quads = p.T * p.ldt / 4;
+    hipLaunchKernelGGL(down_finish_kernel, dim3(static_cast<unsigned>((quads + 255) / 256)), dim3(256), 0, s, p, S);
+  }
   return hipGetLastError();
 }
 
@@ -1540,12 +1527,12 @@ hipError_t launch_split(const LinearProblem& p, hipStream_t s) { return launch_c
 
 using MainCfg = Cfg<256, 256, 128, 64>;  // 8 waves: 2 along tokens x 4 along outputs
 
-template <typename TA, typename TL, bool NF4>
+template <typename TA, typename TL>
 hipError_t launch_fused(const LinearProblem& p, hipStream_t s) {
   using C = MainCfg;
   const int mt = static_cast<int>((p.T + C::BM - 1) / C::BM);
   const int nt = static_cast<int>((p.N + C::BN - 1) / C::BN);
-  hipLaunchKernelGGL((fused_gemm_kernel<C, TA, TL, NF4>), dim3(mt * nt), dim3(C::THREADS), 0, s, p, mt, nt);
+  hipLaunchKernelGGL((fused_gemm_kernel<C, TA, TL>), dim3(mt * nt), dim3(C::THREADS), 0, s, p, mt, nt);
   return hipGetLastError();
 }
 
@@ -2038,11 +2025,9 @@ hipError_t launch_lossless(const LinearProblem& p, hipStream_t s, int phase) {
     if (e != hipSuccess) return e;
   }
   if (phase == 1) return hipSuccess;
-  if (p.nf4) {
-    return ad_bf16 ? launch_fused<bf16_bits, bf16_bits, true>(p, s) : launch_fused<bf16_bits, float, true>(p, s);
-  }
-  if (act_bf16) return launch_fused<bf16_bits, bf16_bits, false>(p, s);  // (an fp32 adapter took the split path)
-  return launch_fused<float, float, false>(p, s);
+  // (a 4-bit weight took the few-token path or the panel, an fp32 adapter on bf16 activations the split path)
+  if (act_bf16) return launch_fused<bf16_bits, bf16_bits>(p, s);
+  return launch_fused<float, float>(p, s);
 }
 
 }  // namespace lora

@@ -65,6 +65,31 @@ inline size_t skinny_bytes(int64_t T, int64_t K, int64_t N, int64_t ldt) {
   return static_cast<size_t>(S) * static_cast<size_t>(T) * static_cast<size_t>(skinny_npad(N) + ldt) * 4;
 }
 
+// The rank-wide producer of the lossless bf16 path takes 128 tokens per
+// workgroup; with fewer than 128 such tiles it also splits K (stages of 64
+// elements, at least 4 per split, at most kMaxProducerSplits splits, chosen by T
+// and K alone), each split writing fp32 partial sums [S, T, ldt] that a second
+// kernel adds in split order before the scale and the rounding.
+constexpr int kMaxProducerSplits = 8;
+inline void producer_plan(int64_t T, int64_t K, int* S, int* ks) {
+  const int64_t mt = (T + 127) / 128, nk = (K * 2 + 127) / 128;
+  int64_t s = 1;
+  if (mt > 0 && mt < 128) {
+    s = (256 + mt - 1) / mt;
+    s = s > kMaxProducerSplits ? kMaxProducerSplits : s;
+    const int64_t smax = nk / 4 > 1 ? nk / 4 : 1;
+    s = s > smax ? smax : s;
+  }
+  const int64_t k = nk > 0 ? (nk + s - 1) / s : 1;
+  *ks = static_cast<int>(k);
+  *S = nk > 0 ? static_cast<int>((nk + k - 1) / k) : 1;
+}
+inline size_t producer_partial_bytes(int64_t T, int64_t K, int64_t ldt) {
+  int S, ks;
+  producer_plan(T, K, &S, &ks);
+  return S > 1 ? static_cast<size_t>(S) * static_cast<size_t>(T) * static_cast<size_t>(ldt) * 4 : 0;
+}
+
 // Lossless 4-bit weight beyond the skinny range: the weight is dequantized once
 // per call into a bf16 panel [N, K] in the workspace and the bf16 GEMM runs on
 // it (dequantizing inside the GEMM would repeat the work once per 256-token
@@ -84,6 +109,7 @@ struct LinearProblem {
   const uint8_t* codes; const float* absmax; const float* codebook;  // 4-bit weight
   void* panel;       // 4-bit weight, lossless, T > kSkinnyMaxT: bf16 [N, K] dequantized copy in the workspace
   float* skinny;     // skinny path: fp32 partial sums in the workspace (null otherwise)
+  float* tpart;      // bf16 adapter, lossless: the producer's K-split partial sums (null: no split)
   const void* bias;
   void* y; int64_t ldy;
   int64_t T, N, K;

@@ -115,6 +115,13 @@ def test_workspace_size():
     assert ws(65, 128, 96, [8], F32) == r256(65 * 192 * 2) + r256(2 * 64 * 128 * 2) + r256(96 * 192 * 2)
     assert ws(100, 200, 300, [8, 70], F32) == (r256(100 * 3 * 192 * 2) + r256(2 * 64 * 200 * 2) + r256(300 * 192 * 2)
                                                + r256(2 * 128 * 200 * 2) + r256(300 * 384 * 2))
+    # fewer than 128 producer tiles of 128 tokens: K split into S chunks (stages of 64, at least 4 per
+    # chunk, at most 8 chunks), fp32 partial sums [S, T, R] after t~ (256-byte aligned)
+    assert ws(4352, 8960, 1536, [32], BF16) == r256(4352 * 64 * 2) + 8 * 4352 * 64 * 4
+    assert ws(10000, 1536, 8960, [64], BF16) == r256(10000 * 64 * 2) + 4 * 10000 * 64 * 4
+    assert ws(18871, 1536, 8960, [64], BF16) == 18871 * 64 * 2          # 148 tiles: no split
+    assert ws(16384, 1536, 8960, [64], BF16) == 16384 * 64 * 2          # 128 tiles: no split
+    assert ws(4352, 8960, 1536, [32], BF16, EXACT) == 4352 * 64 * 2
     assert ws(0, 128, 96, [8], BF16) == 0
     assert ws(65, 128, 96, [], BF16) == 0
     assert ws(10, 0, 96, [8], BF16) == 0

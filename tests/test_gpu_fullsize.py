@@ -47,6 +47,18 @@ def test_ffn_pair_full():
     _linear_case(down, "ffn_down")
 
 
+@pytest.mark.parametrize("pair", ["zimage", "h3", "few"])
+def test_other_token_regimes_full(pair):
+    """Z-Image-Turbo (4352 tokens, rank 32), MiniMax-H3 per rank (18871, rank 64), 64 tokens."""
+    up, down = {"zimage": (lw.ZIMAGE_FFN_UP, lw.ZIMAGE_FFN_DOWN), "h3": (lw.H3_FFN_UP, lw.H3_FFN_DOWN),
+                "few": (lw.FEW_FFN_UP, lw.FEW_FFN_DOWN)}[pair]
+    u, d = lw.ffn_pair_inputs(up, down)
+    _linear_case(u, up.name)
+    _linear_case(d, down.name)
+    if pair == "zimage":
+        _linear_case(lw.linear_inputs(lw.ZIMAGE_ATTN), lw.ZIMAGE_ATTN.name)
+
+
 @pytest.mark.parametrize("adapter", ["bf16", "f32"])
 def test_qkv_stacked_full(adapter):
     spec = lw.QKV_STACKED if adapter == "bf16" else lw.StackedSpec(
@@ -69,8 +81,8 @@ def test_qkv_stacked_full(adapter):
     assert_bitwise(ye[idx], yc, f"stacked {adapter} exact (sampled rows)")
 
 
-def test_nf4_layer_full():
-    s = lw.NF4_LAYER
+@pytest.mark.parametrize("s", [lw.NF4_LAYER, lw.NF4_VECTOR], ids=["tokens8192", "single_vector"])
+def test_nf4_layer_full(s):
     d = lw.nf4_inputs(s)
     rows = sample_rows(s.T, n_each=24, seed=3)
     say(f"case full-size nf4 T={s.T} K={s.K} N={s.N} r={s.rank} rows={len(rows)}")

@@ -179,7 +179,8 @@ def test_default_quality_is_lossless_and_deterministic():
 
 
 @pytest.mark.parametrize("T,K,N,r,adapter", [(300, 200, 520, 24, "bf16"), (513, 384, 768, 64, "bf16"),
-                                              (257, 512, 300, 64, "f32"), (64, 136, 96, 5, "bf16")])
+                                              (257, 512, 300, 64, "f32"), (64, 136, 96, 5, "bf16"),
+                                              (300, 2048, 520, 32, "bf16")])  # the last: producer K split
 def test_phases_compose_to_the_fused_call(T, K, N, r, adapter):
     """Phase 1 (rank-wide producer) then phase 2 (fused GEMM) equal lora_linear_fwd bit for bit."""
     d = lw.small_linear_inputs(T, K, N, r, 21, bias=True, alpha=2.0 * r, strength=0.8, request_scale=0.7)
