@@ -223,6 +223,8 @@ def main():
         del layers, L, d
         torch.cuda.empty_cache()
         configs = config_sweep(torch, dev, stream, with_oracle=not args.no_cpu_baseline)
+        torch.cuda.empty_cache()
+        configs["token_regimes"] = token_regimes(torch, dev, with_oracle=not args.no_cpu_baseline)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -255,6 +257,108 @@ def _launch_stats(torch, stream, fn, n=100, warm=10):
     torch.cuda.synchronize()
     t = sorted(a.elapsed_time(b) for a, b in ev)
     return {"median": round(t[n // 2], 5), "p10": round(t[n // 10], 5), "p90": round(t[(9 * n) // 10], 5)}
+
+
+def _graph_stats(torch, fn, out, n=50, reps=5):
+    """GPU time (ms) of one call of fn, replayed from a captured HIP graph (no host time per
+    call): median, p10, p90 over `reps` batches of n replays. Before timing, three replays
+    each separated by eager work are checked bit for bit against the eager result in `out`."""
+    fn()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref):
+            raise RuntimeError("graph replay differs from the eager call")
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / n)
+    ts.sort()
+    return {"median": round(ts[len(ts) // 2], 5), "p10": round(ts[0], 5), "p90": round(ts[-1], 5),
+            "timing": f"HIP graph replay, {reps} x {n}"}
+
+
+def token_regimes(torch, dev, with_oracle=True):
+    """The pages' other token regimes: Z-Image-Turbo (4352 tokens, rank 32: attention
+    projection and FFN pair), MiniMax-H3 per rank (18871 tokens, rank 64: FFN pair), a
+    64-token FFN pair and the single-vector 4-bit layer. Each call is timed by graph replay
+    (fused, this library's base-only path, torch F.linear); MFMA-bound entries report
+    TFLOP/s, the few-token ones HBM GB/s on the algorithmic bytes."""
+    import lora_workloads as lw
+    import rank_gemm_lora_amd as rg
+    F = torch.nn.functional
+    out = {}
+
+    def d2(t):
+        return None if t is None else t.to(dev)
+
+    def entry(name, spec, h):
+        x, W, b, A, B = (d2(h[k]) for k in ("x", "W", "b", "A", "B"))
+        T, K, N, r = spec.T, spec.K, spec.N, spec.rank
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, K, N, [r], rg.LORA_BF16)), dtype=torch.uint8,
+                         device=dev)
+        fused = _graph_stats(torch, lambda: rg.lora_linear(x, W, b, A, B, spec.alpha, spec.strength,
+                                                            spec.request_scale, out=y, workspace=ws), y)
+        own = _graph_stats(torch, lambda: rg.lora_linear(x, W, b, None, None, 1.0, out=y, workspace=ws), y)["median"]
+        yt = torch.empty_like(y)
+        tor = _graph_stats(torch, lambda: yt.copy_(F.linear(x, W, b)), yt)["median"]
+        byt = 2 * (T * K + N * K + T * N + (N if b is not None else 0) + r * (K + N))
+        fl = 2.0 * T * (K * N + K * r + r * N)
+        e = _gemm_entry(fl, fused, own, tor, byt)
+        e["workload"] = f"{name}: T={T} K={K} N={N} r={r} bf16/bf16"
+        if T <= 64:
+            gbs = byt / (fused["median"] * 1e-3) / 1e9
+            e.update(bound="hbm", achieved_gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4))
+        if with_oracle:
+            e["cpu_oracle"] = _oracle_time(lambda: _oracle_linear(h, spec), fl)
+        return e
+
+    out["zimage_attn"] = entry("Z-Image attention projection", lw.ZIMAGE_ATTN, lw.linear_inputs(lw.ZIMAGE_ATTN))
+    for tag, (su, sd) in (("zimage", (lw.ZIMAGE_FFN_UP, lw.ZIMAGE_FFN_DOWN)), ("h3", (lw.H3_FFN_UP, lw.H3_FFN_DOWN)),
+                          ("few", (lw.FEW_FFN_UP, lw.FEW_FFN_DOWN))):
+        hu, hd = lw.ffn_pair_inputs(su, sd)
+        out[f"{tag}_ffn_up"] = entry(f"{tag} FFN up", su, hu)
+        out[f"{tag}_ffn_down"] = entry(f"{tag} FFN down", sd, hd)
+        del hu, hd
+        torch.cuda.empty_cache()
+
+    spec = lw.NF4_VECTOR
+    h = lw.nf4_inputs(spec)
+    x, codes, absmax, cb, A, B, b = (d2(h[k]) for k in ("x", "codes", "absmax", "codebook", "A", "B", "b"))
+    T, K, N, r = spec.T, spec.K, spec.N, spec.rank
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, rg.lora_linear_nf4_workspace_size(T, K, N, r, rg.LORA_BF16)), dtype=torch.uint8,
+                     device=dev)
+    fused = _graph_stats(torch, lambda: rg.lora_linear_nf4(x, codes, absmax, cb, N, b, A, B, spec.alpha, out=y,
+                                                            workspace=ws), y)
+    own = _graph_stats(torch, lambda: rg.lora_linear_nf4(x, codes, absmax, cb, N, b, None, None, spec.alpha,
+                                                          out=y, workspace=ws), y)["median"]
+    byt = 2 * (T * K + T * N) + N * K // 2 + 4 * (N * K // spec.blocksize) + 2 * r * (K + N)
+    gbs = byt / (fused["median"] * 1e-3) / 1e9
+    e = _gemm_entry(2.0 * T * (K * N + K * r + r * N), fused, own, None, byt)
+    e.update(workload=f"4-bit weight, single vector: T={T} K={K} N={N} r={r}", bound="hbm",
+             achieved_gbs=round(gbs, 1), hbm_frac=round(gbs / PEAK_HBM_GBS, 4),
+             note="overhead against the 4-bit base path")
+    out["nf4_vector"] = e
+    return out
 
 
 def _gemm_entry(flops, ms, base_own, base_torch, bytes_alg):
@@ -338,7 +442,8 @@ def config_sweep(torch, dev, stream, with_oracle=True):
     x, codes, absmax, cb, A, B, b = (d2(h[k]) for k in ("x", "codes", "absmax", "codebook", "A", "B", "b"))
     T, K, N, r = spec.T, spec.K, spec.N, spec.rank
     y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, K, N, [r], rg.LORA_BF16)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(1, rg.lora_linear_nf4_workspace_size(T, K, N, r, rg.LORA_BF16)), dtype=torch.uint8,
+                     device=dev)
     fused = _launch_stats(torch, stream, lambda: rg.lora_linear_nf4(x, codes, absmax, cb, N, b, A, B, spec.alpha,
                                                                      out=y, workspace=ws))
     own = _launch_stats(torch, stream, lambda: rg.lora_linear_nf4(x, codes, absmax, cb, N, b, None, None,
