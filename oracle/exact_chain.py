@@ -33,7 +33,7 @@ import numpy as np
 
 from .lora_oracle import f64, nf4_unpack_codes
 
-__all__ = ["rn_f32", "rn_bf16", "rn", "gemm_ordered", "chain_linear", "chain_stacked",
+__all__ = ["rn_f32", "rn_bf16", "rn", "gemm_ordered", "chain_linear", "chain_stacked", "chain_multi",
            "chain_nf4_weight", "chain_nf4", "chain_dense_patch"]
 
 
@@ -121,6 +121,29 @@ def chain_stacked(x, W, b, groups, strength, request_scale, act: str = "bf16",
             continue
         o, n = int(g["col_offset"]), int(g["n_cols"])
         d = _delta(x, g["A"], g["B"], factors, adapter)
+        y[:, o:o + n] = rn(rn_f32(y[:, o:o + n] + d), act)
+    return y
+
+
+def chain_multi(x, W, b, adapters, request_scale, act: str = "bf16", adapter: str = "bf16") -> np.ndarray:
+    """E1-E5 per adapter, in the order given, on its column range of one base output.
+
+    Each adapter has its own strength; its legacy lora_B bias c (or None) is the
+    bias of the second rank GEMM, added before that GEMM's rounding as the base
+    bias is in E2: d = RN_adt(RN_f32(G(t, B) + c)); then the scale passes (E4)
+    and the add (E5). Adapters on the same columns add one after another.
+    """
+    y = _base(x, W, b, act).copy()
+    for a in adapters:
+        factors = (float(a["alpha"]) / float(a["rank"]), float(a["strength"]), float(request_scale))
+        if a["A"] is None or a["B"] is None or (factors[0] * factors[1] * factors[2]) == 0.0:
+            continue
+        o, n = int(a["col_offset"]), int(a["n_cols"])
+        t = rn(gemm_ordered(x, a["A"]), adapter)
+        g = gemm_ordered(t, a["B"])
+        if a.get("c") is not None:
+            g = rn_f32(g + f64(a["c"])[None, :])
+        d = _scale_passes(rn(g, adapter), factors, adapter)
         y[:, o:o + n] = rn(rn_f32(y[:, o:o + n] + d), act)
     return y
 

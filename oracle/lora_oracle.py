@@ -23,7 +23,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["f64", "combined_scale", "lora_linear", "lora_linear_stacked", "merged_weight",
+__all__ = ["f64", "combined_scale", "lora_linear", "lora_linear_stacked", "lora_linear_multi", "merged_weight",
            "nf4_unpack_codes", "nf4_dequant", "lora_linear_nf4", "dense_patch", "rel_rms"]
 
 
@@ -82,6 +82,36 @@ def lora_linear_stacked(x, W, b, groups, strength, request_scale) -> np.ndarray:
             continue
         o, n = int(g["col_offset"]), int(g["n_cols"])
         y[:, o:o + n] += s * ((x @ f64(g["A"]).T) @ f64(g["B"]).T)
+    return y
+
+
+def lora_linear_multi(x, W, b, adapters, request_scale) -> np.ndarray:
+    """Several adapters on one layer: y = x.W^T + b + sum_i s_i.((x.A_i^T).B_i^T + c_i)
+    over adapter i's columns, s_i = (alpha_i / r_i) . strength_i . request_scale.
+
+    piper-offload README, routed mode: the output residual is the strength
+    times (B.A.x plus the legacy bias), and several LoRAs on one target are
+    summed independently; its LoRA resource section: an older adapter may carry
+    a lora_B.bias vector c_i, applied with that adapter's strength. InvokeAI
+    article, section 3: a layer keeps a list of (patch, weight) pairs whose
+    contributions add up. Reading: c_i sits inside the bracket that the
+    adapter's whole combined scale multiplies. ``adapters`` are dicts with A,
+    B, c (or None), rank, alpha, strength, col_offset, n_cols; an adapter with
+    A or B None or s_i == +-0 contributes nothing (its bias included).
+    """
+    x, W, b = f64(x), f64(W), f64(b)
+    y = x @ W.T
+    if b is not None:
+        y = y + b[None, :]
+    for a in adapters:
+        s = combined_scale(a["alpha"], a["rank"], a["strength"], request_scale)
+        if a["A"] is None or a["B"] is None or s == 0.0:
+            continue
+        o, n = int(a["col_offset"]), int(a["n_cols"])
+        upd = (x @ f64(a["A"]).T) @ f64(a["B"]).T
+        if a.get("c") is not None:
+            upd = upd + f64(a["c"])[None, :]
+        y[:, o:o + n] += s * upd
     return y
 
 

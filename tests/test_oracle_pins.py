@@ -373,3 +373,106 @@ def test_chain_error_is_within_gate_and_nonzero():
     # a single bf16 rounding of the fp64 result is better than the chain
     e1 = lo.rel_rms(ec.rn_bf16(ec.rn_f32(y64)), y64)
     assert e1 < e
+
+
+# ------------------------------------------------------------------ several adapters on one layer
+
+def _int_mat(rng, shape, lo=-3, hi=4, dtype="bf16"):
+    """Small integers: every product and sum below is exact in float64 (and in bf16 inputs)."""
+    return lw.to_dtype(rng.integers(lo, hi, size=shape).astype(np.float64), dtype)
+
+
+def _multi_case(seed, T=5, K=6, N=7, ranks=(2, 3, 1), spans=((0, 7), (2, 4), (5, 2)), with_c=True):
+    rng = np.random.default_rng(seed)
+    x, W, b = _int_mat(rng, (T, K)), _int_mat(rng, (N, K)), _int_mat(rng, (N,))
+    ads = []
+    for i, (r, (o, n)) in enumerate(zip(ranks, spans)):
+        ads.append(dict(A=_int_mat(rng, (r, K)), B=_int_mat(rng, (n, r)),
+                        c=_int_mat(rng, (n,)) if with_c and i != 1 else None,
+                        rank=r, alpha=[2.0, 1.5, 4.0][i] * r, strength=[1.0, 0.5, -2.0][i],
+                        col_offset=o, n_cols=n))
+    return x, W, b, ads
+
+
+def test_multi_brute_force_fraction():
+    """Overlapping adapters with legacy biases against exact rationals, element by element."""
+    x, W, b, ads = _multi_case(0)
+    rs = 0.75
+    y = lo.lora_linear_multi(x, W, b, ads, rs)
+    X, Wn, bn = (lo.f64(v) for v in (x, W, b))
+    T, N = y.shape
+    for t in range(T):
+        for n in range(N):
+            v = dot_exact(X[t], Wn[n]) + exact(bn[n])
+            for a in ads:
+                o, nc = a["col_offset"], a["n_cols"]
+                if not o <= n < o + nc:
+                    continue
+                s = Fraction(a["alpha"]) / a["rank"] * Fraction(a["strength"]) * Fraction(rs)
+                A, B = lo.f64(a["A"]), lo.f64(a["B"])
+                u = sum((dot_exact(X[t], A[q]) * exact(B[n - o, q]) for q in range(a["rank"])), Fraction(0))
+                if a["c"] is not None:
+                    u += exact(lo.f64(a["c"])[n - o])
+                v += s * u
+            assert y[t, n] == float(v), (t, n)
+
+
+def test_multi_one_adapter_reduces_to_the_single_layer():
+    d = lw.small_linear_inputs(9, 16, 11, 4, 5, bias=True, alpha=6.0)
+    ad = dict(A=d["A"], B=d["B"], c=None, rank=4, alpha=6.0, strength=0.8, col_offset=0, n_cols=11)
+    y = lo.lora_linear_multi(d["x"], d["W"], d["b"], [ad], 0.7)
+    assert np.array_equal(y, lo.lora_linear(d["x"], d["W"], d["b"], d["A"], d["B"], 6.0, 4, 0.8, 0.7))
+    yc = ec.chain_multi(d["x"], d["W"], d["b"], [ad], 0.7)
+    assert np.array_equal(yc, ec.chain_linear(d["x"], d["W"], d["b"], d["A"], d["B"], 6.0, 4, 0.8, 0.7))
+
+
+def test_multi_disjoint_adapters_equal_stacked_groups():
+    rng = np.random.default_rng(3)
+    x, W, b = _int_mat(rng, (4, 8)), _int_mat(rng, (10, 8)), _int_mat(rng, (10,))
+    groups = [dict(A=_int_mat(rng, (2, 8)), B=_int_mat(rng, (4, 2)), rank=2, alpha=3.0, col_offset=0, n_cols=4),
+              dict(A=_int_mat(rng, (3, 8)), B=_int_mat(rng, (5, 3)), rank=3, alpha=1.5, col_offset=5, n_cols=5)]
+    ads = [dict(g, c=None, strength=0.5) for g in groups]
+    assert np.array_equal(lo.lora_linear_multi(x, W, b, ads, 2.0), lo.lora_linear_stacked(x, W, b, groups, 0.5, 2.0))
+    assert np.array_equal(ec.chain_multi(x, W, b, ads, 2.0), ec.chain_stacked(x, W, b, groups, 0.5, 2.0))
+
+
+def test_multi_equals_one_adapter_of_concatenated_rank_and_merged_weight():
+    """Two adapters on all columns == one adapter [A1; A2], [s1 B1 | s2 B2] with unit scale and the
+    bias b + s1 c1 + s2 c2 == the merged weight W + s1 B1 A1 + s2 B2 A2 (integer data: exact)."""
+    x, W, b, ads = _multi_case(7, ranks=(2, 3), spans=((0, 7), (0, 7)))
+    ads[1]["c"] = _int_mat(np.random.default_rng(8), (7,))
+    rs = 0.5
+    y = lo.lora_linear_multi(x, W, b, ads, rs)
+    s = [lo.combined_scale(a["alpha"], a["rank"], a["strength"], rs) for a in ads]
+    A_cat = np.concatenate([lo.f64(a["A"]) for a in ads])
+    B_cat = np.concatenate([si * lo.f64(a["B"]) for si, a in zip(s, ads)], axis=1)
+    b_all = lo.f64(b) + sum(si * lo.f64(a["c"]) for si, a in zip(s, ads))
+    assert np.array_equal(y, lo.lora_linear(x, W, b_all, A_cat, B_cat, 5.0, 5, 1.0, 1.0))
+    W_m = lo.f64(W) + sum(si * (lo.f64(a["B"]) @ lo.f64(a["A"])) for si, a in zip(s, ads))
+    assert np.array_equal(y, lo.f64(x) @ W_m.T + b_all[None, :])
+
+
+def test_multi_chain_bias_rounds_with_the_rank_gemm_and_adapters_add_in_turn():
+    """Hand-worked (bf16 throughout):
+    (a) t = [1, 1], B = [1, 2^-8]: G = 1 + 2^-8; with c = 2^-8 the biased GEMM output 1 + 2^-7 is a
+        bf16 value, so d = 1 + 2^-7 (adding c after rounding G would give RN(1 + 2^-8) = 1, a tie to even);
+        base 0, unit scales: y = 1 + 2^-7.
+    (b) base 1, two adapters each with d = 2^-8 on the same column: 1 + 2^-8 rounds to 1 (tie to even)
+        after the first and again after the second, so y = 1 (adding 2^-8 + 2^-8 first would give 1 + 2^-7)."""
+    bf = lambda rows: lw.to_dtype(np.array(rows, dtype=np.float64), "bf16")
+    a = dict(A=bf([[1.0, 0.0], [0.0, 1.0]]), B=bf([[1.0, 2.0 ** -8]]), c=bf([2.0 ** -8]), rank=2, alpha=2.0,
+             strength=1.0, col_offset=0, n_cols=1)
+    y = ec.chain_multi(bf([[1.0, 1.0]]), bf([[0.0, 0.0]]), None, [a], 1.0)
+    assert y[0, 0] == 1.0 + 2.0 ** -7
+    one = dict(A=bf([[1.0]]), B=bf([[2.0 ** -8]]), c=None, rank=1, alpha=1.0, strength=1.0, col_offset=0, n_cols=1)
+    y2 = ec.chain_multi(bf([[1.0]]), bf([[1.0]]), None, [one, dict(one)], 1.0)
+    assert y2[0, 0] == 1.0
+    assert lo.lora_linear_multi(bf([[1.0]]), bf([[1.0]]), None, [one, dict(one)], 1.0)[0, 0] == 1.0 + 2.0 ** -7
+
+
+def test_multi_inactive_adapter_drops_its_bias():
+    x, W, b, ads = _multi_case(11)
+    ads0 = [dict(a) for a in ads]
+    ads0[0]["strength"] = 0.0
+    y = lo.lora_linear_multi(x, W, b, ads0, 1.0)
+    assert np.array_equal(y, lo.lora_linear_multi(x, W, b, ads0[1:], 1.0))
