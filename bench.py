@@ -437,6 +437,33 @@ def config_sweep(torch, dev, stream, with_oracle=True):
         del x, W, b, groups, y, ws, h
         torch.cuda.empty_cache()
 
+    spec = lw.MULTI_FFN_UP
+    h = lw.multi_inputs(spec)
+    x, W, b = d2(h["x"]), d2(h["W"]), d2(h["b"])
+    ads = [dict(a, A=d2(a["A"]), B=d2(a["B"]), c=d2(a["c"])) for a in h["adapters"]]
+    T, K, N = spec.T, spec.K, spec.N
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    cads = [rg.LoraAdapter(a["A"].data_ptr(), a["B"].data_ptr(), 0 if a["c"] is None else a["c"].data_ptr(),
+                           a["rank"], 0, a["alpha"], a["strength"], a["col_offset"], a["n_cols"]) for a in ads]
+    ws = torch.empty(max(1, rg.lora_linear_multi_workspace_size(T, K, N, cads, rg.LORA_BF16)), dtype=torch.uint8,
+                     device=dev)
+    fused = _launch_stats(torch, stream, lambda: rg.lora_linear_multi(x, W, b, ads, spec.request_scale, out=y,
+                                                                       workspace=ws))
+    own = _launch_stats(torch, stream, lambda: rg.lora_linear(x, W, b, None, None, 1.0, out=y,
+                                                               workspace=ws))["median"]
+    tor = _launch_stats(torch, stream, lambda: F.linear(x, W, b))["median"]
+    rs = [a["rank"] for a in ads]
+    fl = 2.0 * T * (K * N + sum(r * (K + a["n_cols"]) for r, a in zip(rs, ads)))
+    byt = 2 * (T * K + N * K + T * N) + 2 * sum(r * (K + a["n_cols"]) + a["n_cols"] for r, a in zip(rs, ads))
+    e = _gemm_entry(fl, fused, own, tor, byt)
+    e["workload"] = (f"two adapters on one layer: T={T} K={K} N={N}, r=64 (strength 1) + r=32 (strength 0.5, "
+                     f"legacy lora_B bias)")
+    if with_oracle:
+        e["cpu_oracle"] = _oracle_time(lambda: _oracle_multi(h, spec), fl)
+    out["multi_ffn_up"] = e
+    del x, W, b, ads, y, ws, h
+    torch.cuda.empty_cache()
+
     spec = lw.NF4_LAYER
     h = lw.nf4_inputs(spec)
     x, codes, absmax, cb, A, B, b = (d2(h[k]) for k in ("x", "codes", "absmax", "codebook", "A", "B", "b"))
@@ -521,6 +548,11 @@ def _oracle_linear(h, spec):
     from oracle import lora_oracle as lo
     return lo.lora_linear(h["x"], h["W"], h["b"], h["A"], h["B"], spec.alpha, spec.rank, spec.strength,
                           spec.request_scale)
+
+
+def _oracle_multi(h, spec):
+    from oracle import lora_oracle as lo
+    return lo.lora_linear_multi(h["x"], h["W"], h["b"], h["adapters"], spec.request_scale)
 
 
 def _oracle_stacked(h, spec):

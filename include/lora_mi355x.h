@@ -173,6 +173,51 @@ int lora_linear_stacked_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One adapter of lora_linear_multi_fwd: like lora_group, plus its own strength
+ * and the optional legacy lora_B bias of older adapters (piper-offload README,
+ * LoRA resource: a <module>.lora_B.bias vector applied with the adapter's
+ * strength). Its combined scale is s = (alpha / rank) . strength . request_scale.
+ */
+typedef struct lora_adapter {
+  const void* A;       /* [rank, K] adapter dtype (device)                        */
+  const void* B;       /* [n_cols, rank] adapter dtype (device)                   */
+  const void* B_bias;  /* [n_cols] adapter dtype (device), or NULL                */
+  int32_t rank;
+  int32_t reserved;    /* set to 0 */
+  double alpha;
+  double strength;
+  int64_t col_offset;  /* columns [col_offset, col_offset + n_cols) of y          */
+  int64_t n_cols;
+} lora_adapter;
+
+/*
+ * lora_linear_multi_fwd -- several adapters on one layer, summed independently
+ * (piper-offload README, routed mode: y = base(x) + strength . (B.A.x + bias),
+ * several LoRAs on one target summed independently; InvokeAI article,
+ * section 3: a layer's list of (patch, weight) pairs):
+ *
+ *     y = x.W^T + b + sum_i s_i . ((x.A_i^T).B_i^T + c_i)   on adapter i's columns
+ *
+ * where c_i is adapter i's B_bias (0 when NULL). Column ranges may overlap; an
+ * adapter with s_i == +-0 (or A = B = NULL) contributes nothing, its bias
+ * included. Lossless tier: each t~_i = RN_adt(s_i . x.A_i^T) is a K-extension
+ * of the same accumulator; b + sum_i s_i . c_i is formed in fp32 and added in
+ * the epilogue before the one rounding. Exact tier: the chain of each adapter
+ * in the order given, c_i added to the second rank GEMM's fp32 result before
+ * its rounding to the adapter dtype (as the base bias is added to the base
+ * GEMM's), then the scale passes, then y = RN_dt(RN_f32(y + d_i)).
+ *   adapters  HOST array of n_adapters (0 <= n_adapters <= LORA_MAX_GROUPS)
+ *   workspace at least lora_linear_multi_workspace_size(...) bytes
+ * Other arguments as lora_linear_fwd; B_bias must be naturally aligned and must
+ * not overlap y.
+ */
+int lora_linear_multi_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
+                          const void* W, int64_t N, const void* bias,
+                          const lora_adapter* adapters, int32_t n_adapters, int32_t adapter_dtype,
+                          double request_scale, void* y, int64_t ldy, int32_t act_dtype, int32_t quality,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * lora_linear_nf4_fwd -- LoRA linear over a 4-bit codebook base weight,
  * dequantized inside the GEMM (Unsloth fast-LoRA chapter, section 3,
  * matmul_lora; 4-bit formats are blockwise -- piper-offload README
@@ -247,6 +292,15 @@ size_t lora_linear_workspace_size(int64_t T, int64_t K, int64_t N, const int32_t
  */
 size_t lora_linear_nf4_workspace_size(int64_t T, int64_t K, int64_t N, int32_t rank, int32_t adapter_dtype,
                                       int32_t quality);
+
+/*
+ * Workspace bytes of a lora_linear_multi_fwd call: as lora_linear_workspace_size
+ * over the adapters' ranks, plus, in the lossless tier when an adapter with a
+ * nonzero strength has a B_bias, an fp32 vector [N] at the front (256-byte
+ * aligned). Returns 0 when T, K or N <= 0 (or as lora_linear_workspace_size).
+ */
+size_t lora_linear_multi_workspace_size(int64_t T, int64_t K, int64_t N, const lora_adapter* adapters,
+                                        int32_t n_adapters, int32_t adapter_dtype, int32_t quality);
 
 /* Static, human-readable text for a status code. */
 const char* lora_status_string(int status);

@@ -29,7 +29,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "LinearSpec", "StackedSpec", "Nf4Spec", "PatchSpec",
+    "LinearSpec", "StackedSpec", "Nf4Spec", "PatchSpec", "MultiSpec", "MULTI_FFN_UP", "multi_inputs",
     "TINY_FP32", "ATTN_PROJ", "FFN_UP", "FFN_DOWN", "QKV_STACKED", "NF4_LAYER",
     "PATCH_WEIGHT", "PATCH_NORM", "ZIMAGE_ATTN", "ZIMAGE_FFN_UP", "ZIMAGE_FFN_DOWN", "H3_FFN_UP",
     "H3_FFN_DOWN", "FEW_FFN_UP", "FEW_FFN_DOWN", "NF4_VECTOR",
@@ -119,6 +119,21 @@ class Nf4Spec:
 
 
 @dataclass(frozen=True)
+class MultiSpec:
+    """Several adapters on one layer: ``adapters`` holds (rank, alpha, strength, col_offset,
+    n_cols, legacy lora_B bias present) per adapter; ranges may overlap."""
+    name: str
+    T: int
+    K: int
+    N: int
+    adapters: tuple
+    request_scale: float
+    bias: bool
+    seed: int
+    adapter: str = "bf16"
+
+
+@dataclass(frozen=True)
 class PatchSpec:
     """Dense payload applied to a parameter of ``shape``."""
     name: str
@@ -166,6 +181,12 @@ FEW_FFN_DOWN = LinearSpec("few_ffn_down", T=64, K=8960, N=1536, rank=64, alpha=6
                           request_scale=0.7, bias=True, seed=11)
 NF4_VECTOR = Nf4Spec("nf4_vector", T=1, K=4096, N=14336, rank=16, alpha=32.0, strength=1.0,
                      request_scale=1.0, bias=False, seed=12)
+
+# Two adapters on the FFN up layer (piper-offload routed mode: several LoRAs on one target), the
+# second an older adapter with a lora_B bias.
+MULTI_FFN_UP = MultiSpec("multi_ffn_up", T=32760, K=1536, N=8960,
+                         adapters=((64, 64.0, 1.0, 0, 8960, False), (32, 32.0, 0.5, 0, 8960, True)),
+                         request_scale=0.7, bias=False, seed=13)
 
 PATCH_WEIGHT = PatchSpec("patch_weight", shape=(14336, 4096), strength=0.8, seed=6,
                          base_mean=0.0, base_var=1.0 / 4096, diff_var=(1e-3) ** 2 / 4096)
@@ -218,6 +239,21 @@ def stacked_inputs(s: StackedSpec, spread: str = "variance") -> dict:
         off += n
     b = _normal(rng, (n_total,), 0.02, s.act, spread) if s.bias else None
     return dict(x=x, W=W, b=b, groups=groups, strength=s.strength, request_scale=s.request_scale)
+
+
+def multi_inputs(s: MultiSpec, spread: str = "variance") -> dict:
+    """x, W, b and one dict per adapter (A, B, c or None, rank, alpha, strength, col_offset, n_cols)."""
+    rng = np.random.default_rng(s.seed)
+    x = _normal(rng, (s.T, s.K), 1.0, "bf16", spread)
+    W = _normal(rng, (s.N, s.K), 1.0 / s.K, "bf16", spread)
+    b = _normal(rng, (s.N,), 0.02, "bf16", spread) if s.bias else None
+    ads = []
+    for r, a, st, o, n, has_c in s.adapters:
+        A = _normal(rng, (r, s.K), 1.0 / s.K, s.adapter, spread)
+        B = _normal(rng, (n, r), 0.02, s.adapter, spread)
+        c = _normal(rng, (n,), 0.02, s.adapter, spread) if has_c else None
+        ads.append(dict(A=A, B=B, c=c, rank=r, alpha=a, strength=st, col_offset=o, n_cols=n))
+    return dict(x=x, W=W, b=b, adapters=ads, request_scale=s.request_scale)
 
 
 def nf4_style_codebook() -> torch.Tensor:

@@ -25,7 +25,8 @@ __all__ = [
     "LIB_PATH", "LoraError", "LORA_F32", "LORA_BF16", "LORA_LOSSLESS", "LORA_EXACT",
     "LORA_PATCH_ADD", "LORA_PATCH_REPLACE", "lora_linear_fwd", "lora_linear_stacked_fwd",
     "lora_linear_nf4_fwd", "dense_patch_apply", "lora_linear_fwd_phase", "lora_linear_workspace_size",
-    "lora_linear_nf4_workspace_size",
+    "lora_linear_nf4_workspace_size", "lora_linear_multi_fwd", "lora_linear_multi_workspace_size",
+    "lora_linear_multi", "LoraAdapter",
     "lora_status_string",
     "lora_device_check", "lora_linear", "lora_linear_stacked", "lora_linear_nf4", "dense_patch",
     "LoraGroup", "hip_runtimes_mapped",
@@ -53,6 +54,12 @@ class LoraGroup(ctypes.Structure):
                 ("col_offset", _i64), ("n_cols", _i64)]
 
 
+class LoraAdapter(ctypes.Structure):
+    """C ``lora_adapter``: one of several adapters on one layer."""
+    _fields_ = [("A", _p), ("B", _p), ("B_bias", _p), ("rank", _i32), ("reserved", _i32), ("alpha", _f64),
+                ("strength", _f64), ("col_offset", _i64), ("n_cols", _i64)]
+
+
 _lib.lora_linear_fwd.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _f64, _f64, _f64,
                                  _p, _i64, _i32, _i32, _p, _sz, _p]
 _lib.lora_linear_fwd.restype = ctypes.c_int
@@ -70,6 +77,11 @@ _lib.dense_patch_apply.argtypes = [_p, _i32, ctypes.POINTER(_i64), _i32, _p, _i3
 _lib.dense_patch_apply.restype = ctypes.c_int
 _lib.lora_linear_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_i32), _i32, _i32, _i32]
 _lib.lora_linear_workspace_size.restype = _sz
+_lib.lora_linear_multi_fwd.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, ctypes.POINTER(LoraAdapter), _i32, _i32,
+                                       _f64, _p, _i64, _i32, _i32, _p, _sz, _p]
+_lib.lora_linear_multi_fwd.restype = ctypes.c_int
+_lib.lora_linear_multi_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(LoraAdapter), _i32, _i32, _i32]
+_lib.lora_linear_multi_workspace_size.restype = _sz
 _lib.lora_linear_nf4_workspace_size.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32]
 _lib.lora_linear_nf4_workspace_size.restype = _sz
 _lib.lora_status_string.argtypes = [ctypes.c_int]
@@ -112,6 +124,19 @@ def lora_linear_stacked_fwd(x, T, K, ldx, W, N_total, bias, groups, n_groups, ad
     return _check(_lib.lora_linear_stacked_fwd(x, T, K, ldx, W, N_total, bias, arr, n_groups, adapter_dtype,
                                                strength, request_scale, y, ldy, act_dtype, quality, workspace,
                                                workspace_bytes, stream), "lora_linear_stacked_fwd")
+
+
+def lora_linear_multi_fwd(x, T, K, ldx, W, N, bias, adapters, n_adapters, adapter_dtype, request_scale, y, ldy,
+                          act_dtype, quality, workspace, workspace_bytes, stream):
+    arr = (LoraAdapter * max(1, n_adapters))(*adapters)
+    return _check(_lib.lora_linear_multi_fwd(x, T, K, ldx, W, N, bias, arr, n_adapters, adapter_dtype, request_scale,
+                                             y, ldy, act_dtype, quality, workspace, workspace_bytes, stream),
+                  "lora_linear_multi_fwd")
+
+
+def lora_linear_multi_workspace_size(T, K, N, adapters, adapter_dtype, quality=LORA_LOSSLESS) -> int:
+    arr = (LoraAdapter * max(1, len(adapters)))(*adapters)
+    return int(_lib.lora_linear_multi_workspace_size(T, K, N, arr, len(adapters), adapter_dtype, quality))
 
 
 def lora_linear_nf4_fwd(x, T, K, ldx, codes, absmax, codebook, blocksize, N, bias, A, B, rank, adapter_dtype,
@@ -223,6 +248,28 @@ def lora_linear_stacked(x, W, b, groups, strength=1.0, request_scale=1.0, out=No
     lora_linear_stacked_fwd(x.data_ptr(), T, K, ldx, W.data_ptr(), N, _ptr(b), cg, len(cg), adt, float(strength),
                             float(request_scale), out.data_ptr(), ldy, _dt(x), q, ws.data_ptr(), ws.numel(),
                             _stream(stream))
+    return out
+
+
+def lora_linear_multi(x, W, b, adapters, request_scale=1.0, out=None, quality="lossless", workspace=None,
+                      stream=None):
+    """Several adapters on one layer: ``adapters`` is a list of dicts with A, B, c (legacy
+    lora_B bias or None), alpha, strength, col_offset, n_cols; column ranges may overlap."""
+    T, K = x.shape
+    N = W.shape[0]
+    ldx = _row_major(x, "x")
+    if out is None:
+        out = torch.empty((T, N), dtype=x.dtype, device=x.device)
+    ldy = _row_major(out, "out")
+    adt = _dt(adapters[0]["A"]) if adapters else _dt(x)
+    ca = [LoraAdapter(_ptr(a["A"]), _ptr(a["B"]), _ptr(a.get("c")), 0 if a["A"] is None else a["A"].shape[0], 0,
+                      float(a["alpha"]), float(a["strength"]), int(a["col_offset"]), int(a["n_cols"]))
+          for a in adapters]
+    q = _QUALITY[quality]
+    need = lora_linear_multi_workspace_size(T, K, N, ca, adt, q)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    lora_linear_multi_fwd(x.data_ptr(), T, K, ldx, W.data_ptr(), N, _ptr(b), ca, len(ca), adt, float(request_scale),
+                          out.data_ptr(), ldy, _dt(x), q, ws.data_ptr(), ws.numel(), _stream(stream))
     return out
 
 

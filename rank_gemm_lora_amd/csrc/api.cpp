@@ -45,21 +45,24 @@ bool finite_scale(double v) { return std::isfinite(v); }
 // The staging kernels address one tile of rows with 32-bit byte offsets.
 constexpr int64_t kMaxRowBytes = int64_t(1) << 22;
 
-// Adapter description shared by the three linear entry points.
+// Adapter description shared by the linear entry points.
 struct Adapter {
   const void* A;
   const void* B;
   int32_t rank;
   double alpha;
   int64_t col_off, n_cols;
+  double strength;
+  const void* Bb;  // legacy lora_B bias [n_cols], or null
 };
 
-int fill_groups(LinearProblem& p, const Adapter* ads, int n, double strength, double request_scale) {
+int fill_groups(LinearProblem& p, const Adapter* ads, int n, double request_scale) {
   p.n_groups = 0;
   int64_t tcol = 0;
   for (int i = 0; i < n; ++i) {
     const Adapter& a = ads[i];
     if (a.A == nullptr && a.B == nullptr) continue;  // no adapter on these columns
+    const double strength = a.strength;
     const double s = (a.alpha / static_cast<double>(a.rank)) * strength * request_scale;
     if (s == 0.0) continue;  // a zero combined scale leaves the adapter inactive
     if (std::fabs(s) > FLT_MAX) return LORA_ERR_NONFINITE;
@@ -75,6 +78,7 @@ int fill_groups(LinearProblem& p, const Adapter* ads, int n, double strength, do
     g.f[0] = static_cast<float>(a.alpha / static_cast<double>(a.rank));
     g.f[1] = static_cast<float>(strength);
     g.f[2] = static_cast<float>(request_scale);
+    g.Bb = a.Bb;
     tcol += g.r_pad;
   }
   p.ldt = tcol;
@@ -112,7 +116,24 @@ size_t adapter_bytes_for(const LinearProblem& p, bool lossless, bool gemm_nf4) {
 
 size_t panel_bytes(int64_t N, int64_t K) { return static_cast<size_t>(N) * static_cast<size_t>(K) * 2; }
 
+size_t workspace_rest_for(const LinearProblem& p, bool lossless);
+
+// Lossless: b + sum_g s_g . c_g as one fp32 vector [N] at the front of the
+// workspace when an active adapter has a legacy lora_B bias.
+bool needs_bias32(const LinearProblem& p, bool lossless) {
+  if (!lossless) return false;
+  for (int i = 0; i < p.n_groups; ++i)
+    if (p.g[i].Bb != nullptr) return true;
+  return false;
+}
+
 size_t workspace_bytes_for(const LinearProblem& p, bool lossless) {
+  if (p.T == 0) return 0;
+  const size_t front = needs_bias32(p, lossless) ? round_up(static_cast<size_t>(p.N) * 4) : 0;
+  return front + workspace_rest_for(p, lossless);
+}
+
+size_t workspace_rest_for(const LinearProblem& p, bool lossless) {
   if (lora::skinny_path(p.act, lossless, p.T, p.ldt)) return lora::skinny_bytes(p.T, p.K, p.N, p.ldt);
   const bool panel = lora::nf4_uses_panel(p.nf4, lossless, p.T);
   const size_t ad = adapter_bytes_for(p, lossless, p.nf4 && !panel);
@@ -135,14 +156,16 @@ void assign_split(LinearProblem& p) {
 // Shared validation + dispatch for lora_linear_fwd / _stacked_fwd / _nf4_fwd.
 int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, const uint8_t* codes,
                const float* absmax, const float* codebook, bool nf4, int64_t N, const void* bias,
-               const Adapter* ads, int n_ads, int adapter_dtype, double strength, double request_scale,
+               const Adapter* ads, int n_ads, int adapter_dtype, double request_scale,
                void* y, int64_t ldy, int act_dtype, int quality, void* workspace, size_t workspace_bytes,
-               void* stream, int phase = 0) {
+               void* stream, int phase = 0, bool overlap_ok = false) {
   if (!dtype_ok(act_dtype) || !dtype_ok(adapter_dtype)) return LORA_ERR_DTYPE;
   if (act_dtype == LORA_F32 && adapter_dtype != LORA_F32) return LORA_ERR_DTYPE;
   if (quality != LORA_LOSSLESS && quality != LORA_EXACT) return LORA_ERR_UNSUPPORTED;
   if (T < 0 || K < 1 || N < 1 || ldx < K || ldy < N) return LORA_ERR_SHAPE;
-  if (!finite_scale(strength) || !finite_scale(request_scale)) return LORA_ERR_NONFINITE;
+  if (!finite_scale(request_scale)) return LORA_ERR_NONFINITE;
+  for (int i = 0; i < n_ads; ++i)
+    if (!finite_scale(ads[i].strength)) return LORA_ERR_NONFINITE;
   if (nf4) {
     if (codes == nullptr || absmax == nullptr || codebook == nullptr) return LORA_ERR_NULL_PTR;
     if (K % 64 != 0) return LORA_ERR_SHAPE;
@@ -159,8 +182,8 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
     if (a.rank > LORA_MAX_RANK) return LORA_ERR_UNSUPPORTED;
     if (a.n_cols < 1 || a.col_off < 0 || a.col_off + a.n_cols > N) return LORA_ERR_SHAPE;
   }
-  // stacked groups must be disjoint
-  for (int i = 0; i < n_ads; ++i)
+  // stacked groups must be disjoint (several adapters on one layer may overlap)
+  for (int i = 0; i < n_ads && !overlap_ok; ++i)
     for (int j = i + 1; j < n_ads; ++j) {
       const Adapter &a = ads[i], &b = ads[j];
       if (a.A == nullptr || b.A == nullptr) continue;
@@ -176,12 +199,12 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
     if (!aligned(x, 16) || !aligned(W, 16) || !aligned(y, ea) || !aligned(codes, 16)) return LORA_ERR_ALIGN;
     if (K % vec != 0 || ldx % vec != 0) return LORA_ERR_ALIGN;
     for (int i = 0; i < n_ads; ++i)
-      if (!aligned(ads[i].A, 16) || !aligned(ads[i].B, 16)) return LORA_ERR_ALIGN;
+      if (!aligned(ads[i].A, 16) || !aligned(ads[i].B, 16) || !aligned(ads[i].Bb, el)) return LORA_ERR_ALIGN;
     if (!aligned(workspace, 16)) return LORA_ERR_ALIGN;
   } else {
     if (!aligned(x, ea) || !aligned(W, ea) || !aligned(y, ea)) return LORA_ERR_ALIGN;
     for (int i = 0; i < n_ads; ++i)
-      if (!aligned(ads[i].A, el) || !aligned(ads[i].B, el)) return LORA_ERR_ALIGN;
+      if (!aligned(ads[i].A, el) || !aligned(ads[i].B, el) || !aligned(ads[i].Bb, el)) return LORA_ERR_ALIGN;
     if (!aligned(workspace, 4)) return LORA_ERR_ALIGN;
   }
   if (!aligned(bias, ea) || !aligned(absmax, 4) || !aligned(codebook, 4)) return LORA_ERR_ALIGN;
@@ -191,7 +214,7 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
   p.x = x; p.ldx = ldx; p.W = W; p.codes = codes; p.absmax = absmax; p.codebook = codebook;
   p.bias = bias; p.y = y; p.ldy = ldy; p.T = T; p.N = N; p.K = K;
   p.act = to_elt(act_dtype); p.adapter = to_elt(adapter_dtype); p.nf4 = nf4;
-  const int st = fill_groups(p, ads, n_ads, strength, request_scale);
+  const int st = fill_groups(p, ads, n_ads, request_scale);
   if (st != LORA_OK) return st;
 
   const bool lossless = quality == LORA_LOSSLESS;
@@ -199,15 +222,19 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
   const bool use_panel = !use_skinny && lora::nf4_uses_panel(nf4, lossless, T);
   const size_t need = workspace_bytes_for(p, lossless);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LORA_ERR_WORKSPACE;
-  p.work = workspace;
+  char* ws = static_cast<char*>(workspace);
+  if (need > 0 && needs_bias32(p, lossless)) {
+    p.bias32 = reinterpret_cast<float*>(ws);
+    ws += round_up(static_cast<size_t>(N) * 4);
+  }
+  p.work = ws;
   if (use_skinny) {
-    p.skinny = static_cast<float*>(workspace);
+    p.skinny = reinterpret_cast<float*>(ws);
   } else {
     if (p.n_groups > 0 && lossless && lora::split_fp32_adapter(p.act, p.adapter, nf4 && !use_panel)) assign_split(p);
     if (producer_split(p, lossless))
-      p.tpart = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                         round_up(static_cast<size_t>(T) * static_cast<size_t>(p.ldt) * 2));
-    if (use_panel) p.panel = static_cast<char*>(workspace) + round_up(adapter_bytes_for(p, lossless, false));
+      p.tpart = reinterpret_cast<float*>(ws + round_up(static_cast<size_t>(T) * static_cast<size_t>(p.ldt) * 2));
+    if (use_panel) p.panel = ws + round_up(adapter_bytes_for(p, lossless, false));
   }
 
   // the output must not overlap any input or the workspace
@@ -227,7 +254,10 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
       const Adapter& a = ads[i];
       if (a.A == nullptr) continue;
       const Span sa = span2d(a.A, a.rank, K, K, el), sb = span2d(a.B, a.n_cols, a.rank, a.rank, el);
-      if (overlaps(sy, sa) || overlaps(sy, sb) || overlaps(sws, sa) || overlaps(sws, sb)) return LORA_ERR_OVERLAP;
+      const Span sc = span2d(a.Bb, 1, a.n_cols, a.n_cols, el);
+      if (overlaps(sy, sa) || overlaps(sy, sb) || overlaps(sws, sa) || overlaps(sws, sb) || overlaps(sy, sc) ||
+          overlaps(sws, sc))
+        return LORA_ERR_OVERLAP;
     }
     for (int i = 0; i < 5; ++i)
       if (overlaps(sws, inputs[i])) return LORA_ERR_OVERLAP;
@@ -235,6 +265,10 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
   if (T == 0) return LORA_OK;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.bias32 != nullptr && phase != 1) {
+    const hipError_t eb = lora::launch_bias32(p, s);
+    if (eb != hipSuccess) return LORA_ERR_HIP;
+  }
   const hipError_t e = (quality == LORA_EXACT) ? lora::launch_exact(p, s) : lora::launch_lossless(p, s, phase);
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
@@ -247,8 +281,8 @@ int lora_linear_fwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void
                     const void* A, const void* B, int32_t rank, int32_t adapter_dtype, double alpha,
                     double strength, double request_scale, void* y, int64_t ldy, int32_t act_dtype,
                     int32_t quality, void* workspace, size_t workspace_bytes, void* stream) {
-  const Adapter a{A, B, rank, alpha, 0, N};
-  return run_linear(x, T, K, ldx, W, nullptr, nullptr, nullptr, false, N, bias, &a, 1, adapter_dtype, strength,
+  const Adapter a{A, B, rank, alpha, 0, N, strength, nullptr};
+  return run_linear(x, T, K, ldx, W, nullptr, nullptr, nullptr, false, N, bias, &a, 1, adapter_dtype,
                     request_scale, y, ldy, act_dtype, quality, workspace, workspace_bytes, stream);
 }
 
@@ -258,8 +292,8 @@ int lora_linear_fwd_phase(int32_t phase, const void* x, int64_t T, int64_t K, in
                           int32_t act_dtype, int32_t quality, void* workspace, size_t workspace_bytes, void* stream) {
   if (phase != 1 && phase != 2) return LORA_ERR_UNSUPPORTED;
   if (quality != LORA_LOSSLESS) return LORA_ERR_UNSUPPORTED;
-  const Adapter a{A, B, rank, alpha, 0, N};
-  return run_linear(x, T, K, ldx, W, nullptr, nullptr, nullptr, false, N, bias, &a, 1, adapter_dtype, strength,
+  const Adapter a{A, B, rank, alpha, 0, N, strength, nullptr};
+  return run_linear(x, T, K, ldx, W, nullptr, nullptr, nullptr, false, N, bias, &a, 1, adapter_dtype,
                     request_scale, y, ldy, act_dtype, quality, workspace, workspace_bytes, stream, phase);
 }
 
@@ -273,10 +307,27 @@ int lora_linear_stacked_fwd(const void* x, int64_t T, int64_t K, int64_t ldx, co
   Adapter ads[LORA_MAX_GROUPS];
   for (int i = 0; i < n_groups; ++i)
     ads[i] = Adapter{groups[i].A, groups[i].B, groups[i].rank, groups[i].alpha, groups[i].col_offset,
-                     groups[i].n_cols};
+                     groups[i].n_cols, strength, nullptr};
   return run_linear(x, T, K, ldx, W, nullptr, nullptr, nullptr, false, N_total, bias, ads, n_groups,
-                    adapter_dtype, strength, request_scale, y, ldy, act_dtype, quality, workspace,
+                    adapter_dtype, request_scale, y, ldy, act_dtype, quality, workspace,
                     workspace_bytes, stream);
+}
+
+int lora_linear_multi_fwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, int64_t N,
+                          const void* bias, const lora_adapter* adapters, int32_t n_adapters, int32_t adapter_dtype,
+                          double request_scale, void* y, int64_t ldy, int32_t act_dtype, int32_t quality,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_adapters < 0) return LORA_ERR_SHAPE;
+  if (n_adapters > LORA_MAX_GROUPS) return LORA_ERR_UNSUPPORTED;
+  if (n_adapters > 0 && adapters == nullptr) return LORA_ERR_NULL_PTR;
+  Adapter ads[LORA_MAX_GROUPS];
+  for (int i = 0; i < n_adapters; ++i) {
+    const lora_adapter& a = adapters[i];
+    if (a.B_bias != nullptr && a.A == nullptr) return LORA_ERR_NULL_PTR;  // a bias without its adapter
+    ads[i] = Adapter{a.A, a.B, a.rank, a.alpha, a.col_offset, a.n_cols, a.strength, a.B_bias};
+  }
+  return run_linear(x, T, K, ldx, W, nullptr, nullptr, nullptr, false, N, bias, ads, n_adapters, adapter_dtype,
+                    request_scale, y, ldy, act_dtype, quality, workspace, workspace_bytes, stream, 0, true);
 }
 
 int lora_linear_nf4_fwd(const void* x, int64_t T, int64_t K, int64_t ldx, const uint8_t* codes,
@@ -285,9 +336,9 @@ int lora_linear_nf4_fwd(const void* x, int64_t T, int64_t K, int64_t ldx, const 
                         double strength, double request_scale, void* y, int64_t ldy, int32_t quality,
                         void* workspace, size_t workspace_bytes, void* stream) {
   if (blocksize != 64) return LORA_ERR_UNSUPPORTED;
-  const Adapter a{A, B, rank, alpha, 0, N};
+  const Adapter a{A, B, rank, alpha, 0, N, strength, nullptr};
   return run_linear(x, T, K, ldx, nullptr, codes, absmax, codebook, true, N, bias, &a, 1, adapter_dtype,
-                    strength, request_scale, y, ldy, LORA_BF16, quality, workspace, workspace_bytes, stream);
+                    request_scale, y, ldy, LORA_BF16, quality, workspace, workspace_bytes, stream);
 }
 
 int dense_patch_apply(void* dst, int32_t dst_dtype, const int64_t* dst_shape, int32_t dst_ndim, const void* src,
@@ -359,6 +410,21 @@ size_t lora_linear_nf4_workspace_size(int64_t T, int64_t K, int64_t N, int32_t r
   const size_t ad = rank > 0 ? lora_linear_workspace_size(T, K, N, &rank, 1, adapter_dtype, quality) : 0;
   if (!lora::nf4_uses_panel(true, quality == LORA_LOSSLESS, T)) return ad;
   return round_up(ad) + panel_bytes(N, K);
+}
+
+size_t lora_linear_multi_workspace_size(int64_t T, int64_t K, int64_t N, const lora_adapter* adapters,
+                                        int32_t n_adapters, int32_t adapter_dtype, int32_t quality) {
+  if (T <= 0 || K <= 0 || N <= 0 || n_adapters < 0 || n_adapters > LORA_MAX_GROUPS ||
+      (n_adapters > 0 && adapters == nullptr))
+    return 0;
+  int32_t ranks[LORA_MAX_GROUPS];
+  bool legacy = false;
+  for (int i = 0; i < n_adapters; ++i) {
+    ranks[i] = adapters[i].A != nullptr ? adapters[i].rank : 0;
+    legacy = legacy || (adapters[i].A != nullptr && adapters[i].B_bias != nullptr && adapters[i].strength != 0.0);
+  }
+  const size_t rest = lora_linear_workspace_size(T, K, N, ranks, n_adapters, adapter_dtype, quality);
+  return (legacy && quality == LORA_LOSSLESS) ? round_up(static_cast<size_t>(N) * 4) + rest : rest;
 }
 
 const char* lora_status_string(int status) {

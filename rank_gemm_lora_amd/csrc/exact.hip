@@ -183,9 +183,15 @@ __global__ __launch_bounds__(256) void exact_out_kernel(LinearProblem p) {
     for (int j = 0; j < 4; ++j) {
       const int64_t n = n0 + tx + 16 * j;
       if (n < g.col_off || n >= g.col_off + g.n_cols) continue;
+      float cb = 0.f;
+      if (g.Bb != nullptr)
+        cb = ad_bf16 ? bf16_to_f32(static_cast<const bf16_bits*>(g.Bb)[n - g.col_off])
+                     : static_cast<const float*>(g.Bb)[n - g.col_off];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float d = rn_dt(static_cast<float>(dacc[i][j]), ad_bf16);  // E3
+        // E3 (a legacy lora_B bias is added to the fp32 GEMM result before the rounding, as in E2)
+        const float gd = static_cast<float>(dacc[i][j]);
+        float d = rn_dt(g.Bb != nullptr ? gd + cb : gd, ad_bf16);
 #pragma unroll
         for (int f = 0; f < 3; ++f) {                                 // E4
           if (g.f[f] != 1.0f) d = rn_dt(d * g.f[f], ad_bf16);

@@ -181,7 +181,11 @@ __device__ __forceinline__ void epilogue(const f32x16 (&acc)[C::NI][C::NJ], cons
     for (int gq = 0; gq < 4; ++gq) {
       const int64_t n = n0 + wn0 + i * 32 + gq * 8 + h * 4;
       float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bias != nullptr) {
+      if (p.bias32 != nullptr) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.N) bv[e] = p.bias32[n + e];
+      } else if (bias != nullptr) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (n + e < p.N) {
@@ -874,7 +878,8 @@ __device__ __forceinline__ void mfma_frags16(f32x4 (&acc)[P::NI][P::NJ], const F
 // rounding, staged in the wave's 32 KB of LDS as token rows (16-byte chunks
 // XOR-swizzled by row), then written as whole 256-byte output rows, as in the
 // 32 x 32 epilogue.
-template <class P, bool BIAS>
+// BIAS: 0 none, 1 the bf16 bias, 2 the fp32 bias vector p.bias32.
+template <class P, int BIAS>
 __device__ __forceinline__ void stage_out16(const f32x4 (&acc)[P::NI][P::NJ], const LinearProblem& p, int64_t n0,
                                             int wn0, int lane, char* st) {
   const int r = lane & 15, q = lane >> 4;
@@ -883,7 +888,17 @@ __device__ __forceinline__ void stage_out16(const f32x4 (&acc)[P::NI][P::NJ], co
   for (int i = 0; i < P::NI; ++i) {
     const int cl = i * 16 + q * 4;  // first of 4 columns, local to the wave block
     float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (BIAS) {
+    if (BIAS == 2) {
+      const int64_t n = n0 + wn0 + cl;
+      if (n + 3 < p.N) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(p.bias32 + n);  // 16-byte aligned: n is a multiple of 4
+        bv[0] = w[0]; bv[1] = w[1]; bv[2] = w[2]; bv[3] = w[3];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < p.N) bv[e] = p.bias32[n + e];
+      }
+    } else if (BIAS == 1) {
       const int64_t n = n0 + wn0 + cl;
       if (n + 3 < p.N) {
         const uint2 w = *reinterpret_cast<const uint2*>(bias + n);  // 8-byte aligned: n is a multiple of 4
@@ -899,7 +914,7 @@ __device__ __forceinline__ void stage_out16(const f32x4 (&acc)[P::NI][P::NJ], co
     for (int j = 0; j < P::NJ; ++j) {
       const int row = j * 16 + r;
       uint2 w;
-      if (BIAS) {
+      if (BIAS != 0) {
         w.x = pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]);
         w.y = pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]);
       } else {
@@ -921,8 +936,9 @@ __device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[P::NI][P::NJ],
   char* st = smem + wave * (128 * 256);
   // (only this wave reads its staging, and a wave's LDS operations run in
   // order, so the reads below see the writes without a wait)
-  if (p.bias != nullptr) stage_out16<P, true>(acc, p, n0, wn0, lane, st);
-  else stage_out16<P, false>(acc, p, n0, wn0, lane, st);
+  if (p.bias32 != nullptr) stage_out16<P, 2>(acc, p, n0, wn0, lane, st);
+  else if (p.bias != nullptr) stage_out16<P, 1>(acc, p, n0, wn0, lane, st);
+  else stage_out16<P, 0>(acc, p, n0, wn0, lane, st);
   const int c = lane & 15, rr = lane >> 4;
   const int64_t mb = m0 + wm0;  // first token of the wave block
   const int64_t n = n0 + wn0 + c * 8;
@@ -1822,8 +1838,9 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(LinearProblem p, int
       for (int i = 0; i < kFinishTokens; ++i) acc[i] = fmaf(tg[i * ldt + qq], bv, acc[i]);
     }
   }
-  const bool has_bias = p.bias != nullptr;
-  const float bias = has_bias ? bf16_to_f32(static_cast<const bf16_bits*>(p.bias)[n]) : 0.f;
+  const bool has_bias = p.bias != nullptr || p.bias32 != nullptr;
+  const float bias = p.bias32 != nullptr ? p.bias32[n]
+                     : (p.bias != nullptr ? bf16_to_f32(static_cast<const bf16_bits*>(p.bias)[n]) : 0.f);
 #pragma unroll
   for (int i = 0; i < kFinishTokens; ++i) {
     if (t0 + i < p.T)
@@ -1976,6 +1993,29 @@ hipError_t split_gemm(const LinearProblem& p, hipStream_t s) {
     g.t_col = 3 * g.t_col;
   }
   return pipe::launch(q, s);
+}
+
+// b + sum_g s_g . c_g over the legacy lora_B biases, fp32, groups in order (one thread per column).
+__global__ __launch_bounds__(256) void bias32_kernel(LinearProblem p) {
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (n >= p.N) return;
+  float v = 0.f;
+  if (p.bias != nullptr)
+    v = p.act == Elt::BF16 ? bf16_to_f32(static_cast<const bf16_bits*>(p.bias)[n]) : static_cast<const float*>(p.bias)[n];
+  for (int gi = 0; gi < p.n_groups; ++gi) {
+    const GroupDev& g = p.g[gi];
+    if (g.Bb == nullptr || n < g.col_off || n >= g.col_off + g.n_cols) continue;
+    const int64_t j = n - g.col_off;
+    const float c = p.adapter == Elt::BF16 ? bf16_to_f32(static_cast<const bf16_bits*>(g.Bb)[j])
+                                           : static_cast<const float*>(g.Bb)[j];
+    v += g.scale * c;
+  }
+  p.bias32[n] = v;
+}
+
+hipError_t launch_bias32(const LinearProblem& p, hipStream_t s) {
+  hipLaunchKernelGGL(bias32_kernel, dim3(static_cast<unsigned>((p.N + 255) / 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_lossless(const LinearProblem& p, hipStream_t s, int phase) {

@@ -33,6 +33,7 @@ struct GroupDev {
   // (hi(v) = RN_bf16(v), lo(v) = RN_bf16(v - hi(v)); padding zero).
   void* A2;
   void* B2;
+  const void* Bb;    // legacy lora_B bias [n_cols] in the adapter dtype, or null
 };
 
 // Few tokens (lossless, bf16 activations, T <= kSkinnyMaxT): the weight read is
@@ -110,6 +111,8 @@ struct LinearProblem {
   void* panel;       // 4-bit weight, lossless, T > kSkinnyMaxT: bf16 [N, K] dequantized copy in the workspace
   float* skinny;     // skinny path: fp32 partial sums in the workspace (null otherwise)
   float* tpart;      // bf16 adapter, lossless: the producer's K-split partial sums (null: no split)
+  float* bias32;     // lossless with legacy lora_B biases: b + sum_g s_g . c_g, fp32 [N] (null otherwise);
+                     // the epilogues add it instead of `bias`
   const void* bias;
   void* y; int64_t ldy;
   int64_t T, N, K;
@@ -125,6 +128,8 @@ struct LinearProblem {
 // phase 0 runs both, 1 only the rank-wide producer, 2 only the fused GEMM
 // (which reads the t~ a phase-1 call left in the workspace).
 hipError_t launch_lossless(const LinearProblem& p, hipStream_t s, int phase = 0);
+// Lossless with legacy lora_B biases: p.bias32 = fp32(b) + s_g . fp32(c_g) summed in group order.
+hipError_t launch_bias32(const LinearProblem& p, hipStream_t s);
 // Exact tier: the ordered-fp64 separate-pass chain.
 hipError_t launch_exact(const LinearProblem& p, hipStream_t s);
 // Dense payload over n contiguous elements.

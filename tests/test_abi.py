@@ -170,6 +170,38 @@ def test_stacked_group_validation():
     assert stacked([(0, 0, 10)]) == SHAPE
 
 
+def multi(ads, n=None, **kw):
+    a = dict(x=X, T=0, K=128, ldx=128, W=W, N=300, bias=None, adt=BF16, rs=1.0, y=Y, ldy=304, act=BF16,
+             q=LOSSLESS, ws=WSP, wsb=1 << 30)
+    a.update(kw)
+    arr = [rg.LoraAdapter(A + i * 0x1000_0000, B + i * 0x1000_0000, c, r, 0, 8.0, st, o, nc)
+           for i, (r, o, nc, st, c) in enumerate(ads)]
+    n = len(arr) if n is None else n
+    return rg._lib.lora_linear_multi_fwd(a["x"], a["T"], a["K"], a["ldx"], a["W"], a["N"], a["bias"],
+                                         (rg.LoraAdapter * max(1, len(arr)))(*arr), n, a["adt"], a["rs"],
+                                         a["y"], a["ldy"], a["act"], a["q"], a["ws"], a["wsb"], None)
+
+
+def test_multi_validation():
+    C = BIAS + 0x100
+    assert multi([(8, 0, 300, 1.0, None), (16, 0, 300, 0.5, C), (4, 100, 50, 2.0, None)]) == OK  # overlap allowed
+    assert multi([(8, 0, 300, 1.0, None)] * 9) == UNSUP
+    assert multi([], n=-1) == SHAPE
+    assert multi([(8, 0, 301, 1.0, None)]) == SHAPE                  # past N
+    assert multi([(8, 0, 300, math.inf, None)]) == NONFIN            # per-adapter strength checked
+    assert multi([(8, 0, 300, 1.0, C + 1)]) == ALIGN                 # bf16 bias needs 2-byte alignment
+    assert multi([(8, 0, 300, 1.0, Y + 2)], T=4) == OVERLAP          # legacy bias inside the output
+    assert multi([(8, 0, 300, 1.0, None)], rs=math.nan) == NONFIN
+    # a legacy bias of an active adapter adds an fp32 [N] vector at the front of the workspace
+    mk = lambda c, st=1.0: [rg.LoraAdapter(A, B, c, 8, 0, 8.0, st, 0, 300)]
+    ws = rg.lora_linear_multi_workspace_size
+    plain = rg.lora_linear_workspace_size(4096, 128, 300, [8], BF16)
+    assert ws(4096, 128, 300, mk(None), BF16) == plain
+    assert ws(4096, 128, 300, mk(C), BF16) == (300 * 4 + 255) // 256 * 256 + plain
+    assert ws(4096, 128, 300, mk(C, 0.0), BF16) == plain           # zero strength: inactive
+    assert ws(4096, 128, 300, mk(C), BF16, EXACT) == rg.lora_linear_workspace_size(4096, 128, 300, [8], BF16, EXACT)
+
+
 def nf4(**kw):
     a = dict(x=X, T=0, K=128, ldx=128, codes=W, absmax=W + 0x1000_0000, cb=W + 0x2000_0000, bs=64, N=96,
              bias=None, A=A, B=B, rank=16, adt=BF16, alpha=32.0, y=Y, ldy=96, q=LOSSLESS)

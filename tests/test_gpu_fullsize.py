@@ -59,6 +59,24 @@ def test_other_token_regimes_full(pair):
         _linear_case(lw.linear_inputs(lw.ZIMAGE_ATTN), lw.ZIMAGE_ATTN.name)
 
 
+def test_multi_adapters_full():
+    s = lw.MULTI_FFN_UP
+    d = lw.multi_inputs(s)
+    rows = sample_rows(s.T, n_each=24, seed=4)
+    say(f"case full-size two adapters on FFN up T={s.T} rows={len(rows)}")
+    gg = [dict(a, A=dev(a["A"]), B=dev(a["B"]), c=dev(a["c"])) for a in d["adapters"]]
+    y = rg.lora_linear_multi(dev(d["x"]), dev(d["W"]), dev(d["b"]), gg, s.request_scale)
+    torch.cuda.synchronize()
+    xs = d["x"][rows]
+    y64 = lo.lora_linear_multi(xs, d["W"], d["b"], d["adapters"], s.request_scale)
+    yc = ec.chain_multi(xs, d["W"], d["b"], d["adapters"], s.request_scale)
+    idx = torch.from_numpy(rows).to(y.device)
+    assert_gate(y[idx], y64, yc, what="multi lossless (sampled rows)")
+    ye = rg.lora_linear_multi(dev(d["x"]), dev(d["W"]), dev(d["b"]), gg, s.request_scale, quality="exact")
+    torch.cuda.synchronize()
+    assert_bitwise(ye[idx], yc, "multi exact (sampled rows)")
+
+
 @pytest.mark.parametrize("adapter", ["bf16", "f32"])
 def test_qkv_stacked_full(adapter):
     spec = lw.QKV_STACKED if adapter == "bf16" else lw.StackedSpec(

@@ -452,3 +452,52 @@ def test_dense_patch_unaligned_and_goldens():
         rg.dense_patch(gd, dev(src), _hex(c["strength"]), c["mode"])
         torch.cuda.synchronize()
         assert bool((host64(gd) == _hex(c["expected"])).all()), c["name"]
+
+
+# ------------------------------------------------------------------ several adapters on one layer
+
+def _multi_inputs(seed, T, adapter="bf16", n_ads=3, K=256, N=520):
+    rng = np.random.default_rng(seed)
+    x = lw.to_dtype(rng.standard_normal((T, K)), "bf16")
+    W = lw.to_dtype(rng.standard_normal((N, K)) / np.sqrt(K), "bf16")
+    b = lw.to_dtype(rng.standard_normal(N) * np.sqrt(0.02), "bf16")
+    # rank, alpha, strength, column range, legacy lora_B bias: overlapping ranges, ragged edges
+    specs = [(16, 32.0, 1.0, 0, N, True), (24, 24.0, 0.6, 130, 300, False), (64, 16.0, -0.8, 200, 320, True),
+             (8, 8.0, 0.9, 0, 257, True)][:n_ads]
+    ads = [dict(A=lw.to_dtype(rng.standard_normal((r, K)) / np.sqrt(K), adapter),
+                B=lw.to_dtype(rng.standard_normal((n, r)) * np.sqrt(0.02), adapter),
+                c=lw.to_dtype(rng.standard_normal(n) * np.sqrt(0.02), adapter) if has_c else None,
+                rank=r, alpha=a, strength=st, col_offset=o, n_cols=n) for r, a, st, o, n, has_c in specs]
+    return x, W, b, ads
+
+
+@pytest.mark.parametrize("T,adapter,n_ads", [(300, "bf16", 2), (300, "bf16", 3), (300, "f32", 3), (20, "bf16", 4),
+                                             (20, "f32", 2)])
+def test_multi_adapters(T, adapter, n_ads):
+    """Overlapping adapters with their own strengths and legacy lora_B biases (2 per tile: the hot
+    kernel; 3: the general pipelined kernel; 20 tokens: the few-token path)."""
+    x, W, b, ads = _multi_inputs(81 + n_ads, T, adapter, n_ads)
+    say(f"case multi T={T} adapter={adapter} n={n_ads}")
+    y64 = lo.lora_linear_multi(x, W, b, ads, 0.7)
+    yc = ec.chain_multi(x, W, b, ads, 0.7, "bf16", adapter)
+    gg = [dict(a, A=dev(a["A"]), B=dev(a["B"]), c=dev(a["c"])) for a in ads]
+    y = rg.lora_linear_multi(dev(x), dev(W), dev(b), gg, 0.7)
+    torch.cuda.synchronize()
+    assert_gate(y, y64, yc, what="multi lossless")
+    ye = rg.lora_linear_multi(dev(x), dev(W), dev(b), gg, 0.7, quality="exact")
+    torch.cuda.synchronize()
+    assert_bitwise(ye, yc, "multi exact")
+
+
+@pytest.mark.parametrize("T", [300, 20])
+def test_multi_disjoint_equals_stacked(T):
+    """Disjoint adapters, one strength, no legacy bias: the multi call is the stacked call, bit for bit."""
+    x, W, b, groups = _stacked_inputs(33, "bf16", T=T)
+    gg = [dict(g, A=dev(g["A"]), B=dev(g["B"])) for g in groups]
+    say(f"case multi == stacked T={T}")
+    for q in ("lossless", "exact"):
+        ys = rg.lora_linear_stacked(dev(x), dev(W), dev(b), gg, 0.9, 0.8, quality=q)
+        ym = rg.lora_linear_multi(dev(x), dev(W), dev(b), [dict(g, c=None, strength=0.9) for g in gg], 0.8,
+                                  quality=q)
+        torch.cuda.synchronize()
+        assert torch.equal(ys, ym), q
