@@ -34,7 +34,7 @@ import numpy as np
 from .lora_oracle import f64, nf4_unpack_codes
 
 __all__ = ["rn_f32", "rn_bf16", "rn", "gemm_ordered", "chain_linear", "chain_stacked", "chain_multi",
-           "chain_nf4_weight", "chain_nf4", "chain_dense_patch"]
+           "chain_merge", "chain_nf4_weight", "chain_nf4", "chain_dense_patch"]
 
 
 def rn_f32(a) -> np.ndarray:
@@ -146,6 +146,17 @@ def chain_multi(x, W, b, adapters, request_scale, act: str = "bf16", adapter: st
         d = _scale_passes(rn(g, adapter), factors, adapter)
         y[:, o:o + n] = rn(rn_f32(y[:, o:o + n] + d), act)
     return y
+
+
+def chain_merge(W, A, B, alpha, rank, strength, wdt: str = "bf16") -> np.ndarray:
+    """Exact tier of the merge W <- W + s.B.A (piper-offload README, LoRA merge: an in-place
+    addmm_ into a plain dense base), as the chain of a dense payload whose delta is the rank
+    product: G = E1(B, A^T) (fp32, q ascending), then E7's add with s = RN_f32((alpha / rank) .
+    strength): d = RN_f32(G . s) (skipped when s == 1), W' = RN_wdt(RN_f32(W + d))."""
+    G = gemm_ordered(B, f64(A).T)
+    s32 = float(rn_f32((float(alpha) / float(rank)) * float(strength)))
+    d = G if s32 == 1.0 else rn_f32(G * s32)
+    return rn(rn_f32(f64(W) + d), wdt)
 
 
 def chain_nf4_weight(codes, absmax, codebook, K: int, blocksize: int = 64) -> np.ndarray:

@@ -476,3 +476,47 @@ def test_multi_inactive_adapter_drops_its_bias():
     ads0[0]["strength"] = 0.0
     y = lo.lora_linear_multi(x, W, b, ads0, 1.0)
     assert np.array_equal(y, lo.lora_linear_multi(x, W, b, ads0[1:], 1.0))
+
+
+# ------------------------------------------------------------------ merge W <- W + s.B.A
+
+def test_merge_chain_against_exact_rounding():
+    """Each rounding point of the exact merge against Fraction arithmetic rounded by the IEEE rules."""
+    rng = np.random.default_rng(21)
+    N, K, r = 5, 7, 3
+    W = lw.to_dtype(rng.standard_normal((N, K)) * 0.05, "bf16")
+    A = lw.to_dtype(rng.standard_normal((r, K)) / 3, "bf16")
+    B = lw.to_dtype(rng.standard_normal((N, r)) * 0.1, "bf16")
+    for alpha, strength in ((3.0, 0.7), (3.0, 1.0)):
+        got = ec.chain_merge(W, A, B, alpha, r, strength)
+        s32 = round_fraction(Fraction(alpha) / r * Fraction(strength), "f32")
+        Wn, An, Bn = lo.f64(W), lo.f64(A), lo.f64(B)
+        for n in range(N):
+            for k in range(K):
+                g = round_fraction(sum((exact(Bn[n, q]) * exact(An[q, k]) for q in range(r)), Fraction(0)), "f32")
+                d = g if s32 == 1.0 else round_fraction(exact(g) * exact(s32), "f32")
+                v = round_fraction(exact(Wn[n, k]) + exact(d), "f32")
+                assert got[n, k] == round_fraction(exact(v), "bf16"), (alpha, strength, n, k)
+
+
+def test_merge_chain_hand_worked():
+    """W = 1, B.A = 2^-8: 1 + 2^-8 is half the bf16 spacing (2^-7) above 1, a tie, and rounds to the
+    even neighbour 1 -- the update is rounded away entirely. With s = 3, 1 + 3 . 2^-8 is 1.5 spacings
+    above 1, again a tie, between 1 + 2^-7 (odd) and 1 + 2^-6 (even): the merge gives 1 + 2^-6, twice
+    the 1 + 3 . 2^-8 the plain definition keeps."""
+    bf = lambda rows: lw.to_dtype(np.array(rows, dtype=np.float64), "bf16")
+    W, A, B = bf([[1.0]]), bf([[2.0 ** -4]]), bf([[2.0 ** -4]])
+    assert ec.chain_merge(W, A, B, 1.0, 1, 1.0)[0, 0] == 1.0
+    assert ec.chain_merge(W, A, B, 3.0, 1, 1.0)[0, 0] == 1.0 + 2.0 ** -6
+    # the plain definition keeps the whole update (fp64)
+    assert lo.merged_weight(W, A, B, 3.0)[0, 0] == 1.0 + 3 * 2.0 ** -8
+
+
+def test_merged_weight_linear_equals_the_adapter_layer():
+    """x.(W + s.B.A)^T + b == the LoRA linear (integer data: exact)."""
+    rng = np.random.default_rng(22)
+    x, W, b = _int_mat(rng, (4, 6)), _int_mat(rng, (5, 6)), _int_mat(rng, (5,))
+    A, B = _int_mat(rng, (2, 6)), _int_mat(rng, (5, 2))
+    s = lo.combined_scale(3.0, 2, 0.5, 1.0)
+    y_merged = lo.f64(x) @ lo.merged_weight(W, A, B, s).T + lo.f64(b)[None, :]
+    assert np.array_equal(y_merged, lo.lora_linear(x, W, b, A, B, 3.0, 2, 0.5, 1.0))
