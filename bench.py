@@ -510,6 +510,31 @@ def config_sweep(torch, dev, stream, with_oracle=True):
         del dst, diff, h
         torch.cuda.empty_cache()
 
+    # merge W <- W + s.B.A (merge mode): HBM-bound rewrite of the weight; and how much of the update
+    # a bf16 merge keeps -- the data behind keeping an adapter dynamic
+    for spec in (lw.MERGE_WEIGHT, lw.MERGE_WEIGHT_SMALL):
+        h = lw.merge_inputs(spec)
+        W0, A, B = d2(h["W"]), d2(h["A"]), d2(h["B"])
+        Wm = W0.clone()
+        ms = _launch_stats(torch, stream, lambda: rg.lora_merge(Wm, A, B, spec.alpha, spec.strength))
+        Wm.copy_(W0)
+        rg.lora_merge(Wm, A, B, spec.alpha, spec.strength)
+        s_ = spec.alpha / spec.rank * spec.strength
+        upd = s_ * (B.double() @ A.double())
+        kept = (Wm.double() - W0.double())
+        lost = float((kept - upd).norm() / upd.norm())
+        N, K, r = spec.N, spec.K, spec.rank
+        byt = 2 * (2 * N * K + r * (N + K))
+        gbs = byt / (ms["median"] * 1e-3) / 1e9
+        e = {"workload": f"merge W += s.B.A: W=[{N}, {K}] bf16, r={r}, B~N(0, {spec.b_var:g})", "ms": ms,
+             "bound": "hbm", "achieved_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+             "algorithmic_bytes": byt, "algorithmic_flop": 2.0 * N * K * r,
+             "update_lost_fraction": round(lost, 4),
+             "elements_changed_fraction": round(float((Wm != W0).double().mean()), 4)}
+        out[spec.name] = e
+        del W0, A, B, Wm, upd, kept, h
+        torch.cuda.empty_cache()
+
     spec = lw.TINY_FP32
     h = lw.linear_inputs(spec)
     x, W, b, A, B = (d2(h[k]) for k in ("x", "W", "b", "A", "B"))

@@ -266,6 +266,29 @@ int dense_patch_apply(void* dst, int32_t dst_dtype, const int64_t* dst_shape, in
                       double strength, int32_t mode, void* stream);
 
 /*
+ * lora_merge_apply -- merge an adapter into a plain dense weight, in place
+ * (piper-offload README, LoRA merge and merge_lora: an in-place addmm_ into a
+ * plain dense base; FastVideo lora_patch page: the sum in fp32, one cast back):
+ *
+ *     W <- RN_w( W + s . B.A ),   s = (alpha / rank) . strength
+ *
+ *   W      [N, K] w_dtype (bf16 or fp32), row-major, updated in place
+ *   A, B   [rank, K], [N, rank] adapter_dtype
+ *   LORA_LOSSLESS  the rank product summed in fp32, s . (B.A) added to fp32(W)
+ *                  in one multiply-add, one rounding to w_dtype; needs W, A, B
+ *                  16-byte aligned and K a multiple of 8
+ *   LORA_EXACT     G = RN_f32(sum over q ascending of B[n,q] A[q,k], in fp64),
+ *                  d = RN_f32(G . RN_f32(s)) (skipped when RN_f32(s) == 1),
+ *                  W <- RN_w(RN_f32(W + d)): the dense-payload chain with the
+ *                  rank product as its delta
+ * s == +-0 leaves W unchanged (nothing is launched); W must not overlap A or B.
+ * A bf16 merge rounds away every part of the update below half a bf16 spacing
+ * of the weight: the reason the SGLang PR keeps such adapters dynamic.
+ */
+int lora_merge_apply(void* W, int32_t w_dtype, int64_t N, int64_t K, const void* A, const void* B, int32_t rank,
+                     int32_t adapter_dtype, double alpha, double strength, int32_t quality, void* stream);
+
+/*
  * Workspace bytes a call with T tokens, K inputs and N outputs needs for
  * adapters of the given ranks (`ranks` is a HOST array of n_ranks entries: one
  * for lora_linear_fwd and lora_linear_nf4_fwd, one per group for

@@ -30,6 +30,7 @@ import torch
 
 __all__ = [
     "LinearSpec", "StackedSpec", "Nf4Spec", "PatchSpec", "MultiSpec", "MULTI_FFN_UP", "multi_inputs",
+    "MergeSpec", "MERGE_WEIGHT", "MERGE_WEIGHT_SMALL", "merge_inputs",
     "TINY_FP32", "ATTN_PROJ", "FFN_UP", "FFN_DOWN", "QKV_STACKED", "NF4_LAYER",
     "PATCH_WEIGHT", "PATCH_NORM", "ZIMAGE_ATTN", "ZIMAGE_FFN_UP", "ZIMAGE_FFN_DOWN", "H3_FFN_UP",
     "H3_FFN_DOWN", "FEW_FFN_UP", "FEW_FFN_DOWN", "NF4_VECTOR",
@@ -134,6 +135,19 @@ class MultiSpec:
 
 
 @dataclass(frozen=True)
+class MergeSpec:
+    """An adapter merged into a dense weight: W [N, K], A [r, K], B [N, r]."""
+    name: str
+    N: int
+    K: int
+    rank: int
+    alpha: float
+    strength: float
+    seed: int
+    b_var: float = 0.02
+
+
+@dataclass(frozen=True)
 class PatchSpec:
     """Dense payload applied to a parameter of ``shape``."""
     name: str
@@ -187,6 +201,12 @@ NF4_VECTOR = Nf4Spec("nf4_vector", T=1, K=4096, N=14336, rank=16, alpha=32.0, st
 MULTI_FFN_UP = MultiSpec("multi_ffn_up", T=32760, K=1536, N=8960,
                          adapters=((64, 64.0, 1.0, 0, 8960, False), (32, 32.0, 0.5, 0, 8960, True)),
                          request_scale=0.7, bias=False, seed=13)
+
+# The rank-16 adapter of the 4-bit layer's shape merged into a bf16 weight of that shape (merge mode);
+# the second reads "N(0, 0.02)" of B as a standard deviation: the small update a bf16 merge loses.
+MERGE_WEIGHT = MergeSpec("merge_weight", N=14336, K=4096, rank=16, alpha=32.0, strength=0.8, seed=14)
+MERGE_WEIGHT_SMALL = MergeSpec("merge_weight_small_update", N=14336, K=4096, rank=16, alpha=32.0, strength=0.8,
+                               seed=14, b_var=0.02 ** 2)
 
 PATCH_WEIGHT = PatchSpec("patch_weight", shape=(14336, 4096), strength=0.8, seed=6,
                          base_mean=0.0, base_var=1.0 / 4096, diff_var=(1e-3) ** 2 / 4096)
@@ -254,6 +274,15 @@ def multi_inputs(s: MultiSpec, spread: str = "variance") -> dict:
         c = _normal(rng, (n,), 0.02, s.adapter, spread) if has_c else None
         ads.append(dict(A=A, B=B, c=c, rank=r, alpha=a, strength=st, col_offset=o, n_cols=n))
     return dict(x=x, W=W, b=b, adapters=ads, request_scale=s.request_scale)
+
+
+def merge_inputs(s: MergeSpec) -> dict:
+    """W, A, B (bf16) of a merge workload."""
+    rng = np.random.default_rng(s.seed)
+    W = _normal(rng, (s.N, s.K), 1.0 / s.K, "bf16")
+    A = _normal(rng, (s.rank, s.K), 1.0 / s.K, "bf16")
+    B = _normal(rng, (s.N, s.rank), s.b_var, "bf16")
+    return dict(W=W, A=A, B=B, rank=s.rank, alpha=s.alpha, strength=s.strength)
 
 
 def nf4_style_codebook() -> torch.Tensor:

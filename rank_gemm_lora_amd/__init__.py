@@ -26,7 +26,7 @@ __all__ = [
     "LORA_PATCH_ADD", "LORA_PATCH_REPLACE", "lora_linear_fwd", "lora_linear_stacked_fwd",
     "lora_linear_nf4_fwd", "dense_patch_apply", "lora_linear_fwd_phase", "lora_linear_workspace_size",
     "lora_linear_nf4_workspace_size", "lora_linear_multi_fwd", "lora_linear_multi_workspace_size",
-    "lora_linear_multi", "LoraAdapter",
+    "lora_linear_multi", "LoraAdapter", "lora_merge_apply", "lora_merge",
     "lora_status_string",
     "lora_device_check", "lora_linear", "lora_linear_stacked", "lora_linear_nf4", "dense_patch",
     "LoraGroup", "hip_runtimes_mapped",
@@ -82,6 +82,8 @@ _lib.lora_linear_multi_fwd.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, ctype
 _lib.lora_linear_multi_fwd.restype = ctypes.c_int
 _lib.lora_linear_multi_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(LoraAdapter), _i32, _i32, _i32]
 _lib.lora_linear_multi_workspace_size.restype = _sz
+_lib.lora_merge_apply.argtypes = [_p, _i32, _i64, _i64, _p, _p, _i32, _i32, _f64, _f64, _i32, _p]
+_lib.lora_merge_apply.restype = ctypes.c_int
 _lib.lora_linear_nf4_workspace_size.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32]
 _lib.lora_linear_nf4_workspace_size.restype = _sz
 _lib.lora_status_string.argtypes = [ctypes.c_int]
@@ -132,6 +134,11 @@ def lora_linear_multi_fwd(x, T, K, ldx, W, N, bias, adapters, n_adapters, adapte
     return _check(_lib.lora_linear_multi_fwd(x, T, K, ldx, W, N, bias, arr, n_adapters, adapter_dtype, request_scale,
                                              y, ldy, act_dtype, quality, workspace, workspace_bytes, stream),
                   "lora_linear_multi_fwd")
+
+
+def lora_merge_apply(W, w_dtype, N, K, A, B, rank, adapter_dtype, alpha, strength, quality, stream):
+    return _check(_lib.lora_merge_apply(W, w_dtype, N, K, A, B, rank, adapter_dtype, alpha, strength, quality, stream),
+                  "lora_merge_apply")
 
 
 def lora_linear_multi_workspace_size(T, K, N, adapters, adapter_dtype, quality=LORA_LOSSLESS) -> int:
@@ -290,6 +297,16 @@ def lora_linear_nf4(x, codes, absmax, codebook, N, b, A, B, alpha, strength=1.0,
                         float(request_scale), out.data_ptr(), ldy, q, ws.data_ptr(), ws.numel(),
                         _stream(stream))
     return out
+
+
+def lora_merge(W, A, B, alpha, strength=1.0, quality="lossless", stream=None):
+    """W <- RN(W + (alpha / rank) . strength . B.A) in place on the GPU; returns ``W``."""
+    N, K = W.shape
+    if not (W.is_contiguous() and A.is_contiguous() and B.is_contiguous()):
+        raise ValueError("lora_merge needs contiguous tensors")
+    lora_merge_apply(W.data_ptr(), _dt(W), N, K, A.data_ptr(), B.data_ptr(), A.shape[0], _dt(A), float(alpha),
+                     float(strength), _QUALITY[quality], _stream(stream))
+    return W
 
 
 def dense_patch(dst, src, strength, mode="add", stream=None):

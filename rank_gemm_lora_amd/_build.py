@@ -28,6 +28,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
 # file -> extra flags
 SOURCES = {
     "gemm.hip": [],
+    "merge.hip": [],
     "exact.hip": ["-ffp-contract=off"],
     "patch.hip": ["-ffp-contract=off"],
     "api.cpp": [],

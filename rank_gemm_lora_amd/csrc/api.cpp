@@ -367,6 +367,37 @@ int dense_patch_apply(void* dst, int32_t dst_dtype, const int64_t* dst_shape, in
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+int lora_merge_apply(void* W, int32_t w_dtype, int64_t N, int64_t K, const void* A, const void* B, int32_t rank,
+                     int32_t adapter_dtype, double alpha, double strength, int32_t quality, void* stream) {
+  if (!dtype_ok(w_dtype) || !dtype_ok(adapter_dtype)) return LORA_ERR_DTYPE;
+  if (quality != LORA_LOSSLESS && quality != LORA_EXACT) return LORA_ERR_UNSUPPORTED;
+  if (N < 0 || K < 0) return LORA_ERR_SHAPE;
+  if (!std::isfinite(alpha) || !std::isfinite(strength)) return LORA_ERR_NONFINITE;
+  if (A == nullptr || B == nullptr || (N > 0 && K > 0 && W == nullptr)) return LORA_ERR_NULL_PTR;
+  if (rank < 1) return LORA_ERR_SHAPE;
+  if (rank > LORA_MAX_RANK || K * 4 > kMaxRowBytes) return LORA_ERR_UNSUPPORTED;
+  const double s = (alpha / static_cast<double>(rank)) * strength;
+  if (std::fabs(s) > FLT_MAX) return LORA_ERR_NONFINITE;
+  const int ew = esz(w_dtype), el = esz(adapter_dtype);
+  if (quality == LORA_LOSSLESS) {
+    if (!aligned(W, 16) || !aligned(A, 16) || !aligned(B, 16)) return LORA_ERR_ALIGN;
+    if (K % 8 != 0) return LORA_ERR_ALIGN;
+  } else if (!aligned(W, ew) || !aligned(A, el) || !aligned(B, el)) {
+    return LORA_ERR_ALIGN;
+  }
+  if (N == 0 || K == 0) return LORA_OK;
+  const Span sw = span2d(W, N, K, K, ew);
+  if (overlaps(sw, span2d(A, rank, K, K, el)) || overlaps(sw, span2d(B, N, rank, rank, el))) return LORA_ERR_OVERLAP;
+  if (s == 0.0) return LORA_OK;  // a zero strength (or alpha) leaves the weight as it is
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = quality == LORA_EXACT
+                           ? lora::launch_exact_merge(W, to_elt(w_dtype), N, K, A, B, rank, to_elt(adapter_dtype),
+                                                      static_cast<float>(s), st)
+                           : lora::launch_merge(W, to_elt(w_dtype), N, K, A, B, rank, to_elt(adapter_dtype),
+                                                static_cast<float>(s), st);
+  return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
 size_t lora_linear_workspace_size(int64_t T, int64_t K, int64_t N, const int32_t* ranks, int32_t n_ranks,
                                   int32_t adapter_dtype, int32_t quality) {
   if (T <= 0 || K <= 0 || N <= 0 || n_ranks < 0 || (n_ranks > 0 && ranks == nullptr) || !dtype_ok(adapter_dtype))

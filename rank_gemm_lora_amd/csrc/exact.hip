@@ -232,7 +232,47 @@ hipError_t launch_exact_t(const LinearProblem& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Exact merge: W[n,k] <- RN_w(RN_f32(W + d)), d = RN_f32(G . s) (no multiply when s == 1),
+// G = RN_f32(sum over q ascending of B[n,q] . A[q,k] in fp64 from +0.0). One thread per element.
+template <typename TW, typename TL>
+__global__ __launch_bounds__(256) void exact_merge_kernel(TW* W, int64_t N, int64_t K, const TL* A, const TL* B,
+                                                          int rank, float s32) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= N * K) return;
+  const int64_t n = i / K, k = i - n * K;
+  auto ld = [](const auto& v) -> float {
+    if constexpr (sizeof(v) == 2) return bf16_to_f32(v);
+    else return v;
+  };
+  double acc = 0.0;
+  for (int q = 0; q < rank; ++q)
+    acc = acc + static_cast<double>(ld(B[n * rank + q])) * static_cast<double>(ld(A[static_cast<int64_t>(q) * K + k]));
+  const float g = static_cast<float>(acc);
+  const float d = s32 == 1.0f ? g : g * s32;
+  const float v = ld(W[i]) + d;
+  if constexpr (sizeof(TW) == 2) W[i] = f32_to_bf16_rne(v);
+  else W[i] = v;
+}
+
 }  // namespace
+
+hipError_t launch_exact_merge(void* W, Elt wdt, int64_t N, int64_t K, const void* A, const void* B, int rank,
+                              Elt adt, float s32, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((N * K + 255) / 256));
+  if (wdt == Elt::BF16 && adt == Elt::BF16)
+    hipLaunchKernelGGL((exact_merge_kernel<bf16_bits, bf16_bits>), grid, dim3(256), 0, st, static_cast<bf16_bits*>(W),
+                       N, K, static_cast<const bf16_bits*>(A), static_cast<const bf16_bits*>(B), rank, s32);
+  else if (wdt == Elt::BF16)
+    hipLaunchKernelGGL((exact_merge_kernel<bf16_bits, float>), grid, dim3(256), 0, st, static_cast<bf16_bits*>(W),
+                       N, K, static_cast<const float*>(A), static_cast<const float*>(B), rank, s32);
+  else if (adt == Elt::BF16)
+    hipLaunchKernelGGL((exact_merge_kernel<float, bf16_bits>), grid, dim3(256), 0, st, static_cast<float*>(W),
+                       N, K, static_cast<const bf16_bits*>(A), static_cast<const bf16_bits*>(B), rank, s32);
+  else
+    hipLaunchKernelGGL((exact_merge_kernel<float, float>), grid, dim3(256), 0, st, static_cast<float*>(W),
+                       N, K, static_cast<const float*>(A), static_cast<const float*>(B), rank, s32);
+  return hipGetLastError();
+}
 
 hipError_t launch_exact(const LinearProblem& p, hipStream_t s) {
   if (p.T == 0) return hipSuccess;

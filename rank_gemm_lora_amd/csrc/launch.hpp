@@ -132,6 +132,11 @@ hipError_t launch_lossless(const LinearProblem& p, hipStream_t s, int phase = 0)
 hipError_t launch_bias32(const LinearProblem& p, hipStream_t s);
 // Exact tier: the ordered-fp64 separate-pass chain.
 hipError_t launch_exact(const LinearProblem& p, hipStream_t s);
+// Merge W <- RN_w(W + s . B.A): lossless (fp32 sum, one rounding) and exact tier.
+hipError_t launch_merge(void* W, Elt wdt, int64_t N, int64_t K, const void* A, const void* B, int rank, Elt adt,
+                        float s, hipStream_t st);
+hipError_t launch_exact_merge(void* W, Elt wdt, int64_t N, int64_t K, const void* A, const void* B, int rank,
+                              Elt adt, float s32, hipStream_t st);
 // Dense payload over n contiguous elements.
 hipError_t launch_dense_patch(void* dst, Elt dst_t, const void* src, Elt src_t, int64_t n,
                               float strength32, int mode, hipStream_t s);

@@ -202,6 +202,29 @@ def test_multi_validation():
     assert ws(4096, 128, 300, mk(C), BF16, EXACT) == rg.lora_linear_workspace_size(4096, 128, 300, [8], BF16, EXACT)
 
 
+def merge(**kw):
+    a = dict(W=W, wdt=BF16, N=300, K=128, A=A, B=B, rank=8, adt=BF16, alpha=8.0, strength=1.0, q=LOSSLESS)
+    a.update(kw)
+    return rg._lib.lora_merge_apply(a["W"], a["wdt"], a["N"], a["K"], a["A"], a["B"], a["rank"], a["adt"],
+                                    a["alpha"], a["strength"], a["q"], None)
+
+
+def test_merge_validation():
+    assert merge(strength=0.0, N=0) == OK          # empty weight: nothing to do
+    assert merge(wdt=7) == DTYPE
+    assert merge(q=5) == UNSUP
+    assert merge(N=-1) == SHAPE
+    assert merge(rank=0) == SHAPE
+    assert merge(rank=2000) == UNSUP
+    assert merge(alpha=math.nan) == NONFIN
+    assert merge(strength=math.inf) == NONFIN
+    assert merge(A=None) == NULL
+    assert merge(K=100) == ALIGN                    # lossless: K a multiple of 8
+    assert merge(W=W + 8) == ALIGN                  # lossless: 16-byte aligned weight
+    assert merge(B=W + 0x100) == OVERLAP            # B inside the weight
+    assert merge(strength=0.0) == OK                # zero scale: nothing launched
+
+
 def nf4(**kw):
     a = dict(x=X, T=0, K=128, ldx=128, codes=W, absmax=W + 0x1000_0000, cb=W + 0x2000_0000, bs=64, N=96,
              bias=None, A=A, B=B, rank=16, adt=BF16, alpha=32.0, y=Y, ldy=96, q=LOSSLESS)

@@ -141,3 +141,22 @@ def test_dense_patch_full(spec):
     rg.dense_patch(g2, dev(d["diff"]), spec.strength, "replace")
     torch.cuda.synchronize()
     assert_bitwise(g2, want_r.reshape(spec.shape), "dense patch replace")
+
+
+@pytest.mark.parametrize("spec", [lw.MERGE_WEIGHT, lw.MERGE_WEIGHT_SMALL], ids=["variance", "small_update"])
+def test_merge_full(spec):
+    d = lw.merge_inputs(spec)
+    rows = sample_rows(spec.N, n_each=24, seed=5)
+    say(f"case full-size merge {spec.N}x{spec.K} r={spec.rank} rows={len(rows)}")
+    g = dev(d["W"])
+    rg.lora_merge(g, dev(d["A"]), dev(d["B"]), spec.alpha, spec.strength)
+    ge = dev(d["W"])
+    rg.lora_merge(ge, dev(d["A"]), dev(d["B"]), spec.alpha, spec.strength, quality="exact")
+    torch.cuda.synchronize()
+    idx = torch.from_numpy(rows).to(g.device)
+    want = ec.chain_merge(d["W"][rows], d["A"], d["B"][rows], spec.alpha, spec.rank, spec.strength)
+    assert_bitwise(ge[idx], want, "merge exact (sampled rows)")
+    # lossless: the exact tier's value, or one bf16 spacing away where the fp32 sums round differently
+    got, ref = host64(g[idx]), want
+    assert (got != ref).mean() < 1e-3
+    assert (np.abs(got - ref) <= np.abs(ref) * 2.0 ** -7 + 2.0 ** -20).all()

@@ -501,3 +501,65 @@ def test_multi_disjoint_equals_stacked(T):
                                   quality=q)
         torch.cuda.synchronize()
         assert torch.equal(ys, ym), q
+
+
+# ------------------------------------------------------------------ merge W <- W + s.B.A
+
+def _ulp_bf16(v):
+    """Spacing of bf16 values at |v| (normal range)."""
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+@pytest.mark.parametrize("N,K,r,wdt,adt", [(300, 520, 64, "bf16", "bf16"), (257, 1000, 100, "bf16", "bf16"),
+                                           (130, 264, 5, "bf16", "bf16"), (300, 520, 24, "f32", "bf16"),
+                                           (300, 520, 24, "bf16", "f32"), (64, 136, 8, "f32", "f32")])
+def test_merge(N, K, r, wdt, adt):
+    rng = np.random.default_rng(90 + r)
+    W = lw.to_dtype(rng.standard_normal((N, K)) / np.sqrt(K), wdt)
+    A = lw.to_dtype(rng.standard_normal((r, K)) / np.sqrt(K), adt)
+    B = lw.to_dtype(rng.standard_normal((N, r)) * np.sqrt(0.02), adt)
+    alpha, strength = 2.0 * r, 0.7
+    say(f"case merge N={N} K={K} r={r} w={wdt} adapter={adt}")
+    W64 = lo.merged_weight(W, A, B, lo.combined_scale(alpha, r, strength, 1.0))
+    g = dev(W)
+    rg.lora_merge(g, dev(A), dev(B), alpha, strength)
+    torch.cuda.synchronize()
+    got = host64(g)
+    if wdt == "bf16":
+        # one rounding of the fp32 sum: the correctly rounded merge, except where the fp32 sum sits
+        # within its own rounding of a bf16 tie (then one bf16 spacing away)
+        want = ec.rn(ec.rn_f32(W64), "bf16")  # (through fp32: a double-rounding tie is within the allowance)
+        diff = np.abs(got - want)
+        # the fp32 sum of r products and the fp32 add err by at most r 2^-23 |s| (|B| |A|) + 2^-23 |W'|
+        # (standard summation bound), which can cross one bf16 rounding boundary
+        sc = lo.combined_scale(alpha, r, strength, 1.0)
+        fp32_err = r * 2.0 ** -23 * abs(sc) * (np.abs(lo.f64(B)) @ np.abs(lo.f64(A))) + 2.0 ** -23 * np.abs(W64)
+        assert (diff <= _ulp_bf16(want) * 1.0001 + 2 * fp32_err).all()
+        assert (diff > 0).mean() < 1e-3
+    else:
+        assert lo.rel_rms(got, W64) <= 1e-6
+    ge = dev(W)
+    rg.lora_merge(ge, dev(A), dev(B), alpha, strength, quality="exact")
+    torch.cuda.synchronize()
+    assert_bitwise(ge, ec.chain_merge(W, A, B, alpha, r, strength, wdt), "merge exact")
+
+
+def test_merge_zero_strength_and_merged_layer():
+    d = lw.small_linear_inputs(300, 256, 520, 32, 95, bias=True, alpha=32.0, strength=0.8, request_scale=1.0)
+    say("case merge: zero strength, merged layer vs dynamic layer")
+    g = dev(d["W"])
+    rg.lora_merge(g, dev(d["A"]), dev(d["B"]), 32.0, 0.0)
+    rg.lora_merge(g, dev(d["A"]), dev(d["B"]), 32.0, -0.0, quality="exact")
+    torch.cuda.synchronize()
+    assert torch.equal(g, dev(d["W"]))
+    # the layer over the merged bf16 weight loses what the merge rounded away; the fused dynamic
+    # layer keeps it (its error is no larger than the merged layer's against fp64)
+    rg.lora_merge(g, dev(d["A"]), dev(d["B"]), 32.0, 0.8)
+    y_merged = rg.lora_linear(dev(d["x"]), g, dev(d["b"]), None, None, 1.0)
+    y_dyn = rg.lora_linear(dev(d["x"]), dev(d["W"]), dev(d["b"]), dev(d["A"]), dev(d["B"]), 32.0, 0.8, 1.0)
+    torch.cuda.synchronize()
+    y64 = lo.lora_linear(d["x"], d["W"], d["b"], d["A"], d["B"], 32.0, 32, 0.8, 1.0)
+    e_m, e_d = lo.rel_rms(host64(y_merged), y64), lo.rel_rms(host64(y_dyn), y64)
+    say(f"  merged-weight layer rel_rms {e_m:.3e}, dynamic {e_d:.3e}")
+    assert e_d <= e_m and e_m <= 4e-3
