@@ -23,7 +23,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["f64", "combined_scale", "lora_linear", "lora_linear_stacked", "lora_linear_multi", "merged_weight",
+__all__ = ["f64", "combined_scale", "lora_linear", "lora_linear_stacked", "lora_linear_multi", "lora_linear_backward", "merged_weight",
            "nf4_unpack_codes", "nf4_dequant", "lora_linear_nf4", "dense_patch", "rel_rms"]
 
 
@@ -113,6 +113,31 @@ def lora_linear_multi(x, W, b, adapters, request_scale) -> np.ndarray:
             upd = upd + f64(a["c"])[None, :]
         y[:, o:o + n] += s * upd
     return y
+
+
+def lora_linear_backward(x, W, A, B, dy, alpha, rank, strength, request_scale):
+    """Gradients of the LoRA linear y = x.W^T + b + s.(x.A^T).B^T for an output gradient dy
+    (the base W frozen), in float64:
+
+        u  = dy.B                       [T, r]
+        dx = dy.W + s.u.A               [T, K]
+        dA = s.u^T.x                    [r, K]
+        dB = s.dy^T.(x.A^T)             [N, r]
+        db = sum over tokens of dy      [N]
+
+    Unsloth fast-LoRA chapter, sections 2 and 4: the backward of a LoRA layer has a closed form
+    (dC/dA and dC/dB as products of X, the incoming gradient and the other factor), computed
+    directly instead of through autograd, with the frozen weight only needed for dX. Written in
+    this library's orientation (delta B @ A, FastVideo lora_patch page). Returns (dx, dA, dB, db).
+    """
+    x, W, A, B, dy = f64(x), f64(W), f64(A), f64(B), f64(dy)
+    s = combined_scale(alpha, rank, strength, request_scale)
+    u = dy @ B
+    dx = dy @ W + s * (u @ A)
+    dA = s * (u.T @ x)
+    dB = s * (dy.T @ (x @ A.T))
+    db = dy.sum(axis=0)
+    return dx, dA, dB, db
 
 
 def merged_weight(W, A, B, s) -> np.ndarray:

@@ -520,3 +520,51 @@ def test_merged_weight_linear_equals_the_adapter_layer():
     s = lo.combined_scale(3.0, 2, 0.5, 1.0)
     y_merged = lo.f64(x) @ lo.merged_weight(W, A, B, s).T + lo.f64(b)[None, :]
     assert np.array_equal(y_merged, lo.lora_linear(x, W, b, A, B, 3.0, 2, 0.5, 1.0))
+
+
+# ------------------------------------------------------------------ backward
+
+def test_backward_matches_central_differences():
+    """The loss L = <G, y> is linear in x, in A (B fixed), in B (A fixed) and in b, so a central
+    difference along any direction equals the directional derivative up to float64 rounding."""
+    rng = np.random.default_rng(31)
+    T, K, N, r = 5, 7, 6, 3
+    x, W, A, B = (rng.standard_normal(sh) for sh in ((T, K), (N, K), (r, K), (N, r)))
+    b, G = rng.standard_normal(N), rng.standard_normal((T, N))
+    alpha, st, rs = 4.5, 0.8, 0.7
+    L = lambda x_, A_, B_, b_: float((G * lo.lora_linear(x_, W, b_, A_, B_, alpha, r, st, rs)).sum())
+    dx, dA, dB, db = lo.lora_linear_backward(x, W, A, B, G, alpha, r, st, rs)
+    h = 1e-3
+    for grad, idx in ((dx, 0), (dA, 1), (dB, 2), (db, 3)):
+        E = rng.standard_normal(grad.shape)
+        args_p = [x, A, B, b]
+        args_m = [x, A, B, b]
+        args_p[idx] = args_p[idx] + h * E
+        args_m[idx] = args_m[idx] - h * E
+        fd = (L(*args_p) - L(*args_m)) / (2 * h)
+        assert abs(fd - float((grad * E).sum())) <= 1e-9 * max(1.0, abs(fd)), idx
+
+
+def test_backward_brute_force_fraction():
+    """Element by element against exact rationals (small integers, dyadic scale)."""
+    rng = np.random.default_rng(32)
+    T, K, N, r = 3, 4, 5, 2
+    x, W, A, B = (rng.integers(-3, 4, size=sh).astype(np.float64) for sh in ((T, K), (N, K), (r, K), (N, r)))
+    G = rng.integers(-3, 4, size=(T, N)).astype(np.float64)
+    alpha, st, rs = 3.0, 0.5, 0.75
+    s = Fraction(alpha) / r * Fraction(st) * Fraction(rs)
+    dx, dA, dB, db = lo.lora_linear_backward(x, W, A, B, G, alpha, r, st, rs)
+    F = lambda v: Fraction(float(v))
+    u = [[sum(F(G[t, n]) * F(B[n, q]) for n in range(N)) for q in range(r)] for t in range(T)]
+    tt = [[sum(F(x[t, k]) * F(A[q, k]) for k in range(K)) for q in range(r)] for t in range(T)]
+    for t in range(T):
+        for k in range(K):
+            v = sum(F(G[t, n]) * F(W[n, k]) for n in range(N)) + s * sum(u[t][q] * F(A[q, k]) for q in range(r))
+            assert dx[t, k] == float(v)
+    for q in range(r):
+        for k in range(K):
+            assert dA[q, k] == float(s * sum(u[t][q] * F(x[t, k]) for t in range(T)))
+    for n in range(N):
+        for q in range(r):
+            assert dB[n, q] == float(s * sum(F(G[t, n]) * tt[t][q] for t in range(T)))
+        assert db[n] == float(sum(F(G[t, n]) for t in range(T)))
