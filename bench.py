@@ -510,6 +510,34 @@ def config_sweep(torch, dev, stream, with_oracle=True):
         del dst, diff, h
         torch.cuda.empty_cache()
 
+    # backward of the FFN pair (dx, dA, dB, db), against hipBLASLt's dy.W alone
+    up_h, down_h = lw.ffn_pair_inputs()
+    for spec, h in ((lw.FFN_UP, up_h), (lw.FFN_DOWN, down_h)):
+        x, W, A, B = d2(h["x"]), d2(h["W"]), d2(h["A"]), d2(h["B"])
+        T, K, N, r = spec.T, spec.K, spec.N, spec.rank
+        dy = torch.randn((T, N), device=dev, generator=torch.Generator(device=dev).manual_seed(17)).to(torch.bfloat16)
+        ws = torch.empty(max(1, rg.lora_linear_bwd_workspace_size(T, K, N, r)), dtype=torch.uint8, device=dev)
+        outs = (torch.empty((T, K), dtype=torch.bfloat16, device=dev), torch.empty((r, K), device=dev),
+                torch.empty((N, r), device=dev), torch.empty((N,), device=dev))
+        sp = stream.cuda_stream
+
+        def bwd():
+            rg.lora_linear_bwd(x.data_ptr(), T, K, K, W.data_ptr(), N, A.data_ptr(), B.data_ptr(), r, spec.alpha,
+                               spec.strength, spec.request_scale, dy.data_ptr(), N, outs[0].data_ptr(), K,
+                               outs[1].data_ptr(), outs[2].data_ptr(), outs[3].data_ptr(), ws.data_ptr(), ws.numel(),
+                               sp)
+        ms = _launch_stats(torch, stream, bwd, n=30)
+        tor = _launch_stats(torch, stream, lambda: torch.matmul(dy, W), n=30)["median"]
+        fl = 2.0 * T * (N * K + 2 * N * r + 3 * r * K)
+        byt = 2 * (2 * T * N + 2 * T * K + N * K + r * (N + K)) + 4 * (r * K + N * r + N)
+        e = _gemm_entry(fl, ms, None, tor, byt)
+        e["workload"] = (f"backward (dx, dA, dB, db): T={T} K={K} N={N} r={r}; base = hipBLASLt dy.W (dx "
+                         f"without the adapter)")
+        out[f"backward_{spec.name}"] = e
+        del x, W, A, B, dy, ws, outs
+    del up_h, down_h
+    torch.cuda.empty_cache()
+
     # merge W <- W + s.B.A (merge mode): HBM-bound rewrite of the weight; and how much of the update
     # a bf16 merge keeps -- the data behind keeping an adapter dynamic
     for spec in (lw.MERGE_WEIGHT, lw.MERGE_WEIGHT_SMALL):

@@ -289,6 +289,32 @@ int lora_merge_apply(void* W, int32_t w_dtype, int64_t N, int64_t K, const void*
                      int32_t adapter_dtype, double alpha, double strength, int32_t quality, void* stream);
 
 /*
+ * lora_linear_bwd -- gradients of the lossless bf16 LoRA linear for an output
+ * gradient dy, the base weight frozen (Unsloth fast-LoRA chapter, sections 2
+ * and 4: closed-form dX, dA, dB computed directly, the frozen weight needed
+ * only for dX):
+ *
+ *     u = dy.B,  dx = dy.W + s.u.A,  dA = s.u^T.x,  dB = s.dy^T.(x.A^T),  db = sum over tokens of dy
+ *
+ * with s = (alpha / rank) . strength . request_scale.
+ *   x [T, K] (ldx), W [N, K], A [rank, K], B [N, rank], dy [T, N] (lddy): bf16, 16-byte aligned,
+ *   K, N, ldx and lddy multiples of 8
+ *   dx [T, K] bf16 (row stride lddx), dA [rank, K], dB [N, rank], db [N] fp32: each optional (NULL = not
+ *   computed); they must not overlap the inputs, the workspace or each other
+ * Rounding: u~ = RN_bf16(s.u) and t~ = RN_bf16(s.x.A^T) as in the forward; dx = RN_bf16(dy.W + u~.A)
+ * with one fp32 accumulator; dA = u~^T.x, dB = dy^T.t~ and db summed in fp32 over token chunks added in
+ * a fixed order. T == 0 writes zero gradients.
+ *   workspace at least lora_linear_bwd_workspace_size(T, K, N, rank, dx != NULL) bytes
+ */
+int lora_linear_bwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, int64_t N, const void* A,
+                    const void* B, int32_t rank, double alpha, double strength, double request_scale, const void* dy,
+                    int64_t lddy, void* dx, int64_t lddx, float* dA, float* dB, float* db, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of lora_linear_bwd (transposed copies, the rank-wide intermediates, partial sums). */
+size_t lora_linear_bwd_workspace_size(int64_t T, int64_t K, int64_t N, int32_t rank, int32_t want_dx);
+
+/*
  * Workspace bytes a call with T tokens, K inputs and N outputs needs for
  * adapters of the given ranks (`ranks` is a HOST array of n_ranks entries: one
  * for lora_linear_fwd and lora_linear_nf4_fwd, one per group for

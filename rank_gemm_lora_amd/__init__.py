@@ -26,7 +26,8 @@ __all__ = [
     "LORA_PATCH_ADD", "LORA_PATCH_REPLACE", "lora_linear_fwd", "lora_linear_stacked_fwd",
     "lora_linear_nf4_fwd", "dense_patch_apply", "lora_linear_fwd_phase", "lora_linear_workspace_size",
     "lora_linear_nf4_workspace_size", "lora_linear_multi_fwd", "lora_linear_multi_workspace_size",
-    "lora_linear_multi", "LoraAdapter", "lora_merge_apply", "lora_merge",
+    "lora_linear_multi", "LoraAdapter", "lora_merge_apply", "lora_merge", "lora_linear_bwd",
+    "lora_linear_bwd_workspace_size", "lora_linear_backward",
     "lora_status_string",
     "lora_device_check", "lora_linear", "lora_linear_stacked", "lora_linear_nf4", "dense_patch",
     "LoraGroup", "hip_runtimes_mapped",
@@ -82,6 +83,11 @@ _lib.lora_linear_multi_fwd.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, ctype
 _lib.lora_linear_multi_fwd.restype = ctypes.c_int
 _lib.lora_linear_multi_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(LoraAdapter), _i32, _i32, _i32]
 _lib.lora_linear_multi_workspace_size.restype = _sz
+_lib.lora_linear_bwd.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i32, _f64, _f64, _f64, _p, _i64, _p, _i64,
+                                 _p, _p, _p, _p, _sz, _p]
+_lib.lora_linear_bwd.restype = ctypes.c_int
+_lib.lora_linear_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i32, _i32]
+_lib.lora_linear_bwd_workspace_size.restype = _sz
 _lib.lora_merge_apply.argtypes = [_p, _i32, _i64, _i64, _p, _p, _i32, _i32, _f64, _f64, _i32, _p]
 _lib.lora_merge_apply.restype = ctypes.c_int
 _lib.lora_linear_nf4_workspace_size.argtypes = [_i64, _i64, _i64, _i32, _i32, _i32]
@@ -134,6 +140,16 @@ def lora_linear_multi_fwd(x, T, K, ldx, W, N, bias, adapters, n_adapters, adapte
     return _check(_lib.lora_linear_multi_fwd(x, T, K, ldx, W, N, bias, arr, n_adapters, adapter_dtype, request_scale,
                                              y, ldy, act_dtype, quality, workspace, workspace_bytes, stream),
                   "lora_linear_multi_fwd")
+
+
+def lora_linear_bwd(x, T, K, ldx, W, N, A, B, rank, alpha, strength, request_scale, dy, lddy, dx, lddx, dA, dB, db,
+                    workspace, workspace_bytes, stream):
+    return _check(_lib.lora_linear_bwd(x, T, K, ldx, W, N, A, B, rank, alpha, strength, request_scale, dy, lddy, dx,
+                                       lddx, dA, dB, db, workspace, workspace_bytes, stream), "lora_linear_bwd")
+
+
+def lora_linear_bwd_workspace_size(T, K, N, rank, want_dx=True) -> int:
+    return int(_lib.lora_linear_bwd_workspace_size(T, K, N, rank, 1 if want_dx else 0))
 
 
 def lora_merge_apply(W, w_dtype, N, K, A, B, rank, adapter_dtype, alpha, strength, quality, stream):
@@ -307,6 +323,27 @@ def lora_merge(W, A, B, alpha, strength=1.0, quality="lossless", stream=None):
     lora_merge_apply(W.data_ptr(), _dt(W), N, K, A.data_ptr(), B.data_ptr(), A.shape[0], _dt(A), float(alpha),
                      float(strength), _QUALITY[quality], _stream(stream))
     return W
+
+
+def lora_linear_backward(x, W, A, B, dy, alpha, strength=1.0, request_scale=1.0, want=("dx", "dA", "dB", "db"),
+                         workspace=None, stream=None):
+    """Gradients of the LoRA linear for the output gradient ``dy``: returns (dx, dA, dB, db),
+    each None unless named in ``want`` (dx bf16; dA, dB, db fp32)."""
+    T, K = x.shape
+    N = W.shape[0]
+    r = A.shape[0]
+    ldx, lddy = _row_major(x, "x"), _row_major(dy, "dy")
+    dev = x.device
+    dx = torch.empty((T, K), dtype=torch.bfloat16, device=dev) if "dx" in want else None
+    dA = torch.empty((r, K), dtype=torch.float32, device=dev) if "dA" in want else None
+    dB = torch.empty((N, r), dtype=torch.float32, device=dev) if "dB" in want else None
+    db = torch.empty((N,), dtype=torch.float32, device=dev) if "db" in want else None
+    need = lora_linear_bwd_workspace_size(T, K, N, r, dx is not None)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    lora_linear_bwd(x.data_ptr(), T, K, ldx, W.data_ptr(), N, A.data_ptr(), B.data_ptr(), r, float(alpha),
+                    float(strength), float(request_scale), dy.data_ptr(), lddy, _ptr(dx), K, _ptr(dA), _ptr(dB),
+                    _ptr(db), ws.data_ptr(), ws.numel(), _stream(stream))
+    return dx, dA, dB, db
 
 
 def dense_patch(dst, src, strength, mode="add", stream=None):

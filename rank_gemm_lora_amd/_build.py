@@ -29,6 +29,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
 SOURCES = {
     "gemm.hip": [],
     "merge.hip": [],
+    "backward.hip": [],
     "exact.hip": ["-ffp-contract=off"],
     "patch.hip": ["-ffp-contract=off"],
     "api.cpp": [],

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstring>
 
+#include "backward.hpp"
 #include "lora_mi355x.h"
 #include "launch.hpp"
 
@@ -367,6 +368,39 @@ int dense_patch_apply(void* dst, int32_t dst_dtype, const int64_t* dst_shape, in
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+// Workspace of lora_linear_bwd: W^T (when dx is wanted), B^T, A^T, u~ (+ its producer's partial
+// sums), t~ (+ partial sums), the token contractions' partial sums; each region 256-byte aligned.
+struct BwdLayout {
+  size_t wt = 0, bt = 0, at = 0, ut = 0, upart = 0, tt = 0, tpart = 0, qt = 0, tn = 0, total = 0;
+  bool has_upart = false, has_tpart = false;
+};
+
+BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int64_t rp, bool want_dx) {
+  BwdLayout L;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off = round_up(off + n);
+    return o;
+  };
+  if (want_dx) L.wt = take(static_cast<size_t>(K) * N * 2);
+  L.bt = take(static_cast<size_t>(rp) * N * 2);
+  L.at = take(static_cast<size_t>(K) * rp * 2);
+  L.ut = take(static_cast<size_t>(T) * rp * 2);
+  const size_t up = lora::producer_partial_bytes(T, N, rp), tp = lora::producer_partial_bytes(T, K, rp);
+  L.has_upart = up > 0;
+  L.has_tpart = tp > 0;
+  if (up > 0) L.upart = take(up);
+  L.tt = take(static_cast<size_t>(T) * rp * 2);
+  if (tp > 0) L.tpart = take(tp);
+  L.qt = take(static_cast<size_t>(rp) * lora::tn_tpad(T) * 2);  // u~ or t~ transposed, one at a time
+  const int js = static_cast<int>((rp + 127) / 128);
+  L.tn = take(std::max(lora::tn_partial_bytes(T, K, static_cast<int>(rp), js),
+                       lora::tn_partial_bytes(T, N, static_cast<int>(rp) + 16, js)));
+  L.total = off;
+  return L;
+}
+
 int lora_merge_apply(void* W, int32_t w_dtype, int64_t N, int64_t K, const void* A, const void* B, int32_t rank,
                      int32_t adapter_dtype, double alpha, double strength, int32_t quality, void* stream) {
   if (!dtype_ok(w_dtype) || !dtype_ok(adapter_dtype)) return LORA_ERR_DTYPE;
@@ -396,6 +430,114 @@ int lora_merge_apply(void* W, int32_t w_dtype, int64_t N, int64_t K, const void*
                            : lora::launch_merge(W, to_elt(w_dtype), N, K, A, B, rank, to_elt(adapter_dtype),
                                                 static_cast<float>(s), st);
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+int lora_linear_bwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, int64_t N, const void* A,
+                    const void* B, int32_t rank, double alpha, double strength, double request_scale, const void* dy,
+                    int64_t lddy, void* dx, int64_t lddx, float* dA, float* dB, float* db, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (T < 0 || K < 1 || N < 1 || ldx < K || lddy < N || (dx != nullptr && lddx < K)) return LORA_ERR_SHAPE;
+  if (rank < 1) return LORA_ERR_SHAPE;
+  if (rank > LORA_MAX_RANK || K * 4 > kMaxRowBytes || N * 4 > kMaxRowBytes || ldx * 2 > kMaxRowBytes ||
+      lddy * 2 > kMaxRowBytes || lddx * 2 > kMaxRowBytes)
+    return LORA_ERR_UNSUPPORTED;
+  if (!finite_scale(alpha) || !finite_scale(strength) || !finite_scale(request_scale)) return LORA_ERR_NONFINITE;
+  const double sd = (alpha / static_cast<double>(rank)) * strength * request_scale;
+  if (std::fabs(sd) > FLT_MAX) return LORA_ERR_NONFINITE;
+  if (A == nullptr || B == nullptr || (dx != nullptr && W == nullptr)) return LORA_ERR_NULL_PTR;
+  if (T > 0 && (x == nullptr || dy == nullptr)) return LORA_ERR_NULL_PTR;
+  if (!aligned(x, 16) || !aligned(W, 16) || !aligned(A, 16) || !aligned(B, 16) || !aligned(dy, 16) ||
+      !aligned(dx, 2) || !aligned(dA, 4) || !aligned(dB, 4) || !aligned(db, 4) || !aligned(workspace, 16))
+    return LORA_ERR_ALIGN;
+  if (K % 8 != 0 || N % 8 != 0 || ldx % 8 != 0 || lddy % 8 != 0) return LORA_ERR_ALIGN;
+  const int64_t rp = lora::rank_pad(rank);
+  const BwdLayout L = T > 0 ? bwd_layout(T, K, N, rp, dx != nullptr) : BwdLayout{};
+  const size_t need = L.total;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LORA_ERR_WORKSPACE;
+  // outputs must not overlap the inputs, the workspace or each other
+  const Span outs[4] = {span2d(dx, T, lddx, K, 2), span2d(dA, 1, rank * K, rank * K, 4),
+                        span2d(dB, 1, N * rank, N * rank, 4), span2d(db, 1, N, N, 4)};
+  const Span ins[6] = {span2d(x, T, ldx, K, 2), span2d(W, N, K, K, 2), span2d(A, rank, K, K, 2),
+                       span2d(B, N, rank, rank, 2), span2d(dy, T, lddy, N, 2),
+                       need ? Span{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need}
+                            : Span{}};
+  for (int i = 0; i < 4; ++i) {
+    for (const Span& in : ins)
+      if (overlaps(outs[i], in)) return LORA_ERR_OVERLAP;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], outs[j])) return LORA_ERR_OVERLAP;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (T == 0) {  // an empty batch: zero gradients
+    hipError_t e = hipSuccess;
+    if (dA != nullptr) e = hipMemsetAsync(dA, 0, static_cast<size_t>(rank) * K * 4, st);
+    if (e == hipSuccess && dB != nullptr) e = hipMemsetAsync(dB, 0, static_cast<size_t>(N) * rank * 4, st);
+    if (e == hipSuccess && db != nullptr) e = hipMemsetAsync(db, 0, static_cast<size_t>(N) * 4, st);
+    return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  }
+  char* ws = static_cast<char*>(workspace);
+  auto* wt = reinterpret_cast<uint16_t*>(ws + L.wt);
+  auto* bt = reinterpret_cast<uint16_t*>(ws + L.bt);
+  auto* at = reinterpret_cast<uint16_t*>(ws + L.at);
+  const float s32 = static_cast<float>(sd);
+  hipError_t e = hipSuccess;
+  // transposed copies: B^T [rp, N] (rows past the rank zero), A^T [K, rp] (columns past the rank zero), W^T [K, N]
+  e = lora::transpose_pad(static_cast<const uint16_t*>(B), rank, N, rank, bt, N, rp, st);
+  if (e == hipSuccess) e = lora::transpose_pad(static_cast<const uint16_t*>(A), K, rank, K, at, rp, K, st);
+  if (e == hipSuccess && dx != nullptr)
+    e = lora::transpose_pad(static_cast<const uint16_t*>(W), K, N, K, wt, N, K, st);
+  if (e != hipSuccess) return LORA_ERR_HIP;
+  // u~ = RN(s . dy.B) and, when wanted, dx = RN(dy.W + u~.A): the forward path over (dy, W^T, B^T, A^T)
+  LinearProblem q;
+  std::memset(&q, 0, sizeof(q));
+  q.x = dy; q.ldx = lddy; q.W = wt; q.y = dx; q.ldy = lddx; q.T = T; q.K = N; q.N = K;
+  q.act = Elt::BF16; q.adapter = Elt::BF16; q.n_groups = 1;
+  GroupDev& gq = q.g[0];
+  gq.A = bt; gq.B = at; gq.col_off = 0; gq.n_cols = K; gq.rank = static_cast<int32_t>(rp);
+  gq.r_pad = static_cast<int32_t>(rp); gq.t_col = 0; gq.scale = s32;
+  q.work = ws + L.ut; q.ldt = rp;
+  if (L.has_upart) q.tpart = reinterpret_cast<float*>(ws + L.upart);
+  e = lora::launch_lossless(q, st, dx != nullptr ? 0 : 1);
+  if (e != hipSuccess) return LORA_ERR_HIP;
+  if (dA == nullptr && dB == nullptr && db == nullptr) return LORA_OK;
+  // t~ = RN(s . x.A^T): the forward's producer
+  LinearProblem p2;
+  std::memset(&p2, 0, sizeof(p2));
+  p2.x = x; p2.ldx = ldx; p2.W = W; p2.T = T; p2.K = K; p2.N = N; p2.act = Elt::BF16; p2.adapter = Elt::BF16;
+  p2.n_groups = 1;
+  GroupDev& g2 = p2.g[0];
+  g2.A = A; g2.B = B; g2.col_off = 0; g2.n_cols = N; g2.rank = rank; g2.r_pad = static_cast<int32_t>(rp);
+  g2.t_col = 0; g2.scale = s32;
+  p2.work = ws + L.tt; p2.ldt = rp;
+  if (L.has_tpart) p2.tpart = reinterpret_cast<float*>(ws + L.tpart);
+  if (dB != nullptr || db != nullptr) {
+    e = lora::launch_lossless(p2, st, 1);
+    if (e != hipSuccess) return LORA_ERR_HIP;
+  }
+  float* part = reinterpret_cast<float*>(ws + L.tn);
+  auto* qt = reinterpret_cast<uint16_t*>(ws + L.qt);
+  const int64_t tpad = lora::tn_tpad(T);
+  const int J = static_cast<int>(rp);
+  if (dA != nullptr) {  // dA = u~^T x: [K, rp] contraction written transposed into [rank, K]
+    e = lora::transpose_pad(reinterpret_cast<const uint16_t*>(ws + L.ut), rp, T, rp, qt, tpad, rp, st);
+    if (e == hipSuccess)
+      e = lora::tn_contract(static_cast<const uint16_t*>(x), ldx, K, qt, tpad, J, T, false, part, dA, K, rank, true,
+                            nullptr, st);
+    if (e != hipSuccess) return LORA_ERR_HIP;
+  }
+  if (dB != nullptr || db != nullptr) {  // dB = dy^T t~ and db = column sums of dy
+    e = lora::transpose_pad(reinterpret_cast<const uint16_t*>(ws + L.tt), rp, T, rp, qt, tpad, rp, st);
+    if (e == hipSuccess)
+      e = lora::tn_contract(static_cast<const uint16_t*>(dy), lddy, N, qt, tpad, J, T, db != nullptr, part, dB, rank,
+                            dB != nullptr ? rank : 0, false, db, st);
+    if (e != hipSuccess) return LORA_ERR_HIP;
+  }
+  return LORA_OK;
+}
+
+size_t lora_linear_bwd_workspace_size(int64_t T, int64_t K, int64_t N, int32_t rank, int32_t want_dx) {
+  if (T <= 0 || K <= 0 || N <= 0 || rank < 1) return 0;
+  return bwd_layout(T, K, N, lora::rank_pad(rank), want_dx != 0).total;
 }
 
 size_t lora_linear_workspace_size(int64_t T, int64_t K, int64_t N, const int32_t* ranks, int32_t n_ranks,

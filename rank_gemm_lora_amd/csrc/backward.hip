@@ -1,0 +1,212 @@
+// Backward of the LoRA linear, lossless tier, bf16 (Unsloth fast-LoRA chapter,
+// sections 2 and 4: the gradients have a closed form, computed directly, the
+// frozen base weight needed only for dX):
+//
+//   u~ = RN_bf16(s . dy.B)                   rank-wide producer over dy and B^T
+//   dx = RN_bf16(dy.W + u~.A)                the fused forward GEMM over W^T and A^T
+//   t~ = RN_bf16(s . x.A^T)                  the forward's rank-wide producer
+//   dA = u~^T . x,  dB = dy^T . t~,  db = sum_t dy      token contractions (fp32)
+//
+// The first two reuse the forward kernels unchanged: with W^T [K, N], B^T
+// [r_pad, N] and A^T [K, r_pad] (transposed copies in the workspace, ranks
+// zero-padded to a multiple of 64) dx is the forward layer of the input dy.
+// The token contractions (both operands token-major) run on
+// v_mfma_f32_16x16x32_bf16 after each 32-token slice of both operands is staged
+// transposed in LDS; token chunks write fp32 partial sums that a second kernel
+// adds in chunk order. db is the contraction with a column of ones.
+#include "backward.hpp"
+
+#include "common.hpp"
+
+namespace lora {
+namespace {
+
+// ---------------------------------------------------------------------------
+// dst[c][r] = src[r][c] for r < R, c < C, zero elsewhere in dst [Cpad, Rpad] (row stride Rpad).
+// 64 x 64 tiles through LDS: coalesced reads of src rows and writes of dst rows.
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const bf16_bits* __restrict__ src, int64_t lds_,
+                                                            int64_t R, int64_t C, bf16_bits* __restrict__ dst,
+                                                            int64_t Rpad, int64_t Cpad) {
+  __shared__ bf16_bits tile[64][66];
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64, c0 = static_cast<int64_t>(blockIdx.y) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i, c = c0 + tx;
+    tile[i][tx] = (r < R && c < C) ? src[r * lds_ + c] : static_cast<bf16_bits>(0);
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t c = c0 + i, r = r0 + tx;
+    if (c < Cpad && r < Rpad) dst[c * Rpad + r] = tile[tx][i];
+  }
+}
+
+hipError_t transpose_pad_impl(const bf16_bits* src, int64_t ld, int64_t R, int64_t C, bf16_bits* dst, int64_t Rpad,
+                              int64_t Cpad, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((Rpad + 63) / 64), static_cast<unsigned>((Cpad + 63) / 64));
+  hipLaunchKernelGGL(transpose_pad_kernel, grid, dim3(256), 0, s, src, ld, R, C, dst, Rpad, Cpad);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Token contraction: part[z][i][j] = sum over tokens t of chunk z of P[t][i] . Q[t][j],
+// P [T, M] (row stride ldp) token-major, Q given transposed as Qt [J, Tpad] (token-contiguous
+// rows, zero past T), bf16; i < M, j in the grid's 128-column slice of J; with ONES, one more
+// 16-column block whose column 0 is 1 (the column sums of P, written at column J).
+// Workgroup: 64 values of i (4 waves of 16) x up to 128 (+16) values of j, tokens in 32-token
+// slices: the P slice is staged transposed in LDS (two buffers), the Q fragments (8
+// consecutive tokens of one j per lane) come straight from Qt.
+constexpr int kTnI = 64, kTnJ = 128, kTnT = 32;
+
+// P^T slice in LDS: row = i, 32 tokens = 64 bytes = 4 chunks of 16 bytes, the chunk index
+// XOR-swizzled by (row / 4) so that 16 rows x 4 chunks spread over the banks.
+__device__ __forceinline__ int tsw(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
+
+template <bool ONES>
+__global__ __launch_bounds__(256) void tn_kernel(const bf16_bits* __restrict__ P, int64_t ldp, int64_t M,
+                                                 const bf16_bits* __restrict__ Qt, int64_t tpad, int J, int64_t T,
+                                                 int64_t tchunk, float* __restrict__ part, int Jt) {
+  __shared__ __attribute__((aligned(256))) char buf[2][kTnI * kTnT * 2];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, q = lane >> 4;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kTnI;
+  const int z = blockIdx.y;
+  const int j0 = blockIdx.z * kTnJ;
+  const int jn = min(kTnJ, J - j0);         // columns of Q in this slice (a multiple of 16)
+  const int nj = jn / 16;
+  const bool ones = ONES && blockIdx.z == 0;  // the column-of-ones block rides with the first slice
+  const int64_t t_lo = z * tchunk, t_hi = min<int64_t>(T, t_lo + tchunk);
+  const int nsteps = static_cast<int>((t_hi - t_lo + kTnT - 1) / kTnT);
+
+  // this thread's copy of a P slice: one 16-byte piece (32 tokens x 64 i = 256 pieces)
+  const int pt = threadIdx.x >> 3, pi = (threadIdx.x & 7) * 8;
+  u32x4 pv;
+  auto load = [&](int step) {
+    const int64_t t = t_lo + step * kTnT + pt;
+    pv = u32x4{0u, 0u, 0u, 0u};
+    if (t < t_hi && i0 + pi < M) pv = *reinterpret_cast<const u32x4*>(P + t * ldp + i0 + pi);  // M % 8 == 0
+  };
+  auto stage = [&](int b) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      *reinterpret_cast<bf16_bits*>(buf[b] + tsw(pi + e, pt >> 3) * 16 + (pt & 7) * 2) =
+          static_cast<bf16_bits>(pv[e >> 1] >> (16 * (e & 1)));
+  };
+  // Q fragments of a slice: Qt rows j0 + 16 jb + r, tokens 8 q .. 8 q + 7 of the slice (zeros past
+  // T in Qt; a chunk's last slice never passes the next chunk's first token: chunks are whole slices)
+  const bf16_bits* qrow = Qt + static_cast<int64_t>(j0 + r) * tpad + 8 * q;
+
+  f32x4 acc[kTnJ / 16 + 1];
+#pragma unroll
+  for (int jb = 0; jb <= kTnJ / 16; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the ones operand: row 0 of the block is 1 for every token, the other rows 0
+  const bf16_bits one = 0x3f80;
+  const uint32_t ow = r == 0 ? (static_cast<uint32_t>(one) | (static_cast<uint32_t>(one) << 16)) : 0u;
+  const bf16x8 ones_frag = __builtin_bit_cast(bf16x8, u32x4{ow, ow, ow, ow});
+
+  if (nsteps > 0) {
+    load(0);
+    stage(0);
+  }
+  __syncthreads();
+  for (int step = 0; step < nsteps; ++step) {
+    const int b = step & 1;
+    if (step + 1 < nsteps) load(step + 1);
+    const int64_t ts = t_lo + step * kTnT;
+    bf16x8 qf[kTnJ / 16];
+#pragma unroll
+    for (int jb = 0; jb < kTnJ / 16; ++jb)
+      if (jb < nj) qf[jb] = *reinterpret_cast<const bf16x8*>(qrow + static_cast<int64_t>(jb * 16) * tpad + ts);
+    const bf16x8 af = *reinterpret_cast<const bf16x8*>(buf[b] + tsw(wave * 16 + r, q) * 16);
+#pragma unroll
+    for (int jb = 0; jb < kTnJ / 16; ++jb)
+      if (jb < nj) acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[jb], acc[jb], 0, 0, 0);
+    if (ones) acc[kTnJ / 16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, ones_frag, acc[kTnJ / 16], 0, 0, 0);
+    if (step + 1 < nsteps) stage(b ^ 1);  // (buffer b ^ 1 was last read before the previous barrier)
+    __syncthreads();
+  }
+  // lane (r, q) of block jb holds D[i = 16 wave + 4 q + e][j = 16 jb + r]
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int64_t i = i0 + wave * 16 + 4 * q + e;
+    if (i >= M) continue;
+    float* row = part + (static_cast<int64_t>(z) * M + i) * Jt;
+#pragma unroll
+    for (int jb = 0; jb < kTnJ / 16; ++jb)
+      if (jb < nj) row[j0 + jb * 16 + r] = acc[jb][e];
+    if (ones && r == 0) row[J] = acc[kTnJ / 16][e];
+  }
+}
+
+// out = sum over z (in order) of part[z]: dA^T layout (TRANSPOSE: out[j][i], j < jvalid) or
+// dB layout (out[i][j], j < jvalid) plus, with a column of ones, its sums to col_out[i].
+__global__ __launch_bounds__(256) void tn_reduce_kernel(const float* __restrict__ part, int S, int64_t M, int Jt,
+                                                        int jvalid, bool transpose, float* __restrict__ out,
+                                                        int64_t ldo, int ones_col, float* __restrict__ col_out) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= M * Jt) return;
+  const int64_t i = idx / Jt;
+  const int j = static_cast<int>(idx - i * Jt);
+  const bool is_ones = ones_col >= 0 && j == ones_col;
+  if (!is_ones && j >= jvalid) return;
+  if (is_ones && col_out == nullptr) return;
+  float v = 0.f;
+  for (int z = 0; z < S; ++z) v += part[(static_cast<int64_t>(z) * M + i) * Jt + j];
+  if (is_ones) col_out[i] = v;
+  else if (transpose) out[static_cast<int64_t>(j) * ldo + i] = v;
+  else out[i * ldo + j] = v;
+}
+
+}  // namespace
+
+hipError_t transpose_pad(const uint16_t* src, int64_t ld, int64_t R, int64_t C, uint16_t* dst, int64_t Rpad,
+                         int64_t Cpad, hipStream_t s) {
+  return transpose_pad_impl(src, ld, R, C, dst, Rpad, Cpad, s);
+}
+
+// Token chunks of a contraction over T tokens with `tiles` workgroups per chunk:
+// about 512 workgroups, chunks a multiple of 32 tokens.
+void tn_plan(int64_t T, int64_t tiles, int* S, int64_t* tchunk) {
+  if (T <= 0 || tiles <= 0) {  // nothing to contract
+    *S = 1;
+    *tchunk = kTnT;
+    return;
+  }
+  int64_t s = (512 + tiles - 1) / tiles;
+  const int64_t smax = (T + 255) / 256;  // at least 256 tokens per chunk
+  s = s < 1 ? 1 : (s > smax ? smax : s);
+  s = s > 64 ? 64 : s;
+  int64_t c = (T + s - 1) / s;
+  c = (c + kTnT - 1) / kTnT * kTnT;
+  *tchunk = c;
+  *S = static_cast<int>((T + c - 1) / c);
+}
+
+size_t tn_partial_bytes(int64_t T, int64_t M, int Jt, int jslices) {
+  int S;
+  int64_t c;
+  tn_plan(T, ((M + kTnI - 1) / kTnI) * jslices, &S, &c);
+  return static_cast<size_t>(S) * static_cast<size_t>(M) * static_cast<size_t>(Jt) * 4;
+}
+
+hipError_t tn_contract(const bf16_bits* P, int64_t ldp, int64_t M, const bf16_bits* Qt, int64_t tpad, int J,
+                       int64_t T, bool ones, float* part, float* out, int64_t ldo, int jvalid, bool transpose,
+                       float* col_out, hipStream_t s) {
+  const int jslices = (J + kTnJ - 1) / kTnJ;
+  const int Jt = J + (ones ? 16 : 0);
+  int S;
+  int64_t tchunk;
+  const int64_t itiles = (M + kTnI - 1) / kTnI;
+  tn_plan(T, itiles * jslices, &S, &tchunk);
+  const dim3 grid(static_cast<unsigned>(itiles), static_cast<unsigned>(S), static_cast<unsigned>(jslices));
+  if (ones) hipLaunchKernelGGL(tn_kernel<true>, grid, dim3(256), 0, s, P, ldp, M, Qt, tpad, J, T, tchunk, part, Jt);
+  else hipLaunchKernelGGL(tn_kernel<false>, grid, dim3(256), 0, s, P, ldp, M, Qt, tpad, J, T, tchunk, part, Jt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = M * Jt;
+  hipLaunchKernelGGL(tn_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, part, S, M, Jt,
+                     jvalid, transpose, out, ldo, ones ? J : -1, col_out);
+  return hipGetLastError();
+}
+
+}  // namespace lora

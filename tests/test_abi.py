@@ -295,3 +295,28 @@ def test_product_path_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, flags=re.M), f
                 assert "exact_chain" not in text and "lora_oracle" not in text, f
+
+
+def bwd(**kw):
+    a = dict(x=X, T=0, K=128, ldx=128, W=W, N=96, A=A, B=B, rank=8, alpha=8.0, dy=Y, lddy=96, dx=BIAS, lddx=128,
+             dA=WSP + 0x1000_0000, dB=WSP + 0x2000_0000, db=WSP + 0x3000_0000)
+    a.update(kw)
+    return rg._lib.lora_linear_bwd(a["x"], a["T"], a["K"], a["ldx"], a["W"], a["N"], a["A"], a["B"], a["rank"],
+                                   a["alpha"], 1.0, 1.0, a["dy"], a["lddy"], a["dx"], a["lddx"], a["dA"], a["dB"],
+                                   a["db"], WSP, 1 << 30, None)
+
+
+def test_backward_validation():
+    assert bwd(dA=None, dB=None, db=None, dx=None) == OK     # (T = 0 with nothing to write)
+    assert bwd(rank=0) == SHAPE
+    assert bwd(lddy=90) == SHAPE
+    assert bwd(N=100, lddy=104) == ALIGN                      # N a multiple of 8
+    assert bwd(alpha=math.nan) == NONFIN
+    assert bwd(A=None) == NULL
+    assert bwd(dx=BIAS, W=None) == NULL                       # dx needs the weight
+    assert bwd(dx=None, W=None, dA=None, dB=None, db=None) == OK
+    assert bwd(db=X + 64, T=4) == OVERLAP                     # a gradient inside the input
+    assert bwd(dB=WSP + 0x3000_0000 - 8, T=4) == OVERLAP      # dB runs into db
+    sz = rg.lora_linear_bwd_workspace_size
+    assert sz(32760, 1536, 8960, 64) > sz(32760, 1536, 8960, 64, False) > 0   # W^T only with dx
+    assert sz(0, 1536, 8960, 64) == 0

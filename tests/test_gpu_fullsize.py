@@ -160,3 +160,22 @@ def test_merge_full(spec):
     got, ref = host64(g[idx]), want
     assert (got != ref).mean() < 1e-3
     assert (np.abs(got - ref) <= np.abs(ref) * 2.0 ** -7 + 2.0 ** -20).all()
+
+
+def test_backward_ffn_up_full():
+    """Backward of the 32760-token FFN up layer (r 64) against the fp64 oracle over every token."""
+    up, _ = lw.ffn_pair_inputs()
+    rng = np.random.default_rng(16)
+    T, N = up["x"].shape[0], up["W"].shape[0]
+    dy = lw.to_dtype(rng.standard_normal((T, N)), "bf16")
+    say(f"case full-size backward FFN up T={T} N={N}")
+    g = rg.lora_linear_backward(dev(up["x"]), dev(up["W"]), dev(up["A"]), dev(up["B"]), dev(dy), up["alpha"],
+                                up["strength"], up["request_scale"])
+    torch.cuda.synchronize()
+    o = lo.lora_linear_backward(up["x"], up["W"], up["A"], up["B"], dy, up["alpha"], up["rank"], up["strength"],
+                                up["request_scale"])
+    for name, got, want, gate in (("dx", g[0], o[0], 4e-3), ("dA", g[1], o[1], 4e-3), ("dB", g[2], o[2], 4e-3),
+                                  ("db", g[3], o[3], 1e-5)):
+        e = lo.rel_rms(host64(got), want)
+        say(f"  {name} rel_rms {e:.3e}")
+        assert e <= gate, (name, e)

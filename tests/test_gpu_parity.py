@@ -563,3 +563,44 @@ def test_merge_zero_strength_and_merged_layer():
     e_m, e_d = lo.rel_rms(host64(y_merged), y64), lo.rel_rms(host64(y_dyn), y64)
     say(f"  merged-weight layer rel_rms {e_m:.3e}, dynamic {e_d:.3e}")
     assert e_d <= e_m and e_m <= 4e-3
+
+
+# ------------------------------------------------------------------ backward
+
+@pytest.mark.parametrize("T,K,N,r", [(300, 256, 520, 24), (513, 384, 768, 64), (100, 136, 96, 5), (40, 64, 1000, 128),
+                                     (700, 512, 392, 200)])
+def test_backward(T, K, N, r):
+    d = lw.small_linear_inputs(T, K, N, r, 100 + r, bias=False, alpha=2.0 * r, strength=0.8, request_scale=0.7)
+    rng = np.random.default_rng(200 + r)
+    dy = lw.to_dtype(rng.standard_normal((T, N)), "bf16")
+    say(f"case backward T={T} K={K} N={N} r={r}")
+    dx, dA, dB, db = rg.lora_linear_backward(dev(d["x"]), dev(d["W"]), dev(d["A"]), dev(d["B"]), dev(dy), d["alpha"],
+                                             0.8, 0.7)
+    torch.cuda.synchronize()
+    o = lo.lora_linear_backward(d["x"], d["W"], d["A"], d["B"], dy, d["alpha"], r, 0.8, 0.7)
+    for name, got, want, gate in (("dx", dx, o[0], 4e-3), ("dA", dA, o[1], 4e-3), ("dB", dB, o[2], 4e-3),
+                                  ("db", db, o[3], 1e-5)):
+        e = lo.rel_rms(host64(got), want)
+        say(f"  {name} rel_rms {e:.3e}")
+        assert e <= gate, (name, e)
+    # dx is the forward layer of dy over W^T with the adapter (B^T, A^T), bit for bit
+    Wt, Bt, At = dev(d["W"]).t().contiguous(), dev(d["B"]).t().contiguous(), dev(d["A"]).t().contiguous()
+    y = rg.lora_linear(dev(dy), Wt, None, Bt, At, d["alpha"], 0.8, 0.7)
+    torch.cuda.synchronize()
+    assert torch.equal(y, dx)
+
+
+def test_backward_partial_outputs_and_empty_batch():
+    d = lw.small_linear_inputs(300, 256, 520, 24, 150, bias=False, alpha=48.0)
+    rng = np.random.default_rng(151)
+    dy = dev(lw.to_dtype(rng.standard_normal((300, 520)), "bf16"))
+    say("case backward partial outputs")
+    full = rg.lora_linear_backward(dev(d["x"]), dev(d["W"]), dev(d["A"]), dev(d["B"]), dy, 48.0)
+    only_db = rg.lora_linear_backward(dev(d["x"]), dev(d["W"]), dev(d["A"]), dev(d["B"]), dy, 48.0, want=("db",))
+    only_dA = rg.lora_linear_backward(dev(d["x"]), dev(d["W"]), dev(d["A"]), dev(d["B"]), dy, 48.0, want=("dA",))
+    torch.cuda.synchronize()
+    assert torch.equal(full[3], only_db[3]) and torch.equal(full[1], only_dA[1])
+    assert only_db[0] is None and only_db[1] is None and only_db[2] is None
+    e = rg.lora_linear_backward(dev(d["x"])[:0], dev(d["W"]), dev(d["A"]), dev(d["B"]), dy[:0], 48.0)
+    torch.cuda.synchronize()
+    assert e[0].numel() == 0 and not e[1].any() and not e[2].any() and not e[3].any()
