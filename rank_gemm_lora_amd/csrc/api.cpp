@@ -394,9 +394,8 @@ BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int64_t rp, bool want_dx) 
   L.tt = take(static_cast<size_t>(T) * rp * 2);
   if (tp > 0) L.tpart = take(tp);
   L.qt = take(static_cast<size_t>(rp) * lora::tn_tpad(T) * 2);  // u~ or t~ transposed, one at a time
-  const int js = static_cast<int>((rp + 127) / 128);
-  L.tn = take(std::max(lora::tn_partial_bytes(T, K, static_cast<int>(rp), js),
-                       lora::tn_partial_bytes(T, N, static_cast<int>(rp) + 16, js)));
+  L.tn = take(std::max(lora::tn_partial_bytes(T, K, static_cast<int>(rp), false),
+                       lora::tn_partial_bytes(T, N, static_cast<int>(rp), true)));
   L.total = off;
   return L;
 }

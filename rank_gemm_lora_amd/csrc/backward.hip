@@ -11,7 +11,7 @@
 // [r_pad, N] and A^T [K, r_pad] (transposed copies in the workspace, ranks
 // zero-padded to a multiple of 64) dx is the forward layer of the input dy.
 // The token contractions (both operands token-major) run on
-// v_mfma_f32_16x16x32_bf16 after each 32-token slice of both operands is staged
+// v_mfma_f32_16x16x32_bf16 after each 64-token slice of both operands is staged
 // transposed in LDS; token chunks write fp32 partial sums that a second kernel
 // adds in chunk order. db is the contraction with a column of ones.
 #include "backward.hpp"
@@ -50,23 +50,28 @@ hipError_t transpose_pad_impl(const bf16_bits* src, int64_t ld, int64_t R, int64
 
 // ---------------------------------------------------------------------------
 // Token contraction: part[z][i][j] = sum over tokens t of chunk z of P[t][i] . Q[t][j],
-// P [T, M] (row stride ldp) token-major, Q given transposed as Qt [J, Tpad] (token-contiguous
-// rows, zero past T), bf16; i < M, j in the grid's 128-column slice of J; with ONES, one more
-// 16-column block whose column 0 is 1 (the column sums of P, written at column J).
-// Workgroup: 64 values of i (4 waves of 16) x up to 128 (+16) values of j, tokens in 32-token
-// slices: the P slice is staged transposed in LDS (two buffers), the Q fragments (8
-// consecutive tokens of one j per lane) come straight from Qt.
-constexpr int kTnI = 64, kTnJ = 128, kTnT = 32;
+// P [T, M] (row stride ldp, M % 8 == 0) token-major, Q given transposed as Qt [J, Tpad]
+// (token-contiguous rows, zero past T), bf16; i < M, j in the grid's 64-column slice of J;
+// with ONES, one more 16-column block whose column 0 is 1 (the column sums of P, written at
+// column J).
+// Workgroup: 256 values of i (4 waves of 64) x 64 values of j, tokens in 64-token steps. Each
+// thread loads an 8-token x 8-column block of P (eight 16-byte loads, 512 contiguous bytes per
+// half wave and token), transposes it in registers and writes 8 row pieces of P^T to LDS; the Q
+// slice (64 j x 64 tokens) is staged in LDS once for the 4 waves. Two LDS buffers, the next
+// step's loads in flight during the current step's MFMAs.
+constexpr int kTnI = 256, kTnJ = 64, kTnT = 64;
 
-// P^T slice in LDS: row = i, 32 tokens = 64 bytes = 4 chunks of 16 bytes, the chunk index
-// XOR-swizzled by (row / 4) so that 16 rows x 4 chunks spread over the banks.
-__device__ __forceinline__ int tsw(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 2) & 3)); }
+// A staged slice in LDS: row = i (or j), 64 tokens = 128 bytes = 8 pieces of 16 bytes, the piece
+// index XOR-swizzled by bits 0-2 and 3-5 of the row: 8 lanes that write 8 rows 8 apart, or read 8
+// consecutive rows, touch 8 different bank groups.
+__device__ __forceinline__ int tsw(int row, int piece) { return row * 8 + (piece ^ ((row ^ (row >> 3)) & 7)); }
 
 template <bool ONES>
-__global__ __launch_bounds__(256) void tn_kernel(const bf16_bits* __restrict__ P, int64_t ldp, int64_t M,
-                                                 const bf16_bits* __restrict__ Qt, int64_t tpad, int J, int64_t T,
-                                                 int64_t tchunk, float* __restrict__ part, int Jt) {
-  __shared__ __attribute__((aligned(256))) char buf[2][kTnI * kTnT * 2];
+__global__ __launch_bounds__(256, 2) void tn_kernel(const bf16_bits* __restrict__ P, int64_t ldp, int64_t M,
+                                                    const bf16_bits* __restrict__ Qt, int64_t tpad, int J, int64_t T,
+                                                    int64_t tchunk, float* __restrict__ part, int Jt) {
+  constexpr int kPBytes = kTnI * kTnT * 2, kQBytes = kTnJ * kTnT * 2;
+  __shared__ __attribute__((aligned(256))) char buf[2][kPBytes + kQBytes];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, q = lane >> 4;
   const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kTnI;
@@ -78,28 +83,55 @@ __global__ __launch_bounds__(256) void tn_kernel(const bf16_bits* __restrict__ P
   const int64_t t_lo = z * tchunk, t_hi = min<int64_t>(T, t_lo + tchunk);
   const int nsteps = static_cast<int>((t_hi - t_lo + kTnT - 1) / kTnT);
 
-  // this thread's copy of a P slice: one 16-byte piece (32 tokens x 64 i = 256 pieces)
-  const int pt = threadIdx.x >> 3, pi = (threadIdx.x & 7) * 8;
-  u32x4 pv;
+  // this thread's P block: columns i0 + 8 c .. + 7, tokens 8 g .. 8 g + 7 of the step
+  const int c = threadIdx.x & 31, g = threadIdx.x >> 5;
+  const bool pcol = i0 + 8 * c < M;
+  const bf16_bits* prow = P + i0 + 8 * c;
+  // this thread's two Q pieces: rows j0 + (k >> 3), tokens 8 (k & 7) .. + 7, k = tid, tid + 256
+  u32x4 pv[8], qv[2];
   auto load = [&](int step) {
-    const int64_t t = t_lo + step * kTnT + pt;
-    pv = u32x4{0u, 0u, 0u, 0u};
-    if (t < t_hi && i0 + pi < M) pv = *reinterpret_cast<const u32x4*>(P + t * ldp + i0 + pi);  // M % 8 == 0
+    const int64_t t = t_lo + static_cast<int64_t>(step) * kTnT + 8 * g;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pv[e] = u32x4{0u, 0u, 0u, 0u};
+      if (pcol && t + e < t_hi) pv[e] = *reinterpret_cast<const u32x4*>(prow + (t + e) * ldp);
+    }
+    const int64_t ts = t_lo + static_cast<int64_t>(step) * kTnT;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = threadIdx.x + 256 * h, jr = k >> 3;
+      qv[h] = u32x4{0u, 0u, 0u, 0u};
+      if (jr < jn) qv[h] = *reinterpret_cast<const u32x4*>(Qt + static_cast<int64_t>(j0 + jr) * tpad + ts + 8 * (k & 7));
+    }
   };
   auto stage = [&](int b) {
+    char* pb = buf[b];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<bf16_bits*>(buf[b] + tsw(pi + e, pt >> 3) * 16 + (pt & 7) * 2) =
-          static_cast<bf16_bits>(pv[e >> 1] >> (16 * (e & 1)));
+    for (int ii = 0; ii < 8; ++ii) {  // row 8 c + ii of P^T: tokens 8 g .. 8 g + 7
+      u32x4 o;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t lo = pv[2 * m][ii >> 1], hi = pv[2 * m + 1][ii >> 1];
+        o[m] = (ii & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+      }
+      *reinterpret_cast<u32x4*>(pb + tsw(8 * c + ii, g) * 16) = o;
+    }
+    char* qb = pb + kPBytes;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = threadIdx.x + 256 * h;
+      *reinterpret_cast<u32x4*>(qb + tsw(k >> 3, k & 7) * 16) = qv[h];
+    }
   };
-  // Q fragments of a slice: Qt rows j0 + 16 jb + r, tokens 8 q .. 8 q + 7 of the slice (zeros past
-  // T in Qt; a chunk's last slice never passes the next chunk's first token: chunks are whole slices)
-  const bf16_bits* qrow = Qt + static_cast<int64_t>(j0 + r) * tpad + 8 * q;
 
-  f32x4 acc[kTnJ / 16 + 1];
+  f32x4 acc[4][kTnJ / 16], acc1[4];
 #pragma unroll
-  for (int jb = 0; jb <= kTnJ / 16; ++jb) acc[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // the ones operand: row 0 of the block is 1 for every token, the other rows 0
+  for (int ib = 0; ib < 4; ++ib) {
+    acc1[ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jb = 0; jb < kTnJ / 16; ++jb) acc[ib][jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // the ones operand: column 0 of the block is 1 for every token, the other columns 0
   const bf16_bits one = 0x3f80;
   const uint32_t ow = r == 0 ? (static_cast<uint32_t>(one) | (static_cast<uint32_t>(one) << 16)) : 0u;
   const bf16x8 ones_frag = __builtin_bit_cast(bf16x8, u32x4{ow, ow, ow, ow});
@@ -112,29 +144,41 @@ __global__ __launch_bounds__(256) void tn_kernel(const bf16_bits* __restrict__ P
   for (int step = 0; step < nsteps; ++step) {
     const int b = step & 1;
     if (step + 1 < nsteps) load(step + 1);
-    const int64_t ts = t_lo + step * kTnT;
-    bf16x8 qf[kTnJ / 16];
+    const char* pb = buf[b];
+    const char* qb = pb + kPBytes;
 #pragma unroll
-    for (int jb = 0; jb < kTnJ / 16; ++jb)
-      if (jb < nj) qf[jb] = *reinterpret_cast<const bf16x8*>(qrow + static_cast<int64_t>(jb * 16) * tpad + ts);
-    const bf16x8 af = *reinterpret_cast<const bf16x8*>(buf[b] + tsw(wave * 16 + r, q) * 16);
+    for (int kk = 0; kk < 2; ++kk) {  // 32-token halves of the step
+      bf16x8 af[4], bq[kTnJ / 16];
 #pragma unroll
-    for (int jb = 0; jb < kTnJ / 16; ++jb)
-      if (jb < nj) acc[jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, qf[jb], acc[jb], 0, 0, 0);
-    if (ones) acc[kTnJ / 16] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, ones_frag, acc[kTnJ / 16], 0, 0, 0);
+      for (int ib = 0; ib < 4; ++ib)
+        af[ib] = *reinterpret_cast<const bf16x8*>(pb + tsw(wave * 64 + ib * 16 + r, 4 * kk + q) * 16);
+#pragma unroll
+      for (int jb = 0; jb < kTnJ / 16; ++jb)
+        if (jb < nj) bq[jb] = *reinterpret_cast<const bf16x8*>(qb + tsw(jb * 16 + r, 4 * kk + q) * 16);
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+#pragma unroll
+        for (int jb = 0; jb < kTnJ / 16; ++jb)
+          if (jb < nj) acc[ib][jb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ib], bq[jb], acc[ib][jb], 0, 0, 0);
+        if (ones) acc1[ib] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ib], ones_frag, acc1[ib], 0, 0, 0);
+      }
+    }
     if (step + 1 < nsteps) stage(b ^ 1);  // (buffer b ^ 1 was last read before the previous barrier)
     __syncthreads();
   }
-  // lane (r, q) of block jb holds D[i = 16 wave + 4 q + e][j = 16 jb + r]
+  // lane (r, q) of block (ib, jb) holds D[i = 64 wave + 16 ib + 4 q + e][j = 16 jb + r]
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int64_t i = i0 + wave * 16 + 4 * q + e;
-    if (i >= M) continue;
-    float* row = part + (static_cast<int64_t>(z) * M + i) * Jt;
+  for (int ib = 0; ib < 4; ++ib) {
 #pragma unroll
-    for (int jb = 0; jb < kTnJ / 16; ++jb)
-      if (jb < nj) row[j0 + jb * 16 + r] = acc[jb][e];
-    if (ones && r == 0) row[J] = acc[kTnJ / 16][e];
+    for (int e = 0; e < 4; ++e) {
+      const int64_t i = i0 + wave * 64 + ib * 16 + 4 * q + e;
+      if (i >= M) continue;
+      float* row = part + (static_cast<int64_t>(z) * M + i) * Jt;
+#pragma unroll
+      for (int jb = 0; jb < kTnJ / 16; ++jb)
+        if (jb < nj) row[j0 + jb * 16 + r] = acc[ib][jb][e];
+      if (ones && r == 0) row[J] = acc1[ib][e];
+    }
   }
 }
 
@@ -164,16 +208,17 @@ hipError_t transpose_pad(const uint16_t* src, int64_t ld, int64_t R, int64_t C, 
   return transpose_pad_impl(src, ld, R, C, dst, Rpad, Cpad, s);
 }
 
-// Token chunks of a contraction over T tokens with `tiles` workgroups per chunk:
-// about 512 workgroups, chunks a multiple of 32 tokens.
+// Token chunks of a contraction over T tokens with `tiles` workgroups per chunk: at most 512
+// workgroups (two per compute unit, all resident at once), chunks a multiple of 64 tokens and
+// of at least 256 tokens, at most 64 chunks.
 void tn_plan(int64_t T, int64_t tiles, int* S, int64_t* tchunk) {
   if (T <= 0 || tiles <= 0) {  // nothing to contract
     *S = 1;
     *tchunk = kTnT;
     return;
   }
-  int64_t s = (512 + tiles - 1) / tiles;
-  const int64_t smax = (T + 255) / 256;  // at least 256 tokens per chunk
+  int64_t s = 512 / tiles;
+  const int64_t smax = (T + 255) / 256;
   s = s < 1 ? 1 : (s > smax ? smax : s);
   s = s > 64 ? 64 : s;
   int64_t c = (T + s - 1) / s;
@@ -182,7 +227,9 @@ void tn_plan(int64_t T, int64_t tiles, int* S, int64_t* tchunk) {
   *S = static_cast<int>((T + c - 1) / c);
 }
 
-size_t tn_partial_bytes(int64_t T, int64_t M, int Jt, int jslices) {
+size_t tn_partial_bytes(int64_t T, int64_t M, int J, bool ones) {
+  const int jslices = (J + kTnJ - 1) / kTnJ;
+  const int Jt = J + (ones ? 16 : 0);
   int S;
   int64_t c;
   tn_plan(T, ((M + kTnI - 1) / kTnI) * jslices, &S, &c);

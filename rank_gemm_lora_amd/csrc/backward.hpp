@@ -12,7 +12,7 @@ hipError_t transpose_pad(const uint16_t* src, int64_t ld, int64_t R, int64_t C, 
 // Token chunks of a contraction over T tokens with `tiles` workgroups per chunk.
 void tn_plan(int64_t T, int64_t tiles, int* S, int64_t* tchunk);
 // fp32 partial sums of one contraction: P [T, M] against Q [T, J] (+ a column of ones).
-size_t tn_partial_bytes(int64_t T, int64_t M, int Jt, int jslices);
+size_t tn_partial_bytes(int64_t T, int64_t M, int J, bool ones);
 
 // Token padding of the transposed rank-wide operand Qt [J, tpad] (zeros past T).
 inline int64_t tn_tpad(int64_t T) { return (T + 63) / 64 * 64; }
