@@ -357,6 +357,17 @@ const char* lora_status_string(int status);
 /* LORA_OK when the current HIP device is a gfx950; LORA_ERR_UNSUPPORTED otherwise. */
 int lora_device_check(void);
 
+/*
+ * Output tile of the hot GEMM of the lossless tier, process-wide (for tuning and for
+ * tests that compare the two): 0 (the default) picks it from the layer's shape
+ * (128 x 128 when the 256 x 256 tiles would fill less than three quarters of the
+ * compute units), 1 always 256 x 256, 2 always 128 x 128. Both accumulate every
+ * output in the same order and give bitwise-identical results; only speed differs.
+ * Returns LORA_ERR_UNSUPPORTED for any other value. Not synchronised with calls in
+ * flight on other host threads (a call reads the setting once, at launch).
+ */
+int lora_set_gemm_tile(int32_t policy);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ __all__ = [
     "lora_linear_multi", "LoraAdapter", "lora_merge_apply", "lora_merge", "lora_linear_bwd",
     "lora_linear_bwd_workspace_size", "lora_linear_backward",
     "lora_status_string",
-    "lora_device_check", "lora_linear", "lora_linear_stacked", "lora_linear_nf4", "dense_patch",
+    "lora_device_check", "lora_set_gemm_tile", "lora_linear", "lora_linear_stacked", "lora_linear_nf4", "dense_patch",
     "LoraGroup", "hip_runtimes_mapped",
 ]
 
@@ -96,6 +96,8 @@ _lib.lora_status_string.argtypes = [ctypes.c_int]
 _lib.lora_status_string.restype = ctypes.c_char_p
 _lib.lora_device_check.argtypes = []
 _lib.lora_device_check.restype = ctypes.c_int
+_lib.lora_set_gemm_tile.argtypes = [_i32]
+_lib.lora_set_gemm_tile.restype = ctypes.c_int
 
 
 class LoraError(RuntimeError):
@@ -191,6 +193,11 @@ def lora_status_string(status: int) -> str:
 
 def lora_device_check() -> int:
     return int(_lib.lora_device_check())
+
+
+def lora_set_gemm_tile(policy: int) -> int:
+    """Hot-GEMM output tile: 0 automatic, 1 256 x 256, 2 128 x 128 (bitwise-identical results)."""
+    return _check(int(_lib.lora_set_gemm_tile(int(policy))), "lora_set_gemm_tile")
 
 
 def hip_runtimes_mapped() -> list:

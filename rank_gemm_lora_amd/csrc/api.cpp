@@ -615,6 +615,12 @@ const char* lora_status_string(int status) {
   }
 }
 
+int lora_set_gemm_tile(int32_t policy) {
+  if (policy < 0 || policy > 2) return LORA_ERR_UNSUPPORTED;
+  lora::set_gemm_tile_policy(policy);
+  return LORA_OK;
+}
+
 int lora_device_check(void) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return LORA_ERR_HIP;

@@ -24,6 +24,8 @@
 // global->LDS directly by buffer_load ... lds (no VGPR round trip), double
 // buffered; out-of-range rows and K tails read as zero through the buffer
 // resource's range check.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -817,9 +819,10 @@ __device__ __forceinline__ void dma_one(int it, char* lds, __amdgpu_buffer_rsrc_
 // than the 32 x 32 x 16 one for the same work per cycle (measured on MI355X:
 // about 2.05 against 1.77 GHz with LDS operand reads), which is where the
 // kernel's throughput is decided once the copies are hidden.
-template <int BM_, int BN_, int WM_, int WN_, int RB_, int SLOTS_>
+template <int BM_, int BN_, int WM_, int WN_, int RB_, int SLOTS_, int OCC_ = 1>
 struct QCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, RB = RB_, SLOTS = SLOTS_;
+  static constexpr int OCC = OCC_;                    // workgroups resident per CU (waves per SIMD)
   static constexpr int WAVES_M = BM / WM, WAVES_N = BN / WN, WAVES = WAVES_M * WAVES_N;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int NI = WN / 16, NJ = WM / 16;   // 16 x 16 blocks per wave
@@ -829,7 +832,7 @@ struct QCfg {
   static constexpr int GROUP_M = 4;
   static_assert(BM == BN && RB == 128 && KK == 2, "x and W units share one slot size; two k-steps per stage");
   static_assert((BM * CPR / 64) % WAVES == 0, "uneven load split");
-  static_assert(SLOTS == 5 && SLOTS * SLOT_BYTES <= 160 * 1024, "LDS");
+  static_assert(SLOTS == 5 && OCC * SLOTS * SLOT_BYTES <= 160 * 1024, "LDS");
 };
 
 template <class P>
@@ -982,6 +985,95 @@ __device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[P::NI][P::NJ],
   }
 }
 
+// Epilogue of 64 x 64 wave blocks (the 128 x 128 tile): lane (r, q) of block (i, j) holds
+// outputs i*16 + 4q .. +3 of token j*16 + r. Bias in fp32 (no add without a bias), one
+// rounding, staged in the wave's 8 KB of LDS as token rows of 128 bytes (16-byte chunks
+// XOR-swizzled by row / 2, so that 16 consecutive rows of one chunk column and 8 rows of one
+// row pair spread over the banks), then written as whole 128-byte output row pieces.
+template <class P, int BIAS>
+__device__ __forceinline__ void stage_out16s(const f32x4 (&acc)[P::NI][P::NJ], const LinearProblem& p, int64_t n0,
+                                             int wn0, int lane, char* st) {
+  const int r = lane & 15, q = lane >> 4;
+  const bf16_bits* bias = static_cast<const bf16_bits*>(p.bias);
+#pragma unroll
+  for (int i = 0; i < P::NI; ++i) {
+    const int cl = i * 16 + q * 4;  // first of 4 columns, local to the wave block
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    const int64_t n = n0 + wn0 + cl;
+    if (BIAS == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < p.N) bv[e] = p.bias32[n + e];
+    } else if (BIAS == 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (n + e < p.N) bv[e] = bf16_to_f32(bias[n + e]);
+    }
+#pragma unroll
+    for (int j = 0; j < P::NJ; ++j) {
+      const int row = j * 16 + r;
+      uint2 w;
+      if (BIAS != 0) {
+        w.x = pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]);
+        w.y = pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]);
+      } else {
+        w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+      }
+      const int chunk = (cl >> 3) ^ ((row >> 1) & 7);
+      *reinterpret_cast<uint2*>(st + row * 128 + chunk * 16 + (q & 1) * 8) = w;
+    }
+  }
+}
+
+template <class P>
+__device__ __forceinline__ void epilogue_lds16s(const f32x4 (&acc)[P::NI][P::NJ], const LinearProblem& p,
+                                                int64_t m0, int64_t n0, int wm0, int wn0, int lane, int wave,
+                                                char* smem) {
+  static_assert(P::WM == 64 && P::WN == 64, "staging written for 64 x 64 wave blocks");
+  char* st = smem + wave * (64 * 128);
+  // (only this wave reads its staging, and a wave's LDS operations run in
+  // order, so the reads below see the writes without a wait)
+  if (p.bias32 != nullptr) stage_out16s<P, 2>(acc, p, n0, wn0, lane, st);
+  else if (p.bias != nullptr) stage_out16s<P, 1>(acc, p, n0, wn0, lane, st);
+  else stage_out16s<P, 0>(acc, p, n0, wn0, lane, st);
+  const int c = lane & 7, rr = lane >> 3;
+  const int64_t mb = m0 + wm0;  // first token of the wave block
+  const int64_t n = n0 + wn0 + c * 8;
+  bf16_bits* y = static_cast<bf16_bits*>(p.y);
+  const bool aligned16 = (reinterpret_cast<uintptr_t>(p.y) % 16 == 0) && (p.ldy % 8 == 0);
+  if (aligned16 && n0 + wn0 + 64 <= p.N) {
+    // all 64 columns exist: buffer stores over the block's valid rows; a row past T
+    // has its offset beyond the range and is dropped
+    const int64_t rows = min<int64_t>(64, p.T - mb);
+    if (rows <= 0) return;
+    const uint32_t ldb = static_cast<uint32_t>(p.ldy * 2);
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(y + mb * p.ldy + n0 + wn0, static_cast<uint32_t>(rows) * ldb);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int row = it * 8 + rr;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * 128 + ((c ^ ((row >> 1) & 7)) * 16));
+      __builtin_amdgcn_raw_buffer_store_b128(v, yr, static_cast<uint32_t>(row) * ldb + static_cast<uint32_t>(c) * 16, 0,
+                                             kCachePolicyNT);
+    }
+    return;
+  }
+  for (int it = 0; it < 8; ++it) {
+    const int row = it * 8 + rr;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * 128 + ((c ^ ((row >> 1) & 7)) * 16));
+    const int64_t m = mb + row;
+    if (m < p.T) {
+      bf16_bits* dst = y + m * p.ldy + n;
+      if (aligned16 && n + 7 < p.N) {
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+        for (int e = 0; e < 8; ++e)
+          if (n + e < p.N) dst[e] = static_cast<bf16_bits>(v[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+}
+
 // K-extension plan of one adapter group for one output tile: where its t~
 // columns and B rows are, which tile rows its B rows cover, and how many
 // 64-k stages its padded rank takes.
@@ -1004,20 +1096,25 @@ __device__ __forceinline__ void ext_stage_loads(const ExtPlan& g, int e, const T
   ob.load(wdst, br, e * P::RB, (e + 1) * P::RB > g.rkb, g.rkb);
 }
 
-// Stage t of the 16 x 16 kernel is 128 MFMA bundles (k-step kk = bundle / 64).
-// Copies, one every eighth bundle: the 8 loads of x of stage t + 2 in the
-// first half (its slot was released by the previous stage's barrier), the 8 of
-// W of stage t + 2 in the second (into the slot of x of stage t, released by
-// this stage's barrier at the first bundle of k-step 1). The barrier waits for
-// everything but the x loads of this stage. Fragment reads: k-step 1 of this
-// stage one every fourth bundle of k-step 0, k-step 0 of stage t + 1 one every
-// fourth bundle after the barrier.
+// Stage t of the 16 x 16 kernel is 2 NB MFMA bundles (NB = NI NJ per k-step: 64 for
+// the 256 x 256 tile, 16 for the 128 x 128 tile). Copies, one every LS-th bundle:
+// the NL loads of x of stage t + 2 in the first half (its slot was released by the
+// previous stage's barrier), the NL of W of stage t + 2 in the second (into the slot
+// of x of stage t, released by this stage's barrier at the first bundle of k-step 1).
+// The barrier waits for everything but the x loads of this stage. Fragment reads:
+// k-step 1 of this stage one every RS-th bundle of k-step 0, k-step 0 of stage t + 1
+// one every RS-th bundle after the barrier. Both tiles accumulate every output in the
+// same order (K-extension stages, then the main stages, 32 k per MFMA), so they give
+// bitwise-identical results.
 template <class P>
-__global__ __launch_bounds__(P::THREADS) void gemm_flow16_kernel(LinearProblem p, int mt, int nt) {
-  static_assert(P::NI == 8 && P::NJ == 8 && P::WAVES == 4, "schedule written for 4 waves of 8 x 8 blocks");
+__global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearProblem p, int mt, int nt) {
+  static_assert(P::WAVES == 4, "schedule written for 4 waves");
   __shared__ __attribute__((aligned(1024))) char smem[P::SLOTS * P::SLOT_BYTES];
   constexpr int NL = TileOffsets<P, P::BM>::N;  // copy loads per wave per unit
-  static_assert(NL == 8, "copy schedule assumes 8 loads per unit");
+  constexpr int NB = P::NI * P::NJ;             // MFMA bundles per k-step
+  constexpr int RS = NB / (P::NI + P::NJ);      // bundles per fragment read
+  constexpr int LS = NB / NL;                   // bundles per copy load
+  static_assert(NB % (P::NI + P::NJ) == 0 && NB % NL == 0 && LS % 2 == 0 && RS >= 2, "bundle schedule");
 
   const int G = mt * nt;
   const int L = xcd_remap(blockIdx.x, G);
@@ -1153,7 +1250,7 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow16_kernel(LinearProblem p
   stage_barrier();
   const FragOffsets fo = frag_offsets<P>(wn0, wm0, lane);
   Frags16<P> fr[2];
-  // fragment q of a k-step, in order of first use: a0, b0 .. b7, a1 .. a7
+  // fragment q of a k-step, in order of first use: a0, b0 .. b(NJ-1), a1 .. a(NI-1)
   auto read_frag = [&](Frags16<P>& f, int q, const char* xs, const char* ws, int kk) {
     const uint32_t flip = kk ? 64u : 0u;
     if (q == 0 || q > P::NJ) {
@@ -1164,7 +1261,7 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow16_kernel(LinearProblem p
     }
   };
 #pragma unroll
-  for (int q = 0; q < 16; ++q) read_frag(fr[0], q, slot(0), slot(1), 0);
+  for (int q = 0; q < P::NI + P::NJ; ++q) read_frag(fr[0], q, slot(0), slot(1), 0);
 
   // stage t whose copies all belong to main stage t + 2 - NE, which is neither
   // past the last nor the K-tail stage
@@ -1180,26 +1277,28 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow16_kernel(LinearProblem p
     const int kb2 = (t + 2 - NE) * P::RB;
     char* const xdst = smem + a3 * P::SLOT_BYTES;
     char* const wdst = smem + a * P::SLOT_BYTES;
-    // (two loops of 64 bundles: one loop of 128 is past the compiler's full-unroll limit)
+    // (one loop per k-step: one loop over both is past the compiler's full-unroll limit)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int m = 0; m < 64; ++m) {  // k-step 0
-      acc[m >> 3][m & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0].a[m >> 3], fr[0].b[m & 7], acc[m >> 3][m & 7], 0, 0, 0);
-      if ((m & 3) == 0) read_frag(fr[1], m >> 2, xs, ws, 1);
-      if ((m & 7) == 4) ox.load_one(m >> 3, xdst, xr, kb2);
+    for (int m = 0; m < NB; ++m) {  // k-step 0
+      const int i = m / P::NJ, j = m % P::NJ;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0].a[i], fr[0].b[j], acc[i][j], 0, 0, 0);
+      if (m % RS == 0) read_frag(fr[1], m / RS, xs, ws, 1);
+      if (m % LS == LS / 2) ox.load_one(m / LS, xdst, xr, kb2);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int m = 0; m < 64; ++m) {  // k-step 1
-      acc[m >> 3][m & 7] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[1].a[m >> 3], fr[1].b[m & 7], acc[m >> 3][m & 7], 0, 0, 0);
+    for (int m = 0; m < NB; ++m) {  // k-step 1
+      const int i = m / P::NJ, j = m % P::NJ;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[1].a[i], fr[1].b[j], acc[i][j], 0, 0, 0);
       if (m == 0) {
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));  // x of stage t + 2 may still be in flight
         stage_barrier();  // stage t + 1 landed and visible; every wave is done reading stage t
-      } else if ((m & 3) == 1) {
-        read_frag(fr[0], m >> 2, xs2, ws2, 0);
+      } else if (m % RS == 1) {
+        read_frag(fr[0], m / RS, xs2, ws2, 0);
       }
-      if ((m & 7) == 4) ow.load_one(m >> 3, wdst, wr, kb2);
+      if (m % LS == LS / 2) ow.load_one(m / LS, wdst, wr, kb2);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -1276,7 +1375,8 @@ __global__ __launch_bounds__(P::THREADS) void gemm_flow16_kernel(LinearProblem p
   }
 
   __syncthreads();  // every wave is done reading the ring; LDS becomes the staging area
-  epilogue_lds16<P>(acc, p, m0, n0, wm0, wn0, lane, wave, smem);
+  if constexpr (P::WM == 128) epilogue_lds16<P>(acc, p, m0, n0, wm0, wn0, lane, wave, smem);
+  else epilogue_lds16s<P>(acc, p, m0, n0, wm0, wn0, lane, wave, smem);
 }
 
 template <class P>
@@ -1291,6 +1391,22 @@ hipError_t launch_flow16(const LinearProblem& p, hipStream_t s) {
 // General pipelined kernel (used when more than two adapter groups meet one tile).
 using HotCfg = PCfg<256, 256, 64, 128, 64, 4>;
 using Flow16Cfg = QCfg<256, 256, 128, 128, 128, 5>;
+// 128 x 128 tiles, 4 waves of 64 x 64, two workgroups per CU: for layers whose
+// 256 x 256 tiles would leave compute units idle (few tokens or narrow outputs).
+using Flow16SCfg = QCfg<128, 128, 64, 64, 128, 5, 2>;
+
+// Compute units of the current device (cached per device; 0 when the query fails).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
 
 // Largest number of adapter groups whose columns meet one BN-wide output tile.
 int max_groups_per_tile(const LinearProblem& p, int bn) {
@@ -1310,9 +1426,17 @@ int max_groups_per_tile(const LinearProblem& p, int bn) {
 // The hot kernel's entry point, named here so that its launch stub is always
 // emitted (a kernel template used only through a launcher has lost it before).
 template __global__ void gemm_flow16_kernel<Flow16Cfg>(LinearProblem, int, int);
+template __global__ void gemm_flow16_kernel<Flow16SCfg>(LinearProblem, int, int);
 
 hipError_t launch(const LinearProblem& p, hipStream_t s) {
-  if (max_groups_per_tile(p, Flow16Cfg::BN) <= 2) return launch_flow16<Flow16Cfg>(p, s);
+  if (max_groups_per_tile(p, Flow16Cfg::BN) <= 2) {
+    // the 128 x 128 tile when the 256 x 256 tiles fill less than three quarters of the
+    // compute units (or when asked for); both give the same bits
+    const int64_t tiles = ((p.T + 255) / 256) * ((p.N + 255) / 256);
+    const int policy = gemm_tile_policy();
+    const bool small = policy == 2 || (policy == 0 && 4 * tiles < 3 * static_cast<int64_t>(device_cus()));
+    return small ? launch_flow16<Flow16SCfg>(p, s) : launch_flow16<Flow16Cfg>(p, s);
+  }
   using P = HotCfg;
   const int mt = static_cast<int>((p.T + P::BM - 1) / P::BM);
   const int nt = static_cast<int>((p.N + P::BN - 1) / P::BN);
@@ -1885,6 +2009,13 @@ hipError_t launch_skinny(const LinearProblem& p, hipStream_t s) {
 }
 
 }  // namespace
+
+namespace {
+std::atomic<int> g_tile_policy{0};
+}  // namespace
+
+int gemm_tile_policy() { return g_tile_policy.load(std::memory_order_relaxed); }
+void set_gemm_tile_policy(int policy) { g_tile_policy.store(policy, std::memory_order_relaxed); }
 
 // Split copies of an fp32 adapter (layout in GroupDev): hi(v) = RN_bf16(v) and
 // lo(v) = RN_bf16(v - hi(v)), where v - hi(v) is exact in fp32, so hi + lo

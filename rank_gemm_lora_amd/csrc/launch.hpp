@@ -128,6 +128,11 @@ struct LinearProblem {
 // phase 0 runs both, 1 only the rank-wide producer, 2 only the fused GEMM
 // (which reads the t~ a phase-1 call left in the workspace).
 hipError_t launch_lossless(const LinearProblem& p, hipStream_t s, int phase = 0);
+
+// Output tile of the hot GEMM: 0 chosen from the layer's shape, 1 always 256 x 256,
+// 2 always 128 x 128 (process-wide; both tiles give bitwise-identical results).
+int gemm_tile_policy();
+void set_gemm_tile_policy(int policy);
 // Lossless with legacy lora_B biases: p.bias32 = fp32(b) + s_g . fp32(c_g) summed in group order.
 hipError_t launch_bias32(const LinearProblem& p, hipStream_t s);
 // Exact tier: the ordered-fp64 separate-pass chain.

@@ -287,6 +287,18 @@ def test_status_strings():
     assert "unknown" in rg.lora_status_string(99)
 
 
+def test_gemm_tile_policy_values():
+    """0 (automatic), 1 and 2 are accepted; anything else is rejected and leaves the setting alone."""
+    lib = rg._lib
+    try:
+        for v in (1, 2, 0):
+            assert lib.lora_set_gemm_tile(v) == 0
+        for v in (-1, 3, 1 << 20):
+            assert lib.lora_set_gemm_tile(v) == 8  # LORA_ERR_UNSUPPORTED
+    finally:
+        lib.lora_set_gemm_tile(0)
+
+
 def test_product_path_never_touches_the_oracle():
     pkg = os.path.join(ROOT, "rank_gemm_lora_amd")
     for dirpath, _, files in os.walk(pkg):
