@@ -1690,10 +1690,13 @@ hipError_t launch_down(const LinearProblem& p, hipStream_t s) {
 // Few tokens (skinny_path): row block b of 64 rows, 4 waves of 16; blocks
 // b < nbw are weight rows, the rest the padded A rows of the groups in order
 // (block b - nbw starts at column 64 (b - nbw) of the rank-wide layout). Grid y
-// is the K chunk (a multiple of 128). Fragments go from global memory straight
-// to registers through range-checked buffer loads (rows past the end, tokens
-// past T and k past the chunk read as zeros), one 128-k group ahead of the
-// MFMAs. Within a group lane (r, q) takes the 32 consecutive k at 32 q and
+// is the K chunk (a multiple of 128). Weight fragments go from global memory
+// straight to registers through range-checked buffer loads (rows past the end
+// and k past the chunk read as zeros), one 128-k group ahead of the MFMAs. The
+// tokens' 128-k slice of a group is copied once per workgroup into LDS (two
+// buffers, 16-byte pieces of a token row XOR-swizzled by the token's low 4 bits;
+// tokens past T and k past the chunk read as zeros) and the 4 waves read their
+// fragments from there. Within a group lane (r, q) takes the 32 consecutive k at 32 q and
 // feeds them to v_mfma_f32_16x16x32_bf16 as 4 steps of 8 (step s: k = 32 q +
 // 8 s + 0..7) for row r (the "A" operand) and for token 16 tb + r (the "B"
 // operand) alike, so each step sums 32 distinct k and the 4 steps cover the
@@ -1714,8 +1717,12 @@ struct SkGroup {
   static constexpr int NW = KIND == kRowsBf16 ? 4 : (KIND == kRowsNf4 ? 1 : 8);  // 16-byte pieces of the row
   u32x4 w[NW];
   float am;          // 4-bit: the block's absmax
-  u32x4 x[TB][4];    // token fragments of the 4 steps
+  u32x4 x[TB][4];    // token fragments of the 4 steps (read from LDS just before the MFMAs)
 };
+
+// LDS copy of a group's token slice: 16 tb + r tokens x 256 bytes, piece p of token row t
+// at position p ^ (t & 15).
+constexpr int kSkXBytes = 64 * 256;
 
 struct SkSrc {
   __amdgpu_buffer_rsrc_t w, am, x;  // rows of this wave (from its first row), absmax likewise, all tokens
@@ -1723,7 +1730,7 @@ struct SkSrc {
   int64_t K;
 };
 
-template <int KIND, int TB>
+template <int KIND, int TB, bool XLDS>
 __device__ __forceinline__ void sk_load(SkGroup<KIND, TB>& f, const SkSrc& src, int r, int q, int64_t kg,
                                         int64_t k_hi) {
   const int64_t kl = kg + 32 * q;  // the lane's first k of the group
@@ -1744,14 +1751,41 @@ __device__ __forceinline__ void sk_load(SkGroup<KIND, TB>& f, const SkSrc& src, 
           src.w, ke < k_hi ? row + static_cast<uint32_t>(ke * EB) : kOutOfRange, 0, 0);
     }
   }
+  if constexpr (!XLDS) {  // token fragments straight from global memory (L2)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int64_t ke = kl + 8 * st;
+        const uint32_t off = static_cast<uint32_t>(tb * 16 + r) * src.ldx_b + static_cast<uint32_t>(ke * 2);
+        f.x[tb][st] = __builtin_amdgcn_raw_buffer_load_b128(src.x, ke < k_hi ? off : kOutOfRange, 0, 0);
+      }
+  }
+}
+
+// Copy of the token slice of the group at kg into the LDS buffer xb: TB pieces per thread.
+template <int TB>
+__device__ __forceinline__ void sk_stage_x(char* xb, const SkSrc& src, int64_t kg, int64_t k_hi) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int it = 0; it < TB; ++it) {
+    const int slot0 = it * 256 + wave * 64;  // wave-uniform LDS destination (16-byte slots)
+    const int sl = slot0 + lane;
+    const int row = sl >> 4, gp = (sl & 15) ^ (row & 15);  // token row, piece of the row it holds
+    const int64_t ke = kg + 8 * gp;
+    const uint32_t voff = ke < k_hi ? static_cast<uint32_t>(row) * src.ldx_b + static_cast<uint32_t>(ke * 2) : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.x, (lds_void*)(xb + slot0 * 16), 16, voff, 0, 0, 0);
+  }
+}
+
+// This lane's token fragments of a staged group: token 16 tb + r, pieces 4 q + st.
+template <int KIND, int TB>
+__device__ __forceinline__ void sk_read_x(SkGroup<KIND, TB>& f, const char* xb, int r, int q) {
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int64_t ke = kl + 8 * st;
-      const uint32_t off = static_cast<uint32_t>(tb * 16 + r) * src.ldx_b + static_cast<uint32_t>(ke * 2);
-      f.x[tb][st] = __builtin_amdgcn_raw_buffer_load_b128(src.x, ke < k_hi ? off : kOutOfRange, 0, 0);
-    }
+    for (int st = 0; st < 4; ++st)
+      f.x[tb][st] = *reinterpret_cast<const u32x4*>(xb + ((tb * 16 + r) * 16 + ((4 * q + st) ^ r)) * 16);
 }
 
 template <int KIND, int TB>
@@ -1799,25 +1833,52 @@ __device__ __forceinline__ void sk_mma(f32x4 (&acc)[TB], const SkGroup<KIND, TB>
   }
 }
 
-// The chunk [k_lo, k_hi) of this wave's 16 rows, one group of loads ahead.
-template <int KIND, int TB>
+// The chunk [k_lo, k_hi) of this wave's 16 rows, one group of loads ahead. With XLDS every
+// wave of the workgroup runs the same groups (the token slices are shared through LDS);
+// without it (at most 8 tokens, where the slice is at most 2 KB) each wave loads its token
+// fragments itself and no barrier is needed.
+template <int KIND, int TB, bool XLDS>
 __device__ __forceinline__ void sk_chunk(f32x4 (&acc)[TB], const SkSrc& src, int r, int q, int64_t k_lo,
-                                         int64_t k_hi, const f32x2* pair) {
+                                         int64_t k_hi, const f32x2* pair, char* xs) {
   SkGroup<KIND, TB> cur;
-  sk_load<KIND, TB>(cur, src, r, q, k_lo, k_hi);
-  int64_t kg = k_lo;
-  for (; kg + 128 < k_hi; kg += 128) {
-    SkGroup<KIND, TB> nxt;
-    sk_load<KIND, TB>(nxt, src, r, q, kg + 128, k_hi);
+  if constexpr (!XLDS) {
+    sk_load<KIND, TB, false>(cur, src, r, q, k_lo, k_hi);
+    int64_t kg = k_lo;
+    for (; kg + 128 < k_hi; kg += 128) {
+      SkGroup<KIND, TB> nxt;
+      sk_load<KIND, TB, false>(nxt, src, r, q, kg + 128, k_hi);
+      sk_mma<KIND, TB>(acc, cur, pair);
+      cur = nxt;
+    }
     sk_mma<KIND, TB>(acc, cur, pair);
-    cur = nxt;
+  } else {
+    sk_stage_x<TB>(xs, src, k_lo, k_hi);
+    sk_load<KIND, TB, true>(cur, src, r, q, k_lo, k_hi);
+    __builtin_amdgcn_s_waitcnt(pipe::waitcnt_vm(0));
+    __syncthreads();  // the first token slice is in LDS for every wave
+    int64_t kg = k_lo;
+    int b = 0;
+    for (; kg + 128 < k_hi; kg += 128) {
+      SkGroup<KIND, TB> nxt;
+      // (buffer b ^ 1 was last read before the previous barrier)
+      sk_stage_x<TB>(xs + (b ^ 1) * kSkXBytes, src, kg + 128, k_hi);
+      sk_load<KIND, TB, true>(nxt, src, r, q, kg + 128, k_hi);
+      sk_read_x<KIND, TB>(cur, xs + b * kSkXBytes, r, q);
+      sk_mma<KIND, TB>(acc, cur, pair);
+      __builtin_amdgcn_s_waitcnt(pipe::waitcnt_vm(0));
+      __syncthreads();  // the next slice landed; every wave is done reading this one
+      cur = nxt;
+      b ^= 1;
+    }
+    sk_read_x<KIND, TB>(cur, xs + b * kSkXBytes, r, q);
+    sk_mma<KIND, TB>(acc, cur, pair);
   }
-  sk_mma<KIND, TB>(acc, cur, pair);
 }
 
-template <bool NF4, bool AF32, int TB>
+template <bool NF4, bool AF32, int TB, bool XLDS>
 __global__ __launch_bounds__(256) void skinny_kernel(LinearProblem p, int nbw, int64_t kchunk, int64_t npad) {
   __shared__ f32x2 pair[256];
+  __shared__ __attribute__((aligned(16))) char xs[XLDS ? 2 * kSkXBytes : 16];
   if constexpr (NF4) {
     pair[threadIdx.x] = f32x2{p.codebook[threadIdx.x & 15], p.codebook[threadIdx.x >> 4]};
     __syncthreads();
@@ -1843,11 +1904,11 @@ __global__ __launch_bounds__(256) void skinny_kernel(LinearProblem p, int nbw, i
       src.w_row_b = static_cast<uint32_t>(p.K / 2);
       src.w = make_rsrc(p.codes + n0 * (p.K / 2), static_cast<uint32_t>(rows) * src.w_row_b);
       src.am = make_rsrc(p.absmax + n0 * (p.K / 64), static_cast<uint32_t>(rows * (p.K / 64) * 4));
-      sk_chunk<kRowsNf4, TB>(acc, src, r, q, k_lo, k_hi, pair);
+      sk_chunk<kRowsNf4, TB, XLDS>(acc, src, r, q, k_lo, k_hi, pair, xs);
     } else {
       src.w_row_b = static_cast<uint32_t>(p.K * 2);
       src.w = make_rsrc(static_cast<const bf16_bits*>(p.W) + n0 * p.K, static_cast<uint32_t>(rows) * src.w_row_b);
-      sk_chunk<kRowsBf16, TB>(acc, src, r, q, k_lo, k_hi, pair);
+      sk_chunk<kRowsBf16, TB, XLDS>(acc, src, r, q, k_lo, k_hi, pair, xs);
     }
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
@@ -1867,12 +1928,12 @@ __global__ __launch_bounds__(256) void skinny_kernel(LinearProblem p, int nbw, i
     src.w_row_b = static_cast<uint32_t>(p.K * 4);
     src.w = make_rsrc(static_cast<const float*>(g.A) + static_cast<int64_t>(q0) * p.K,
                       static_cast<uint32_t>(rows) * src.w_row_b);
-    sk_chunk<kRowsF32, TB>(acc, src, r, q, k_lo, k_hi, pair);
+    sk_chunk<kRowsF32, TB, XLDS>(acc, src, r, q, k_lo, k_hi, pair, xs);
   } else {
     src.w_row_b = static_cast<uint32_t>(p.K * 2);
     src.w = make_rsrc(static_cast<const bf16_bits*>(g.A) + static_cast<int64_t>(q0) * p.K,
                       static_cast<uint32_t>(rows) * src.w_row_b);
-    sk_chunk<kRowsBf16, TB>(acc, src, r, q, k_lo, k_hi, pair);
+    sk_chunk<kRowsBf16, TB, XLDS>(acc, src, r, q, k_lo, k_hi, pair, xs);
   }
   float* pt = p.skinny + static_cast<int64_t>(gridDim.y) * p.T * npad;
 #pragma unroll
@@ -1975,11 +2036,16 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(LinearProblem p, int
 template <bool NF4, bool AF32>
 hipError_t launch_skinny_tb(const LinearProblem& p, hipStream_t s, dim3 grid, int nbw, int64_t kchunk,
                             int64_t npad) {
+  // (token slices through LDS from 9 tokens on: below that they are at most 2 KB per group and
+  // the per-group barrier costs about what the shared copy saves; the results are the same)
   switch ((p.T + 15) / 16) {
-    case 1: hipLaunchKernelGGL((skinny_kernel<NF4, AF32, 1>), grid, dim3(256), 0, s, p, nbw, kchunk, npad); break;
-    case 2: hipLaunchKernelGGL((skinny_kernel<NF4, AF32, 2>), grid, dim3(256), 0, s, p, nbw, kchunk, npad); break;
-    case 3: hipLaunchKernelGGL((skinny_kernel<NF4, AF32, 3>), grid, dim3(256), 0, s, p, nbw, kchunk, npad); break;
-    default: hipLaunchKernelGGL((skinny_kernel<NF4, AF32, 4>), grid, dim3(256), 0, s, p, nbw, kchunk, npad); break;
+    case 1:
+      if (p.T <= 8) hipLaunchKernelGGL((skinny_kernel<NF4, AF32, 1, false>), grid, dim3(256), 0, s, p, nbw, kchunk, npad);
+      else hipLaunchKernelGGL((skinny_kernel<NF4, AF32, 1, true>), grid, dim3(256), 0, s, p, nbw, kchunk, npad);
+      break;
+    case 2: hipLaunchKernelGGL((skinny_kernel<NF4, AF32, 2, true>), grid, dim3(256), 0, s, p, nbw, kchunk, npad); break;
+    case 3: hipLaunchKernelGGL((skinny_kernel<NF4, AF32, 3, true>), grid, dim3(256), 0, s, p, nbw, kchunk, npad); break;
+    default: hipLaunchKernelGGL((skinny_kernel<NF4, AF32, 4, true>), grid, dim3(256), 0, s, p, nbw, kchunk, npad); break;
   }
   return hipGetLastError();
 }
