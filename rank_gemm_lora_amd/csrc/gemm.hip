@@ -1943,17 +1943,17 @@ __global__ __launch_bounds__(256) void skinny_kernel(LinearProblem p, int nbw, i
   }
 }
 
-// Second kernel of the skinny path: grid (ceil(N / 256), ceil(T / 4)). The
-// block first forms t~ = RN_adt(s . t) of its 4 tokens in LDS (t = the K
+// Second kernel of the skinny path: grid (ceil(N / 256), ceil(T / TOK)), TOK = 8
+// tokens per block (4 when 8 x ldt fp32 would pass 64 KB of LDS). The
+// block first forms t~ = RN_adt(s . t) of its TOK tokens in LDS (t = the K
 // chunks' partial sums added in chunk order), then each thread takes one output
 // column: acc = the weight partial sums in chunk order, += t~ . B_g^T in fp32
 // (rank index ascending) for the group covering the column, + bias, one
 // rounding. Token rows past T repeat the last token (valid memory) and are
 // never stored; all partial sums of a thread are loaded before they are added.
-constexpr int kFinishTokens = 4;
 constexpr int kMaxChunks = 8;  // skinny_plan never makes more
 
-template <bool AF32>
+template <bool AF32, int kFinishTokens>
 __global__ __launch_bounds__(256) void skinny_finish_kernel(LinearProblem p, int S, int64_t npad) {
   extern __shared__ float tt[];  // [kFinishTokens, ldt]
   const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kFinishTokens;
@@ -2065,12 +2065,17 @@ hipError_t launch_skinny(const LinearProblem& p, hipStream_t s) {
   else e = af32 ? launch_skinny_tb<false, true>(p, s, grid, nbw, kchunk, npad)
                 : launch_skinny_tb<false, false>(p, s, grid, nbw, kchunk, npad);
   if (e != hipSuccess) return e;
-  // t~ of a block's tokens in LDS: 4 x ldt fp32, ldt <= 8 x 1024 (at most 128 KB)
-  const dim3 fgrid(static_cast<unsigned>((p.N + 255) / 256),
-                   static_cast<unsigned>((p.T + kFinishTokens - 1) / kFinishTokens));
-  const size_t shmem = static_cast<size_t>(kFinishTokens) * static_cast<size_t>(p.ldt) * 4;
-  if (af32) hipLaunchKernelGGL(skinny_finish_kernel<true>, fgrid, dim3(256), shmem, s, p, S, npad);
-  else hipLaunchKernelGGL(skinny_finish_kernel<false>, fgrid, dim3(256), shmem, s, p, S, npad);
+  // t~ of a block's tokens in LDS: TOK x ldt fp32, at most 64 KB (ldt <= 4096)
+  const int tok = p.ldt <= 2048 ? 8 : 4;
+  const dim3 fgrid(static_cast<unsigned>((p.N + 255) / 256), static_cast<unsigned>((p.T + tok - 1) / tok));
+  const size_t shmem = static_cast<size_t>(tok) * static_cast<size_t>(p.ldt) * 4;
+  if (tok == 8) {
+    if (af32) hipLaunchKernelGGL((skinny_finish_kernel<true, 8>), fgrid, dim3(256), shmem, s, p, S, npad);
+    else hipLaunchKernelGGL((skinny_finish_kernel<false, 8>), fgrid, dim3(256), shmem, s, p, S, npad);
+  } else {
+    if (af32) hipLaunchKernelGGL((skinny_finish_kernel<true, 4>), fgrid, dim3(256), shmem, s, p, S, npad);
+    else hipLaunchKernelGGL((skinny_finish_kernel<false, 4>), fgrid, dim3(256), shmem, s, p, S, npad);
+  }
   return hipGetLastError();
 }
 
