@@ -876,6 +876,11 @@ __device__ __forceinline__ void mfma_frags16(f32x4 (&acc)[P::NI][P::NJ], const F
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
 }
 
+// A staged 16-byte chunk with its two 8-byte halves back in column order (swapped when sw).
+__device__ __forceinline__ u32x4 unswap_halves(u32x4 v, int sw) {
+  return sw ? u32x4{v[2], v[3], v[0], v[1]} : v;
+}
+
 // Epilogue of the 16 x 16 layout: lane (r, q) of block (i, j) holds outputs
 // i*16 + 4q .. +3 of token j*16 + r. Bias in fp32 (no add without a bias), one
 // rounding, staged in the wave's 32 KB of LDS as token rows (16-byte chunks
@@ -924,8 +929,11 @@ __device__ __forceinline__ void stage_out16(const f32x4 (&acc)[P::NI][P::NJ], co
         w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
         w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
       }
+      // 16-byte chunk XOR-swizzled by row; the two 8-byte halves of a chunk swap places in rows
+      // 8 .. 15 of every 16, so that the 16 lanes of one write (rows r = 0 .. 15, one half each)
+      // cover all 32 banks
       const int chunk = (cl >> 3) ^ (row & 15);
-      *reinterpret_cast<uint2*>(st + row * 256 + chunk * 16 + (q & 1) * 8) = w;
+      *reinterpret_cast<uint2*>(st + row * 256 + chunk * 16 + ((q & 1) ^ ((row >> 3) & 1)) * 8) = w;
     }
     __builtin_amdgcn_sched_barrier(0);  // keeps accumulator reads from being hoisted (register pressure)
   }
@@ -958,7 +966,8 @@ __device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[P::NI][P::NJ],
 #pragma unroll 8
     for (int it = 0; it < 32; ++it) {
       const int row = it * 4 + rr;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * 256 + ((c ^ (row & 15)) * 16));
+      const u32x4 v = unswap_halves(*reinterpret_cast<const u32x4*>(st + row * 256 + ((c ^ (row & 15)) * 16)),
+                                    (row >> 3) & 1);
       // non-temporal (cache-policy bit nt): an output of hundreds of MB does not stay in the
       // Infinity Cache, where its dirty lines would be written back while the next kernel
       // streams its own inputs (measured: the next layer's producer 142 -> 106 us)
@@ -970,7 +979,8 @@ __device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[P::NI][P::NJ],
 #pragma unroll 8
   for (int it = 0; it < 32; ++it) {
     const int row = it * 4 + rr;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * 256 + ((c ^ (row & 15)) * 16));
+    const u32x4 v = unswap_halves(*reinterpret_cast<const u32x4*>(st + row * 256 + ((c ^ (row & 15)) * 16)),
+                                  (row >> 3) & 1);
     const int64_t m = mb + row;
     if (m < p.T) {
       bf16_bits* dst = y + m * p.ldy + n;
@@ -1020,8 +1030,9 @@ __device__ __forceinline__ void stage_out16s(const f32x4 (&acc)[P::NI][P::NJ], c
         w.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
         w.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
       }
+      // (halves swapped in odd rows: the 16 lanes of one write then cover all 32 banks)
       const int chunk = (cl >> 3) ^ ((row >> 1) & 7);
-      *reinterpret_cast<uint2*>(st + row * 128 + chunk * 16 + (q & 1) * 8) = w;
+      *reinterpret_cast<uint2*>(st + row * 128 + chunk * 16 + ((q & 1) ^ (row & 1)) * 8) = w;
     }
   }
 }
@@ -1052,7 +1063,8 @@ __device__ __forceinline__ void epilogue_lds16s(const f32x4 (&acc)[P::NI][P::NJ]
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int row = it * 8 + rr;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * 128 + ((c ^ ((row >> 1) & 7)) * 16));
+      const u32x4 v = unswap_halves(*reinterpret_cast<const u32x4*>(st + row * 128 + ((c ^ ((row >> 1) & 7)) * 16)),
+                                    row & 1);
       __builtin_amdgcn_raw_buffer_store_b128(v, yr, static_cast<uint32_t>(row) * ldb + static_cast<uint32_t>(c) * 16, 0,
                                              kCachePolicyNT);
     }
@@ -1060,7 +1072,8 @@ __device__ __forceinline__ void epilogue_lds16s(const f32x4 (&acc)[P::NI][P::NJ]
   }
   for (int it = 0; it < 8; ++it) {
     const int row = it * 8 + rr;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * 128 + ((c ^ ((row >> 1) & 7)) * 16));
+    const u32x4 v = unswap_halves(*reinterpret_cast<const u32x4*>(st + row * 128 + ((c ^ ((row >> 1) & 7)) * 16)),
+                                  row & 1);
     const int64_t m = mb + row;
     if (m < p.T) {
       bf16_bits* dst = y + m * p.ldy + n;

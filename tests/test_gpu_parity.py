@@ -359,6 +359,25 @@ def test_few_tokens_linear(T, K, N, r, bias):
     assert_bitwise(run_linear(d, "exact"), yc, "few-token exact")
 
 
+@pytest.mark.parametrize("adapter", ["bf16", "f32"])
+def test_few_tokens_rows_do_not_depend_on_the_batch(adapter):
+    """Up to 8 tokens each wave loads its token fragments itself; from 9 on the workgroup shares
+    them through LDS. Every token is computed on its own (K chunks fixed by K alone), so the
+    rows of a 9-, 33- or 64-token call equal the same rows in 1-, 4- and 8-token calls bit for bit."""
+    T, K, N, r = 64, 2056, 520, 24
+    d = lw.small_linear_inputs(T, K, N, r, 91, adapter=adapter, bias=True, alpha=2.0 * r, strength=0.8,
+                               request_scale=0.7)
+    say(f"case few tokens rows vs batch adapter={adapter}")
+    x, W, b, A, B = dev(d["x"]), dev(d["W"]), dev(d["b"]), dev(d["A"]), dev(d["B"])
+    call = lambda xs: rg.lora_linear(xs, W, b, A, B, d["alpha"], 0.8, 0.7)
+    big = {t: call(x[:t]) for t in (9, 33, 64)}
+    small = {t: call(x[:t]) for t in (1, 4, 8)}
+    torch.cuda.synchronize()
+    for tb, yb in big.items():
+        for ts, ys in small.items():
+            assert torch.equal(yb[:ts], ys), (tb, ts)
+
+
 @pytest.mark.parametrize("T,K,N,r", [(40, 256, 520, 24), (3, 512, 300, 64)])
 def test_few_tokens_fp32_adapter(T, K, N, r):
     d = lw.small_linear_inputs(T, K, N, r, 70 + T, adapter="f32", bias=True, alpha=2.0 * r, strength=0.8,
