@@ -1956,9 +1956,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(LinearProblem p, int nbw, i
   }
 }
 
-// Second kernel of the skinny path: grid (ceil(N / 256), ceil(T / TOK)), TOK = 8
-// tokens per block (4 when 8 x ldt fp32 would pass 64 KB of LDS). The
-// block first forms t~ = RN_adt(s . t) of its TOK tokens in LDS (t = the K
+// Second kernel of the skinny path: grid (ceil(N / 256), ceil(T / TOK)), TOK = 4
+// tokens per block. The block first forms t~ = RN_adt(s . t) of its TOK tokens in LDS (t = the K
 // chunks' partial sums added in chunk order), then each thread takes one output
 // column: acc = the weight partial sums in chunk order, += t~ . B_g^T in fp32
 // (rank index ascending) for the group covering the column, + bias, one
@@ -1972,6 +1971,15 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(LinearProblem p, int
   const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kFinishTokens;
   const int ldt = static_cast<int>(p.ldt);
   const float* pt = p.skinny + static_cast<int64_t>(S) * p.T * npad;
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  // this thread's weight partial sums, loaded first: their latency overlaps the t~ phase
+  float v[kFinishTokens][kMaxChunks];
+#pragma unroll
+  for (int i = 0; i < kFinishTokens; ++i) {
+    const int64_t t = min<int64_t>(t0 + i, p.T - 1);
+#pragma unroll
+    for (int s = 0; s < kMaxChunks; ++s) v[i][s] = (s < S && n < p.N) ? p.skinny[(s * p.T + t) * npad + n] : 0.f;
+  }
   for (int c = threadIdx.x; c < kFinishTokens * ldt; c += 256) {
     const int j = c / ldt, col = c - j * ldt;
     const int64_t t = min<int64_t>(t0 + j, p.T - 1);
@@ -1989,24 +1997,14 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(LinearProblem p, int
     tt[c] = AF32 ? sum : bf16_to_f32(f32_to_bf16_rne(sum));
   }
   __syncthreads();
-  const int64_t n = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (n >= p.N) return;
   float acc[kFinishTokens];
-  {
-    float v[kFinishTokens][kMaxChunks];
 #pragma unroll
-    for (int i = 0; i < kFinishTokens; ++i) {
-      const int64_t t = min<int64_t>(t0 + i, p.T - 1);
+  for (int i = 0; i < kFinishTokens; ++i) {
+    acc[i] = 0.f;
 #pragma unroll
-      for (int s = 0; s < kMaxChunks; ++s) v[i][s] = s < S ? p.skinny[(s * p.T + t) * npad + n] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < kFinishTokens; ++i) {
-      acc[i] = 0.f;
-#pragma unroll
-      for (int s = 0; s < kMaxChunks; ++s)
-        if (s < S) acc[i] += v[i][s];
-    }
+    for (int s = 0; s < kMaxChunks; ++s)
+      if (s < S) acc[i] += v[i][s];
   }
   for (int gi = 0; gi < p.n_groups; ++gi) {
     const GroupDev& g = p.g[gi];
@@ -2078,17 +2076,14 @@ hipError_t launch_skinny(const LinearProblem& p, hipStream_t s) {
   else e = af32 ? launch_skinny_tb<false, true>(p, s, grid, nbw, kchunk, npad)
                 : launch_skinny_tb<false, false>(p, s, grid, nbw, kchunk, npad);
   if (e != hipSuccess) return e;
-  // t~ of a block's tokens in LDS: TOK x ldt fp32, at most 64 KB (ldt <= 4096)
-  const int tok = p.ldt <= 2048 ? 8 : 4;
+  // t~ of a block's tokens in LDS: 4 x ldt fp32, at most 64 KB (ldt <= 4096). (8 tokens per
+  // block halves the re-reads of B but measured slower at every token count from 1 to 64:
+  // half the blocks, and below 8 tokens duplicated work.)
+  constexpr int tok = 4;
   const dim3 fgrid(static_cast<unsigned>((p.N + 255) / 256), static_cast<unsigned>((p.T + tok - 1) / tok));
   const size_t shmem = static_cast<size_t>(tok) * static_cast<size_t>(p.ldt) * 4;
-  if (tok == 8) {
-    if (af32) hipLaunchKernelGGL((skinny_finish_kernel<true, 8>), fgrid, dim3(256), shmem, s, p, S, npad);
-    else hipLaunchKernelGGL((skinny_finish_kernel<false, 8>), fgrid, dim3(256), shmem, s, p, S, npad);
-  } else {
-    if (af32) hipLaunchKernelGGL((skinny_finish_kernel<true, 4>), fgrid, dim3(256), shmem, s, p, S, npad);
-    else hipLaunchKernelGGL((skinny_finish_kernel<false, 4>), fgrid, dim3(256), shmem, s, p, S, npad);
-  }
+  if (af32) hipLaunchKernelGGL((skinny_finish_kernel<true, tok>), fgrid, dim3(256), shmem, s, p, S, npad);
+  else hipLaunchKernelGGL((skinny_finish_kernel<false, tok>), fgrid, dim3(256), shmem, s, p, S, npad);
   return hipGetLastError();
 }
 

@@ -44,7 +44,7 @@ struct GroupDev {
 // rank-wide intermediate, adds the rank-r update and the bias, and rounds once.
 constexpr int64_t kSkinnyMaxT = 64;
 constexpr int kSkinnyRows = 64;      // weight rows per workgroup (4 waves of 16)
-constexpr int64_t kSkinnyMaxLdt = 4096;  // sum of the padded ranks (the finishing block holds 4 or 8 x ldt fp32 in LDS, <= 64 KB)
+constexpr int64_t kSkinnyMaxLdt = 4096;  // sum of the padded ranks (the finishing block holds 4 x ldt fp32 in LDS, <= 64 KB)
 inline bool skinny_path(Elt act, bool lossless, int64_t T, int64_t ldt) {
   return lossless && act == Elt::BF16 && T > 0 && T <= kSkinnyMaxT && ldt <= kSkinnyMaxLdt;
 }
