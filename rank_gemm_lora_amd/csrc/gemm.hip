@@ -1408,17 +1408,18 @@ using Flow16Cfg = QCfg<256, 256, 128, 128, 128, 5>;
 // 256 x 256 tiles would leave compute units idle (few tokens or narrow outputs).
 using Flow16SCfg = QCfg<128, 128, 64, 64, 128, 5, 2>;
 
-// Compute units of the current device (cached per device; 0 when the query fails).
+// Compute units of the current device (cached per device, safe to call from several host
+// threads; 0 when the query fails).
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];  // zero-initialized (static storage)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0) {
-    int n = 0;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev] = n;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // Largest number of adapter groups whose columns meet one BN-wide output tile.
