@@ -363,6 +363,9 @@ int lora_device_check(void);
  * (128 x 128 when the 256 x 256 tiles would fill less than three quarters of the
  * compute units), 1 always 256 x 256, 2 always 128 x 128. Both accumulate every
  * output in the same order and give bitwise-identical results; only speed differs.
+ * Calls that do not reach the hot GEMM are not affected: 64 tokens or fewer (the
+ * few-token kernels), more than two stacked adapter groups meeting one 256-column
+ * tile, fp32 activations, and the exact tier.
  * Returns LORA_ERR_UNSUPPORTED for any other value. Not synchronised with calls in
  * flight on other host threads (a call reads the setting once, at launch).
  */
