@@ -114,7 +114,7 @@ def main():
         if phase == 0:
             rg.lora_linear_fwd(*args)
         else:
-            rg.lora_linear_fwd_phase(phase, *args)
+            rg.lora_linear_fwd_phase(phase, 0, *args)
 
     def step():
         for L in layers:

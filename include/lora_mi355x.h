@@ -132,21 +132,30 @@ int lora_linear_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * lora_linear_fwd_phase -- one half of the lossless lora_linear_fwd, for
- * callers that schedule or time the two kernels of the path separately
- * (SGLang PR #43501, Modifications: the scale is applied to the rank-wide
- * intermediate, then the second LoRA product lands on the base output).
+ * lora_linear_fwd_phase -- lora_linear_fwd (lossless tier) with its two launches
+ * selectable and the hot GEMM's output tile fixed by the caller, for callers
+ * that schedule, time or compare the kernels of the path (SGLang PR #43501,
+ * Modifications: the scale is applied to the rank-wide intermediate, then the
+ * second LoRA product lands on the base output).
  *
+ *   phase 0  the whole call, exactly lora_linear_fwd
  *   phase 1  writes the rank-wide intermediate RN_adt(s . x A^T) into the workspace
  *            (nothing when the adapter is inactive: s == 0 or A == B == NULL)
  *   phase 2  runs the fused GEMM y = RN(x W^T + t~ B^T + bias) reading that
  *            intermediate; the workspace must still hold what a phase-1 call with
  *            the same x, A, ranks and scales wrote (the library cannot check this)
+ *   gemm_tile  0 picks the output tile from the layer's shape (128 x 128 when the
+ *            256 x 256 tiles would fill less than three quarters of the compute
+ *            units), 1 always 256 x 256, 2 always 128 x 128. Both tiles accumulate
+ *            every output in the same order and give bitwise-identical results;
+ *            only speed differs. Calls that do not reach the hot GEMM ignore it
+ *            (64 tokens or fewer, fp32 activations, bf16 ranks not a multiple of 8).
  * Phase 1 then phase 2 on one stream gives exactly the output of lora_linear_fwd.
- * Arguments, validation and status codes as lora_linear_fwd; phase not 1 or 2, or
- * quality other than LORA_LOSSLESS, returns LORA_ERR_UNSUPPORTED.
+ * Arguments, validation and status codes as lora_linear_fwd; phase or gemm_tile
+ * outside 0..2, or quality other than LORA_LOSSLESS, returns LORA_ERR_UNSUPPORTED.
+ * Nothing is kept between calls.
  */
-int lora_linear_fwd_phase(int32_t phase, const void* x, int64_t T, int64_t K, int64_t ldx,
+int lora_linear_fwd_phase(int32_t phase, int32_t gemm_tile, const void* x, int64_t T, int64_t K, int64_t ldx,
                           const void* W, int64_t N, const void* bias,
                           const void* A, const void* B, int32_t rank, int32_t adapter_dtype,
                           double alpha, double strength, double request_scale,
@@ -175,8 +184,10 @@ int lora_linear_stacked_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
 /*
  * One adapter of lora_linear_multi_fwd: like lora_group, plus its own strength
  * and the optional legacy lora_B bias of older adapters (piper-offload README,
- * LoRA resource: a <module>.lora_B.bias vector applied with the adapter's
- * strength). Its combined scale is s = (alpha / rank) . strength . request_scale.
+ * LoRA resource: a <module>.lora_B.bias vector that merge mode adds to the
+ * layer's bias with the same adapter strength). Its combined scale is
+ * s = (alpha / rank) . strength . request_scale; its legacy vector takes
+ * u = strength . request_scale (alpha / rank belongs to the factor pair).
  */
 typedef struct lora_adapter {
   const void* A;       /* [rank, K] adapter dtype (device)                        */
@@ -196,20 +207,23 @@ typedef struct lora_adapter {
  * several LoRAs on one target summed independently; InvokeAI article,
  * section 3: a layer's list of (patch, weight) pairs):
  *
- *     y = x.W^T + b + sum_i s_i . ((x.A_i^T).B_i^T + c_i)   on adapter i's columns
+ *     y = x.W^T + b + sum_i [ s_i . (x.A_i^T).B_i^T + u_i . c_i ]   on adapter i's columns
  *
- * where c_i is adapter i's B_bias (0 when NULL). Column ranges may overlap; an
- * adapter with s_i == +-0 (or A = B = NULL) contributes nothing, its bias
- * included. Lossless tier: each t~_i = RN_adt(s_i . x.A_i^T) is a K-extension
- * of the same accumulator; b + sum_i s_i . c_i is formed in fp32 and added in
- * the epilogue before the one rounding. Exact tier: the chain of each adapter
- * in the order given, c_i added to the second rank GEMM's fp32 result before
- * its rounding to the adapter dtype (as the base bias is added to the base
- * GEMM's), then the scale passes, then y = RN_dt(RN_f32(y + d_i)).
+ * where c_i is adapter i's B_bias (0 when NULL), s_i its combined scale and
+ * u_i = strength_i . request_scale. Column ranges may overlap; an adapter with
+ * s_i == +-0 (or A = B = NULL) contributes nothing, its bias included.
+ * Lossless tier: each t~_i = RN_adt(s_i . x.A_i^T) is a K-extension of the same
+ * accumulator; b + sum_i u_i . c_i is formed in fp32 (u_i rounded to fp32 once)
+ * and added in the epilogue before the one rounding. Exact tier: per adapter in
+ * the order given, its delta chain and add (as lora_linear_fwd's), then its
+ * legacy vector as its own payload: e = c_i multiplied by strength_i and then
+ * request_scale (each rounded to fp32, skipped when exactly 1, rounding to the
+ * adapter dtype after each), y = RN_dt(RN_f32(y + e)).
  *   adapters  HOST array of n_adapters (0 <= n_adapters <= LORA_MAX_GROUPS)
  *   workspace at least lora_linear_multi_workspace_size(...) bytes
  * Other arguments as lora_linear_fwd; B_bias must be naturally aligned and must
- * not overlap y.
+ * not overlap y. LORA_ERR_NONFINITE also when |u_i| of an active adapter with a
+ * B_bias exceeds the fp32 range.
  */
 int lora_linear_multi_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
                           const void* W, int64_t N, const void* bias,
@@ -356,20 +370,6 @@ const char* lora_status_string(int status);
 
 /* LORA_OK when the current HIP device is a gfx950; LORA_ERR_UNSUPPORTED otherwise. */
 int lora_device_check(void);
-
-/*
- * Output tile of the hot GEMM of the lossless tier, process-wide (for tuning and for
- * tests that compare the two): 0 (the default) picks it from the layer's shape
- * (128 x 128 when the 256 x 256 tiles would fill less than three quarters of the
- * compute units), 1 always 256 x 256, 2 always 128 x 128. Both accumulate every
- * output in the same order and give bitwise-identical results; only speed differs.
- * Calls that do not reach the hot GEMM are not affected: 64 tokens or fewer (the
- * few-token kernels), more than two stacked adapter groups meeting one 256-column
- * tile, fp32 activations, and the exact tier.
- * Returns LORA_ERR_UNSUPPORTED for any other value. Not synchronised with calls in
- * flight on other host threads (a call reads the setting once, at launch).
- */
-int lora_set_gemm_tile(int32_t policy);
 
 #ifdef __cplusplus
 }

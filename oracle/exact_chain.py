@@ -128,10 +128,12 @@ def chain_stacked(x, W, b, groups, strength, request_scale, act: str = "bf16",
 def chain_multi(x, W, b, adapters, request_scale, act: str = "bf16", adapter: str = "bf16") -> np.ndarray:
     """E1-E5 per adapter, in the order given, on its column range of one base output.
 
-    Each adapter has its own strength; its legacy lora_B bias c (or None) is the
-    bias of the second rank GEMM, added before that GEMM's rounding as the base
-    bias is in E2: d = RN_adt(RN_f32(G(t, B) + c)); then the scale passes (E4)
-    and the add (E5). Adapters on the same columns add one after another.
+    Each adapter has its own strength. Its legacy lora_B bias c (or None) is a
+    dense payload of the adapter on its output columns, applied after the
+    adapter's own delta: the scale passes of E4 over (strength, request_scale)
+    only -- alpha / rank belongs to the factor pair -- then the add of E5:
+    e = passes(c), y = RN_dt(RN_f32(y + e)). Adapters on the same columns add
+    one after another.
     """
     y = _base(x, W, b, act).copy()
     for a in adapters:
@@ -139,12 +141,11 @@ def chain_multi(x, W, b, adapters, request_scale, act: str = "bf16", adapter: st
         if a["A"] is None or a["B"] is None or (factors[0] * factors[1] * factors[2]) == 0.0:
             continue
         o, n = int(a["col_offset"]), int(a["n_cols"])
-        t = rn(gemm_ordered(x, a["A"]), adapter)
-        g = gemm_ordered(t, a["B"])
-        if a.get("c") is not None:
-            g = rn_f32(g + f64(a["c"])[None, :])
-        d = _scale_passes(rn(g, adapter), factors, adapter)
+        d = _delta(x, a["A"], a["B"], factors, adapter)
         y[:, o:o + n] = rn(rn_f32(y[:, o:o + n] + d), act)
+        if a.get("c") is not None:
+            e = _scale_passes(f64(a["c"]), factors[1:], adapter)
+            y[:, o:o + n] = rn(rn_f32(y[:, o:o + n] + e[None, :]), act)
     return y
 
 

@@ -86,18 +86,23 @@ def lora_linear_stacked(x, W, b, groups, strength, request_scale) -> np.ndarray:
 
 
 def lora_linear_multi(x, W, b, adapters, request_scale) -> np.ndarray:
-    """Several adapters on one layer: y = x.W^T + b + sum_i s_i.((x.A_i^T).B_i^T + c_i)
-    over adapter i's columns, s_i = (alpha_i / r_i) . strength_i . request_scale.
+    """Several adapters on one layer, each on its own columns:
+
+        y = x.W^T + b + sum_i [ s_i.(x.A_i^T).B_i^T + u_i.c_i ]
+
+    with s_i = (alpha_i / r_i) . strength_i . request_scale and u_i = strength_i . request_scale.
 
     piper-offload README, routed mode: the output residual is the strength
     times (B.A.x plus the legacy bias), and several LoRAs on one target are
     summed independently; its LoRA resource section: an older adapter may carry
-    a lora_B.bias vector c_i, applied with that adapter's strength. InvokeAI
-    article, section 3: a layer keeps a list of (patch, weight) pairs whose
-    contributions add up. Reading: c_i sits inside the bracket that the
-    adapter's whole combined scale multiplies. ``adapters`` are dicts with A,
-    B, c (or None), rank, alpha, strength, col_offset, n_cols; an adapter with
-    A or B None or s_i == +-0 contributes nothing (its bias included).
+    a lora_B.bias vector c_i, which merge mode adds to the layer's bias with the
+    same adapter strength. InvokeAI article, section 3: a layer keeps a list of
+    (patch, weight) pairs whose contributions add up. Reading: alpha_i / r_i
+    belongs to the factor pair (SGLang PR #43501, Motivation), so the legacy
+    vector takes the adapter strength and the request scale only. ``adapters``
+    are dicts with A, B, c (or None), rank, alpha, strength, col_offset,
+    n_cols; an adapter with A or B None or s_i == +-0 is inactive as a whole
+    (its legacy vector included).
     """
     x, W, b = f64(x), f64(W), f64(b)
     y = x @ W.T
@@ -108,10 +113,10 @@ def lora_linear_multi(x, W, b, adapters, request_scale) -> np.ndarray:
         if a["A"] is None or a["B"] is None or s == 0.0:
             continue
         o, n = int(a["col_offset"]), int(a["n_cols"])
-        upd = (x @ f64(a["A"]).T) @ f64(a["B"]).T
+        y[:, o:o + n] += s * ((x @ f64(a["A"]).T) @ f64(a["B"]).T)
         if a.get("c") is not None:
-            upd = upd + f64(a["c"])[None, :]
-        y[:, o:o + n] += s * upd
+            u = float(a["strength"]) * float(request_scale)
+            y[:, o:o + n] += u * f64(a["c"])[None, :]
     return y
 
 

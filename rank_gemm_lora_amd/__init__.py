@@ -29,7 +29,7 @@ __all__ = [
     "lora_linear_multi", "LoraAdapter", "lora_merge_apply", "lora_merge", "lora_linear_bwd",
     "lora_linear_bwd_workspace_size", "lora_linear_backward",
     "lora_status_string",
-    "lora_device_check", "lora_set_gemm_tile", "lora_linear", "lora_linear_stacked", "lora_linear_nf4", "dense_patch",
+    "lora_device_check", "lora_linear", "lora_linear_stacked", "lora_linear_nf4", "dense_patch",
     "LoraGroup", "hip_runtimes_mapped",
 ]
 
@@ -64,8 +64,8 @@ class LoraAdapter(ctypes.Structure):
 _lib.lora_linear_fwd.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _f64, _f64, _f64,
                                  _p, _i64, _i32, _i32, _p, _sz, _p]
 _lib.lora_linear_fwd.restype = ctypes.c_int
-_lib.lora_linear_fwd_phase.argtypes = [_i32, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _f64, _f64,
-                                       _f64, _p, _i64, _i32, _i32, _p, _sz, _p]
+_lib.lora_linear_fwd_phase.argtypes = [_i32, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _f64,
+                                       _f64, _f64, _p, _i64, _i32, _i32, _p, _sz, _p]
 _lib.lora_linear_fwd_phase.restype = ctypes.c_int
 _lib.lora_linear_stacked_fwd.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, ctypes.POINTER(LoraGroup), _i32,
                                          _i32, _f64, _f64, _p, _i64, _i32, _i32, _p, _sz, _p]
@@ -96,8 +96,6 @@ _lib.lora_status_string.argtypes = [ctypes.c_int]
 _lib.lora_status_string.restype = ctypes.c_char_p
 _lib.lora_device_check.argtypes = []
 _lib.lora_device_check.restype = ctypes.c_int
-_lib.lora_set_gemm_tile.argtypes = [_i32]
-_lib.lora_set_gemm_tile.restype = ctypes.c_int
 
 
 class LoraError(RuntimeError):
@@ -121,10 +119,10 @@ def lora_linear_fwd(x, T, K, ldx, W, N, bias, A, B, rank, adapter_dtype, alpha, 
                                        stream), "lora_linear_fwd")
 
 
-def lora_linear_fwd_phase(phase, x, T, K, ldx, W, N, bias, A, B, rank, adapter_dtype, alpha, strength,
+def lora_linear_fwd_phase(phase, gemm_tile, x, T, K, ldx, W, N, bias, A, B, rank, adapter_dtype, alpha, strength,
                           request_scale, y, ldy, act_dtype, quality, workspace, workspace_bytes, stream):
-    return _check(_lib.lora_linear_fwd_phase(phase, x, T, K, ldx, W, N, bias, A, B, rank, adapter_dtype, alpha,
-                                             strength, request_scale, y, ldy, act_dtype, quality, workspace,
+    return _check(_lib.lora_linear_fwd_phase(phase, gemm_tile, x, T, K, ldx, W, N, bias, A, B, rank, adapter_dtype,
+                                             alpha, strength, request_scale, y, ldy, act_dtype, quality, workspace,
                                              workspace_bytes, stream), "lora_linear_fwd_phase")
 
 
@@ -195,11 +193,6 @@ def lora_device_check() -> int:
     return int(_lib.lora_device_check())
 
 
-def lora_set_gemm_tile(policy: int) -> int:
-    """Hot-GEMM output tile: 0 automatic, 1 256 x 256, 2 128 x 128 (bitwise-identical results)."""
-    return _check(int(_lib.lora_set_gemm_tile(int(policy))), "lora_set_gemm_tile")
-
-
 def hip_runtimes_mapped() -> list:
     """Distinct libamdhip64 files mapped into this process (exactly one is expected)."""
     paths = set()
@@ -243,8 +236,11 @@ def _workspace(T, K, N, ranks, adapter_dtype, quality, workspace, device):
 
 
 def lora_linear(x, W, b, A, B, alpha, strength=1.0, request_scale=1.0, out=None, quality="lossless",
-                workspace=None, stream=None):
-    """y = x.W^T + b + s.(x.A^T).B^T on the GPU; returns ``out`` (allocated when None)."""
+                workspace=None, stream=None, gemm_tile=None):
+    """y = x.W^T + b + s.(x.A^T).B^T on the GPU; returns ``out`` (allocated when None).
+
+    ``gemm_tile`` (lossless only): None or 0 lets the library pick the hot GEMM's output
+    tile, 1 fixes 256 x 256, 2 fixes 128 x 128 (same bits, different speed)."""
     T, K = x.shape
     N = W.shape[0]
     ldx = _row_major(x, "x")
@@ -255,9 +251,13 @@ def lora_linear(x, W, b, A, B, alpha, strength=1.0, request_scale=1.0, out=None,
     adt = _dt(A) if A is not None else _dt(x)
     q = _QUALITY[quality]
     ws, need = _workspace(T, K, N, [rank] if rank else [], adt, q, workspace, x.device)
-    lora_linear_fwd(x.data_ptr(), T, K, ldx, W.data_ptr(), N, _ptr(b), _ptr(A), _ptr(B), rank, adt,
-                    float(alpha), float(strength), float(request_scale), out.data_ptr(), ldy, _dt(x), q,
-                    ws.data_ptr(), ws.numel(), _stream(stream))
+    args = (x.data_ptr(), T, K, ldx, W.data_ptr(), N, _ptr(b), _ptr(A), _ptr(B), rank, adt, float(alpha),
+            float(strength), float(request_scale), out.data_ptr(), ldy, _dt(x), q, ws.data_ptr(), ws.numel(),
+            _stream(stream))
+    if gemm_tile:
+        lora_linear_fwd_phase(0, int(gemm_tile), *args)
+    else:
+        lora_linear_fwd(*args)
     return out
 
 

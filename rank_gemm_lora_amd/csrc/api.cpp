@@ -67,6 +67,7 @@ int fill_groups(LinearProblem& p, const Adapter* ads, int n, double request_scal
     const double s = (a.alpha / static_cast<double>(a.rank)) * strength * request_scale;
     if (s == 0.0) continue;  // a zero combined scale leaves the adapter inactive
     if (std::fabs(s) > FLT_MAX) return LORA_ERR_NONFINITE;
+    if (a.Bb != nullptr && std::fabs(strength * request_scale) > FLT_MAX) return LORA_ERR_NONFINITE;
     GroupDev& g = p.g[p.n_groups++];
     g.A = a.A;
     g.B = a.B;
@@ -76,6 +77,7 @@ int fill_groups(LinearProblem& p, const Adapter* ads, int n, double request_scal
     g.r_pad = static_cast<int32_t>(lora::rank_pad(a.rank));
     g.t_col = static_cast<int32_t>(tcol);
     g.scale = static_cast<float>(s);
+    g.bscale = static_cast<float>(strength * request_scale);
     g.f[0] = static_cast<float>(a.alpha / static_cast<double>(a.rank));
     g.f[1] = static_cast<float>(strength);
     g.f[2] = static_cast<float>(request_scale);
@@ -119,8 +121,9 @@ size_t panel_bytes(int64_t N, int64_t K) { return static_cast<size_t>(N) * stati
 
 size_t workspace_rest_for(const LinearProblem& p, bool lossless);
 
-// Lossless: b + sum_g s_g . c_g as one fp32 vector [N] at the front of the
-// workspace when an active adapter has a legacy lora_B bias.
+// Lossless: b + sum_g u_g . c_g (u_g = strength_g . request_scale) as one fp32
+// vector [N] at the front of the workspace when an active adapter has a legacy
+// lora_B bias.
 bool needs_bias32(const LinearProblem& p, bool lossless) {
   if (!lossless) return false;
   for (int i = 0; i < p.n_groups; ++i)
@@ -159,7 +162,7 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
                const float* absmax, const float* codebook, bool nf4, int64_t N, const void* bias,
                const Adapter* ads, int n_ads, int adapter_dtype, double request_scale,
                void* y, int64_t ldy, int act_dtype, int quality, void* workspace, size_t workspace_bytes,
-               void* stream, int phase = 0, bool overlap_ok = false) {
+               void* stream, int phase = 0, bool overlap_ok = false, int tile = 0) {
   if (!dtype_ok(act_dtype) || !dtype_ok(adapter_dtype)) return LORA_ERR_DTYPE;
   if (act_dtype == LORA_F32 && adapter_dtype != LORA_F32) return LORA_ERR_DTYPE;
   if (quality != LORA_LOSSLESS && quality != LORA_EXACT) return LORA_ERR_UNSUPPORTED;
@@ -214,7 +217,7 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
   std::memset(&p, 0, sizeof(p));
   p.x = x; p.ldx = ldx; p.W = W; p.codes = codes; p.absmax = absmax; p.codebook = codebook;
   p.bias = bias; p.y = y; p.ldy = ldy; p.T = T; p.N = N; p.K = K;
-  p.act = to_elt(act_dtype); p.adapter = to_elt(adapter_dtype); p.nf4 = nf4;
+  p.act = to_elt(act_dtype); p.adapter = to_elt(adapter_dtype); p.nf4 = nf4; p.tile = tile;
   const int st = fill_groups(p, ads, n_ads, request_scale);
   if (st != LORA_OK) return st;
 
@@ -287,15 +290,17 @@ int lora_linear_fwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void
                     request_scale, y, ldy, act_dtype, quality, workspace, workspace_bytes, stream);
 }
 
-int lora_linear_fwd_phase(int32_t phase, const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, int64_t N,
-                          const void* bias, const void* A, const void* B, int32_t rank, int32_t adapter_dtype,
-                          double alpha, double strength, double request_scale, void* y, int64_t ldy,
-                          int32_t act_dtype, int32_t quality, void* workspace, size_t workspace_bytes, void* stream) {
-  if (phase != 1 && phase != 2) return LORA_ERR_UNSUPPORTED;
+int lora_linear_fwd_phase(int32_t phase, int32_t gemm_tile, const void* x, int64_t T, int64_t K, int64_t ldx,
+                          const void* W, int64_t N, const void* bias, const void* A, const void* B, int32_t rank,
+                          int32_t adapter_dtype, double alpha, double strength, double request_scale, void* y,
+                          int64_t ldy, int32_t act_dtype, int32_t quality, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (phase < 0 || phase > 2 || gemm_tile < 0 || gemm_tile > 2) return LORA_ERR_UNSUPPORTED;
   if (quality != LORA_LOSSLESS) return LORA_ERR_UNSUPPORTED;
   const Adapter a{A, B, rank, alpha, 0, N, strength, nullptr};
   return run_linear(x, T, K, ldx, W, nullptr, nullptr, nullptr, false, N, bias, &a, 1, adapter_dtype,
-                    request_scale, y, ldy, act_dtype, quality, workspace, workspace_bytes, stream, phase);
+                    request_scale, y, ldy, act_dtype, quality, workspace, workspace_bytes, stream, phase, false,
+                    gemm_tile);
 }
 
 int lora_linear_stacked_fwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, int64_t N_total,
@@ -551,9 +556,12 @@ size_t lora_linear_workspace_size(int64_t T, int64_t K, int64_t N, const int32_t
       ++n;
     }
   // few tokens (lossless, bf16 activations): fp32 partial sums instead of the
-  // intermediate; the activation dtype is not an argument, so the larger of the two
-  const size_t skinny = (quality == LORA_LOSSLESS && T <= lora::kSkinnyMaxT && cols <= lora::kSkinnyMaxLdt)
-                            ? lora::skinny_bytes(T, K, N, cols) : 0;
+  // intermediate; the activation dtype is not an argument, so the larger of the two.
+  // A call takes the few-token layout when its ACTIVE adapters' padded ranks sum to at
+  // most kSkinnyMaxLdt, whatever the ranks passed here add up to (an adapter with a
+  // zero scale drops out), so that layout is sized for the largest such sum.
+  const size_t skinny = (quality == LORA_LOSSLESS && T <= lora::kSkinnyMaxT)
+                            ? lora::skinny_bytes(T, K, N, std::min<int64_t>(cols, lora::kSkinnyMaxLdt)) : 0;
   if (cols == 0) return skinny;
   if (quality == LORA_LOSSLESS && adapter_dtype == LORA_F32) {
     // the bf16-activation layout (the larger of the two an fp32 adapter can need);
@@ -613,12 +621,6 @@ const char* lora_status_string(int status) {
     case LORA_ERR_HIP: return "HIP runtime error";
     default: return "unknown status";
   }
-}
-
-int lora_set_gemm_tile(int32_t policy) {
-  if (policy < 0 || policy > 2) return LORA_ERR_UNSUPPORTED;
-  lora::set_gemm_tile_policy(policy);
-  return LORA_OK;
 }
 
 int lora_device_check(void) {

@@ -187,16 +187,22 @@ __global__ __launch_bounds__(256) void exact_out_kernel(LinearProblem p) {
       if (g.Bb != nullptr)
         cb = ad_bf16 ? bf16_to_f32(static_cast<const bf16_bits*>(g.Bb)[n - g.col_off])
                      : static_cast<const float*>(g.Bb)[n - g.col_off];
+      // the legacy lora_B bias: its own passes over strength and request scale (not alpha / rank),
+      // added after the adapter's delta
+      float e = cb;
+#pragma unroll
+      for (int f = 1; f < 3; ++f) {
+        if (g.f[f] != 1.0f) e = rn_dt(e * g.f[f], ad_bf16);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // E3 (a legacy lora_B bias is added to the fp32 GEMM result before the rounding, as in E2)
-        const float gd = static_cast<float>(dacc[i][j]);
-        float d = rn_dt(g.Bb != nullptr ? gd + cb : gd, ad_bf16);
+        float d = rn_dt(static_cast<float>(dacc[i][j]), ad_bf16);     // E3
 #pragma unroll
         for (int f = 0; f < 3; ++f) {                                 // E4
           if (g.f[f] != 1.0f) d = rn_dt(d * g.f[f], ad_bf16);
         }
         out[i][j] = rn_dt(out[i][j] + d, act_bf16);                   // E5
+        if (g.Bb != nullptr) out[i][j] = rn_dt(out[i][j] + e, act_bf16);
       }
     }
   }

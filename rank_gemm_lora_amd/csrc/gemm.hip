@@ -24,8 +24,6 @@
 // global->LDS directly by buffer_load ... lds (no VGPR round trip), double
 // buffered; out-of-range rows and K tails read as zero through the buffer
 // resource's range check.
-#include <atomic>
-
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -1408,17 +1406,11 @@ using Flow16Cfg = QCfg<256, 256, 128, 128, 128, 5>;
 // 256 x 256 tiles would leave compute units idle (few tokens or narrow outputs).
 using Flow16SCfg = QCfg<128, 128, 64, 64, 128, 5, 2>;
 
-// Compute units of the current device (cached per device, safe to call from several host
-// threads; 0 when the query fails).
+// Compute units of the current device (0 when the query fails).
 int device_cus() {
-  static std::atomic<int> cus[64];  // zero-initialized (static storage)
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int n = cus[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cus[dev].store(n, std::memory_order_relaxed);
-  }
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   return n;
 }
 
@@ -1447,8 +1439,7 @@ hipError_t launch(const LinearProblem& p, hipStream_t s) {
     // the 128 x 128 tile when the 256 x 256 tiles fill less than three quarters of the
     // compute units (or when asked for); both give the same bits
     const int64_t tiles = ((p.T + 255) / 256) * ((p.N + 255) / 256);
-    const int policy = gemm_tile_policy();
-    const bool small = policy == 2 || (policy == 0 && 4 * tiles < 3 * static_cast<int64_t>(device_cus()));
+    const bool small = p.tile == 2 || (p.tile == 0 && 4 * tiles < 3 * static_cast<int64_t>(device_cus()));
     return small ? launch_flow16<Flow16SCfg>(p, s) : launch_flow16<Flow16Cfg>(p, s);
   }
   using P = HotCfg;
@@ -2090,13 +2081,6 @@ hipError_t launch_skinny(const LinearProblem& p, hipStream_t s) {
 
 }  // namespace
 
-namespace {
-std::atomic<int> g_tile_policy{0};
-}  // namespace
-
-int gemm_tile_policy() { return g_tile_policy.load(std::memory_order_relaxed); }
-void set_gemm_tile_policy(int policy) { g_tile_policy.store(policy, std::memory_order_relaxed); }
-
 // Split copies of an fp32 adapter (layout in GroupDev): hi(v) = RN_bf16(v) and
 // lo(v) = RN_bf16(v - hi(v)), where v - hi(v) is exact in fp32, so hi + lo
 // carries v to about 16 significant bits.
@@ -2206,7 +2190,8 @@ hipError_t split_gemm(const LinearProblem& p, hipStream_t s) {
   return pipe::launch(q, s);
 }
 
-// b + sum_g s_g . c_g over the legacy lora_B biases, fp32, groups in order (one thread per column).
+// b + sum_g u_g . c_g over the legacy lora_B biases, fp32, groups in order (one thread per column);
+// u_g = strength_g . request_scale: the legacy vector takes the adapter strength, not alpha / rank.
 __global__ __launch_bounds__(256) void bias32_kernel(LinearProblem p) {
   const int64_t n = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (n >= p.N) return;
@@ -2219,7 +2204,7 @@ __global__ __launch_bounds__(256) void bias32_kernel(LinearProblem p) {
     const int64_t j = n - g.col_off;
     const float c = p.adapter == Elt::BF16 ? bf16_to_f32(static_cast<const bf16_bits*>(g.Bb)[j])
                                            : static_cast<const float*>(g.Bb)[j];
-    v += g.scale * c;
+    v += g.bscale * c;
   }
   p.bias32[n] = v;
 }

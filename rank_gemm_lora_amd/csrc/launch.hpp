@@ -26,6 +26,7 @@ struct GroupDev {
   int32_t t_col;     // first column of this group's block in the t workspace
   int32_t r_pad;     // padded rank (multiple of kRankPad)
   float scale;       // lossless: combined scale rounded to fp32
+  float bscale;      // lossless: legacy lora_B bias factor strength . request_scale, rounded to fp32
   float f[3];        // exact tier: alpha/rank, strength, request_scale, each rounded to fp32
   // Lossless tier, fp32 adapter on bf16 activations: bf16 split copies in the
   // workspace. A2 [2 r_pad, K]: row 2q = hi(A[q]), row 2q + 1 = lo(A[q]);
@@ -111,7 +112,7 @@ struct LinearProblem {
   void* panel;       // 4-bit weight, lossless, T > kSkinnyMaxT: bf16 [N, K] dequantized copy in the workspace
   float* skinny;     // skinny path: fp32 partial sums in the workspace (null otherwise)
   float* tpart;      // bf16 adapter, lossless: the producer's K-split partial sums (null: no split)
-  float* bias32;     // lossless with legacy lora_B biases: b + sum_g s_g . c_g, fp32 [N] (null otherwise);
+  float* bias32;     // lossless with legacy lora_B biases: b + sum_g u_g . c_g, fp32 [N] (null otherwise);
                      // the epilogues add it instead of `bias`
   const void* bias;
   void* y; int64_t ldy;
@@ -122,6 +123,7 @@ struct LinearProblem {
   GroupDev g[kMaxGroups];
   void* work;        // t workspace, [T, ldt] in adapter dtype
   int64_t ldt;       // sum of r_pad over groups
+  int tile;          // output tile of the hot GEMM: 0 chosen from the shape, 1 256 x 256, 2 128 x 128
 };
 
 // Lossless tier: t~ = RN_adt(s . x A^T) into the workspace, then the fused GEMM.
@@ -129,11 +131,8 @@ struct LinearProblem {
 // (which reads the t~ a phase-1 call left in the workspace).
 hipError_t launch_lossless(const LinearProblem& p, hipStream_t s, int phase = 0);
 
-// Output tile of the hot GEMM: 0 chosen from the layer's shape, 1 always 256 x 256,
-// 2 always 128 x 128 (process-wide; both tiles give bitwise-identical results).
-int gemm_tile_policy();
-void set_gemm_tile_policy(int policy);
-// Lossless with legacy lora_B biases: p.bias32 = fp32(b) + s_g . fp32(c_g) summed in group order.
+// Lossless with legacy lora_B biases: p.bias32 = fp32(b) + u_g . fp32(c_g) summed in group order,
+// u_g = strength_g . request_scale (the legacy vector does not take alpha / rank).
 hipError_t launch_bias32(const LinearProblem& p, hipStream_t s);
 // Exact tier: the ordered-fp64 separate-pass chain.
 hipError_t launch_exact(const LinearProblem& p, hipStream_t s);

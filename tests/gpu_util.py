@@ -49,11 +49,21 @@ def assert_gate(y_gpu, y64, y_chain=None, gate=LOSSLESS_BF16_GATE, what=""):
     return e
 
 
-def sample_rows(T, n_each=32, seed=0, tile=256):
-    """First rows, the last (ragged) tile's rows, and random rows in between."""
+def sample_rows(T, seed=0, n_head=16, n_rand=16, min_rows=256, tile=256):
+    """The first rows, every row of the last (ragged) 256-token tile and random rows in between:
+    at least ``min_rows`` rows, or all of them when T is smaller."""
+    if T <= min_rows:
+        return np.arange(T)
     rng = np.random.default_rng(seed)
-    head = np.arange(min(n_each, T))
-    last_tile = (T - 1) // tile * tile
-    tail = np.arange(max(last_tile, T - n_each), T)
-    mid = rng.choice(T, size=min(n_each, T), replace=False)
-    return np.unique(np.concatenate([head, tail, mid]))
+    head = np.arange(min(n_head, T))
+    tail = np.arange((T - 1) // tile * tile, T)
+    chosen = np.union1d(head, tail)
+    pool = np.setdiff1d(np.arange(T), chosen)
+    need = max(n_rand, min_rows - len(chosen))
+    mid = rng.choice(pool, size=min(need, len(pool)), replace=False)
+    return np.union1d(chosen, mid)
+
+
+def nan_out(T, N, dtype=torch.bfloat16):
+    """An output buffer filled with NaN: after the call, no NaN left means every element was written."""
+    return torch.full((T, N), float("nan"), dtype=dtype, device=DEV)

@@ -82,19 +82,21 @@ def test_linear_valid_noop_and_inactive_need_no_workspace():
     assert lin(T=0, x=X + 1, q=EXACT) == ALIGN
 
 
-def phase(ph, **kw):
+def phase(ph, tile=0, **kw):
     a = dict(x=X, T=64, K=128, ldx=128, W=W, N=96, bias=BIAS, A=A, B=B, rank=8, adt=BF16, alpha=16.0,
              strength=1.0, rs=1.0, y=Y, ldy=96, act=BF16, q=LOSSLESS, ws=WSP, wsb=1 << 30)
     a.update(kw)
-    return rg._lib.lora_linear_fwd_phase(ph, a["x"], a["T"], a["K"], a["ldx"], a["W"], a["N"], a["bias"], a["A"],
-                                         a["B"], a["rank"], a["adt"], a["alpha"], a["strength"], a["rs"], a["y"],
-                                         a["ldy"], a["act"], a["q"], a["ws"], a["wsb"], None)
+    return rg._lib.lora_linear_fwd_phase(ph, tile, a["x"], a["T"], a["K"], a["ldx"], a["W"], a["N"], a["bias"],
+                                         a["A"], a["B"], a["rank"], a["adt"], a["alpha"], a["strength"], a["rs"],
+                                         a["y"], a["ldy"], a["act"], a["q"], a["ws"], a["wsb"], None)
 
 
 def test_phase_entry_point_validation():
-    assert phase(0) == UNSUP and phase(3) == UNSUP and phase(-1) == UNSUP
-    assert phase(1, q=EXACT) == UNSUP and phase(2, q=EXACT) == UNSUP
-    for ph in (1, 2):                      # the same validation as lora_linear_fwd, before any launch
+    assert phase(3) == UNSUP and phase(-1) == UNSUP
+    assert phase(0, tile=3) == UNSUP and phase(1, tile=-1) == UNSUP and phase(2, tile=1 << 20) == UNSUP
+    assert all(phase(ph, tile=t, T=0) == OK for ph in (0, 1, 2) for t in (0, 1, 2))
+    assert phase(0, q=EXACT) == UNSUP and phase(1, q=EXACT) == UNSUP and phase(2, q=EXACT) == UNSUP
+    for ph in (0, 1, 2):                   # the same validation as lora_linear_fwd, before any launch
         assert phase(ph, T=0) == OK
         assert phase(ph, x=None) == NULL
         assert phase(ph, ldy=95) == SHAPE
@@ -202,6 +204,38 @@ def test_multi_validation():
     assert ws(4096, 128, 300, mk(C), BF16, EXACT) == rg.lora_linear_workspace_size(4096, 128, 300, [8], BF16, EXACT)
 
 
+def _skinny_bytes(T, K, N, ldt):
+    """The few-token layout the header documents: S fp32 partial sums [S, T, round_up(N, 64) + ldt],
+    S = the number of K chunks (about 8, each a multiple of 128)."""
+    c = -(-K // 8)
+    c = -(-c // 128) * 128
+    S = -(-K // c)
+    return S * T * (-(-N // 64) * 64 + ldt) * 4
+
+
+def test_few_token_workspace_covers_active_subsets():
+    """At 64 tokens a call takes the few-token layout when its ACTIVE adapters' padded ranks sum to at
+    most 4096; the query, given every adapter's rank, must cover that layout even when all the
+    ranks together exceed 4096. 8 adapters of rank 1024, 7 of them at strength 0: sized by the query,
+    the call passes the workspace check (it stops at the overlap check that follows, so nothing
+    launches)."""
+    T, K, N = 64, 8960, 8960
+    ranks = [1024] * 8
+    need_active = _skinny_bytes(T, K, N, 1024)
+    q = rg.lora_linear_workspace_size(T, K, N, ranks, BF16)
+    assert q >= _skinny_bytes(T, K, N, 4096) >= need_active
+    arr = [rg.LoraAdapter(A + i * 0x1000_0000, B + i * 0x1000_0000, None, 1024, 0, 1024.0,
+                          1.0 if i == 3 else 0.0, 0, N) for i in range(8)]
+    mq = rg.lora_linear_multi_workspace_size(T, K, N, arr, BF16)
+    assert mq >= q
+    st = rg._lib.lora_linear_multi_fwd(X, T, K, K, W, N, None, (rg.LoraAdapter * 8)(*arr), 8, BF16, 1.0,
+                                       X, N, BF16, LOSSLESS, WSP, mq, None)
+    assert st == OVERLAP, st        # (WORKSPACE here would mean the documented query was too small)
+    st = rg._lib.lora_linear_multi_fwd(X, T, K, K, W, N, None, (rg.LoraAdapter * 8)(*arr), 8, BF16, 1.0,
+                                       X, N, BF16, LOSSLESS, WSP, need_active - 1, None)
+    assert st == WS
+
+
 def merge(**kw):
     a = dict(W=W, wdt=BF16, N=300, K=128, A=A, B=B, rank=8, adt=BF16, alpha=8.0, strength=1.0, q=LOSSLESS)
     a.update(kw)
@@ -285,18 +319,6 @@ def test_status_strings():
     for s in range(10):
         assert rg.lora_status_string(s)
     assert "unknown" in rg.lora_status_string(99)
-
-
-def test_gemm_tile_policy_values():
-    """0 (automatic), 1 and 2 are accepted; anything else is rejected and leaves the setting alone."""
-    lib = rg._lib
-    try:
-        for v in (1, 2, 0):
-            assert lib.lora_set_gemm_tile(v) == 0
-        for v in (-1, 3, 1 << 20):
-            assert lib.lora_set_gemm_tile(v) == 8  # LORA_ERR_UNSUPPORTED
-    finally:
-        lib.lora_set_gemm_tile(0)
 
 
 def test_product_path_never_touches_the_oracle():

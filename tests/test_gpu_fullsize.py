@@ -1,9 +1,15 @@
 """GPU parity at the workloads' full sizes, in the launch configuration bench.py
-uses (same entry points, lossless default), on rows the CPU oracle can afford:
-the first rows, the rows of the ragged last 256-token tile and random rows in
-between. Lossless: relative RMS <= 4e-3 against fp64 and no larger than the
-separate-pass chain's error on the same rows. Exact tier: bit-identical to the
-chain on the same rows. Dense patches: bit-identical over the whole tensor.
+uses (same entry points, lossless default).
+
+Every output buffer starts as NaN, so "no NaN afterwards" proves that every
+element was written (a tile the grid mapping skipped would stay NaN).
+
+Lossless: relative RMS <= 4e-3 against the fp64 plain definition over the
+WHOLE output (numpy float64 BLAS on the host), and, on at least 256 rows (the
+first rows, every row of the ragged last 256-token tile, random rows), no
+larger than the separate-pass chain's error on the same rows. Exact tier:
+bit-identical to the chain on those rows. Dense patches: bit-identical over the
+whole tensor.
 """
 import numpy as np
 import pytest
@@ -13,28 +19,38 @@ import lora_workloads as lw
 import rank_gemm_lora_amd as rg
 from oracle import exact_chain as ec
 from oracle import lora_oracle as lo
-from tests.gpu_util import assert_bitwise, assert_gate, dev, host64, sample_rows, say
+from tests.gpu_util import assert_bitwise, assert_gate, dev, host64, nan_out, sample_rows, say
+from tests.oracle_pool import rows_parallel
 
 pytestmark = pytest.mark.gpu
 
 
+def _check(name, y, ye, y64, rows, chain, what_rows):
+    """y, ye: GPU outputs (lossless, exact); y64: fp64 plain definition of every output; chain: the
+    chain's values on ``rows``."""
+    assert not bool(torch.isnan(y).any()), f"{name}: lossless output not completely written"
+    assert not bool(torch.isnan(ye).any()), f"{name}: exact-tier output not completely written"
+    T, N = y64.shape
+    assert_gate(y, y64, None, what=f"{name} lossless, all {T} x {N} outputs")
+    idx = torch.from_numpy(rows).to(y.device)
+    assert_gate(y[idx], y64[rows], chain, what=f"{name} lossless vs chain, {what_rows}")
+    assert_bitwise(ye[idx], chain, f"{name} exact, {what_rows}")
+
+
 def _linear_case(d, name, act="bf16", adapter="bf16"):
-    T = d["x"].shape[0]
-    rows = sample_rows(T, n_each=32, seed=1)
-    say(f"case full-size {name}: T={T} K={d['x'].shape[1]} N={d['W'].shape[0]} r={d['rank']} rows={len(rows)}")
+    T, K = d["x"].shape
+    N = d["W"].shape[0]
+    rows = sample_rows(T, seed=1)
+    say(f"case full-size {name}: T={T} K={K} N={N} r={d['rank']} sampled rows={len(rows)}")
     args = (dev(d["x"]), dev(d["W"]), dev(d["b"]), dev(d["A"]), dev(d["B"]), d["alpha"], d["strength"],
             d["request_scale"])
-    y = rg.lora_linear(*args)
+    y = rg.lora_linear(*args, out=nan_out(T, N))
+    ye = rg.lora_linear(*args, quality="exact", out=nan_out(T, N))
     torch.cuda.synchronize()
-    xs = d["x"][rows]
-    oargs = (xs, d["W"], d["b"], d["A"], d["B"], d["alpha"], d["rank"], d["strength"], d["request_scale"])
-    y64 = lo.lora_linear(*oargs)
-    yc = ec.chain_linear(*oargs, act, adapter)
-    assert_gate(y[torch.from_numpy(rows).to(y.device)], y64, yc, what=f"{name} lossless (sampled rows)")
-    ye = rg.lora_linear(*args, quality="exact")
-    torch.cuda.synchronize()
-    assert_bitwise(ye[torch.from_numpy(rows).to(ye.device)], yc, f"{name} exact (sampled rows)")
-    assert not bool(torch.isnan(y).any())
+    oargs = (d["W"], d["b"], d["A"], d["B"], d["alpha"], d["rank"], d["strength"], d["request_scale"])
+    y64 = lo.lora_linear(d["x"], *oargs)
+    yc = rows_parallel(ec.chain_linear, d["x"], rows, (*oargs, act, adapter))
+    _check(name, y, ye, y64, rows, yc, f"{len(rows)} rows")
 
 
 def test_attention_projection_full():
@@ -62,19 +78,16 @@ def test_other_token_regimes_full(pair):
 def test_multi_adapters_full():
     s = lw.MULTI_FFN_UP
     d = lw.multi_inputs(s)
-    rows = sample_rows(s.T, n_each=24, seed=4)
-    say(f"case full-size two adapters on FFN up T={s.T} rows={len(rows)}")
+    rows = sample_rows(s.T, seed=4)
+    say(f"case full-size two adapters on FFN up T={s.T} sampled rows={len(rows)}")
     gg = [dict(a, A=dev(a["A"]), B=dev(a["B"]), c=dev(a["c"])) for a in d["adapters"]]
-    y = rg.lora_linear_multi(dev(d["x"]), dev(d["W"]), dev(d["b"]), gg, s.request_scale)
+    y = rg.lora_linear_multi(dev(d["x"]), dev(d["W"]), dev(d["b"]), gg, s.request_scale, out=nan_out(s.T, s.N))
+    ye = rg.lora_linear_multi(dev(d["x"]), dev(d["W"]), dev(d["b"]), gg, s.request_scale, quality="exact",
+                              out=nan_out(s.T, s.N))
     torch.cuda.synchronize()
-    xs = d["x"][rows]
-    y64 = lo.lora_linear_multi(xs, d["W"], d["b"], d["adapters"], s.request_scale)
-    yc = ec.chain_multi(xs, d["W"], d["b"], d["adapters"], s.request_scale)
-    idx = torch.from_numpy(rows).to(y.device)
-    assert_gate(y[idx], y64, yc, what="multi lossless (sampled rows)")
-    ye = rg.lora_linear_multi(dev(d["x"]), dev(d["W"]), dev(d["b"]), gg, s.request_scale, quality="exact")
-    torch.cuda.synchronize()
-    assert_bitwise(ye[idx], yc, "multi exact (sampled rows)")
+    y64 = lo.lora_linear_multi(d["x"], d["W"], d["b"], d["adapters"], s.request_scale)
+    yc = rows_parallel(ec.chain_multi, d["x"], rows, (d["W"], d["b"], d["adapters"], s.request_scale))
+    _check("multi", y, ye, y64, rows, yc, f"{len(rows)} rows")
 
 
 @pytest.mark.parametrize("adapter", ["bf16", "f32"])
@@ -82,48 +95,40 @@ def test_qkv_stacked_full(adapter):
     spec = lw.QKV_STACKED if adapter == "bf16" else lw.StackedSpec(
         **{**lw.QKV_STACKED.__dict__, "name": "qkv_stacked_f32", "adapter": "f32"})
     d = lw.stacked_inputs(spec)
-    T = spec.T
-    rows = sample_rows(T, n_each=24, seed=2)
-    say(f"case full-size qkv stacked adapter={adapter} rows={len(rows)}")
+    T, N = spec.T, d["W"].shape[0]
+    rows = sample_rows(T, seed=2)
+    say(f"case full-size qkv stacked adapter={adapter} sampled rows={len(rows)}")
     gg = [dict(g, A=dev(g["A"]), B=dev(g["B"])) for g in d["groups"]]
-    y = rg.lora_linear_stacked(dev(d["x"]), dev(d["W"]), dev(d["b"]), gg, d["strength"], d["request_scale"])
-    torch.cuda.synchronize()
-    xs = d["x"][rows]
-    y64 = lo.lora_linear_stacked(xs, d["W"], d["b"], d["groups"], d["strength"], d["request_scale"])
-    yc = ec.chain_stacked(xs, d["W"], d["b"], d["groups"], d["strength"], d["request_scale"], "bf16", adapter)
-    idx = torch.from_numpy(rows).to(y.device)
-    assert_gate(y[idx], y64, yc, what=f"stacked {adapter} lossless (sampled rows)")
+    y = rg.lora_linear_stacked(dev(d["x"]), dev(d["W"]), dev(d["b"]), gg, d["strength"], d["request_scale"],
+                               out=nan_out(T, N))
     ye = rg.lora_linear_stacked(dev(d["x"]), dev(d["W"]), dev(d["b"]), gg, d["strength"], d["request_scale"],
-                                quality="exact")
+                                quality="exact", out=nan_out(T, N))
     torch.cuda.synchronize()
-    assert_bitwise(ye[idx], yc, f"stacked {adapter} exact (sampled rows)")
+    y64 = lo.lora_linear_stacked(d["x"], d["W"], d["b"], d["groups"], d["strength"], d["request_scale"])
+    yc = rows_parallel(ec.chain_stacked, d["x"], rows,
+                       (d["W"], d["b"], d["groups"], d["strength"], d["request_scale"], "bf16", adapter))
+    _check(f"stacked {adapter}", y, ye, y64, rows, yc, f"{len(rows)} rows")
 
 
 @pytest.mark.parametrize("s", [lw.NF4_LAYER, lw.NF4_VECTOR], ids=["tokens8192", "single_vector"])
 def test_nf4_layer_full(s):
     d = lw.nf4_inputs(s)
-    # (8 rows per region: the fp64 references of the 4-bit layer take about a second per row on the host)
-    rows = sample_rows(s.T, n_each=8, seed=3)
-    say(f"case full-size nf4 T={s.T} K={s.K} N={s.N} r={s.rank} rows={len(rows)}")
+    rows = sample_rows(s.T, seed=3, min_rows=72)
+    say(f"case full-size nf4 T={s.T} K={s.K} N={s.N} r={s.rank} sampled rows={len(rows)}")
     args = (dev(d["x"]), dev(d["codes"]), dev(d["absmax"]), dev(d["codebook"]), s.N, dev(d["b"]), dev(d["A"]),
             dev(d["B"]), d["alpha"], d["strength"], d["request_scale"])
-    y = rg.lora_linear_nf4(*args)
+    y = rg.lora_linear_nf4(*args, out=nan_out(s.T, s.N))
+    ye = rg.lora_linear_nf4(*args, quality="exact", out=nan_out(s.T, s.N))
     torch.cuda.synchronize()
-    xs = d["x"][rows]
+    # fp64 over every output with the bf16 weight both tiers multiply (E6), and with the exact
+    # codebook x absmax product
     W = ec.chain_nf4_weight(d["codes"], d["absmax"], d["codebook"], s.K, 64)
-    say("  dequantized weight ready")
-    y64 = lo.lora_linear(xs, W, d["b"], d["A"], d["B"], d["alpha"], d["rank"], d["strength"], d["request_scale"])
-    yc = ec.chain_linear(xs, W, d["b"], d["A"], d["B"], d["alpha"], d["rank"], d["strength"], d["request_scale"])
-    say("  rounding chain ready")
-    # the fp64 reference of the 4-bit layer uses the exact codebook x absmax product
-    y64_exact_w = lo.lora_linear_nf4(xs, d["codes"], d["absmax"], d["codebook"], 64, d["b"], d["A"], d["B"],
-                                     d["alpha"], d["rank"], d["strength"], d["request_scale"])
-    idx = torch.from_numpy(rows).to(y.device)
-    assert_gate(y[idx], y64, yc, what="nf4 lossless vs bf16-weight fp64 (sampled rows)")
-    assert_gate(y[idx], y64_exact_w, None, what="nf4 lossless vs exact-weight fp64 (sampled rows)")
-    ye = rg.lora_linear_nf4(*args, quality="exact")
-    torch.cuda.synchronize()
-    assert_bitwise(ye[idx], yc, "nf4 exact (sampled rows)")
+    oargs = (d["b"], d["A"], d["B"], d["alpha"], d["rank"], d["strength"], d["request_scale"])
+    y64 = lo.lora_linear(d["x"], W, *oargs)
+    y64_exact_w = lo.lora_linear_nf4(d["x"], d["codes"], d["absmax"], d["codebook"], 64, *oargs)
+    yc = rows_parallel(ec.chain_linear, d["x"], rows, (W, *oargs))
+    _check("nf4", y, ye, y64, rows, yc, f"{len(rows)} rows")
+    assert_gate(y, y64_exact_w, None, what="nf4 lossless vs exact-weight fp64, all outputs")
 
 
 @pytest.mark.parametrize("spec", [lw.PATCH_WEIGHT, lw.PATCH_NORM], ids=["weight_14336x4096", "rmsnorm_3072"])
@@ -149,7 +154,7 @@ def test_dense_patch_full(spec):
 @pytest.mark.parametrize("spec", [lw.MERGE_WEIGHT, lw.MERGE_WEIGHT_SMALL], ids=["variance", "small_update"])
 def test_merge_full(spec):
     d = lw.merge_inputs(spec)
-    rows = sample_rows(spec.N, n_each=24, seed=5)
+    rows = sample_rows(spec.N, seed=5)
     say(f"case full-size merge {spec.N}x{spec.K} r={spec.rank} rows={len(rows)}")
     g = dev(d["W"])
     rg.lora_merge(g, dev(d["A"]), dev(d["B"]), spec.alpha, spec.strength)

@@ -198,10 +198,10 @@ def test_phases_compose_to_the_fused_call(T, K, N, r, adapter):
     tail = (rg.LORA_BF16, rg.LORA_LOSSLESS, ws.data_ptr(), ws.numel(), sp)
     rg.lora_linear_fwd(*args, y_one.data_ptr(), N, *tail)
     ws.zero_()
-    rg.lora_linear_fwd_phase(1, *args, y_two.data_ptr(), N, *tail)
+    rg.lora_linear_fwd_phase(1, 0, *args, y_two.data_ptr(), N, *tail)
     torch.cuda.synchronize()
     assert bool((y_two == 3.0).all())      # phase 1 writes only the workspace
-    rg.lora_linear_fwd_phase(2, *args, y_two.data_ptr(), N, *tail)
+    rg.lora_linear_fwd_phase(2, 0, *args, y_two.data_ptr(), N, *tail)
     torch.cuda.synchronize()
     assert torch.equal(y_one, y_two)
 
@@ -289,48 +289,28 @@ def test_handworked_goldens_exact_tier():
 # 256 x 256 (one workgroup per CU) and 128 x 128 (two per CU, chosen when the large tiles would
 # leave compute units idle) accumulate every output in the same order: same bits.
 
-def _tile_runs(fn):
-    outs = []
-    try:
-        for policy in (1, 2):
-            rg.lora_set_gemm_tile(policy)
-            outs.append(fn())
-            torch.cuda.synchronize()
-    finally:
-        rg.lora_set_gemm_tile(0)
-    return outs
-
-
-@pytest.mark.parametrize("case", ["ragged_bias", "tail_row", "two_ext_stages", "no_adapter", "f32_adapter",
-                                  "stacked", "multi_legacy_bias", "nf4_panel", "many_tiles"])
+@pytest.mark.parametrize("case", ["ragged_bias", "tail_row", "two_ext_stages", "four_ext_stages", "no_adapter",
+                                  "f32_adapter", "nf4_sized", "many_tiles"])
 def test_gemm_tiles_bitwise_equal(case):
+    """The tile is a per-call argument (lora_linear_fwd_phase, phase 0): 256 x 256 against 128 x 128."""
     say(f"case gemm tiles {case}")
     shapes = {"ragged_bias": (300, 200, 520, 24, True), "tail_row": (513, 384, 768, 64, False),
-              "two_ext_stages": (257, 1536, 300, 128, True), "no_adapter": (300, 200, 520, 24, True),
-              "f32_adapter": (300, 200, 520, 24, True), "many_tiles": (2600, 512, 6000, 100, False)}
-    if case in shapes:
-        T, K, N, r, bias = shapes[case]
-        d = lw.small_linear_inputs(T, K, N, r, 61, adapter="f32" if case == "f32_adapter" else "bf16", bias=bias,
-                                   alpha=2.0 * r, strength=0.8, request_scale=0.7)
-        if case == "no_adapter":
-            fn = lambda: rg.lora_linear(dev(d["x"]), dev(d["W"]), dev(d["b"]), None, None, 1.0)
-        else:
-            fn = lambda: run_linear(d, "lossless")
-    elif case == "stacked":
-        x, W, b, groups = _stacked_inputs(62, "bf16", T=300)
-        gg = [dict(g, A=dev(g["A"]), B=dev(g["B"])) for g in groups]
-        fn = lambda: rg.lora_linear_stacked(dev(x), dev(W), dev(b), gg, 0.9, 0.8)
-    elif case == "multi_legacy_bias":
-        x, W, b, ads = _multi_inputs(63, 300, "bf16", 2)
-        gg = [dict(a, A=dev(a["A"]), B=dev(a["B"]), c=dev(a["c"])) for a in ads]
-        fn = lambda: rg.lora_linear_multi(dev(x), dev(W), dev(b), gg, 0.7)
-    else:  # nf4_panel: more than 64 tokens, the 4-bit weight dequantized to a bf16 panel first
-        d = _nf4_small(T=130, adapter="bf16")
-        args = (dev(d["x"]), dev(d["codes"]), dev(d["absmax"]), dev(d["codebook"]), d["N"], dev(d["b"]),
-                dev(d["A"]), dev(d["B"]), d["alpha"], 1.0, 0.9)
-        fn = lambda: rg.lora_linear_nf4(*args)
-    y256, y128 = _tile_runs(fn)
+              "two_ext_stages": (257, 1536, 300, 128, True), "four_ext_stages": (300, 256, 700, 200, True),
+              "no_adapter": (300, 200, 520, 24, True), "f32_adapter": (300, 200, 520, 24, True),
+              "nf4_sized": (130, 4096, 600, 16, False), "many_tiles": (2600, 512, 6000, 96, False)}
+    T, K, N, r, bias = shapes[case]
+    d = lw.small_linear_inputs(T, K, N, r, 61, adapter="f32" if case == "f32_adapter" else "bf16", bias=bias,
+                               alpha=2.0 * r, strength=0.8, request_scale=0.7)
+    A, B = (None, None) if case == "no_adapter" else (dev(d["A"]), dev(d["B"]))
+    outs = []
+    for tile in (1, 2):
+        outs.append(rg.lora_linear(dev(d["x"]), dev(d["W"]), dev(d["b"]), A, B, d["alpha"], d["strength"],
+                                   d["request_scale"], gemm_tile=tile))
+        torch.cuda.synchronize()
+    y256, y128 = outs
     assert torch.equal(y256, y128), f"{case}: {(y256 != y128).sum().item()} outputs differ"
+    if case != "no_adapter":
+        assert torch.equal(y256, run_linear(d, "lossless")), f"{case}: the automatic choice differs"
 
 
 @pytest.mark.parametrize("T,K,N,r", [(300, 200, 520, 24), (257, 512, 300, 64)])

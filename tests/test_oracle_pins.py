@@ -294,6 +294,113 @@ def test_nf4_weight_rounds_product_to_bf16():
     assert We[0, 1] == 1.0 + 2.0 ** -6    # tie -> even (up)
 
 
+def _nf4_tiny(seed, T=3, N=2, K=128):
+    """A tiny 4-bit layer over two 64-element blocks per row: every code appears in both nibble
+    positions of every block of every row, the NF4-style codebook of the workloads (values with many
+    significant bits), absmax of mixed magnitudes."""
+    rng = np.random.default_rng(seed)
+    codes = np.zeros((N, K // 2), np.uint8)
+    for n in range(N):
+        for j in range(K // 2):
+            codes[n, j] = (j % 16) | (((j // 2 + 5 * n + 3) % 16) << 4)
+    absmax = torch.tensor(np.abs(rng.standard_normal(N * K // 64)) * 0.3 + 0.05, dtype=torch.float32)
+    cb = lw.nf4_style_codebook()
+    x = lw.to_dtype(rng.standard_normal((T, K)), "bf16")
+    A = lw.to_dtype(rng.standard_normal((4, K)) / 11, "bf16")
+    B = lw.to_dtype(rng.standard_normal((N, 4)) * 0.2, "bf16")
+    b = lw.to_dtype(rng.standard_normal(N) * 0.1, "bf16")
+    return torch.from_numpy(codes), absmax, cb, x, A, B, b
+
+
+def test_nf4_layer_against_exact_rationals():
+    """The 4-bit layer (unpacked codes x block absmax, then the LoRA linear) against exact rationals:
+    the only difference allowed is float64 rounding of the sums (a relative 1e-12 of the absolute
+    terms). A wrong nibble, block, operand or scale fails by orders of magnitude more."""
+    codes, absmax, cb, x, A, B, b = _nf4_tiny(40)
+    alpha, rank, strength, rs = 8.0, 4, 0.8, 0.7
+    y = lo.lora_linear_nf4(x, codes, absmax, cb, 64, b, A, B, alpha, rank, strength, rs)
+    X, Am, Bm, bm = (lo.f64(v) for v in (x, A, B, b))
+    am, cbv, cd = lo.f64(absmax), lo.f64(cb), codes.numpy()
+    T, K = X.shape
+    N = cd.shape[0]
+    s = Fraction(alpha) / rank * Fraction(strength) * Fraction(rs)
+    assert y.shape == (T, N)
+    for n in range(N):
+        w = []
+        for k in range(K):
+            byte = int(cd[n, k // 2])
+            c = byte & 0xF if k % 2 == 0 else byte >> 4
+            w.append(exact(cbv[c]) * exact(am[(n * K + k) // 64]))
+        for t in range(T):
+            base = sum((exact(X[t, k]) * w[k] for k in range(K)), Fraction(0)) + exact(bm[n])
+            low = sum((dot_exact(X[t], Am[q]) * exact(Bm[n, q]) for q in range(rank)), Fraction(0))
+            want = base + s * low
+            scale = sum(abs(float(exact(X[t, k]) * w[k])) for k in range(K)) + 1.0
+            assert abs(y[t, n] - float(want)) <= 1e-12 * scale, (t, n, y[t, n], float(want))
+
+
+def test_chain_nf4_hand_worked_rows():
+    """chain_nf4 on a 3 x 128 layer with rows=[2, 0], each rounding point worked with exact rationals
+    and the IEEE rules (tests/fraction_ref.py): W = RN_bf16(RN_f32(cb[c] . absmax)); base =
+    RN_bf16(RN_f32(G(x, W) + b)); t = RN_bf16(G(x, A)); d = RN_bf16(G(t, B)); one pass per non-unit
+    factor; y = RN_bf16(RN_f32(base + d)). x, A and B are small dyadic values, so every float64 sum
+    of E1 is exact and G is the correctly rounded exact dot product."""
+    rng = np.random.default_rng(41)
+    T, N, K, r = 3, 2, 128, 2
+    codes = np.zeros((N, K // 2), np.uint8)
+    for n in range(N):
+        for j in range(K // 2):
+            codes[n, j] = (j % 16) | (((3 * j + n) % 16) << 4)
+    codes = torch.from_numpy(codes)
+    absmax = torch.tensor([0.7, 1.3, 0.45, 2.1], dtype=torch.float32)
+    cb = lw.nf4_style_codebook()
+    x = lw.to_dtype(rng.integers(-4, 5, (T, K)) / 8.0, "bf16")
+    A = lw.to_dtype(rng.integers(-3, 4, (r, K)) / 16.0, "bf16")
+    B = lw.to_dtype(rng.integers(-3, 4, (N, r)) / 4.0, "bf16")
+    b = lw.to_dtype(np.array([0.3, -0.2]), "bf16")
+    alpha, strength, rs = 3.0, 0.8, 1.0   # factors 1.5, 0.8 (request scale 1 skipped)
+    rows = [2, 0]
+    got = ec.chain_nf4(x, codes, absmax, cb, 64, b, A, B, alpha, r, strength, rs, rows=rows)
+    assert got.shape == (len(rows), N)
+    X, Am, Bm, bm, am, cbv = (lo.f64(v) for v in (x, A, B, b, absmax, cb))
+    cd = codes.numpy()
+    R = lambda q, f: Fraction(round_fraction(q, f))
+    Wd = [[R(R(exact(cbv[(int(cd[n, k // 2]) & 0xF) if k % 2 == 0 else int(cd[n, k // 2]) >> 4])
+                   * exact(am[(n * K + k) // 64]), "f32"), "bf16") for k in range(K)] for n in range(N)]
+    f1 = R(Fraction(alpha) / r, "f32")
+    f2 = R(exact(strength), "f32")
+    for i, t in enumerate(rows):
+        tt = [R(R(dot_exact(X[t], Am[q]), "f32"), "bf16") for q in range(r)]
+        for n in range(N):
+            g = R(sum((exact(X[t, k]) * Wd[n][k] for k in range(K)), Fraction(0)), "f32")
+            base = R(R(g + exact(bm[n]), "f32"), "bf16")
+            d = R(R(sum((tt[q] * exact(Bm[n, q]) for q in range(r)), Fraction(0)), "f32"), "bf16")
+            d = R(R(d * f1, "f32"), "bf16")
+            d = R(R(d * f2, "f32"), "bf16")
+            want = R(R(base + d, "f32"), "bf16")
+            assert got[i, n] == float(want), (t, n, got[i, n], float(want))
+    # rows=None is every row in order, and the same values
+    full = ec.chain_nf4(x, codes, absmax, cb, 64, b, A, B, alpha, r, strength, rs)
+    assert np.array_equal(full[rows], got)
+
+
+# ---------------------------------------------------------------- the accuracy metric
+
+def test_rel_rms_hand_computed():
+    """||y - ref||_2 / ||ref||_2 over all elements, divided by the reference's norm."""
+    assert lo.rel_rms(np.array([3.0, 4.5]), np.array([3.0, 4.0])) == pytest.approx(0.1, rel=1e-15)
+    # over the flattened matrix (not a mean of per-row errors: that would give 0.3)
+    ref = np.array([[1.0, 2.0], [2.0, 4.0]])           # norm 5
+    y = ref + np.array([[0.0, 0.0], [0.0, -3.0]])      # error norm 3
+    assert lo.rel_rms(y, ref) == pytest.approx(0.6, rel=1e-15)
+    # the reference's norm, not the result's (that would give 0.5)
+    assert lo.rel_rms(np.array([6.0, 8.0]), np.array([3.0, 4.0])) == pytest.approx(1.0, rel=1e-15)
+    # torch tensors are widened exactly
+    assert lo.rel_rms(torch.tensor([3.0, 4.5], dtype=torch.bfloat16), np.array([3.0, 4.0])) == \
+        pytest.approx(0.1, rel=1e-15)
+    assert lo.rel_rms(ref, ref) == 0.0
+
+
 # ---------------------------------------------------------------- dense patch
 
 def test_dense_patch_chain_matches_exact_rounding_random():
@@ -411,9 +518,9 @@ def test_multi_brute_force_fraction():
                 s = Fraction(a["alpha"]) / a["rank"] * Fraction(a["strength"]) * Fraction(rs)
                 A, B = lo.f64(a["A"]), lo.f64(a["B"])
                 u = sum((dot_exact(X[t], A[q]) * exact(B[n - o, q]) for q in range(a["rank"])), Fraction(0))
-                if a["c"] is not None:
-                    u += exact(lo.f64(a["c"])[n - o])
                 v += s * u
+                if a["c"] is not None:  # the legacy vector: strength and request scale, not alpha / rank
+                    v += Fraction(a["strength"]) * Fraction(rs) * exact(lo.f64(a["c"])[n - o])
             assert y[t, n] == float(v), (t, n)
 
 
@@ -438,7 +545,8 @@ def test_multi_disjoint_adapters_equal_stacked_groups():
 
 def test_multi_equals_one_adapter_of_concatenated_rank_and_merged_weight():
     """Two adapters on all columns == one adapter [A1; A2], [s1 B1 | s2 B2] with unit scale and the
-    bias b + s1 c1 + s2 c2 == the merged weight W + s1 B1 A1 + s2 B2 A2 (integer data: exact)."""
+    bias b + u1 c1 + u2 c2 (u_i = strength_i . request scale) == the merged weight W + s1 B1 A1 +
+    s2 B2 A2 with that bias (integer data: exact)."""
     x, W, b, ads = _multi_case(7, ranks=(2, 3), spans=((0, 7), (0, 7)))
     ads[1]["c"] = _int_mat(np.random.default_rng(8), (7,))
     rs = 0.5
@@ -446,28 +554,35 @@ def test_multi_equals_one_adapter_of_concatenated_rank_and_merged_weight():
     s = [lo.combined_scale(a["alpha"], a["rank"], a["strength"], rs) for a in ads]
     A_cat = np.concatenate([lo.f64(a["A"]) for a in ads])
     B_cat = np.concatenate([si * lo.f64(a["B"]) for si, a in zip(s, ads)], axis=1)
-    b_all = lo.f64(b) + sum(si * lo.f64(a["c"]) for si, a in zip(s, ads))
+    b_all = lo.f64(b) + sum(a["strength"] * rs * lo.f64(a["c"]) for a in ads)
     assert np.array_equal(y, lo.lora_linear(x, W, b_all, A_cat, B_cat, 5.0, 5, 1.0, 1.0))
     W_m = lo.f64(W) + sum(si * (lo.f64(a["B"]) @ lo.f64(a["A"])) for si, a in zip(s, ads))
     assert np.array_equal(y, lo.f64(x) @ W_m.T + b_all[None, :])
 
 
-def test_multi_chain_bias_rounds_with_the_rank_gemm_and_adapters_add_in_turn():
+def test_multi_chain_legacy_bias_is_its_own_pass_after_the_delta():
     """Hand-worked (bf16 throughout):
-    (a) t = [1, 1], B = [1, 2^-8]: G = 1 + 2^-8; with c = 2^-8 the biased GEMM output 1 + 2^-7 is a
-        bf16 value, so d = 1 + 2^-7 (adding c after rounding G would give RN(1 + 2^-8) = 1, a tie to even);
-        base 0, unit scales: y = 1 + 2^-7.
-    (b) base 1, two adapters each with d = 2^-8 on the same column: 1 + 2^-8 rounds to 1 (tie to even)
-        after the first and again after the second, so y = 1 (adding 2^-8 + 2^-8 first would give 1 + 2^-7)."""
+    (a) base 1, one adapter with d = 2^-8 (unit scales) and legacy vector c = 2^-8 on the same column:
+        1 + 2^-8 is half a bf16 spacing above 1, a tie, so y = RN(1 + d) = 1, then RN(1 + c) = 1
+        again; folding c into the rank GEMM before its rounding would give d = 2^-7 and y = 1 + 2^-7.
+    (b) two adapters each with d = 2^-8 on the same column: 1 + 2^-8 rounds to 1 after the first and
+        again after the second, so y = 1 (adding 2^-8 + 2^-8 first would give 1 + 2^-7).
+    (c) alpha / rank = 4, strength 0.5, request scale 0.75, B = 0, c = 1: the vector takes 0.5 then
+        0.75 (bf16 0.375), not 4 . 0.5 . 0.75 = 1.5."""
     bf = lambda rows: lw.to_dtype(np.array(rows, dtype=np.float64), "bf16")
-    a = dict(A=bf([[1.0, 0.0], [0.0, 1.0]]), B=bf([[1.0, 2.0 ** -8]]), c=bf([2.0 ** -8]), rank=2, alpha=2.0,
-             strength=1.0, col_offset=0, n_cols=1)
-    y = ec.chain_multi(bf([[1.0, 1.0]]), bf([[0.0, 0.0]]), None, [a], 1.0)
-    assert y[0, 0] == 1.0 + 2.0 ** -7
     one = dict(A=bf([[1.0]]), B=bf([[2.0 ** -8]]), c=None, rank=1, alpha=1.0, strength=1.0, col_offset=0, n_cols=1)
+    y = ec.chain_multi(bf([[1.0]]), bf([[1.0]]), None, [dict(one, c=bf([2.0 ** -8]))], 1.0)
+    assert y[0, 0] == 1.0
+    assert lo.lora_linear_multi(bf([[1.0]]), bf([[1.0]]), None, [dict(one, c=bf([2.0 ** -8]))], 1.0)[0, 0] == \
+        1.0 + 2.0 ** -7
     y2 = ec.chain_multi(bf([[1.0]]), bf([[1.0]]), None, [one, dict(one)], 1.0)
     assert y2[0, 0] == 1.0
     assert lo.lora_linear_multi(bf([[1.0]]), bf([[1.0]]), None, [one, dict(one)], 1.0)[0, 0] == 1.0 + 2.0 ** -7
+    z = dict(A=bf([[1.0]]), B=bf([[0.0]]), c=bf([1.0]), rank=2, alpha=8.0, strength=0.5, col_offset=0, n_cols=1)
+    z["A"] = bf([[1.0], [1.0]])
+    z["B"] = bf([[0.0, 0.0]])
+    assert ec.chain_multi(bf([[1.0]]), bf([[0.0]]), None, [z], 0.75)[0, 0] == 0.375
+    assert lo.lora_linear_multi(bf([[1.0]]), bf([[0.0]]), None, [z], 0.75)[0, 0] == 0.375
 
 
 def test_multi_inactive_adapter_drops_its_bias():
