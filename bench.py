@@ -167,26 +167,17 @@ def main():
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
     # ---------------- base GEMM alone: own base-only path and torch F.linear (hipBLASLt)
-    def time_fn(fn, iters=10, warm=3):
-        for _ in range(warm):
-            fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(iters):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / iters
-
     base = []
     for L in layers:
         d = L["d"]
-        t_own = time_fn(lambda: call(L, lora=False))
-        t_torch = time_fn(lambda: torch.nn.functional.linear(d["x"], d["W"], d["b"]))
+        t_own = _launch_stats(torch, stream, lambda: call(L, lora=False), n=50)["median"]
+        t_torch = _launch_stats(torch, stream, lambda: torch.nn.functional.linear(d["x"], d["W"], d["b"]),
+                                n=50)["median"]
         base.append(dict(own_ms=t_own, torch_ms=t_torch, min_ms=min(t_own, t_torch)))
     base_ms = sum(b["min_ms"] for b in base)
     overhead = ms_per_step / base_ms - 1.0
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    probe = mfma_probe(torch, stream, cus)
 
     # ---------------- roofline of the dominant kernel: the fused GEMM (phase 2)
     # algorithmic FLOPs per launch 2 T (K N + r N); the producer (phase 1) is HBM-bound:
@@ -218,6 +209,7 @@ def main():
 
     # ---------------- every other workload: fused time, base time, roofline, oracle beside it
     layer_cfg = [{"in": L["K"], "out": L["N"], "rank": L["r"], "bias": L["d"]["b"] is not None} for L in layers]
+    layers_meta = [{"K": L["K"], "N": L["N"]} for L in layers]
     configs = None
     if not args.headline_only:
         del layers, L, d
@@ -226,21 +218,25 @@ def main():
         torch.cuda.empty_cache()
         configs["token_regimes"] = token_regimes(torch, dev, with_oracle=not args.no_cpu_baseline)
 
+    per_layer = [{"layer": f"{L['K']}->{L['N']}", "producer_ms": round(p_, 4), "gemm_ms": round(g_, 4),
+                  "base_own_ms": round(b_["own_ms"], 4), "base_hipblaslt_ms": round(b_["torch_ms"], 4)}
+                 for L, p_, g_, b_ in zip(layers_meta, prod_ms, gemm_ms, base)]
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "ffn_pair_tokens32760_rank64", "tokens": 32760,
-                   "layers": layer_cfg,
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s",
+        "overhead_vs_base": round(overhead, 4), "base_ms": round(base_ms, 4),
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "ffn_pair_tokens32760_rank64", "tokens": 32760, "layers": layer_cfg,
                    "alpha": 64.0, "strength": 1.0, "request_scale": 0.7, "quality": "lossless"},
-        "overhead_vs_base": round(overhead, 4),
-        "base_ms": round(base_ms, 4),
-        "base_detail": [{k: round(v, 4) for k, v in b.items()} for b in base],
+        "per_layer": per_layer,
         "pct_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "mfma_ceiling": probe,
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "configs": configs,
     }
+    if configs is not None:
+        # the other workloads: one JSON line of their own on stderr (stdout carries the headline only)
+        print(json.dumps({"configs": configs}), file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 
@@ -430,7 +426,8 @@ def config_sweep(torch, dev, stream, with_oracle=True):
         e = _gemm_entry(fl, fused, own, tor, byt)
         e["workload"] = f"stacked q/k/v: T={T} K={K} N=3x3072 r=3x128 bf16/{adapter}"
         if adapter == "f32":
-            e["note"] = "the adapter part runs on fp32 MFMA (157 TFLOP/s peak)"
+            e["note"] = ("the fp32 adapter products run on bf16 MFMA over a hi/lo bf16 split of the fp32 values "
+                         "(x.hi(A) + x.lo(A), then a rank-3r K-extension); about 2^-16 relative to fp32 products")
         if with_oracle:
             e["cpu_oracle"] = _oracle_time(lambda: _oracle_stacked(h, spec), fl)
         out["qkv_stacked_" + adapter] = e
@@ -712,7 +709,43 @@ def cpu_baseline(layers, target_s):
         dt, fl = run(rows)
     return {"value": float(f"{fl / dt / 1e12:.4g}"), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {rows} of 32760 tokens of both FFN layers, numpy float64, {dt:.1f}s",
-            "cpu": platform.processor() or platform.machine()}
+            "cpu": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def mfma_probe(torch, stream, cus):
+    """Matrix-core ceiling and shader clock under a pure MFMA load (lora_mfma_probe): one
+    workgroup of 4 waves per compute unit, ~0.2 s of back-to-back MFMAs; rate from HIP events,
+    clock from the shader-cycle / real-time counters of each workgroup."""
+    import rank_gemm_lora_amd as rg
+    sink = torch.empty(cus * 256, dtype=torch.float32, device="cuda")
+    clocks = torch.zeros(2 * cus, dtype=torch.int64, device="cuda")
+    iters = 1 << 16
+    sp = stream.cuda_stream
+    rg.lora_mfma_probe(1024, cus, sink.data_ptr(), clocks.data_ptr(), sp)  # warm-up
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    rg.lora_mfma_probe(iters, cus, sink.data_ptr(), clocks.data_ptr(), sp)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    flops = cus * 4 * iters * 8 * 16384.0
+    c = clocks.view(-1, 2).double().sum(0)
+    ghz = float(c[0] / (c[1] / 100e6)) / 1e9 if c[1] > 0 else None
+    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "clock_ghz": None if ghz is None else round(ghz, 3),
+            "ms": round(ms, 3), "what": "back-to-back v_mfma_f32_16x16x32_bf16, no memory traffic, 1 workgroup per CU"}
 
 
 if __name__ == "__main__":

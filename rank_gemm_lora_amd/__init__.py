@@ -29,7 +29,7 @@ __all__ = [
     "lora_linear_multi", "LoraAdapter", "lora_merge_apply", "lora_merge", "lora_linear_bwd",
     "lora_linear_bwd_workspace_size", "lora_linear_backward",
     "lora_status_string",
-    "lora_device_check", "lora_linear", "lora_linear_stacked", "lora_linear_nf4", "dense_patch",
+    "lora_device_check", "lora_mfma_probe", "lora_linear", "lora_linear_stacked", "lora_linear_nf4", "dense_patch",
     "LoraGroup", "hip_runtimes_mapped",
 ]
 
@@ -64,6 +64,8 @@ class LoraAdapter(ctypes.Structure):
 _lib.lora_linear_fwd.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _f64, _f64, _f64,
                                  _p, _i64, _i32, _i32, _p, _sz, _p]
 _lib.lora_linear_fwd.restype = ctypes.c_int
+_lib.lora_mfma_probe.argtypes = [_i64, _i32, _p, _p, _p]
+_lib.lora_mfma_probe.restype = ctypes.c_int
 _lib.lora_linear_fwd_phase.argtypes = [_i32, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _f64,
                                        _f64, _f64, _p, _i64, _i32, _i32, _p, _sz, _p]
 _lib.lora_linear_fwd_phase.restype = ctypes.c_int
@@ -191,6 +193,10 @@ def lora_status_string(status: int) -> str:
 
 def lora_device_check() -> int:
     return int(_lib.lora_device_check())
+
+
+def lora_mfma_probe(iters, blocks, sink, clocks, stream):
+    return _check(_lib.lora_mfma_probe(iters, blocks, sink, clocks, stream), "lora_mfma_probe")
 
 
 def hip_runtimes_mapped() -> list:

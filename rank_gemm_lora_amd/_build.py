@@ -32,6 +32,7 @@ SOURCES = {
     "backward.hip": [],
     "exact.hip": ["-ffp-contract=off"],
     "patch.hip": ["-ffp-contract=off"],
+    "probe.hip": [],
     "api.cpp": [],
 }
 

@@ -59,7 +59,6 @@ hipError_t transpose_pad_impl(const bf16_bits* src, int64_t ld, int64_t R, int64
 // half wave and token), transposes it in registers and writes 8 row pieces of P^T to LDS; the Q
 // slice (64 j x 64 tokens) is staged in LDS once for the 4 waves. Two LDS buffers, the next
 // step's loads in flight during the current step's MFMAs.
-constexpr int kTnI = 256, kTnJ = 64, kTnT = 64;
 
 // A staged slice in LDS: row = i (or j), 64 tokens = 128 bytes = 8 pieces of 16 bytes, the piece
 // index XOR-swizzled by bits 0-2 and 3-5 of the row: 8 lanes that write 8 rows 8 apart, or read 8
@@ -211,31 +210,6 @@ hipError_t transpose_pad(const uint16_t* src, int64_t ld, int64_t R, int64_t C, 
 // Token chunks of a contraction over T tokens with `tiles` workgroups per chunk: at most 512
 // workgroups (two per compute unit, all resident at once), chunks a multiple of 64 tokens and
 // of at least 256 tokens, at most 64 chunks.
-void tn_plan(int64_t T, int64_t tiles, int* S, int64_t* tchunk) {
-  if (T <= 0 || tiles <= 0) {  // nothing to contract
-    *S = 1;
-    *tchunk = kTnT;
-    return;
-  }
-  int64_t s = 512 / tiles;
-  const int64_t smax = (T + 255) / 256;
-  s = s < 1 ? 1 : (s > smax ? smax : s);
-  s = s > 64 ? 64 : s;
-  int64_t c = (T + s - 1) / s;
-  c = (c + kTnT - 1) / kTnT * kTnT;
-  *tchunk = c;
-  *S = static_cast<int>((T + c - 1) / c);
-}
-
-size_t tn_partial_bytes(int64_t T, int64_t M, int J, bool ones) {
-  const int jslices = (J + kTnJ - 1) / kTnJ;
-  const int Jt = J + (ones ? 16 : 0);
-  int S;
-  int64_t c;
-  tn_plan(T, ((M + kTnI - 1) / kTnI) * jslices, &S, &c);
-  return static_cast<size_t>(S) * static_cast<size_t>(M) * static_cast<size_t>(Jt) * 4;
-}
-
 hipError_t tn_contract(const bf16_bits* P, int64_t ldp, int64_t M, const bf16_bits* Qt, int64_t tpad, int J,
                        int64_t T, bool ones, float* part, float* out, int64_t ldo, int jvalid, bool transpose,
                        float* col_out, hipStream_t s) {

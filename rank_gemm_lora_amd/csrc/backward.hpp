@@ -9,10 +9,36 @@ namespace lora {
 hipError_t transpose_pad(const uint16_t* src, int64_t ld, int64_t R, int64_t C, uint16_t* dst, int64_t Rpad,
                          int64_t Cpad, hipStream_t s);
 
+// Token contractions (tn_kernel): kTnI rows of P per workgroup, kTnJ columns of Q per slice,
+// kTnT tokens per step.
+constexpr int kTnI = 256, kTnJ = 64, kTnT = 64;
+
 // Token chunks of a contraction over T tokens with `tiles` workgroups per chunk.
-void tn_plan(int64_t T, int64_t tiles, int* S, int64_t* tchunk);
+inline void tn_plan(int64_t T, int64_t tiles, int* S, int64_t* tchunk) {
+  if (T <= 0 || tiles <= 0) {  // nothing to contract
+    *S = 1;
+    *tchunk = kTnT;
+    return;
+  }
+  int64_t s = 512 / tiles;
+  const int64_t smax = (T + 255) / 256;
+  s = s < 1 ? 1 : (s > smax ? smax : s);
+  s = s > 64 ? 64 : s;
+  int64_t c = (T + s - 1) / s;
+  c = (c + kTnT - 1) / kTnT * kTnT;
+  *tchunk = c;
+  *S = static_cast<int>((T + c - 1) / c);
+}
+
 // fp32 partial sums of one contraction: P [T, M] against Q [T, J] (+ a column of ones).
-size_t tn_partial_bytes(int64_t T, int64_t M, int J, bool ones);
+inline size_t tn_partial_bytes(int64_t T, int64_t M, int J, bool ones) {
+  const int jslices = (J + kTnJ - 1) / kTnJ;
+  const int Jt = J + (ones ? 16 : 0);
+  int S;
+  int64_t c;
+  tn_plan(T, ((M + kTnI - 1) / kTnI) * jslices, &S, &c);
+  return static_cast<size_t>(S) * static_cast<size_t>(M) * static_cast<size_t>(Jt) * 4;
+}
 
 // Token padding of the transposed rank-wide operand Qt [J, tpad] (zeros past T).
 inline int64_t tn_tpad(int64_t T) { return (T + 63) / 64 * 64; }
