@@ -373,16 +373,16 @@ int lora_device_check(void);
 
 /*
  * lora_mfma_probe -- device measurement for reporting, not part of the layer.
- * Launches `blocks` workgroups of 4 waves, each issuing `iters` x 8 independent
- * v_mfma_f32_16x16x32_bf16 back to back (no memory traffic in the loop): the
+ * Launches `blocks` workgroups of 8 waves, each issuing `iters` x 64 (8 chains of
+ * 8) v_mfma_f32_16x16x32_bf16 back to back (no memory traffic in the loop): the
  * sustained matrix-core rate the device holds under a pure MFMA load, i.e. the
  * ceiling a GEMM reaches at the same clock (MI355X: 1024 dense bf16 FLOP per
  * SIMD per cycle). Per workgroup b, clocks[2b] receives the shader cycles of
  * its loop (s_memtime) and clocks[2b + 1] the 100 MHz real-time ticks
  * (s_memrealtime): their ratio times 100 MHz is the clock under that load.
- *   sink    float [blocks * 256] (device), written with sums that keep the loop
+ *   sink    float [blocks * 512] (device), written with sums that keep the loop
  *   clocks  uint64 [2 * blocks] (device)
- * FLOPs of one launch: blocks * 4 * iters * 8 * 16384. LORA_ERR_SHAPE for
+ * FLOPs of one launch: blocks * 8 * iters * 64 * 16384. LORA_ERR_SHAPE for
  * iters or blocks < 1, LORA_ERR_NULL_PTR / LORA_ERR_ALIGN for the buffers.
  */
 int lora_mfma_probe(int64_t iters, int32_t blocks, float* sink, uint64_t* clocks, void* stream);

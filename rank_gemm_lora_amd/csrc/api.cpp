@@ -277,6 +277,38 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+// Workspace of lora_linear_bwd: W^T (when dx is wanted), B^T, A^T, u~ (+ its producer's partial
+// sums), t~ (+ partial sums), the token contractions' partial sums; each region 256-byte aligned.
+struct BwdLayout {
+  size_t wt = 0, bt = 0, at = 0, ut = 0, upart = 0, tt = 0, tpart = 0, qt = 0, tn = 0, total = 0;
+  bool has_upart = false, has_tpart = false;
+};
+
+BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int64_t rp, bool want_dx) {
+  BwdLayout L;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off = round_up(off + n);
+    return o;
+  };
+  if (want_dx) L.wt = take(static_cast<size_t>(K) * N * 2);
+  L.bt = take(static_cast<size_t>(rp) * N * 2);
+  L.at = take(static_cast<size_t>(K) * rp * 2);
+  L.ut = take(static_cast<size_t>(T) * rp * 2);
+  const size_t up = lora::producer_partial_bytes(T, N, rp), tp = lora::producer_partial_bytes(T, K, rp);
+  L.has_upart = up > 0;
+  L.has_tpart = tp > 0;
+  if (up > 0) L.upart = take(up);
+  L.tt = take(static_cast<size_t>(T) * rp * 2);
+  if (tp > 0) L.tpart = take(tp);
+  L.qt = take(static_cast<size_t>(rp) * lora::tn_tpad(T) * 2);  // u~ or t~ transposed, one at a time
+  L.tn = take(std::max(lora::tn_partial_bytes(T, K, static_cast<int>(rp), false),
+                       lora::tn_partial_bytes(T, N, static_cast<int>(rp), true)));
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -371,38 +403,6 @@ int dense_patch_apply(void* dst, int32_t dst_dtype, const int64_t* dst_shape, in
                                                 static_cast<float>(strength), mode,
                                                 static_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
-}
-
-// Workspace of lora_linear_bwd: W^T (when dx is wanted), B^T, A^T, u~ (+ its producer's partial
-// sums), t~ (+ partial sums), the token contractions' partial sums; each region 256-byte aligned.
-struct BwdLayout {
-  size_t wt = 0, bt = 0, at = 0, ut = 0, upart = 0, tt = 0, tpart = 0, qt = 0, tn = 0, total = 0;
-  bool has_upart = false, has_tpart = false;
-};
-
-BwdLayout bwd_layout(int64_t T, int64_t K, int64_t N, int64_t rp, bool want_dx) {
-  BwdLayout L;
-  size_t off = 0;
-  auto take = [&](size_t n) {
-    const size_t o = off;
-    off = round_up(off + n);
-    return o;
-  };
-  if (want_dx) L.wt = take(static_cast<size_t>(K) * N * 2);
-  L.bt = take(static_cast<size_t>(rp) * N * 2);
-  L.at = take(static_cast<size_t>(K) * rp * 2);
-  L.ut = take(static_cast<size_t>(T) * rp * 2);
-  const size_t up = lora::producer_partial_bytes(T, N, rp), tp = lora::producer_partial_bytes(T, K, rp);
-  L.has_upart = up > 0;
-  L.has_tpart = tp > 0;
-  if (up > 0) L.upart = take(up);
-  L.tt = take(static_cast<size_t>(T) * rp * 2);
-  if (tp > 0) L.tpart = take(tp);
-  L.qt = take(static_cast<size_t>(rp) * lora::tn_tpad(T) * 2);  // u~ or t~ transposed, one at a time
-  L.tn = take(std::max(lora::tn_partial_bytes(T, K, static_cast<int>(rp), false),
-                       lora::tn_partial_bytes(T, N, static_cast<int>(rp), true)));
-  L.total = off;
-  return L;
 }
 
 int lora_merge_apply(void* W, int32_t w_dtype, int64_t N, int64_t K, const void* A, const void* B, int32_t rank,
@@ -549,12 +549,8 @@ size_t lora_linear_workspace_size(int64_t T, int64_t K, int64_t N, const int32_t
   if (T <= 0 || K <= 0 || N <= 0 || n_ranks < 0 || (n_ranks > 0 && ranks == nullptr) || !dtype_ok(adapter_dtype))
     return 0;
   int64_t cols = 0;
-  int n = 0;
   for (int i = 0; i < n_ranks; ++i)
-    if (ranks[i] > 0) {
-      cols += lora::rank_pad(ranks[i]);
-      ++n;
-    }
+    if (ranks[i] > 0) cols += lora::rank_pad(ranks[i]);
   // few tokens (lossless, bf16 activations): fp32 partial sums instead of the
   // intermediate; the activation dtype is not an argument, so the larger of the two.
   // A call takes the few-token layout when its ACTIVE adapters' padded ranks sum to at
