@@ -132,6 +132,32 @@ int lora_linear_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * lora_linear_fwd_noalloc -- lora_linear_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and results (bit for bit), and no allocation of any kind. The
+ * scratch those kernels need comes from one file-scope device array of
+ * LORA_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until the
+ * process ends; its device address is looked up (hipGetSymbolAddress) on the
+ * first call on each device.
+ *   LORA_ERR_UNSUPPORTED when the call would need more scratch than that, i.e.
+ *   when lora_linear_workspace_size(T, K, N, &rank, A || B ? 1 : 0,
+ *   adapter_dtype, quality) > LORA_NOALLOC_SCRATCH_BYTES; otherwise the status
+ *   of lora_linear_fwd.
+ * Every call on one GPU shares that GPU's array and leaves its contents behind:
+ * calls that can overlap in time on one GPU (different streams, or threads
+ * without ordering) race on it and must not be mixed; calls ordered on one
+ * stream are fine. No part of it needs to start at zero: each kernel writes
+ * every scratch element it reads.
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES (32ull * 1024ull * 1024ull)
+int lora_linear_fwd_noalloc(const void* x, int64_t T, int64_t K, int64_t ldx,
+                            const void* W, int64_t N, const void* bias,
+                            const void* A, const void* B, int32_t rank, int32_t adapter_dtype,
+                            double alpha, double strength, double request_scale,
+                            void* y, int64_t ldy, int32_t act_dtype, int32_t quality, void* stream);
+
+/*
  * lora_linear_fwd_phase -- lora_linear_fwd (lossless tier) with its two launches
  * selectable and the hot GEMM's output tile fixed by the caller, for callers
  * that schedule, time or compare the kernels of the path (SGLang PR #43501,

@@ -29,7 +29,7 @@ __all__ = [
     "lora_linear_multi", "LoraAdapter", "lora_merge_apply", "lora_merge", "lora_linear_bwd",
     "lora_linear_bwd_workspace_size", "lora_linear_backward",
     "lora_status_string",
-    "lora_device_check", "lora_mfma_probe", "lora_linear", "lora_linear_stacked", "lora_linear_nf4", "dense_patch",
+    "lora_device_check", "lora_mfma_probe", "lora_linear_fwd_noalloc", "LORA_NOALLOC_SCRATCH_BYTES", "lora_linear", "lora_linear_stacked", "lora_linear_nf4", "dense_patch",
     "LoraGroup", "hip_runtimes_mapped",
 ]
 
@@ -64,6 +64,10 @@ class LoraAdapter(ctypes.Structure):
 _lib.lora_linear_fwd.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _f64, _f64, _f64,
                                  _p, _i64, _i32, _i32, _p, _sz, _p]
 _lib.lora_linear_fwd.restype = ctypes.c_int
+_lib.lora_linear_fwd_noalloc.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _f64, _f64, _f64,
+                                         _p, _i64, _i32, _i32, _p]
+_lib.lora_linear_fwd_noalloc.restype = ctypes.c_int
+LORA_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
 _lib.lora_mfma_probe.argtypes = [_i64, _i32, _p, _p, _p]
 _lib.lora_mfma_probe.restype = ctypes.c_int
 _lib.lora_linear_fwd_phase.argtypes = [_i32, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _f64,
@@ -119,6 +123,13 @@ def lora_linear_fwd(x, T, K, ldx, W, N, bias, A, B, rank, adapter_dtype, alpha, 
     return _check(_lib.lora_linear_fwd(x, T, K, ldx, W, N, bias, A, B, rank, adapter_dtype, alpha, strength,
                                        request_scale, y, ldy, act_dtype, quality, workspace, workspace_bytes,
                                        stream), "lora_linear_fwd")
+
+
+def lora_linear_fwd_noalloc(x, T, K, ldx, W, N, bias, A, B, rank, adapter_dtype, alpha, strength, request_scale,
+                            y, ldy, act_dtype, quality, stream):
+    return _check(_lib.lora_linear_fwd_noalloc(x, T, K, ldx, W, N, bias, A, B, rank, adapter_dtype, alpha, strength,
+                                               request_scale, y, ldy, act_dtype, quality, stream),
+                  "lora_linear_fwd_noalloc")
 
 
 def lora_linear_fwd_phase(phase, gemm_tile, x, T, K, ldx, W, N, bias, A, B, rank, adapter_dtype, alpha, strength,

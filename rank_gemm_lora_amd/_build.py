@@ -33,6 +33,7 @@ SOURCES = {
     "exact.hip": ["-ffp-contract=off"],
     "patch.hip": ["-ffp-contract=off"],
     "probe.hip": [],
+    "noalloc.hip": [],
     "api.cpp": [],
 }
 
