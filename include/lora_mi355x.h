@@ -272,11 +272,11 @@ int lora_linear_multi_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
  * The weight element is W[n,k] = RN_bf16(RN_f32(codebook[code] * absmax[(n*K+k)/64]))
  * in both tiers. Activations, bias and y are bf16; the adapter is bf16 or fp32.
  *   workspace at least lora_linear_nf4_workspace_size(T, K, N, rank, adapter_dtype,
- *             quality) bytes. In the lossless tier with T >= 512 it includes a bf16
+ *             quality) bytes. In the lossless tier with T > 64 it includes a bf16
  *             copy of the dequantized weight ([N, K], rewritten by every call):
  *             dequantizing once per call is cheaper there than once per output
- *             tile. Below 512 tokens each output tile dequantizes its own weight
- *             stages in registers inside the GEMM.
+ *             tile. With T <= 64 (and in the fast tier) the weight is
+ *             dequantized inside the kernel that reads it.
  */
 int lora_linear_nf4_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
                         const uint8_t* codes, const float* absmax, const float* codebook,
@@ -376,7 +376,7 @@ size_t lora_linear_workspace_size(int64_t T, int64_t K, int64_t N, const int32_t
 /*
  * Workspace bytes of a lora_linear_nf4_fwd call: the adapter's share as
  * lora_linear_workspace_size (rank 0 = no adapter), plus, in the lossless tier
- * with T >= 512, the dequantized weight panel (N * K * 2 bytes, 256-byte aligned
+ * with T > 64, the dequantized weight panel (N * K * 2 bytes, 256-byte aligned
  * after the adapter's share). Returns 0 when T, K or N <= 0.
  */
 size_t lora_linear_nf4_workspace_size(int64_t T, int64_t K, int64_t N, int32_t rank, int32_t adapter_dtype,

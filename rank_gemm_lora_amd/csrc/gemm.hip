@@ -24,6 +24,8 @@
 // global->LDS directly by buffer_load ... lds (no VGPR round trip), double
 // buffered; out-of-range rows and K tails read as zero through the buffer
 // resource's range check.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -1276,7 +1278,10 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
 
   // stage t whose copies all belong to main stage t + 2 - NE, which is neither
   // past the last nor the K-tail stage
-  auto stage = [&](int t, int a) {
+  // (ext: the copies of this stage are K-extension units, issued through issue_load; a
+  // compile-time choice, so the main stages keep their precomputed-offset copies)
+  auto stage = [&](int t, int a, auto ext) {
+    constexpr bool EXT = decltype(ext)::value;
     const int b1 = a == 4 ? 0 : a + 1;           // W of stage t
     const int a2 = a >= 3 ? a - 3 : a + 2;       // x of stage t + 1
     const int b2 = a2 == 4 ? 0 : a2 + 1;         // W of stage t + 1
@@ -1295,7 +1300,10 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
       const int i = m / P::NJ, j = m % P::NJ;
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0].a[i], fr[0].b[j], acc[i][j], 0, 0, 0);
       if (m % RS == 0) read_frag(fr[1], m / RS, xs, ws, 1);
-      if (m % LS == LS / 2) ox.load_one(m / LS, xdst, xr, kb2);
+      if (m % LS == LS / 2) {
+        if constexpr (EXT) issue_load(2 * t + 4, m / LS);
+        else ox.load_one(m / LS, xdst, xr, kb2);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -1309,28 +1317,12 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
       } else if (m % RS == 1) {
         read_frag(fr[0], m / RS, xs2, ws2, 0);
       }
-      if (m % LS == LS / 2) ow.load_one(m / LS, wdst, wr, kb2);
+      if (m % LS == LS / 2) {
+        if constexpr (EXT) issue_load(2 * t + 5, m / LS);
+        else ow.load_one(m / LS, wdst, wr, kb2);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-  };
-
-  // The generic stage: same copies as a fast stage, issued in bulk, with
-  // compiler-scheduled MFMA steps (stages whose copies are K-extension units).
-  auto generic_stage = [&](int t, int a) {
-    const int b1 = a == 4 ? 0 : a + 1;
-    const int a2 = a >= 3 ? a - 3 : a + 2;
-    const int b2 = a2 == 4 ? 0 : a2 + 1;
-    const char* xs = smem + a * P::SLOT_BYTES;
-    const char* ws = smem + b1 * P::SLOT_BYTES;
-    for (int l = 0; l < NL; ++l) issue_load(2 * t + 4, l);
-    ring_frags16<P>(fr[1], xs, ws, 1, fo);
-    mfma_frags16<P>(acc, fr[0]);
-    if (2 * t + 4 < NU) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    stage_barrier();  // stage t + 1 landed and visible; every wave is done reading stage t
-    for (int l = 0; l < NL; ++l) issue_load(2 * t + 5, l);
-    ring_frags16<P>(fr[0], smem + a2 * P::SLOT_BYTES, smem + b2 * P::SLOT_BYTES, 0, fo);
-    mfma_frags16<P>(acc, fr[1]);
   };
 
   // The last stages: their copies (if any) are whole main units, one of them
@@ -1359,18 +1351,18 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
     mfma_frags16<P>(acc, fr[1]);
   };
 
-  // stages t < t_first copy K-extension units (generic path); stages from
-  // t_end on copy the last main units or nothing
-  const int t_first = NE > 2 ? NE - 2 : 0;
+  // stages t < NE - 2 copy K-extension units (stage t + 2); stages from t_end on
+  // copy the last main units or nothing
+  const int t_ext = NE > 2 ? NE - 2 : 0;
   const int t_end = NE + nk - 2 - (k_tail ? 1 : 0);
   int a = 0;  // slot of x of stage t
   int t = 0;
-  for (; t < t_first && t + 1 < NS; ++t) {
-    generic_stage(t, a);
+  for (; t < t_ext && t + 1 < NS; ++t) {
+    stage(t, a, std::true_type{});
     a = a >= 3 ? a - 3 : a + 2;
   }
   for (; t < t_end && t + 1 < NS; ++t) {
-    stage(t, a);
+    stage(t, a, std::false_type{});
     a = a >= 3 ? a - 3 : a + 2;
   }
   for (; t + 1 < NS; ++t) {
