@@ -285,6 +285,27 @@ def test_nf4_nibble_order_and_block_index_exhaustive():
     assert len(seen) == 32
 
 
+def test_nf4_unpack_codes_hand_written_bytes():
+    # byte j holds element 2j in bits 0-3 and element 2j+1 in bits 4-7
+    codes = np.array([[0x3A, 0xF0], [0x01, 0x9C]], np.uint8)
+    got = lo.nf4_unpack_codes(codes, 4)
+    assert got.tolist() == [[0xA, 0x3, 0x0, 0xF], [0x1, 0x0, 0xC, 0x9]]
+
+
+def test_rn_dispatches_to_the_named_rounding():
+    # bf16 keeps 8 significant bits (spacing 2^-7 in [1, 2), 2^-6 in [2, 4)), fp32 24; worked by hand:
+    # 1 + 2^-9: a quarter spacing above 1; 1 + 2^-8: a tie, to the even 1; 1 + 3 2^-8: a tie between
+    # 1 + 2^-7 (odd) and 1 + 2^-6 (even); -3 - 2^-7 - 2^-12: past the midpoint -3 - 2^-7, so away;
+    # 1 + 2^-30: below fp32's spacing 2^-23 at 1
+    # (the bf16 rounding takes fp32-representable values, as the chain produces them)
+    v = np.array([1.0 + 2.0 ** -9, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -3.0 - 2.0 ** -7 - 2.0 ** -12])
+    assert ec.rn(v, "bf16").tolist() == [1.0, 1.0, 1.0 + 2.0 ** -6, -3.015625]
+    assert ec.rn(v, "f32").tolist() == v.tolist()
+    assert ec.rn(np.array([1.0 + 2.0 ** -30]), "f32").tolist() == [1.0]
+    with pytest.raises(ValueError):
+        ec.rn(v, "f16")
+
+
 def test_nf4_weight_rounds_product_to_bf16():
     codes = torch.tensor([[0x10]], dtype=torch.uint8)  # element 0: code 0, element 1: code 1
     cb = torch.tensor([1.0 + 2.0 ** -8] + [1.0 + 2.0 ** -7 + 2.0 ** -8] + [0.0] * 14, dtype=torch.float32)
