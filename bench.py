@@ -612,21 +612,28 @@ def config_sweep(torch, dev, stream, with_oracle=True):
         outs = (torch.empty((T, K), dtype=torch.bfloat16, device=dev), torch.empty((r, K), device=dev),
                 torch.empty((N, r), device=dev), torch.empty((N,), device=dev))
         sp = stream.cuda_stream
+        # the forward call of the same layer (untimed): its workspace starts with t~ [T, rank_pad]
+        rp = -(-r // 64) * 64
+        fws = torch.empty(max(1, rg.lora_linear_workspace_size(T, K, N, [r], rg.LORA_BF16)), dtype=torch.uint8,
+                          device=dev)
+        rg.lora_linear(x, W, d2(h["b"]), A, B, spec.alpha, spec.strength, spec.request_scale, workspace=fws)
 
-        def bwd():
+        def bwd(t_tilde):
             rg.lora_linear_bwd(x.data_ptr(), T, K, K, W.data_ptr(), N, A.data_ptr(), B.data_ptr(), r, spec.alpha,
                                spec.strength, spec.request_scale, dy.data_ptr(), N, outs[0].data_ptr(), K,
-                               outs[1].data_ptr(), outs[2].data_ptr(), outs[3].data_ptr(), ws.data_ptr(), ws.numel(),
-                               sp)
-        ms = _launch_stats(torch, stream, bwd, n=30)
+                               outs[1].data_ptr(), outs[2].data_ptr(), outs[3].data_ptr(), t_tilde,
+                               rp if t_tilde else 0, ws.data_ptr(), ws.numel(), sp)
+        ms = _launch_stats(torch, stream, lambda: bwd(fws.data_ptr()), n=30)
+        ms_re = _launch_stats(torch, stream, lambda: bwd(None), n=30)
         tor = _launch_stats(torch, stream, lambda: torch.matmul(dy, W), n=30)["median"]
         fl = 2.0 * T * (N * K + 2 * N * r + 3 * r * K)
         byt = 2 * (2 * T * N + 2 * T * K + N * K + r * (N + K)) + 4 * (r * K + N * r + N)
         e = _gemm_entry(fl, ms, None, tor, byt)
-        e["workload"] = (f"backward (dx, dA, dB, db): T={T} K={K} N={N} r={r}; base = hipBLASLt dy.W (dx "
-                         f"without the adapter)")
+        e["workload"] = (f"backward (dx, dA, dB, db): T={T} K={K} N={N} r={r}, t~ taken from the forward call's "
+                         f"workspace; base = hipBLASLt dy.W (dx without the adapter)")
+        e["ms_recomputing_t"] = ms_re
         out[f"backward_{spec.name}"] = e
-        del x, W, A, B, dy, ws, outs
+        del x, W, A, B, dy, ws, outs, fws
     del up_h, down_h
     torch.cuda.empty_cache()
 

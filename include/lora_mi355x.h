@@ -344,12 +344,21 @@ int lora_merge_apply(void* W, int32_t w_dtype, int64_t N, int64_t K, const void*
  * Rounding: u~ = RN_bf16(s.u) and t~ = RN_bf16(s.x.A^T) as in the forward; dx = RN_bf16(dy.W + u~.A)
  * with one fp32 accumulator; dA = u~^T.x, dB = dy^T.t~ and db summed in fp32 over token chunks added in
  * a fixed order. T == 0 writes zero gradients.
+ *   t_tilde   optional bf16 [T, ldt] (device): t~ of these x, A and s as the forward computed it, its
+ *             first rank_pad(rank) columns read (rank_pad rounds the rank up to a multiple of 64;
+ *             columns past the rank hold zeros). A lossless lora_linear_fwd call with bf16
+ *             activations and adapter, T > 64 and this adapter alone leaves exactly that at the
+ *             start of its workspace, ldt = rank_pad(rank); its workspace must then be kept
+ *             unchanged until this call. Given, the backward does not read x a second time
+ *             to recompute t~ (the gradients are the same bits). NULL: t~ is recomputed.
+ *             ldt >= rank_pad(rank) when t_tilde is given (else LORA_ERR_SHAPE); t_tilde must not
+ *             overlap the outputs or the workspace (LORA_ERR_OVERLAP).
  *   workspace at least lora_linear_bwd_workspace_size(T, K, N, rank, dx != NULL) bytes
  */
 int lora_linear_bwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, int64_t N, const void* A,
                     const void* B, int32_t rank, double alpha, double strength, double request_scale, const void* dy,
-                    int64_t lddy, void* dx, int64_t lddx, float* dA, float* dB, float* db, void* workspace,
-                    size_t workspace_bytes, void* stream);
+                    int64_t lddy, void* dx, int64_t lddx, float* dA, float* dB, float* db, const void* t_tilde,
+                    int64_t ldt, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes of lora_linear_bwd (transposed copies, the rank-wide intermediates, partial sums). */
 size_t lora_linear_bwd_workspace_size(int64_t T, int64_t K, int64_t N, int32_t rank, int32_t want_dx);

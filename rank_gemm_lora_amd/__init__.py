@@ -90,7 +90,7 @@ _lib.lora_linear_multi_fwd.restype = ctypes.c_int
 _lib.lora_linear_multi_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(LoraAdapter), _i32, _i32, _i32]
 _lib.lora_linear_multi_workspace_size.restype = _sz
 _lib.lora_linear_bwd.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i32, _f64, _f64, _f64, _p, _i64, _p, _i64,
-                                 _p, _p, _p, _p, _sz, _p]
+                                 _p, _p, _p, _p, _i64, _p, _sz, _p]
 _lib.lora_linear_bwd.restype = ctypes.c_int
 _lib.lora_linear_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i32, _i32]
 _lib.lora_linear_bwd_workspace_size.restype = _sz
@@ -156,9 +156,10 @@ def lora_linear_multi_fwd(x, T, K, ldx, W, N, bias, adapters, n_adapters, adapte
 
 
 def lora_linear_bwd(x, T, K, ldx, W, N, A, B, rank, alpha, strength, request_scale, dy, lddy, dx, lddx, dA, dB, db,
-                    workspace, workspace_bytes, stream):
+                    t_tilde, ldt, workspace, workspace_bytes, stream):
     return _check(_lib.lora_linear_bwd(x, T, K, ldx, W, N, A, B, rank, alpha, strength, request_scale, dy, lddy, dx,
-                                       lddx, dA, dB, db, workspace, workspace_bytes, stream), "lora_linear_bwd")
+                                       lddx, dA, dB, db, t_tilde, ldt, workspace, workspace_bytes, stream),
+                  "lora_linear_bwd")
 
 
 def lora_linear_bwd_workspace_size(T, K, N, rank, want_dx=True) -> int:
@@ -350,9 +351,11 @@ def lora_merge(W, A, B, alpha, strength=1.0, quality="lossless", stream=None):
 
 
 def lora_linear_backward(x, W, A, B, dy, alpha, strength=1.0, request_scale=1.0, want=("dx", "dA", "dB", "db"),
-                         workspace=None, stream=None):
+                         workspace=None, stream=None, t_tilde=None):
     """Gradients of the LoRA linear for the output gradient ``dy``: returns (dx, dA, dB, db),
-    each None unless named in ``want`` (dx bf16; dA, dB, db fp32)."""
+    each None unless named in ``want`` (dx bf16; dA, dB, db fp32). ``t_tilde``: optional bf16
+    [T, ldt] tensor holding the forward's t~ (for instance a view of the forward call's
+    workspace), so that x is not read again to recompute it."""
     T, K = x.shape
     N = W.shape[0]
     r = A.shape[0]
@@ -364,9 +367,10 @@ def lora_linear_backward(x, W, A, B, dy, alpha, strength=1.0, request_scale=1.0,
     db = torch.empty((N,), dtype=torch.float32, device=dev) if "db" in want else None
     need = lora_linear_bwd_workspace_size(T, K, N, r, dx is not None)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    ldt = _row_major(t_tilde, "t_tilde") if t_tilde is not None else 0
     lora_linear_bwd(x.data_ptr(), T, K, ldx, W.data_ptr(), N, A.data_ptr(), B.data_ptr(), r, float(alpha),
                     float(strength), float(request_scale), dy.data_ptr(), lddy, _ptr(dx), K, _ptr(dA), _ptr(dB),
-                    _ptr(db), ws.data_ptr(), ws.numel(), _stream(stream))
+                    _ptr(db), _ptr(t_tilde), ldt, ws.data_ptr(), ws.numel(), _stream(stream))
     return dx, dA, dB, db
 
 

@@ -438,8 +438,8 @@ int lora_merge_apply(void* W, int32_t w_dtype, int64_t N, int64_t K, const void*
 
 int lora_linear_bwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, int64_t N, const void* A,
                     const void* B, int32_t rank, double alpha, double strength, double request_scale, const void* dy,
-                    int64_t lddy, void* dx, int64_t lddx, float* dA, float* dB, float* db, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    int64_t lddy, void* dx, int64_t lddx, float* dA, float* dB, float* db, const void* t_tilde,
+                    int64_t ldt, void* workspace, size_t workspace_bytes, void* stream) {
   if (T < 0 || K < 1 || N < 1 || ldx < K || lddy < N || (dx != nullptr && lddx < K)) return LORA_ERR_SHAPE;
   if (rank < 1) return LORA_ERR_SHAPE;
   if (rank > LORA_MAX_RANK || K * 4 > kMaxRowBytes || N * 4 > kMaxRowBytes || ldx * 2 > kMaxRowBytes ||
@@ -451,20 +451,24 @@ int lora_linear_bwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void
   if (A == nullptr || B == nullptr || (dx != nullptr && W == nullptr)) return LORA_ERR_NULL_PTR;
   if (T > 0 && (x == nullptr || dy == nullptr)) return LORA_ERR_NULL_PTR;
   if (!aligned(x, 16) || !aligned(W, 16) || !aligned(A, 16) || !aligned(B, 16) || !aligned(dy, 16) ||
-      !aligned(dx, 2) || !aligned(dA, 4) || !aligned(dB, 4) || !aligned(db, 4) || !aligned(workspace, 16))
+      !aligned(dx, 2) || !aligned(dA, 4) || !aligned(dB, 4) || !aligned(db, 4) || !aligned(workspace, 16) ||
+      !aligned(t_tilde, 2))
     return LORA_ERR_ALIGN;
   if (K % 8 != 0 || N % 8 != 0 || ldx % 8 != 0 || lddy % 8 != 0) return LORA_ERR_ALIGN;
   const int64_t rp = lora::rank_pad(rank);
+  if (t_tilde != nullptr && (ldt < rp || ldt * 2 > kMaxRowBytes)) return LORA_ERR_SHAPE;
   const BwdLayout L = T > 0 ? bwd_layout(T, K, N, rp, dx != nullptr) : BwdLayout{};
   const size_t need = L.total;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LORA_ERR_WORKSPACE;
   // outputs must not overlap the inputs, the workspace or each other
   const Span outs[4] = {span2d(dx, T, lddx, K, 2), span2d(dA, 1, rank * K, rank * K, 4),
                         span2d(dB, 1, N * rank, N * rank, 4), span2d(db, 1, N, N, 4)};
-  const Span ins[6] = {span2d(x, T, ldx, K, 2), span2d(W, N, K, K, 2), span2d(A, rank, K, K, 2),
-                       span2d(B, N, rank, rank, 2), span2d(dy, T, lddy, N, 2),
-                       need ? Span{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need}
-                            : Span{}};
+  const Span wsp =
+      need ? Span{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need} : Span{};
+  const Span tts = t_tilde != nullptr ? span2d(t_tilde, T, ldt, rp, 2) : Span{};
+  const Span ins[7] = {span2d(x, T, ldx, K, 2), span2d(W, N, K, K, 2), span2d(A, rank, K, K, 2),
+                       span2d(B, N, rank, rank, 2), span2d(dy, T, lddy, N, 2), wsp, tts};
+  if (overlaps(tts, wsp)) return LORA_ERR_OVERLAP;
   for (int i = 0; i < 4; ++i) {
     for (const Span& in : ins)
       if (overlaps(outs[i], in)) return LORA_ERR_OVERLAP;
@@ -514,7 +518,11 @@ int lora_linear_bwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void
   g2.t_col = 0; g2.scale = s32;
   p2.work = ws + L.tt; p2.ldt = rp;
   if (L.has_tpart) p2.tpart = reinterpret_cast<float*>(ws + L.tpart);
-  if (dB != nullptr || db != nullptr) {
+  // (the caller's copy of t~ from the forward, when given: the same bits, without a second read of x)
+  const uint16_t* tt = t_tilde != nullptr ? static_cast<const uint16_t*>(t_tilde)
+                                          : reinterpret_cast<const uint16_t*>(ws + L.tt);
+  const int64_t ldtt = t_tilde != nullptr ? ldt : rp;
+  if ((dB != nullptr || db != nullptr) && t_tilde == nullptr) {
     e = lora::launch_lossless(p2, st, 1);
     if (e != hipSuccess) return LORA_ERR_HIP;
   }
@@ -530,7 +538,7 @@ int lora_linear_bwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void
     if (e != hipSuccess) return LORA_ERR_HIP;
   }
   if (dB != nullptr || db != nullptr) {  // dB = dy^T t~ and db = column sums of dy
-    e = lora::transpose_pad(reinterpret_cast<const uint16_t*>(ws + L.tt), rp, T, rp, qt, tpad, rp, st);
+    e = lora::transpose_pad(tt, ldtt, T, rp, qt, tpad, rp, st);
     if (e == hipSuccess)
       e = lora::tn_contract(static_cast<const uint16_t*>(dy), lddy, N, qt, tpad, J, T, db != nullptr, part, dB, rank,
                             dB != nullptr ? rank : 0, false, db, st);

@@ -186,12 +186,17 @@ void test_nf4_patch_merge_bwd() {
     const size_t need = lora_linear_bwd_workspace_size(700, 256, 520, 24, want_dx);
     stub::rec.ws_hi = stub::rec.ws_lo + need;
     EXPECT(lora_linear_bwd(X, 700, 256, 256, W, 520, A, B, 24, 48.0, 0.8, 0.7, BIAS, 520, want_dx ? Y : nullptr, 256,
-                           dA, dB, db, WS, need, nullptr) == LORA_ERR_HIP);
+                           dA, dB, db, nullptr, 0, WS, need, nullptr) == LORA_ERR_HIP);
     EXPECT(lora_linear_bwd(X, 700, 256, 256, W, 520, A, B, 24, 48.0, 0.8, 0.7, BIAS, 520, want_dx ? Y : nullptr, 256,
-                           dA, dB, db, WS, need - 1, nullptr) == LORA_ERR_WORKSPACE);
+                           dA, dB, db, nullptr, 0, WS, need - 1, nullptr) == LORA_ERR_WORKSPACE);
+    // the forward's t~ given (rank 24 pads to 64 columns): the same launches without its producer
+    EXPECT(lora_linear_bwd(X, 700, 256, 256, W, 520, A, B, 24, 48.0, 0.8, 0.7, BIAS, 520, want_dx ? Y : nullptr, 256,
+                           dA, dB, db, at(12), 64, WS, need, nullptr) == LORA_ERR_HIP);
+    EXPECT(lora_linear_bwd(X, 700, 256, 256, W, 520, A, B, 24, 48.0, 0.8, 0.7, BIAS, 520, want_dx ? Y : nullptr, 256,
+                           dA, dB, db, at(12), 63, WS, need, nullptr) == LORA_ERR_SHAPE);
   }
-  EXPECT(lora_linear_bwd(X, 700, 256, 256, W, 520, A, B, 24, 48.0, 0.8, 0.7, BIAS, 520, Y, 256, dA, dA, db, WS, big,
-                         nullptr) == LORA_ERR_OVERLAP);
+  EXPECT(lora_linear_bwd(X, 700, 256, 256, W, 520, A, B, 24, 48.0, 0.8, 0.7, BIAS, 520, Y, 256, dA, dA, db, nullptr, 0,
+                         WS, big, nullptr) == LORA_ERR_OVERLAP);
 }
 
 // Random valid calls: sized by the documented query, every call passes the workspace

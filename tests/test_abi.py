@@ -333,11 +333,21 @@ def test_product_path_never_touches_the_oracle():
 
 def bwd(**kw):
     a = dict(x=X, T=0, K=128, ldx=128, W=W, N=96, A=A, B=B, rank=8, alpha=8.0, dy=Y, lddy=96, dx=BIAS, lddx=128,
-             dA=WSP + 0x1000_0000, dB=WSP + 0x2000_0000, db=WSP + 0x3000_0000)
+             dA=WSP + 0x1000_0000, dB=WSP + 0x2000_0000, db=WSP + 0x3000_0000, tt=None, ldt=0)
     a.update(kw)
     return rg._lib.lora_linear_bwd(a["x"], a["T"], a["K"], a["ldx"], a["W"], a["N"], a["A"], a["B"], a["rank"],
                                    a["alpha"], 1.0, 1.0, a["dy"], a["lddy"], a["dx"], a["lddx"], a["dA"], a["dB"],
-                                   a["db"], WSP, 1 << 30, None)
+                                   a["db"], a["tt"], a["ldt"], WSP, 1 << 30, None)
+
+
+def test_backward_forward_t_validation():
+    # (T = 0: validation only, nothing launched; rank 8 pads to 64 columns of t~)
+    tt = WSP + 0x4000_0000
+    assert bwd(dA=None, dB=None, db=None, dx=None, tt=tt, ldt=64) == OK
+    assert bwd(dA=None, dB=None, db=None, dx=None, tt=tt, ldt=63) == SHAPE      # fewer columns than the padded rank
+    assert bwd(dA=None, dB=None, db=None, dx=None, tt=tt + 1, ldt=64) == ALIGN  # not bf16-aligned
+    assert bwd(T=4, dA=None, dB=None, db=tt, dx=None, tt=tt, ldt=64) == OVERLAP  # an output over t~
+    assert bwd(T=4, dA=None, dB=None, db=None, dx=None, tt=WSP, ldt=64) == OVERLAP  # t~ inside the workspace
 
 
 def test_backward_validation():

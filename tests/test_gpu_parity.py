@@ -637,6 +637,26 @@ def test_backward(T, K, N, r):
     assert torch.equal(y, dx)
 
 
+@pytest.mark.parametrize("T,K,N,r", [(300, 256, 520, 24), (513, 384, 768, 64), (700, 512, 392, 200)])
+def test_backward_with_the_forward_t_is_the_same_bits(T, K, N, r):
+    """t~ handed over from the forward call's workspace gives the gradients the backward computes
+    when it recomputes t~ itself, bit for bit."""
+    d = lw.small_linear_inputs(T, K, N, r, 300 + r, bias=True, alpha=2.0 * r, strength=0.8, request_scale=0.7)
+    rng = np.random.default_rng(400 + r)
+    dy = dev(lw.to_dtype(rng.standard_normal((T, N)), "bf16"))
+    x, W, A, B = dev(d["x"]), dev(d["W"]), dev(d["A"]), dev(d["B"])
+    say(f"case backward with the forward t~ T={T} K={K} N={N} r={r}")
+    rp = -(-r // 64) * 64
+    ws = torch.empty(rg.lora_linear_workspace_size(T, K, N, [r], rg.LORA_BF16), dtype=torch.uint8, device=DEV)
+    rg.lora_linear(x, W, dev(d["b"]), A, B, d["alpha"], 0.8, 0.7, workspace=ws)
+    tt = ws[:T * rp * 2].view(torch.bfloat16).view(T, rp)
+    got = rg.lora_linear_backward(x, W, A, B, dy, d["alpha"], 0.8, 0.7, t_tilde=tt)
+    want = rg.lora_linear_backward(x, W, A, B, dy, d["alpha"], 0.8, 0.7)
+    torch.cuda.synchronize()
+    for name, g, w in zip(("dx", "dA", "dB", "db"), got, want):
+        assert torch.equal(g, w), name
+
+
 def test_backward_partial_outputs_and_empty_batch():
     d = lw.small_linear_inputs(300, 256, 520, 24, 150, bias=False, alpha=48.0)
     rng = np.random.default_rng(151)
