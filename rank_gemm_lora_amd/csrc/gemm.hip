@@ -598,36 +598,6 @@ struct TileOffsets {
     const int slot0 = (it * P::WAVES + wave) * 64;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + slot0 * 16), 16, v[it], kb0, 0, 0);
   }
-  // The same with the row's bytes at or past kb_valid reading as zero; c16 is
-  // the lane's chunk offset (chunk_bytes()), the same in every instruction.
-  __device__ __forceinline__ void load_one_masked(int it, char* lds, __amdgpu_buffer_rsrc_t rsrc, int kb0,
-                                                  int kb_valid, int c16) const {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int slot0 = (it * P::WAVES + wave) * 64;
-    const uint32_t voff = kb0 + c16 < kb_valid ? v[it] : 0x80000000u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + slot0 * 16), 16, voff, kb0, 0, 0);
-  }
-  // Byte offset of this lane's 16-byte chunk within its staged row (when it is
-  // the same in every copy instruction).
-  __device__ __forceinline__ static int chunk_bytes() {
-    static_assert((P::WAVES * 64 / P::CPR / P::RPL) % P::CPR == 0, "chunk differs between instructions");
-    const int lane = opaque_int(threadIdx.x & 63);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    return ((lane % P::CPR) ^ (((wave * 64 + lane) / P::CPR / P::RPL) % P::CPR)) * 16;
-  }
-  // The same instruction for the stage holding the K tail: chunks at or past
-  // kb_valid read as zero.
-  __device__ __forceinline__ void load_one_tail(int it, char* lds, __amdgpu_buffer_rsrc_t rsrc, int kb0,
-                                                int kb_valid) const {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int slot0 = (it * P::WAVES + wave) * 64;
-    const int sl = slot0 + lane;
-    const int row = sl / P::CPR;
-    const int c = (sl % P::CPR) ^ ((row / P::RPL) % P::CPR);
-    const uint32_t voff = kb0 + c * 16 < kb_valid ? v[it] : 0x80000000u;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + slot0 * 16), 16, voff, kb0, 0, 0);
-  }
   // Copy the stage at byte offset kb0 into lds. With a K tail, chunks at or past
   // kb_valid are redirected out of range as well.
   __device__ __forceinline__ void load(char* lds, __amdgpu_buffer_rsrc_t rsrc, int kb0, bool tail, int kb_valid) const {
