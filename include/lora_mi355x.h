@@ -193,6 +193,11 @@ int lora_linear_fwd_phase(int32_t phase, int32_t gemm_tile, const void* x, int64
  * LORA_MAX_GROUPS adapters, each added to its own column range of y
  * (SGLang PR #43501, Modifications: stacked q/k/v or gate/up adapters, one
  * update per group on column views of the output).
+ * The result equals one lora_linear_fwd call per group on column views of y, bit
+ * for bit, in the exact tier, at T <= 64, and wherever at most two groups meet any
+ * 256-column block of y (groups of 256 columns or more, as q/k/v and gate/up have).
+ * With more groups per block the lossless result meets the same accuracy bar but
+ * may differ in the last bit (the extension is accumulated in another order).
  *
  *   groups    HOST array of n_groups lora_group (0 <= n_groups <= LORA_MAX_GROUPS);
  *             the A/B pointers inside are device pointers
