@@ -1398,10 +1398,18 @@ template __global__ void gemm_flow16_kernel<Flow16SCfg>(LinearProblem, int, int)
 
 hipError_t launch(const LinearProblem& p, hipStream_t s) {
   if (max_groups_per_tile(p, Flow16Cfg::BN) <= 2) {
-    // the 128 x 128 tile when the 256 x 256 tiles fill less than three quarters of the
-    // compute units (or when asked for); both give the same bits
-    const int64_t tiles = ((p.T + 255) / 256) * ((p.N + 255) / 256);
-    const bool small = p.tile == 2 || (p.tile == 0 && 4 * tiles < 3 * static_cast<int64_t>(device_cus()));
+    // The output tile (both give the same bits): 256 x 256, one workgroup per CU, or 128 x 128,
+    // two per CU. The larger does more MFMA work per LDS byte; the smaller ran at 0.77-0.92 of
+    // its rate on MI355X (1536- and 8960-wide inputs) but fills the last wave of tiles better.
+    // The smaller is taken when its wave fill, discounted by 0.85, beats the larger's (or when
+    // asked for).
+    const int64_t cus = device_cus();
+    auto fill = [](int64_t n, int64_t slots) {  // share of the workgroup slots of all waves in use
+      return static_cast<double>(n) / static_cast<double>((n + slots - 1) / slots * slots);
+    };
+    const int64_t t256 = ((p.T + 255) / 256) * ((p.N + 255) / 256);
+    const int64_t t128 = ((p.T + 127) / 128) * ((p.N + 127) / 128);
+    const bool small = p.tile == 2 || (p.tile == 0 && cus > 0 && 0.85 * fill(t128, 2 * cus) > fill(t256, cus));
     return small ? launch_flow16<Flow16SCfg>(p, s) : launch_flow16<Flow16Cfg>(p, s);
   }
   using P = HotCfg;
