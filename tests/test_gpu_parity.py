@@ -367,6 +367,42 @@ def test_few_tokens_fp32_adapter(T, K, N, r):
     assert_gate(run_linear(d, "lossless"), y64, yc, what="few-token lossless f32-adapter")
 
 
+@pytest.mark.parametrize("T,K,N,r", [(300, 200, 520, 24), (129, 264, 300, 64), (513, 64, 1000, 128)])
+def test_fp32_layer_multi_tile(T, K, N, r):
+    """fp32 activations and adapter over several ragged output tiles (the tiny fp32 layer is one
+    tile): fp32 output within 1e-6 relative RMS of fp64 (fp32 accumulation over K <= 264 terms
+    stays under it), exact tier bit for bit with the chain."""
+    d = lw.small_linear_inputs(T, K, N, r, 31 + r, act="f32", adapter="f32", bias=True, alpha=2.0 * r,
+                               strength=0.8, request_scale=0.7)
+    say(f"case fp32 layer T={T} K={K} N={N} r={r}")
+    y64, yc = oracle_pair(d, "f32", "f32")
+    y = run_linear(d, "lossless")
+    e = lo.rel_rms(host64(y), y64)
+    say(f"  lossless rel_rms {e:.3e}")
+    assert y.dtype == torch.float32 and e <= LOSSLESS_F32_GATE
+    ye = run_linear(d, "exact")
+    assert_bitwise(ye, yc, "fp32 layer exact")
+
+
+@pytest.mark.parametrize("T,K,N,r", [(300, 200, 520, 24), (20, 512, 300, 64), (300, 2048, 520, 32)])
+def test_strided_input_rows_equal_contiguous(T, K, N, r):
+    """x as a column view of a wider tensor (row stride ldx > K, 16-byte aligned start): the same
+    bits as the contiguous input, in both tiers (hot kernel; few-token path; producer K split)."""
+    d = lw.small_linear_inputs(T, K, N, r, 51 + r, bias=True, alpha=2.0 * r, strength=0.8, request_scale=0.7)
+    say(f"case strided x T={T} K={K} N={N} r={r}")
+    x = dev(d["x"])
+    wide = torch.full((T, K + 40), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wide[:, 16:16 + K] = x
+    xv = wide[:, 16:16 + K]
+    assert xv.stride(0) == K + 40 and xv.data_ptr() % 16 == 0
+    W, b, A, B = dev(d["W"]), dev(d["b"]), dev(d["A"]), dev(d["B"])
+    for q in ("lossless", "exact"):
+        want = rg.lora_linear(x, W, b, A, B, d["alpha"], 0.8, 0.7, quality=q)
+        got = rg.lora_linear(xv, W, b, A, B, d["alpha"], 0.8, 0.7, quality=q)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want), q
+
+
 # ------------------------------------------------------------------ stacked groups
 
 def _stacked_inputs(seed, adapter="bf16", bias=True, T=300):
