@@ -68,8 +68,8 @@ def main():
         write_traffic(args.write_traffic)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build runs the layer on a single MI355X "
-              "(token-parallel sharding needs no collective; see the design notes). Use --gpus 1.",
+        print("bench.py measures one GPU: the library runs a layer on a single MI355X "
+              "(token-parallel sharding of a layer needs no collective). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
