@@ -476,11 +476,11 @@ int lora_linear_bwd(const void* x, int64_t T, int64_t K, int64_t ldx, const void
       if (overlaps(outs[i], outs[j])) return LORA_ERR_OVERLAP;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (T == 0) {  // an empty batch: zero gradients
+  if (T == 0) {  // an empty batch: zero gradients (by kernels: the call may be captured in a graph)
     hipError_t e = hipSuccess;
-    if (dA != nullptr) e = hipMemsetAsync(dA, 0, static_cast<size_t>(rank) * K * 4, st);
-    if (e == hipSuccess && dB != nullptr) e = hipMemsetAsync(dB, 0, static_cast<size_t>(N) * rank * 4, st);
-    if (e == hipSuccess && db != nullptr) e = hipMemsetAsync(db, 0, static_cast<size_t>(N) * 4, st);
+    if (dA != nullptr) e = lora::zero_fill(dA, static_cast<int64_t>(rank) * K, st);
+    if (e == hipSuccess && dB != nullptr) e = lora::zero_fill(dB, N * static_cast<int64_t>(rank), st);
+    if (e == hipSuccess && db != nullptr) e = lora::zero_fill(db, N, st);
     return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   }
   char* ws = static_cast<char*>(workspace);

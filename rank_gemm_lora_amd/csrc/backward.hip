@@ -200,7 +200,20 @@ __global__ __launch_bounds__(256) void tn_reduce_kernel(const float* __restrict_
   else out[i * ldo + j] = v;
 }
 
+__global__ __launch_bounds__(256) void zero_fill_kernel(float* __restrict__ dst, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = 0.f;
+}
+
 }  // namespace
+
+hipError_t zero_fill(float* dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<unsigned>(blocks < 1024 ? blocks : 1024)), dim3(256), 0, s,
+                     dst, n);
+  return hipGetLastError();
+}
 
 hipError_t transpose_pad(const uint16_t* src, int64_t ld, int64_t R, int64_t C, uint16_t* dst, int64_t Rpad,
                          int64_t Cpad, hipStream_t s) {

@@ -9,6 +9,9 @@ namespace lora {
 hipError_t transpose_pad(const uint16_t* src, int64_t ld, int64_t R, int64_t C, uint16_t* dst, int64_t Rpad,
                          int64_t Cpad, hipStream_t s);
 
+// dst[0 .. n) = 0.0f by a kernel (a memset node in a captured HIP graph is avoided).
+hipError_t zero_fill(float* dst, int64_t n, hipStream_t s);
+
 // Token contractions (tn_kernel): kTnI rows of P per workgroup, kTnJ columns of Q per slice,
 // kTnT tokens per step.
 constexpr int kTnI = 256, kTnJ = 64, kTnT = 64;

@@ -98,6 +98,10 @@ hipError_t launch_dense_patch(void*, Elt, const void*, Elt, int64_t, float, int,
   ++stub::rec.patch;
   return hipErrorInvalidValue;
 }
+hipError_t zero_fill(float*, int64_t, hipStream_t) {  // (fills a gradient output, not the workspace)
+  ++stub::rec.bwd;
+  return hipSuccess;
+}
 hipError_t transpose_pad(const uint16_t*, int64_t, int64_t, int64_t, uint16_t* dst, int64_t Rpad, int64_t Cpad,
                          hipStream_t) {
   ++stub::rec.bwd;
