@@ -70,6 +70,11 @@ typedef enum { LORA_F32 = 0, LORA_BF16 = 1 } lora_dtype;
 /* Quality tier; LORA_LOSSLESS is the default (SGLang PR #43501, Modifications). */
 typedef enum { LORA_LOSSLESS = 0, LORA_EXACT = 1 } lora_quality;
 
+/* Where a lossless 4-bit call with more than 64 tokens dequantizes its weight
+ * (lora_linear_nf4_fwd_ex): chosen from the shape, once per call into a bf16
+ * panel, or inside the GEMM (Unsloth fast-LoRA chapter, section 3). */
+typedef enum { LORA_NF4_AUTO = 0, LORA_NF4_PANEL = 1, LORA_NF4_IN_GEMM = 2 } lora_nf4_dequant;
+
 /* Dense payloads (FastVideo lora_patch page):
  * LORA_PATCH_ADD     -- .diff / .diff_b  (DenseLoRAPatch.apply_to)
  * LORA_PATCH_REPLACE -- .set_weight      (DenseLoRAPatch.replacement_for) */
@@ -277,11 +282,12 @@ int lora_linear_multi_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
  * The weight element is W[n,k] = RN_bf16(RN_f32(codebook[code] * absmax[(n*K+k)/64]))
  * in both tiers. Activations, bias and y are bf16; the adapter is bf16 or fp32.
  *   workspace at least lora_linear_nf4_workspace_size(T, K, N, rank, adapter_dtype,
- *             quality) bytes. In the lossless tier with T > 64 it includes a bf16
- *             copy of the dequantized weight ([N, K], rewritten by every call):
- *             dequantizing once per call is cheaper there than once per output
- *             tile. With T <= 64 (and in the fast tier) the weight is
- *             dequantized inside the kernel that reads it.
+ *             quality) bytes. In the lossless tier with T > 64 it includes room for
+ *             a bf16 copy of the dequantized weight ([N, K], rewritten by every
+ *             call that uses it): above 256 tokens dequantizing once per call is
+ *             cheaper than once per output tile. Up to 256 tokens (and in the
+ *             exact tier) the weight is dequantized inside the kernel that reads
+ *             it; lora_linear_nf4_fwd_ex names the choice.
  */
 int lora_linear_nf4_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
                         const uint8_t* codes, const float* absmax, const float* codebook,
@@ -290,6 +296,33 @@ int lora_linear_nf4_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
                         double alpha, double strength, double request_scale,
                         void* y, int64_t ldy, int32_t quality,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lora_linear_nf4_fwd_ex -- lora_linear_nf4_fwd with the place of the
+ * dequantization named (Unsloth fast-LoRA chapter, section 3: dequantizing the
+ * whole weight into a temporary per forward, against doing it where the GEMM
+ * reads it). Lossless tier, T > 64 (below that the few-token kernel dequantizes
+ * in registers whatever is asked; the exact tier ignores the argument):
+ *   LORA_NF4_PANEL    once per call into a bf16 copy of the weight in the
+ *                     workspace, then the bf16 GEMM over it
+ *   LORA_NF4_IN_GEMM  inside the GEMM: each output tile of 128 tokens turns the
+ *                     codes of its 128 weight rows into bf16 in registers and
+ *                     LDS; needs a bf16 adapter whose rank is a multiple of 8
+ *                     (or no adapter), LORA_ERR_UNSUPPORTED otherwise
+ *   LORA_NF4_AUTO     what lora_linear_nf4_fwd does: the GEMM form up to 256
+ *                     tokens (where it measured faster on MI355X), the panel above
+ * Both forms give the same weight, RN_bf16(RN_f32(codebook[code] * absmax)),
+ * and the same output bits. Other values: LORA_ERR_UNSUPPORTED.
+ * lora_linear_nf4_workspace_size covers every choice; the in-GEMM form needs only
+ * lora_linear_workspace_size(T, K, N, &rank, 1, adapter_dtype, quality) bytes.
+ */
+int lora_linear_nf4_fwd_ex(const void* x, int64_t T, int64_t K, int64_t ldx,
+                           const uint8_t* codes, const float* absmax, const float* codebook,
+                           int32_t blocksize, int64_t N, const void* bias,
+                           const void* A, const void* B, int32_t rank, int32_t adapter_dtype,
+                           double alpha, double strength, double request_scale,
+                           void* y, int64_t ldy, int32_t quality, int32_t dequant,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * dense_patch_apply -- dense payloads of an adapter, applied in place

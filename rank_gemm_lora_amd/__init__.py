@@ -7,7 +7,8 @@ stream), nothing else. There is no CPU fallback: importing this package
 without the built library raises.
 
 Low-level functions carry the C names and take plain integers for pointers:
-``lora_linear_fwd``, ``lora_linear_stacked_fwd``, ``lora_linear_nf4_fwd``,
+``lora_linear_fwd``, ``lora_linear_stacked_fwd``, ``lora_linear_nf4_fwd`` (and
+``lora_linear_nf4_fwd_ex``, which names where the 4-bit weight is dequantized),
 ``dense_patch_apply``, ``lora_linear_workspace_size``, ``lora_status_string``,
 ``lora_device_check``. Tensor-level helpers (``lora_linear``,
 ``lora_linear_stacked``, ``lora_linear_nf4``, ``dense_patch``) check that the
@@ -24,7 +25,8 @@ import torch  # loads the HIP runtime this library binds to (one runtime per pro
 __all__ = [
     "LIB_PATH", "LoraError", "LORA_F32", "LORA_BF16", "LORA_LOSSLESS", "LORA_EXACT",
     "LORA_PATCH_ADD", "LORA_PATCH_REPLACE", "lora_linear_fwd", "lora_linear_stacked_fwd",
-    "lora_linear_nf4_fwd", "dense_patch_apply", "lora_linear_fwd_phase", "lora_linear_workspace_size",
+    "lora_linear_nf4_fwd", "lora_linear_nf4_fwd_ex", "LORA_NF4_AUTO", "LORA_NF4_PANEL", "LORA_NF4_IN_GEMM",
+    "dense_patch_apply", "lora_linear_fwd_phase", "lora_linear_workspace_size",
     "lora_linear_nf4_workspace_size", "lora_linear_multi_fwd", "lora_linear_multi_workspace_size",
     "lora_linear_multi", "LoraAdapter", "lora_merge_apply", "lora_merge", "lora_linear_bwd",
     "lora_linear_bwd_workspace_size", "lora_linear_backward",
@@ -38,6 +40,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblora_mi3
 LORA_F32, LORA_BF16 = 0, 1
 LORA_LOSSLESS, LORA_EXACT = 0, 1
 LORA_PATCH_ADD, LORA_PATCH_REPLACE = 0, 1
+LORA_NF4_AUTO, LORA_NF4_PANEL, LORA_NF4_IN_GEMM = 0, 1, 2
+_DEQUANT = {"auto": LORA_NF4_AUTO, "panel": LORA_NF4_PANEL, "in_gemm": LORA_NF4_IN_GEMM}
 _QUALITY = {"lossless": LORA_LOSSLESS, "exact": LORA_EXACT}
 _MODE = {"add": LORA_PATCH_ADD, "replace": LORA_PATCH_REPLACE}
 
@@ -79,6 +83,9 @@ _lib.lora_linear_stacked_fwd.restype = ctypes.c_int
 _lib.lora_linear_nf4_fwd.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p, _i32, _i64, _p, _p, _p, _i32, _i32,
                                      _f64, _f64, _f64, _p, _i64, _i32, _p, _sz, _p]
 _lib.lora_linear_nf4_fwd.restype = ctypes.c_int
+_lib.lora_linear_nf4_fwd_ex.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p, _i32, _i64, _p, _p, _p, _i32, _i32,
+                                        _f64, _f64, _f64, _p, _i64, _i32, _i32, _p, _sz, _p]
+_lib.lora_linear_nf4_fwd_ex.restype = ctypes.c_int
 _lib.dense_patch_apply.argtypes = [_p, _i32, ctypes.POINTER(_i64), _i32, _p, _i32, ctypes.POINTER(_i64), _i32,
                                    _f64, _i32, _p]
 _lib.dense_patch_apply.restype = ctypes.c_int
@@ -181,6 +188,14 @@ def lora_linear_nf4_fwd(x, T, K, ldx, codes, absmax, codebook, blocksize, N, bia
     return _check(_lib.lora_linear_nf4_fwd(x, T, K, ldx, codes, absmax, codebook, blocksize, N, bias, A, B, rank,
                                            adapter_dtype, alpha, strength, request_scale, y, ldy, quality,
                                            workspace, workspace_bytes, stream), "lora_linear_nf4_fwd")
+
+
+def lora_linear_nf4_fwd_ex(x, T, K, ldx, codes, absmax, codebook, blocksize, N, bias, A, B, rank, adapter_dtype,
+                           alpha, strength, request_scale, y, ldy, quality, dequant, workspace, workspace_bytes,
+                           stream):
+    return _check(_lib.lora_linear_nf4_fwd_ex(x, T, K, ldx, codes, absmax, codebook, blocksize, N, bias, A, B, rank,
+                                              adapter_dtype, alpha, strength, request_scale, y, ldy, quality,
+                                              dequant, workspace, workspace_bytes, stream), "lora_linear_nf4_fwd_ex")
 
 
 def dense_patch_apply(dst, dst_dtype, dst_shape, src, src_dtype, src_shape, strength, mode, stream):
@@ -322,7 +337,9 @@ def lora_linear_multi(x, W, b, adapters, request_scale=1.0, out=None, quality="l
 
 
 def lora_linear_nf4(x, codes, absmax, codebook, N, b, A, B, alpha, strength=1.0, request_scale=1.0,
-                    blocksize=64, out=None, quality="lossless", workspace=None, stream=None):
+                    blocksize=64, out=None, quality="lossless", workspace=None, stream=None, dequant="auto"):
+    """``dequant``: "auto", "panel" or "in_gemm" (where a lossless call with more than 64 tokens
+    dequantizes the 4-bit weight; the same output bits either way)."""
     T, K = x.shape
     ldx = _row_major(x, "x")
     if out is None:
@@ -333,10 +350,10 @@ def lora_linear_nf4(x, codes, absmax, codebook, N, b, A, B, alpha, strength=1.0,
     q = _QUALITY[quality]
     need = lora_linear_nf4_workspace_size(T, K, N, rank, adt, q)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    lora_linear_nf4_fwd(x.data_ptr(), T, K, ldx, codes.data_ptr(), absmax.data_ptr(), codebook.data_ptr(),
-                        blocksize, N, _ptr(b), _ptr(A), _ptr(B), rank, adt, float(alpha), float(strength),
-                        float(request_scale), out.data_ptr(), ldy, q, ws.data_ptr(), ws.numel(),
-                        _stream(stream))
+    lora_linear_nf4_fwd_ex(x.data_ptr(), T, K, ldx, codes.data_ptr(), absmax.data_ptr(), codebook.data_ptr(),
+                           blocksize, N, _ptr(b), _ptr(A), _ptr(B), rank, adt, float(alpha), float(strength),
+                           float(request_scale), out.data_ptr(), ldy, q, _DEQUANT[dequant], ws.data_ptr(),
+                           ws.numel(), _stream(stream))
     return out
 
 

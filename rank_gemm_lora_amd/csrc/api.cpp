@@ -119,7 +119,7 @@ size_t adapter_bytes_for(const LinearProblem& p, bool lossless, bool gemm_nf4) {
 
 size_t panel_bytes(int64_t N, int64_t K) { return static_cast<size_t>(N) * static_cast<size_t>(K) * 2; }
 
-size_t workspace_rest_for(const LinearProblem& p, bool lossless);
+size_t workspace_rest_for(const LinearProblem& p, bool lossless, bool panel);
 
 // Lossless: b + sum_g u_g . c_g (u_g = strength_g . request_scale) as one fp32
 // vector [N] at the front of the workspace when an active adapter has a legacy
@@ -131,15 +131,20 @@ bool needs_bias32(const LinearProblem& p, bool lossless) {
   return false;
 }
 
-size_t workspace_bytes_for(const LinearProblem& p, bool lossless) {
+size_t workspace_bytes_for(const LinearProblem& p, bool lossless, bool panel) {
   if (p.T == 0) return 0;
   const size_t front = needs_bias32(p, lossless) ? round_up(static_cast<size_t>(p.N) * 4) : 0;
-  return front + workspace_rest_for(p, lossless);
+  return front + workspace_rest_for(p, lossless, panel);
 }
 
-size_t workspace_rest_for(const LinearProblem& p, bool lossless) {
+// 4-bit weight dequantized inside the hot GEMM: bf16 adapter, ranks multiples of 8.
+bool nf4_in_gemm_ok(const LinearProblem& p) {
+  if (p.act != Elt::BF16 || p.adapter != Elt::BF16 || p.n_groups > 1) return false;
+  return p.n_groups == 0 || p.g[0].rank % 8 == 0;
+}
+
+size_t workspace_rest_for(const LinearProblem& p, bool lossless, bool panel) {
   if (lora::skinny_path(p.act, lossless, p.T, p.ldt)) return lora::skinny_bytes(p.T, p.K, p.N, p.ldt);
-  const bool panel = lora::nf4_uses_panel(p.nf4, lossless, p.T);
   const size_t ad = adapter_bytes_for(p, lossless, p.nf4 && !panel);
   return panel ? round_up(ad) + panel_bytes(p.N, p.K) : ad;
 }
@@ -162,7 +167,7 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
                const float* absmax, const float* codebook, bool nf4, int64_t N, const void* bias,
                const Adapter* ads, int n_ads, int adapter_dtype, double request_scale,
                void* y, int64_t ldy, int act_dtype, int quality, void* workspace, size_t workspace_bytes,
-               void* stream, int phase = 0, bool overlap_ok = false, int tile = 0) {
+               void* stream, int phase = 0, bool overlap_ok = false, int tile = 0, int nf4_mode = 0) {
   if (!dtype_ok(act_dtype) || !dtype_ok(adapter_dtype)) return LORA_ERR_DTYPE;
   if (act_dtype == LORA_F32 && adapter_dtype != LORA_F32) return LORA_ERR_DTYPE;
   if (quality != LORA_LOSSLESS && quality != LORA_EXACT) return LORA_ERR_UNSUPPORTED;
@@ -173,6 +178,8 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
   if (nf4) {
     if (codes == nullptr || absmax == nullptr || codebook == nullptr) return LORA_ERR_NULL_PTR;
     if (K % 64 != 0) return LORA_ERR_SHAPE;
+    if (nf4_mode != lora::kNf4Auto && nf4_mode != lora::kNf4Panel && nf4_mode != lora::kNf4InGemm)
+      return LORA_ERR_UNSUPPORTED;
   } else if (W == nullptr) {
     return LORA_ERR_NULL_PTR;
   }
@@ -223,8 +230,10 @@ int run_linear(const void* x, int64_t T, int64_t K, int64_t ldx, const void* W, 
 
   const bool lossless = quality == LORA_LOSSLESS;
   const bool use_skinny = lora::skinny_path(p.act, lossless, T, p.ldt);
-  const bool use_panel = !use_skinny && lora::nf4_uses_panel(nf4, lossless, T);
-  const size_t need = workspace_bytes_for(p, lossless);
+  const bool in_gemm_ok = nf4_in_gemm_ok(p);
+  if (nf4 && lossless && nf4_mode == lora::kNf4InGemm && !in_gemm_ok) return LORA_ERR_UNSUPPORTED;
+  const bool use_panel = !use_skinny && lora::nf4_uses_panel(nf4, lossless, T, in_gemm_ok, nf4_mode);
+  const size_t need = workspace_bytes_for(p, lossless, use_panel);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LORA_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   if (need > 0 && needs_bias32(p, lossless)) {
@@ -368,15 +377,26 @@ int lora_linear_multi_fwd(const void* x, int64_t T, int64_t K, int64_t ldx, cons
                     request_scale, y, ldy, act_dtype, quality, workspace, workspace_bytes, stream, 0, true);
 }
 
+int lora_linear_nf4_fwd_ex(const void* x, int64_t T, int64_t K, int64_t ldx, const uint8_t* codes,
+                           const float* absmax, const float* codebook, int32_t blocksize, int64_t N, const void* bias,
+                           const void* A, const void* B, int32_t rank, int32_t adapter_dtype, double alpha,
+                           double strength, double request_scale, void* y, int64_t ldy, int32_t quality,
+                           int32_t dequant, void* workspace, size_t workspace_bytes, void* stream) {
+  if (blocksize != 64) return LORA_ERR_UNSUPPORTED;
+  const Adapter a{A, B, rank, alpha, 0, N, strength, nullptr};
+  return run_linear(x, T, K, ldx, nullptr, codes, absmax, codebook, true, N, bias, &a, 1, adapter_dtype,
+                    request_scale, y, ldy, LORA_BF16, quality, workspace, workspace_bytes, stream, 0, false, 0,
+                    dequant);
+}
+
 int lora_linear_nf4_fwd(const void* x, int64_t T, int64_t K, int64_t ldx, const uint8_t* codes,
                         const float* absmax, const float* codebook, int32_t blocksize, int64_t N, const void* bias,
                         const void* A, const void* B, int32_t rank, int32_t adapter_dtype, double alpha,
                         double strength, double request_scale, void* y, int64_t ldy, int32_t quality,
                         void* workspace, size_t workspace_bytes, void* stream) {
-  if (blocksize != 64) return LORA_ERR_UNSUPPORTED;
-  const Adapter a{A, B, rank, alpha, 0, N, strength, nullptr};
-  return run_linear(x, T, K, ldx, nullptr, codes, absmax, codebook, true, N, bias, &a, 1, adapter_dtype,
-                    request_scale, y, ldy, LORA_BF16, quality, workspace, workspace_bytes, stream);
+  return lora_linear_nf4_fwd_ex(x, T, K, ldx, codes, absmax, codebook, blocksize, N, bias, A, B, rank, adapter_dtype,
+                                alpha, strength, request_scale, y, ldy, quality, LORA_NF4_AUTO, workspace,
+                                workspace_bytes, stream);
 }
 
 int dense_patch_apply(void* dst, int32_t dst_dtype, const int64_t* dst_shape, int32_t dst_ndim, const void* src,
@@ -592,7 +612,8 @@ size_t lora_linear_nf4_workspace_size(int64_t T, int64_t K, int64_t N, int32_t r
   if (quality == LORA_LOSSLESS && T <= lora::kSkinnyMaxT)  // activations are bf16: the skinny path
     return lora::skinny_bytes(T, K, N, rank > 0 ? lora::rank_pad(rank) : 0);
   const size_t ad = rank > 0 ? lora_linear_workspace_size(T, K, N, &rank, 1, adapter_dtype, quality) : 0;
-  if (!lora::nf4_uses_panel(true, quality == LORA_LOSSLESS, T)) return ad;
+  // (the panel is included whenever a call could use it, so that the size serves either choice)
+  if (!lora::nf4_beyond_skinny(true, quality == LORA_LOSSLESS, T)) return ad;
   return round_up(ad) + panel_bytes(N, K);
 }
 

@@ -851,6 +851,107 @@ __device__ __forceinline__ u32x4 unswap_halves(u32x4 v, int sw) {
   return sw ? u32x4{v[2], v[3], v[0], v[1]} : v;
 }
 
+// 4-bit weight inside the hot kernel. One 64-element block of a weight row (one 64-k stage)
+// has one scale a, so its 16 possible values RN_bf16(RN_f32(codebook[c] . a)) form a table,
+// built with the same multiply and conversion as the panel kernel (the two paths give the
+// same weight bits). The table is kept as low and high bytes of the entries, four per
+// register (lo[i] byte j = low byte of entry 4i + j), so that a byte permute looks up four
+// codes of bits 0-2 at once among 8 entries; bit 3 picks the half.
+struct Nf4Table {
+  uint32_t lo[4], hi[4];
+};
+
+// The table in four steps of 8 instructions (spread over four MFMA bundles): the products of
+// entries 0-7, of entries 8-15, the bf16 conversions, the byte split.
+struct Nf4TableBuild {
+  float v[16];
+  uint32_t t[8];
+};
+__device__ __forceinline__ void nf4_table_step(Nf4TableBuild& b, Nf4Table& r, const float (&cb)[16], float a,
+                                               int step) {
+  if (step == 0 || step == 1) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) b.v[8 * step + c] = cb[8 * step + c] * a;
+  } else if (step == 2) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) b.t[c] = pack_bf16x2(b.v[2 * c], b.v[2 * c + 1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // bytes 0 and 2 (low bytes of entries 4i, 4i + 1) of t[2i], then of t[2i + 1]; then the high bytes
+      r.lo[i] = __builtin_amdgcn_perm(b.t[2 * i + 1], b.t[2 * i], 0x06040200u);
+      r.hi[i] = __builtin_amdgcn_perm(b.t[2 * i + 1], b.t[2 * i], 0x07050301u);
+    }
+  }
+}
+
+// Eight weight elements from one code word (byte j: element 2j in bits 0-3, 2j + 1 in bits
+// 4-7) as four bf16 pairs in element order, in four steps. v_perm_b32 (S0, S1, sel): output
+// byte i is byte sel_i of the 8 bytes S1 (0-3), S0 (4-7); selectors 8-11 give 0xff or 0 by
+// the sign bit of bytes 1, 3, 5, 7. Step 0 gathers the codes four to a register as bytes, in
+// element order (0, 1, 4, 5) and (2, 3, 6, 7), and turns their bit 3 into byte masks through
+// those sign selectors (bit 3 of element 2j + h is bit 8j + 4h + 3 of the word, shifted to a
+// sign position); steps 1 and 2 look the two groups up, low and high bytes; step 3
+// interleaves the bytes back into bf16 values.
+struct Nf4Word {
+  uint32_t xa, xb, ma, mb, la, ha, lb, hb;
+};
+__device__ __forceinline__ void nf4_word_step(Nf4Word& s, u32x4& out, uint32_t w, const Nf4Table& tb, int step) {
+  auto pick = [](uint32_t m, uint32_t hi_half, uint32_t lo_half) { return (hi_half & m) | (lo_half & ~m); };
+  if (step == 0) {
+    const uint32_t wr4 = w >> 4;
+    s.xa = __builtin_amdgcn_perm(wr4, w, 0x06020400u) & 0x07070707u;  // elements 0, 1, 4, 5
+    s.xb = __builtin_amdgcn_perm(wr4, w, 0x07030501u) & 0x07070707u;  // elements 2, 3, 6, 7
+    s.ma = __builtin_amdgcn_perm(w << 8, w << 12, 0x0B090A08u);
+    s.mb = __builtin_amdgcn_perm(w, w << 4, 0x0B090A08u);
+  } else if (step == 1) {
+    s.la = pick(s.ma, __builtin_amdgcn_perm(tb.lo[3], tb.lo[2], s.xa), __builtin_amdgcn_perm(tb.lo[1], tb.lo[0], s.xa));
+    s.ha = pick(s.ma, __builtin_amdgcn_perm(tb.hi[3], tb.hi[2], s.xa), __builtin_amdgcn_perm(tb.hi[1], tb.hi[0], s.xa));
+  } else if (step == 2) {
+    s.lb = pick(s.mb, __builtin_amdgcn_perm(tb.lo[3], tb.lo[2], s.xb), __builtin_amdgcn_perm(tb.lo[1], tb.lo[0], s.xb));
+    s.hb = pick(s.mb, __builtin_amdgcn_perm(tb.hi[3], tb.hi[2], s.xb), __builtin_amdgcn_perm(tb.hi[1], tb.hi[0], s.xb));
+  } else {
+    out = u32x4{__builtin_amdgcn_perm(s.ha, s.la, 0x05010400u), __builtin_amdgcn_perm(s.hb, s.lb, 0x05010400u),
+                __builtin_amdgcn_perm(s.ha, s.la, 0x07030602u), __builtin_amdgcn_perm(s.hb, s.lb, 0x07030602u)};
+  }
+}
+
+template <int WPT>
+struct Nf4Codes {
+  u32x4 q[WPT / 4];  // word j is q[j / 4][j % 4]
+  float a;
+};
+
+// Per-thread share of a 4-bit weight tile: TPR threads per weight row, each with WPT code words
+// (8 elements each) of the row's 64-k stage, and the block's scale.
+template <class P>
+struct Nf4Share {
+  static constexpr int TPR = P::THREADS / P::BN, WPT = 8 / TPR;
+  static_assert(P::THREADS % P::BN == 0 && (WPT == 4 || WPT == 8), "one or two threads per weight row");
+  uint32_t cvo, avo;  // byte offsets of this thread's code words and scale at main stage 0 (past the range: no row)
+  int row, half;
+  __device__ __forceinline__ void init(int tid, int rows_n, int64_t K) {
+    row = tid / TPR;
+    half = tid % TPR;
+    const bool in = row < rows_n;
+    cvo = in ? static_cast<uint32_t>(row * (K / 2) + half * WPT * 4) : 0x80000000u;
+    avo = in ? static_cast<uint32_t>(row * (K / 64) * 4) : 0x80000000u;
+  }
+  // Loads of main stage s (WPT / 4 + 1 buffer loads, issued in this order).
+  __device__ __forceinline__ void load(Nf4Codes<WPT>& c, __amdgpu_buffer_rsrc_t cr, __amdgpu_buffer_rsrc_t ar,
+                                       int s) const {
+#pragma unroll
+    for (int i = 0; i < WPT / 4; ++i)
+      c.q[i] = __builtin_amdgcn_raw_buffer_load_b128(cr, cvo + i * 16, s * 32, 0);
+    c.a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ar, avo, s * 4, 0));
+  }
+  // LDS byte offset of this thread's logical chunk j of its row in a weight slot (the copy layout:
+  // 128-byte rows, 16-byte chunk c of row r at position c ^ ((r / 2) % 8)).
+  __device__ __forceinline__ uint32_t lds_off(int j) const {
+    return static_cast<uint32_t>(row * 128 + (((half * WPT + j) ^ ((row >> 1) & 7)) * 16));
+  }
+};
+
 // Epilogue of the 16 x 16 layout: lane (r, q) of block (i, j) holds outputs
 // i*16 + 4q .. +3 of token j*16 + r. Bias in fp32 (no add without a bias), one
 // rounding, staged in the wave's 32 KB of LDS as token rows (16-byte chunks
@@ -1089,7 +1190,14 @@ __device__ __forceinline__ void ext_stage_loads(const ExtPlan& g, int e, const T
 // one every RS-th bundle after the barrier. Both tiles accumulate every output in the
 // same order (K-extension stages, then the main stages, 32 k per MFMA), so they give
 // bitwise-identical results.
-template <class P>
+// NF4: the base weight is 4-bit codes with one fp32 scale per 64-element block (K a multiple
+// of 64). A main stage's weight unit is then written by the waves themselves instead of
+// copied: the codes of the weight unit of stage t + 2 are loaded into registers during stage
+// t - 1 (after the wait of that stage's code loads, before its x copies), dequantized into
+// registers over k-step 0 of stage t, and written into the slot that the barrier of stage t
+// releases, where the copies would have gone. The weight is the panel kernel's, bit for bit,
+// and so is the result.
+template <class P, bool NF4 = false>
 __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearProblem p, int mt, int nt) {
   static_assert(P::WAVES == 4, "schedule written for 4 waves");
   __shared__ __attribute__((aligned(1024))) char smem[P::SLOTS * P::SLOT_BYTES];
@@ -1130,7 +1238,24 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
   TileOffsets<P, P::BM> ox;
   TileOffsets<P, P::BN> ow;
   ox.init(ldx_b, 0, rows_m, 0);
-  ow.init(ldw_b, 0, rows_n, 0);
+  if constexpr (!NF4) ow.init(ldw_b, 0, rows_n, 0);
+  using Share = Nf4Share<P>;
+  constexpr int WPT = Share::WPT;
+  constexpr int NC = WPT / 4 + 1;  // code loads per stage
+  Share nfs;
+  Nf4Codes<WPT> c_load, c_work;     // codes of a later stage in flight; codes being dequantized
+  u32x4 dq[WPT];                    // dequantized weight words of stage t + 2
+  float cb[16];
+  const __amdgpu_buffer_rsrc_t cr =
+      make_rsrc(NF4 ? p.codes + n0 * (p.K / 2) : nullptr, NF4 ? static_cast<uint32_t>(rows_n * (p.K / 2)) : 0u);
+  const __amdgpu_buffer_rsrc_t ar =
+      make_rsrc(NF4 ? p.absmax + n0 * (p.K / 64) : nullptr, NF4 ? static_cast<uint32_t>(rows_n * (p.K / 64) * 4) : 0u);
+  if constexpr (NF4) {
+    static_assert(WPT == TileOffsets<P, P::BN>::N, "one dequantized word per weight copy slot of the schedule");
+    nfs.init(tid, rows_n, p.K);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) cb[c] = p.codebook[c];
+  }
 
   // K-extension plan of this tile: the (at most two) groups whose columns meet it.
   const uint32_t ldt_b = static_cast<uint32_t>(p.ldt * 2);
@@ -1176,8 +1301,11 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
     const bool is_w = (u & 1) != 0;
     if (s >= NE) {
       const int kb = (s - NE) * P::RB;
-      if (is_w) dma_one<P, P::BN>(l, dst, wr, ldw_b, 0, rows_n, 0, kb, kb_total);
-      else dma_one<P, P::BM>(l, dst, xr, ldx_b, 0, rows_m, 0, kb, kb_total);
+      if (is_w) {
+        if constexpr (!NF4) dma_one<P, P::BN>(l, dst, wr, ldw_b, 0, rows_n, 0, kb, kb_total);
+      } else {
+        dma_one<P, P::BM>(l, dst, xr, ldx_b, 0, rows_m, 0, kb, kb_total);
+      }
       return;
     }
     const bool second = s >= eg0.ns;
@@ -1199,10 +1327,67 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.f;
 
+  // NF4: the dequantized words of a main stage's weight unit go to LDS (thread share of row)
+  auto nf4_write = [&](char* wslot, int j) {
+    *reinterpret_cast<u32x4*>(wslot + nfs.lds_off(j)) = dq[j];
+  };
+  Nf4TableBuild tbb;
+  Nf4Table tb;
+  Nf4Word wst;
+  // Step g of the dequantization of one weight unit: table steps 0-3, then four steps per word.
+  // (Empty asm statements on each step's results keep the step in the MFMA bundle where it is
+  // placed: the compiler would otherwise sink the work to the LDS writes after the barrier.)
+  auto nf4_step = [&](const Nf4Codes<WPT>& c, int g) {
+    if (g < 4) {
+      nf4_table_step(tbb, tb, cb, c.a, g);
+#if defined(__HIP_DEVICE_COMPILE__)
+      if (g < 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(tbb.v[8 * g + e]));
+      } else if (g == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(tbb.t[e]));
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(tb.lo[e]), "+v"(tb.hi[e]));
+      }
+#endif
+    } else if (g < 4 + 4 * WPT) {
+      const int j = (g - 4) / 4, st = (g - 4) % 4;
+      nf4_word_step(wst, dq[j], c.q[j / 4][j % 4], tb, st);
+#if defined(__HIP_DEVICE_COMPILE__)
+      if (st == 0) asm volatile("" : "+v"(wst.xa), "+v"(wst.xb), "+v"(wst.ma), "+v"(wst.mb));
+      else if (st == 1) asm volatile("" : "+v"(wst.la), "+v"(wst.ha));
+      else if (st == 2) asm volatile("" : "+v"(wst.lb), "+v"(wst.hb));
+      else asm volatile("" : "+v"(dq[j][0]), "+v"(dq[j][1]), "+v"(dq[j][2]), "+v"(dq[j][3]));
+#endif
+    }
+  };
+
   // prologue: units 0 .. 3 (stages 0 and 1). Up to two K-extension stages (ranks
   // up to 128) use precomputed per-lane offsets like the main stages; more
   // extension stages take the generic path.
-  if (NE == 0 && nk - (k_tail ? 1 : 0) >= 2) {
+  if constexpr (NF4) {
+    // copies of the x units and of K-extension weight units; main weight units of stages 0
+    // and 1 dequantized here; the codes of the first main stage from 2 on loaded for the
+    // first stage that dequantizes (K-extension stages load no codes: the compiler's own
+    // waits before the first use of loaded registers then stay exact)
+    for (int u = 0; u < 4; ++u) {
+      if ((u & 1) && (u >> 1) >= NE) continue;
+      for (int l = 0; l < NL; ++l) issue_load(u, l);
+    }
+    for (int s = 0; s < 2 && s < NS; ++s) {
+      if (s < NE) continue;
+      nfs.load(c_work, cr, ar, s - NE);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+#pragma unroll
+      for (int g = 0; g < 4 + 4 * WPT; ++g) nf4_step(c_work, g);
+#pragma unroll
+      for (int j = 0; j < WPT; ++j) nf4_write(smem + (2 * s + 1) * P::SLOT_BYTES, j);
+    }
+    const int s_first = NE > 2 ? NE : 2;
+    if (s_first < NS) nfs.load(c_load, cr, ar, s_first - NE);
+  } else if (NE == 0 && nk - (k_tail ? 1 : 0) >= 2) {
 #pragma unroll
     for (int l = 0; l < NL; ++l) ox.load_one(l, smem, xr, 0);
 #pragma unroll
@@ -1228,7 +1413,7 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
     for (int u = 0; u < 4; ++u)
       for (int l = 0; l < NL; ++l) issue_load(u, l);
   }
-  if (NU > 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NL));  // stage 0 landed; stage 1 may be in flight
+  if (NU > 2 && !NF4) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NL));  // stage 0 landed; stage 1 may be in flight
   else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   stage_barrier();
   const FragOffsets fo = frag_offsets<P>(wn0, wm0, lane);
@@ -1245,6 +1430,11 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
   };
 #pragma unroll
   for (int q = 0; q < P::NI + P::NJ; ++q) read_frag(fr[0], q, slot(0), slot(1), 0);
+
+  // stages t < NE - 2 copy K-extension units (stage t + 2); stages from t_end on
+  // copy the last main units or nothing
+  const int t_ext = NE > 2 ? NE - 2 : 0;
+  const int t_end = NE + nk - 2 - (k_tail ? 1 : 0);
 
   // stage t whose copies all belong to main stage t + 2 - NE, which is neither
   // past the last nor the K-tail stage
@@ -1263,13 +1453,41 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
     const int kb2 = (t + 2 - NE) * P::RB;
     char* const xdst = smem + a3 * P::SLOT_BYTES;
     char* const wdst = smem + a * P::SLOT_BYTES;
+    // NF4: a main stage dequantizes the codes of stage t + 2 (loaded during stage t - 1, or by
+    // the prologue for the first one) and loads those of stage t + 3 first thing, before its x
+    // copies.
+    constexpr bool DQ = NF4 && !EXT;
+    const bool load_c = DQ && t + 3 < NS;
+    // the dequantization steps run one per bundle from the first bundle of k-step 0 on; word j
+    // is written at bundle LS j + LS / 2 of k-step 1, after its last step
+    static_assert(!NF4 || (4 + 4 * WPT <= 2 * NB && LS >= 4 && 4 + 3 < NB + LS / 2), "dequantization schedule");
     // (one loop per k-step: one loop over both is past the compiler's full-unroll limit)
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int m = 0; m < NB; ++m) {  // k-step 0
       const int i = m / P::NJ, j = m % P::NJ;
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0].a[i], fr[0].b[j], acc[i][j], 0, 0, 0);
+      if constexpr (DQ) __builtin_amdgcn_sched_barrier(0);  // (the bundle's VALU work after its MFMA)
       if (m % RS == 0) read_frag(fr[1], m / RS, xs, ws, 1);
+      if constexpr (NF4) {
+        if (m == 0) {
+          if constexpr (DQ) {
+            // the codes of stage t + 2 landed: loads issued after them are the previous stage's x
+            // copies (the prologue waited for its own)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
+            c_work = c_load;
+#if defined(__HIP_DEVICE_COMPILE__)
+            // (the copy stays here, after the wait, so that the next load may reuse the registers)
+#pragma unroll
+            for (int i = 0; i < WPT / 4; ++i)
+              asm volatile("" : "+v"(c_work.q[i][0]), "+v"(c_work.q[i][1]), "+v"(c_work.q[i][2]), "+v"(c_work.q[i][3]));
+            asm volatile("" : "+v"(c_work.a));
+#endif
+          }
+          if (load_c) nfs.load(c_load, cr, ar, t + 3 - NE);
+        }
+        if constexpr (DQ) nf4_step(c_work, m);
+      }
       if (m % LS == LS / 2) {
         if constexpr (EXT) issue_load(2 * t + 4, m / LS);
         else ox.load_one(m / LS, xdst, xr, kb2);
@@ -1280,15 +1498,22 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
     for (int m = 0; m < NB; ++m) {  // k-step 1
       const int i = m / P::NJ, j = m % P::NJ;
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[1].a[i], fr[1].b[j], acc[i][j], 0, 0, 0);
+      if constexpr (DQ) {
+        __builtin_amdgcn_sched_barrier(0);
+        nf4_step(c_work, NB + m);
+      }
       if (m == 0) {
         __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));  // x of stage t + 2 may still be in flight
+        // x of stage t + 2 (and codes loaded by this stage) may still be in flight
+        if (load_c) __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL + NC));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(NL));
         stage_barrier();  // stage t + 1 landed and visible; every wave is done reading stage t
       } else if (m % RS == 1) {
         read_frag(fr[0], m / RS, xs2, ws2, 0);
       }
       if (m % LS == LS / 2) {
         if constexpr (EXT) issue_load(2 * t + 5, m / LS);
+        else if constexpr (NF4) nf4_write(wdst, m / LS);
         else ow.load_one(m / LS, wdst, wr, kb2);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1299,6 +1524,8 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
   // possibly the K-tail stage, so they go through the precomputed offsets.
   auto main_unit = [&](int u) {
     if (u >= NU) return;
+    // (NF4: K is a multiple of 64, so the stages from t_end on have no units left to load)
+    if constexpr (NF4) return;
     const int kb = ((u >> 1) - NE) * P::RB;
     const bool tl = k_tail && (u >> 1) == NS - 1;
     if (u & 1) ow.load(slot(u), wr, kb, tl, kb_total);
@@ -1321,10 +1548,6 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
     mfma_frags16<P>(acc, fr[1]);
   };
 
-  // stages t < NE - 2 copy K-extension units (stage t + 2); stages from t_end on
-  // copy the last main units or nothing
-  const int t_ext = NE > 2 ? NE - 2 : 0;
-  const int t_end = NE + nk - 2 - (k_tail ? 1 : 0);
   int a = 0;  // slot of x of stage t
   int t = 0;
   for (; t < t_ext && t + 1 < NS; ++t) {
@@ -1352,11 +1575,11 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
   else epilogue_lds16s<P>(acc, p, m0, n0, wm0, wn0, lane, wave, smem);
 }
 
-template <class P>
+template <class P, bool NF4 = false>
 hipError_t launch_flow16(const LinearProblem& p, hipStream_t s) {
   const int mt = static_cast<int>((p.T + P::BM - 1) / P::BM);
   const int nt = static_cast<int>((p.N + P::BN - 1) / P::BN);
-  hipLaunchKernelGGL(gemm_flow16_kernel<P>, dim3(mt * nt), dim3(P::THREADS), 0, s, p, mt, nt);
+  hipLaunchKernelGGL((gemm_flow16_kernel<P, NF4>), dim3(mt * nt), dim3(P::THREADS), 0, s, p, mt, nt);
   return hipGetLastError();
 }
 
@@ -1395,21 +1618,34 @@ int max_groups_per_tile(const LinearProblem& p, int bn) {
 // emitted (a kernel template used only through a launcher has lost it before).
 template __global__ void gemm_flow16_kernel<Flow16Cfg>(LinearProblem, int, int);
 template __global__ void gemm_flow16_kernel<Flow16SCfg>(LinearProblem, int, int);
+template __global__ void gemm_flow16_kernel<Flow16SCfg, true>(LinearProblem, int, int);
+
+// 4-bit weight dequantized inside the hot kernel (one adapter group at most, K a multiple of
+// 64): the 128 x 128 tile, whose two threads per weight row each dequantize 32 elements per
+// stage into registers the kernel has free at two workgroups per CU.
+hipError_t launch_nf4(const LinearProblem& p, hipStream_t s) {
+  const bool ranks_ok = p.n_groups == 0 || (p.n_groups == 1 && p.g[0].rank % 8 == 0);
+  if (!ranks_ok || p.act != Elt::BF16 || p.adapter != Elt::BF16 || p.K % 64 != 0) return hipErrorInvalidValue;
+  return launch_flow16<Flow16SCfg, true>(p, s);
+}
 
 hipError_t launch(const LinearProblem& p, hipStream_t s) {
   if (max_groups_per_tile(p, Flow16Cfg::BN) <= 2) {
     // The output tile (both give the same bits): 256 x 256, one workgroup per CU, or 128 x 128,
     // two per CU. The larger does more MFMA work per LDS byte; the smaller ran at 0.77-0.92 of
-    // its rate on MI355X (1536- and 8960-wide inputs) but fills the last wave of tiles better.
-    // The smaller is taken when its wave fill, discounted by 0.85, beats the larger's (or when
-    // asked for).
+    // its rate on MI355X (1536- and 8960-wide inputs) but fills the last wave of tiles better and
+    // pads fewer rows when T is not a multiple of 256. Estimated time, in units of one 128 x 128
+    // tile's MFMA work (padding included) at the larger tile's rate: waves of 256 x 256 tiles
+    // (one per CU) take 4 each, waves of 128 x 128 tiles (two per CU at 0.85 of the rate) take
+    // 2 / 0.85. The smaller is taken when its estimate is lower (or when asked for). With T a
+    // multiple of 256 this is the smaller tile's wave fill, discounted by 0.85, beating the
+    // larger's; up to 128 tokens the smaller always wins (the larger's rows are half padding).
     const int64_t cus = device_cus();
-    auto fill = [](int64_t n, int64_t slots) {  // share of the workgroup slots of all waves in use
-      return static_cast<double>(n) / static_cast<double>((n + slots - 1) / slots * slots);
-    };
     const int64_t t256 = ((p.T + 255) / 256) * ((p.N + 255) / 256);
     const int64_t t128 = ((p.T + 127) / 128) * ((p.N + 127) / 128);
-    const bool small = p.tile == 2 || (p.tile == 0 && cus > 0 && 0.85 * fill(t128, 2 * cus) > fill(t256, cus));
+    const double est256 = 4.0 * static_cast<double>((t256 + cus - 1) / (cus > 0 ? cus : 1));
+    const double est128 = 2.0 / 0.85 * static_cast<double>((t128 + 2 * cus - 1) / (cus > 0 ? 2 * cus : 1));
+    const bool small = p.tile == 2 || (p.tile == 0 && cus > 0 && est128 < est256);
     return small ? launch_flow16<Flow16SCfg>(p, s) : launch_flow16<Flow16Cfg>(p, s);
   }
   using P = HotCfg;
@@ -2188,7 +2424,15 @@ hipError_t launch_lossless(const LinearProblem& p, hipStream_t s, int phase) {
   if (p.T == 0) return hipSuccess;
   // few tokens: the rank-wide product runs inside the same launches (phase 1 has nothing to do)
   if (p.skinny != nullptr) return phase == 1 ? hipSuccess : launch_skinny(p, s);
-  if (p.nf4 && p.panel != nullptr) {
+  if (p.nf4 && p.panel == nullptr) {
+    // dequantized inside the hot GEMM (bf16 activations and adapter, ranks multiples of 8)
+    if (p.n_groups > 0 && phase != 2) {
+      const hipError_t e = pipe::down::launch(p, s);
+      if (e != hipSuccess) return e;
+    }
+    return phase == 1 ? hipSuccess : pipe::launch_nf4(p, s);
+  }
+  if (p.nf4) {
     // the weight dequantized once into the panel, then the bf16 path over it
     if (phase != 2) {
       const hipError_t e = launch_nf4_panel(p, s);

@@ -92,11 +92,26 @@ inline size_t producer_partial_bytes(int64_t T, int64_t K, int64_t ldt) {
   return S > 1 ? static_cast<size_t>(S) * static_cast<size_t>(T) * static_cast<size_t>(ldt) * 4 : 0;
 }
 
-// Lossless 4-bit weight beyond the skinny range: the weight is dequantized once
-// per call into a bf16 panel [N, K] in the workspace and the bf16 GEMM runs on
-// it (dequantizing inside the GEMM would repeat the work once per 256-token
-// output tile; measured slower at every token count above the skinny range).
-inline bool nf4_uses_panel(bool nf4, bool lossless, int64_t T) { return nf4 && lossless && T > kSkinnyMaxT; }
+// Lossless 4-bit weight beyond the skinny range, two ways:
+// - the panel: the weight dequantized once per call into a bf16 copy [N, K] in the
+//   workspace, then the bf16 GEMM over it (a write and a re-read of the bf16 weight);
+// - in the GEMM: the hot kernel's 128 x 128 tile dequantizes each weight unit itself,
+//   once per 128-token output tile (VALU work beside the MFMAs that grows with the
+//   token count); bf16 adapters whose ranks are multiples of 8.
+// Both give the same weight bits and the same outputs. The automatic choice takes the
+// GEMM form up to kNf4InGemmMaxT tokens: measured on MI355X (4096 -> 14336, rank 16), it
+// took 67 us against the panel path's 73 up to 256 tokens (the GEMMs are latency-bound
+// there, one workgroup per CU, and the panel kernel costs 25 us), and from 320 tokens on the
+// panel was faster (7% at 320-512, 1.7x at 8192, where the in-GEMM form is bound by its
+// VALU work: 156 VALU instructions per 32 MFMAs of a stage).
+enum Nf4Dequant : int { kNf4Auto = 0, kNf4Panel = 1, kNf4InGemm = 2 };
+constexpr int64_t kNf4InGemmMaxT = 256;
+inline bool nf4_beyond_skinny(bool nf4, bool lossless, int64_t T) { return nf4 && lossless && T > kSkinnyMaxT; }
+inline bool nf4_uses_panel(bool nf4, bool lossless, int64_t T, bool in_gemm_ok, int mode) {
+  if (!nf4_beyond_skinny(nf4, lossless, T)) return false;
+  if (!in_gemm_ok || mode == kNf4Panel) return true;
+  return mode == kNf4Auto && T > kNf4InGemmMaxT;
+}
 
 // Lossless fp32 adapter on bf16 activations: the products run on bf16 MFMA
 // over the hi/lo split (the t~ block of a group is then t_hi | t_hi | t_lo,

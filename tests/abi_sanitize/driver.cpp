@@ -161,6 +161,26 @@ void test_nf4_patch_merge_bwd() {
                                  520, LORA_LOSSLESS, WS, need, nullptr) == LORA_ERR_HIP);
     }
   }
+  // where the 4-bit weight is dequantized: an unknown choice, the in-GEMM form without a bf16
+  // adapter of a rank that is a multiple of 8, and the workspace each choice needs (the in-GEMM
+  // form none of the panel)
+  stub::rec.ws_hi = stub::rec.ws_lo + big;
+  EXPECT(lora_linear_nf4_fwd_ex(X, 300, 256, 256, codes, am, cb, 64, 520, nullptr, A, B, 16, LORA_BF16, 32.0, 1.0,
+                                1.0, Y, 520, LORA_LOSSLESS, 3, WS, big, nullptr) == LORA_ERR_UNSUPPORTED);
+  EXPECT(lora_linear_nf4_fwd_ex(X, 300, 256, 256, codes, am, cb, 64, 520, nullptr, A, B, 16, LORA_F32, 32.0, 1.0,
+                                1.0, Y, 520, LORA_LOSSLESS, LORA_NF4_IN_GEMM, WS, big, nullptr) == LORA_ERR_UNSUPPORTED);
+  EXPECT(lora_linear_nf4_fwd_ex(X, 300, 256, 256, codes, am, cb, 64, 520, nullptr, A, B, 12, LORA_BF16, 32.0, 1.0,
+                                1.0, Y, 520, LORA_LOSSLESS, LORA_NF4_IN_GEMM, WS, big, nullptr) == LORA_ERR_UNSUPPORTED);
+  {
+    const int32_t r16 = 16;
+    const size_t small = lora_linear_workspace_size(300, 256, 520, &r16, 1, LORA_BF16, LORA_LOSSLESS);
+    stub::rec.ws_hi = stub::rec.ws_lo + small;
+    EXPECT(lora_linear_nf4_fwd_ex(X, 300, 256, 256, codes, am, cb, 64, 520, nullptr, A, B, 16, LORA_BF16, 32.0, 1.0,
+                                  1.0, Y, 520, LORA_LOSSLESS, LORA_NF4_IN_GEMM, WS, small, nullptr) == LORA_ERR_HIP);
+    EXPECT(lora_linear_nf4_fwd_ex(X, 300, 256, 256, codes, am, cb, 64, 520, nullptr, A, B, 16, LORA_BF16, 32.0, 1.0,
+                                  1.0, Y, 520, LORA_LOSSLESS, LORA_NF4_PANEL, WS, small, nullptr) ==
+           LORA_ERR_WORKSPACE);
+  }
   const int64_t s34[2] = {3, 4}, s43[2] = {4, 3}, s12[1] = {12};
   EXPECT(dense_patch_apply(Y, LORA_BF16, s34, 2, X, LORA_BF16, s34, 2, 0.8, LORA_PATCH_ADD, nullptr) == LORA_ERR_HIP);
   EXPECT(dense_patch_apply(Y, LORA_BF16, s34, 2, X, LORA_BF16, s43, 2, 0.8, LORA_PATCH_ADD, nullptr) ==

@@ -284,6 +284,32 @@ def test_nf4_workspace_query():
     assert q(0, 256, 300, 16, BF16) == 0
 
 
+def nf4_ex(dequant, **kw):
+    a = dict(x=X, T=0, K=128, ldx=128, codes=W, absmax=W + 0x1000_0000, cb=W + 0x2000_0000, bs=64, N=96,
+             bias=None, A=A, B=B, rank=16, adt=BF16, alpha=32.0, y=Y, ldy=96, q=LOSSLESS)
+    a.update(kw)
+    return rg._lib.lora_linear_nf4_fwd_ex(a["x"], a["T"], a["K"], a["ldx"], a["codes"], a["absmax"], a["cb"],
+                                          a["bs"], a["N"], a["bias"], a["A"], a["B"], a["rank"], a["adt"],
+                                          a["alpha"], 1.0, 1.0, a["y"], a["ldy"], a["q"], dequant, WSP, 1 << 30,
+                                          None)
+
+
+def test_nf4_dequant_choice_validation():
+    for d in (rg.LORA_NF4_AUTO, rg.LORA_NF4_PANEL, rg.LORA_NF4_IN_GEMM):
+        assert nf4_ex(d) == OK
+        assert nf4_ex(d, adt=F32) in (OK, UNSUP)
+    assert nf4_ex(3) == UNSUP and nf4_ex(-1) == UNSUP
+    # the in-GEMM form: bf16 adapter with a rank that is a multiple of 8, or no adapter
+    assert nf4_ex(rg.LORA_NF4_IN_GEMM, adt=F32) == UNSUP
+    assert nf4_ex(rg.LORA_NF4_IN_GEMM, rank=12) == UNSUP
+    assert nf4_ex(rg.LORA_NF4_IN_GEMM, A=None, B=None, rank=0) == OK
+    assert nf4_ex(rg.LORA_NF4_PANEL, adt=F32) == OK and nf4_ex(rg.LORA_NF4_AUTO, rank=12) == OK
+    # the other checks come first, as for lora_linear_nf4_fwd
+    assert nf4_ex(rg.LORA_NF4_IN_GEMM, bs=32) == UNSUP
+    assert nf4_ex(rg.LORA_NF4_IN_GEMM, K=96, ldx=96) == SHAPE
+    assert nf4_ex(rg.LORA_NF4_IN_GEMM, codes=None) == NULL
+
+
 def test_nf4_validation():
     assert nf4() == OK
     assert nf4(bs=32) == UNSUP

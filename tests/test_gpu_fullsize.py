@@ -117,9 +117,13 @@ def test_nf4_layer_full(s):
     say(f"case full-size nf4 T={s.T} K={s.K} N={s.N} r={s.rank} sampled rows={len(rows)}")
     args = (dev(d["x"]), dev(d["codes"]), dev(d["absmax"]), dev(d["codebook"]), s.N, dev(d["b"]), dev(d["A"]),
             dev(d["B"]), d["alpha"], d["strength"], d["request_scale"])
-    y = rg.lora_linear_nf4(*args, out=nan_out(s.T, s.N))
+    y = rg.lora_linear_nf4(*args, out=nan_out(s.T, s.N), dequant="panel")
     ye = rg.lora_linear_nf4(*args, quality="exact", out=nan_out(s.T, s.N))
+    # the weight dequantized inside the GEMM instead: the same bits at full size
+    yg = rg.lora_linear_nf4(*args, out=nan_out(s.T, s.N), dequant="in_gemm")
     torch.cuda.synchronize()
+    assert torch.equal(y, yg), "4-bit weight dequantized in the GEMM differs from the panel path"
+    del yg
     # fp64 over every output with the bf16 weight both tiers multiply (E6), and with the exact
     # codebook x absmax product
     W = ec.chain_nf4_weight(d["codes"], d["absmax"], d["codebook"], s.K, 64)

@@ -3,7 +3,8 @@
 Callers that capture (serving loops, the few-token regimes replayed per step) need every launch of
 a call to be capturable and to give the same result on every replay. Covered: the hot path (one
 adapter and two per tile), the rank-wide producer's K split with its finishing kernel, the
-few-token path, the fp32-adapter split, the 4-bit panel, the no-allocation entry point and the
+few-token path, the fp32-adapter split, the 4-bit panel and the 4-bit weight dequantized inside the
+GEMM, the no-allocation entry point and the
 backward, including its empty batch, which writes zero gradients by kernel. Each graph is replayed
 several times with eager work between the replays (the output is overwritten before each one),
 and each replay is compared with the eager result bit for bit.
@@ -90,6 +91,23 @@ def test_nf4_panel_in_a_graph():
     y = torch.empty((T, N), dtype=torch.bfloat16, device=DEV)
     _replays_equal(lambda: rg.lora_linear_nf4(x, codes, absmax, cb, N, None, A, B, 32.0, 1.0, 1.0, out=y,
                                               workspace=ws), [y])
+
+
+def test_nf4_in_gemm_in_a_graph():
+    rng = np.random.default_rng(43)
+    T, K, N, r = 300, 256, 300, 16
+    x = dev(lw.to_dtype(rng.standard_normal((T, K)), "bf16"))
+    codes = dev(torch.from_numpy(rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)))
+    absmax = dev(torch.from_numpy(np.abs(rng.standard_normal(N * K // 64)) * np.sqrt(0.05)).float())
+    cb = dev(lw.nf4_style_codebook())
+    A = dev(lw.to_dtype(rng.standard_normal((r, K)) / np.sqrt(K), "bf16"))
+    B = dev(lw.to_dtype(rng.standard_normal((N, r)) * np.sqrt(0.02), "bf16"))
+    say("case graph 4-bit in-GEMM")
+    ws = torch.empty(max(1, rg.lora_linear_workspace_size(T, K, N, [r], rg.LORA_BF16)), dtype=torch.uint8,
+                     device=DEV)
+    y = torch.empty((T, N), dtype=torch.bfloat16, device=DEV)
+    _replays_equal(lambda: rg.lora_linear_nf4(x, codes, absmax, cb, N, None, A, B, 32.0, 1.0, 1.0, out=y,
+                                              workspace=ws, dequant="in_gemm"), [y])
 
 
 def test_noalloc_in_a_graph():

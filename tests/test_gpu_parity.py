@@ -497,6 +497,70 @@ def test_nf4_one_hot_returns_dequantized_columns(T):
         assert_bitwise(y, want, f"one-hot {q}")
 
 
+# The 4-bit weight dequantized inside the hot GEMM (128-token tiles) against the panel path: the
+# same weight bits (one table of RN_bf16(RN_f32(codebook[c] . absmax)) per 64-element block, built
+# with the panel kernel's arithmetic) and the same accumulation order, so the same output bits.
+# The cases walk the kernel's stage plans: no adapter; one K-extension stage (rank <= 64); two
+# (<= 128); four (rank 200: the codes of the first main stage are loaded by the prologue ahead of
+# the extension stages); K of one and of two 64-element stages; ragged tiles both ways; a strided
+# input and a column view of a wider output; with and without bias.
+@pytest.mark.parametrize("T,K,N,r,bias", [
+    (65, 256, 300, 16, True), (130, 256, 300, 0, False), (300, 64, 260, 8, True), (257, 128, 520, 128, True),
+    (600, 448, 1000, 200, False), (1000, 1024, 700, 64, True)])
+def test_nf4_in_gemm_equals_panel(T, K, N, r, bias):
+    d = _nf4_small(T=T, K=K, N=N, r=max(r, 8), bias=bias, seed=60 + T)
+    say(f"case nf4 in-GEMM vs panel T={T} K={K} N={N} r={r} bias={bias}")
+    A, B = (dev(d["A"]), dev(d["B"])) if r else (None, None)
+    xs = torch.zeros((T, K + 64), dtype=torch.bfloat16)
+    xs[:, :K] = d["x"]
+    xv = dev(xs)[:, :K]  # row stride K + 64
+    args = (xv, dev(d["codes"]), dev(d["absmax"]), dev(d["codebook"]), N, dev(d["b"]), A, B, d["alpha"], 0.8, 0.9)
+    outs = {}
+    for mode in ("panel", "in_gemm"):
+        wide = torch.full((T, N + 40), float("nan"), dtype=torch.bfloat16, device=DEV)
+        outs[mode] = wide
+        rg.lora_linear_nf4(*args, out=wide[:, 24:24 + N], dequant=mode)
+    torch.cuda.synchronize()
+    y = outs["in_gemm"][:, 24:24 + N]
+    assert torch.equal(outs["panel"][:, 24:24 + N], y), "in-GEMM dequantization differs from the panel"
+    assert torch.isnan(outs["in_gemm"][:, :24]).all(), "wrote left of the column view"
+    assert torch.isnan(outs["in_gemm"][:, 24 + N:]).all(), "wrote right of the column view"
+    y64 = lo.lora_linear_nf4(d["x"], d["codes"], d["absmax"], d["codebook"], 64, d["b"],
+                             d["A"] if r else None, d["B"] if r else None, d["alpha"], max(r, 8), 0.8, 0.9)
+    yc = None  # (without an adapter the chain is the base GEMM summed exactly: only the gate applies)
+    if r and T * K * N <= 300 * 256 * 520:
+        yc = ec.chain_nf4(d["x"], d["codes"], d["absmax"], d["codebook"], 64, d["b"], d["A"] if r else None,
+                          d["B"] if r else None, d["alpha"], max(r, 8), 0.8, 0.9)
+    assert_gate(y, y64, yc, what="nf4 in-GEMM lossless")
+
+
+def test_nf4_in_gemm_workspace_and_choice():
+    """The in-GEMM form needs no panel in the workspace (the panel path refuses that size), and an
+    fp32 adapter or a rank that is not a multiple of 8 is refused for it."""
+    d = _nf4_small(T=300, K=256, N=300, r=16, bias=False, seed=9)
+    say("case nf4 in-GEMM workspace")
+    x, codes, am, cb = dev(d["x"]), dev(d["codes"]), dev(d["absmax"]), dev(d["codebook"])
+    A, B = dev(d["A"]), dev(d["B"])
+    small = rg.lora_linear_workspace_size(300, 256, 300, [16], rg.LORA_BF16)
+    assert small < rg.lora_linear_nf4_workspace_size(300, 256, 300, 16, rg.LORA_BF16)
+    ws = torch.empty(small, dtype=torch.uint8, device=DEV)
+    yp = rg.lora_linear_nf4(x, codes, am, cb, 300, None, A, B, 32.0, dequant="panel")
+    yg = rg.lora_linear_nf4(x, codes, am, cb, 300, None, A, B, 32.0, dequant="in_gemm", workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(yp, yg)
+    WORKSPACE, UNSUPPORTED = 7, 8
+    with pytest.raises(rg.LoraError) as e:
+        rg.lora_linear_nf4(x, codes, am, cb, 300, None, A, B, 32.0, dequant="panel", workspace=ws)
+    assert e.value.status == WORKSPACE
+    with pytest.raises(rg.LoraError) as e:
+        rg.lora_linear_nf4(x, codes, am, cb, 300, None, A.float(), B.float(), 32.0, dequant="in_gemm")
+    assert e.value.status == UNSUPPORTED
+    with pytest.raises(rg.LoraError) as e:
+        rg.lora_linear_nf4(x, codes, am, cb, 300, None, A[:12].contiguous(), B[:, :12].contiguous(), 32.0,
+                           dequant="in_gemm")
+    assert e.value.status == UNSUPPORTED
+
+
 # ------------------------------------------------------------------ dense patches
 
 @pytest.mark.parametrize("shape,dt_dst,dt_src,mode", [
