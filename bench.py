@@ -58,7 +58,8 @@ def main():
                     help="only run a plain 1 GiB device copy (calibrates HBM byte counters) and exit")
     ap.add_argument("--layer-only", action="store_true",
                     help="only run the timed fused steps (for counter collection) and exit")
-    ap.add_argument("--workload", choices=["attn_proj", "qkv_bf16", "qkv_f32", "nf4_layer", "multi_ffn_up"],
+    ap.add_argument("--workload", choices=["attn_proj", "qkv_bf16", "qkv_f32", "nf4_layer", "nf4_layer_in_gemm",
+                                           "nf4_tokens256", "multi_ffn_up"],
                     help="only run this workload's fused call (--warmup + --steps times; for counter runs) and exit")
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="turn the four counter runs in DIR (f/, w/: FETCH_SIZE / WRITE_SIZE of --layer-only; "
@@ -305,15 +306,20 @@ def run_workload(torch, dev, name, warmup, steps):
         ws = torch.empty(rg.lora_linear_workspace_size(sp.T, sp.K, Nt, list(sp.ranks), adt), dtype=torch.uint8,
                          device=dev)
         fn = lambda: rg.lora_linear_stacked(x, W, b, groups, sp.strength, sp.request_scale, out=y, workspace=ws)
-    elif name == "nf4_layer":
+    elif name in ("nf4_layer", "nf4_layer_in_gemm", "nf4_tokens256"):
+        # the 4-bit layer as configured (the automatic choice: the panel at 8192 tokens), the same
+        # with the weight dequantized inside the GEMM, and its first 256 tokens (automatic: in the GEMM)
         sp = lw.NF4_LAYER
         h = lw.nf4_inputs(sp)
         x, codes, absmax, cb, A, B, b = (d2(h[k]) for k in ("x", "codes", "absmax", "codebook", "A", "B", "b"))
-        y = torch.empty((sp.T, sp.N), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(rg.lora_linear_nf4_workspace_size(sp.T, sp.K, sp.N, sp.rank, rg.LORA_BF16),
+        T = 256 if name == "nf4_tokens256" else sp.T
+        x = x[:T]
+        dq = "in_gemm" if name == "nf4_layer_in_gemm" else "auto"
+        y = torch.empty((T, sp.N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(rg.lora_linear_nf4_workspace_size(T, sp.K, sp.N, sp.rank, rg.LORA_BF16),
                          dtype=torch.uint8, device=dev)
         fn = lambda: rg.lora_linear_nf4(x, codes, absmax, cb, sp.N, b, A, B, sp.alpha, sp.strength,
-                                        sp.request_scale, out=y, workspace=ws)
+                                        sp.request_scale, out=y, workspace=ws, dequant=dq)
     else:  # multi_ffn_up
         sp = lw.MULTI_FFN_UP
         h = lw.multi_inputs(sp)
@@ -577,6 +583,14 @@ def config_sweep(torch, dev, stream, with_oracle=True):
     e = _gemm_entry(2.0 * T * (K * N + K * r + r * N), fused, own, None, byt)
     e["workload"] = f"4-bit weight: T={T} K={K} N={N} r={r}, codebook + fp32 absmax per 64"
     e["bf16_hipblaslt_ms"] = tor
+    # the weight dequantized inside the GEMM instead of once into the panel (the same output bits)
+    e["in_gemm_ms"] = _launch_stats(torch, stream, lambda: rg.lora_linear_nf4(
+        x, codes, absmax, cb, N, b, A, B, spec.alpha, out=y, workspace=ws, dequant="in_gemm"))["median"]
+    # the first 256 tokens of the layer: the automatic choice is the in-GEMM form there
+    x256, y256 = x[:256], y[:256]
+    e["tokens256"] = {m + "_ms": _launch_stats(torch, stream, lambda: rg.lora_linear_nf4(
+        x256, codes, absmax, cb, N, b, A, B, spec.alpha, out=y256, workspace=ws, dequant=m))["median"]
+        for m in ("in_gemm", "panel")}
     e["note"] = ("overhead against the 4-bit base path (torch has no 4-bit GEMM); bf16_hipblaslt_ms: "
                  "hipBLASLt on the same GEMM with the weight dequantized to bf16 beforehand, for context")
     if with_oracle:

@@ -25,6 +25,7 @@
 // buffered; out-of-range rows and K tails read as zero through the buffer
 // resource's range check.
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -861,58 +862,120 @@ struct Nf4Table {
   uint32_t lo[4], hi[4];
 };
 
-// The table in four steps of 8 instructions (spread over four MFMA bundles): the products of
-// entries 0-7, of entries 8-15, the bf16 conversions, the byte split.
+// f(0), f(1), .., f(N - 1) with compile-time indices: a loop unrolled whatever the size of its
+// body (past a size, the compiler's own full unrolling gives up and leaves the index a run-time
+// value, which turns register arrays indexed by it into scratch memory).
+template <class F, int... I>
+__device__ __forceinline__ void unrolled_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void unrolled(F& f) {
+  unrolled_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Empty asm on a value: the instructions that produce it stay in the MFMA bundle where they
+// are placed (the compiler would otherwise sink them toward their use, past the bundles the
+// work is spread over, or to the LDS writes after the barrier).
+__device__ __forceinline__ void pin(uint32_t& v) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(v));
+#endif
+}
+
+// The table in 11 sub-steps of at most 3 VALU instructions: s < 8 scales entries 2s and 2s + 1
+// and rounds them to a bf16 pair (two multiplies, one conversion); s = 8, 9, 10 split the pairs
+// into low and high bytes (3, 3 and 2 byte permutes).
+constexpr int kNf4TableSteps = 11;
 struct Nf4TableBuild {
-  float v[16];
   uint32_t t[8];
 };
 __device__ __forceinline__ void nf4_table_step(Nf4TableBuild& b, Nf4Table& r, const float (&cb)[16], float a,
-                                               int step) {
-  if (step == 0 || step == 1) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) b.v[8 * step + c] = cb[8 * step + c] * a;
-  } else if (step == 2) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) b.t[c] = pack_bf16x2(b.v[2 * c], b.v[2 * c + 1]);
+                                               int s) {
+  if (s < 8) {
+    b.t[s] = pack_bf16x2(cb[2 * s] * a, cb[2 * s + 1] * a);
+    pin(b.t[s]);
+    return;
+  }
+  // lo[i] holds bytes 0 and 2 (the low bytes of entries 4i, 4i + 1) of t[2i], then of t[2i + 1];
+  // hi[i] the high bytes
+  auto lo = [&](int i) {
+    r.lo[i] = __builtin_amdgcn_perm(b.t[2 * i + 1], b.t[2 * i], 0x06040200u);
+    pin(r.lo[i]);
+  };
+  auto hi = [&](int i) {
+    r.hi[i] = __builtin_amdgcn_perm(b.t[2 * i + 1], b.t[2 * i], 0x07050301u);
+    pin(r.hi[i]);
+  };
+  if (s == 8) {
+    lo(0), hi(0), lo(1);
+  } else if (s == 9) {
+    hi(1), lo(2), hi(2);
   } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // bytes 0 and 2 (low bytes of entries 4i, 4i + 1) of t[2i], then of t[2i + 1]; then the high bytes
-      r.lo[i] = __builtin_amdgcn_perm(b.t[2 * i + 1], b.t[2 * i], 0x06040200u);
-      r.hi[i] = __builtin_amdgcn_perm(b.t[2 * i + 1], b.t[2 * i], 0x07050301u);
-    }
+    lo(3), hi(3);
   }
 }
 
 // Eight weight elements from one code word (byte j: element 2j in bits 0-3, 2j + 1 in bits
-// 4-7) as four bf16 pairs in element order, in four steps. v_perm_b32 (S0, S1, sel): output
-// byte i is byte sel_i of the 8 bytes S1 (0-3), S0 (4-7); selectors 8-11 give 0xff or 0 by
-// the sign bit of bytes 1, 3, 5, 7. Step 0 gathers the codes four to a register as bytes, in
-// element order (0, 1, 4, 5) and (2, 3, 6, 7), and turns their bit 3 into byte masks through
-// those sign selectors (bit 3 of element 2j + h is bit 8j + 4h + 3 of the word, shifted to a
-// sign position); steps 1 and 2 look the two groups up, low and high bytes; step 3
-// interleaves the bytes back into bf16 values.
+// 4-7) as four bf16 pairs in element order, in 9 sub-steps of at most 4 VALU instructions.
+// v_perm_b32 (S0, S1, sel): output byte i is byte sel_i of the 8 bytes S1 (0-3), S0 (4-7);
+// selectors 8-11 give 0xff or 0 by the sign bit of bytes 1, 3, 5, 7. Sub-steps 0-3 gather the
+// codes four to a register as bytes, in element order (0, 1, 4, 5) and (2, 3, 6, 7), and turn
+// their bit 3 into byte masks through those sign selectors (bit 3 of element 2j + h is bit
+// 8j + 4h + 3 of the word, shifted to a sign position); 4-7 look the two groups up, low and high
+// bytes, in the half that bit 3 picks; 8 interleaves the bytes back into bf16 values.
+constexpr int kNf4WordSteps = 9;
 struct Nf4Word {
-  uint32_t xa, xb, ma, mb, la, ha, lb, hb;
+  uint32_t wr4, xa, xb, ma, mb, la, ha, lb, hb;
 };
 __device__ __forceinline__ void nf4_word_step(Nf4Word& s, u32x4& out, uint32_t w, const Nf4Table& tb, int step) {
   auto pick = [](uint32_t m, uint32_t hi_half, uint32_t lo_half) { return (hi_half & m) | (lo_half & ~m); };
-  if (step == 0) {
-    const uint32_t wr4 = w >> 4;
-    s.xa = __builtin_amdgcn_perm(wr4, w, 0x06020400u) & 0x07070707u;  // elements 0, 1, 4, 5
-    s.xb = __builtin_amdgcn_perm(wr4, w, 0x07030501u) & 0x07070707u;  // elements 2, 3, 6, 7
-    s.ma = __builtin_amdgcn_perm(w << 8, w << 12, 0x0B090A08u);
-    s.mb = __builtin_amdgcn_perm(w, w << 4, 0x0B090A08u);
-  } else if (step == 1) {
-    s.la = pick(s.ma, __builtin_amdgcn_perm(tb.lo[3], tb.lo[2], s.xa), __builtin_amdgcn_perm(tb.lo[1], tb.lo[0], s.xa));
-    s.ha = pick(s.ma, __builtin_amdgcn_perm(tb.hi[3], tb.hi[2], s.xa), __builtin_amdgcn_perm(tb.hi[1], tb.hi[0], s.xa));
-  } else if (step == 2) {
-    s.lb = pick(s.mb, __builtin_amdgcn_perm(tb.lo[3], tb.lo[2], s.xb), __builtin_amdgcn_perm(tb.lo[1], tb.lo[0], s.xb));
-    s.hb = pick(s.mb, __builtin_amdgcn_perm(tb.hi[3], tb.hi[2], s.xb), __builtin_amdgcn_perm(tb.hi[1], tb.hi[0], s.xb));
-  } else {
-    out = u32x4{__builtin_amdgcn_perm(s.ha, s.la, 0x05010400u), __builtin_amdgcn_perm(s.hb, s.lb, 0x05010400u),
-                __builtin_amdgcn_perm(s.ha, s.la, 0x07030602u), __builtin_amdgcn_perm(s.hb, s.lb, 0x07030602u)};
+  auto look = [&](const uint32_t (&t)[4], uint32_t x, uint32_t m) {
+    return pick(m, __builtin_amdgcn_perm(t[3], t[2], x), __builtin_amdgcn_perm(t[1], t[0], x));
+  };
+  switch (step) {
+    case 0:
+      s.wr4 = w >> 4;
+      s.xa = __builtin_amdgcn_perm(s.wr4, w, 0x06020400u);  // elements 0, 1, 4, 5
+      pin(s.wr4);
+      pin(s.xa);
+      break;
+    case 1:
+      s.xa &= 0x07070707u;
+      s.xb = __builtin_amdgcn_perm(s.wr4, w, 0x07030501u) & 0x07070707u;  // elements 2, 3, 6, 7
+      pin(s.xa);
+      pin(s.xb);
+      break;
+    case 2:
+      s.ma = __builtin_amdgcn_perm(w << 8, w << 12, 0x0B090A08u);
+      pin(s.ma);
+      break;
+    case 3:
+      s.mb = __builtin_amdgcn_perm(w, w << 4, 0x0B090A08u);
+      pin(s.mb);
+      break;
+    case 4:
+      s.la = look(tb.lo, s.xa, s.ma);
+      pin(s.la);
+      break;
+    case 5:
+      s.ha = look(tb.hi, s.xa, s.ma);
+      pin(s.ha);
+      break;
+    case 6:
+      s.lb = look(tb.lo, s.xb, s.mb);
+      pin(s.lb);
+      break;
+    case 7:
+      s.hb = look(tb.hi, s.xb, s.mb);
+      pin(s.hb);
+      break;
+    default:  // interleave low and high bytes back into bf16 values
+      out = u32x4{__builtin_amdgcn_perm(s.ha, s.la, 0x05010400u), __builtin_amdgcn_perm(s.hb, s.lb, 0x05010400u),
+                  __builtin_amdgcn_perm(s.ha, s.la, 0x07030602u), __builtin_amdgcn_perm(s.hb, s.lb, 0x07030602u)};
+#if defined(__HIP_DEVICE_COMPILE__)
+      asm volatile("" : "+v"(out[0]), "+v"(out[1]), "+v"(out[2]), "+v"(out[3]));
+#endif
   }
 }
 
@@ -1334,33 +1397,14 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
   Nf4TableBuild tbb;
   Nf4Table tb;
   Nf4Word wst;
-  // Step g of the dequantization of one weight unit: table steps 0-3, then four steps per word.
-  // (Empty asm statements on each step's results keep the step in the MFMA bundle where it is
-  // placed: the compiler would otherwise sink the work to the LDS writes after the barrier.)
-  auto nf4_step = [&](const Nf4Codes<WPT>& c, int g) {
-    if (g < 4) {
+  // Sub-step g of the dequantization of one weight unit: the table's, then each word's.
+  constexpr int NSUB = kNf4TableSteps + kNf4WordSteps * WPT;
+  auto nf4_sub = [&](const Nf4Codes<WPT>& c, int g) {
+    if (g < kNf4TableSteps) {
       nf4_table_step(tbb, tb, cb, c.a, g);
-#if defined(__HIP_DEVICE_COMPILE__)
-      if (g < 2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(tbb.v[8 * g + e]));
-      } else if (g == 2) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) asm volatile("" : "+v"(tbb.t[e]));
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(tb.lo[e]), "+v"(tb.hi[e]));
-      }
-#endif
-    } else if (g < 4 + 4 * WPT) {
-      const int j = (g - 4) / 4, st = (g - 4) % 4;
-      nf4_word_step(wst, dq[j], c.q[j / 4][j % 4], tb, st);
-#if defined(__HIP_DEVICE_COMPILE__)
-      if (st == 0) asm volatile("" : "+v"(wst.xa), "+v"(wst.xb), "+v"(wst.ma), "+v"(wst.mb));
-      else if (st == 1) asm volatile("" : "+v"(wst.la), "+v"(wst.ha));
-      else if (st == 2) asm volatile("" : "+v"(wst.lb), "+v"(wst.hb));
-      else asm volatile("" : "+v"(dq[j][0]), "+v"(dq[j][1]), "+v"(dq[j][2]), "+v"(dq[j][3]));
-#endif
+    } else if (g < NSUB) {
+      const int j = (g - kNf4TableSteps) / kNf4WordSteps;
+      nf4_word_step(wst, dq[j], c.q[j / 4][j % 4], tb, (g - kNf4TableSteps) % kNf4WordSteps);
     }
   };
 
@@ -1380,8 +1424,8 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
       if (s < NE) continue;
       nfs.load(c_work, cr, ar, s - NE);
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-#pragma unroll
-      for (int g = 0; g < 4 + 4 * WPT; ++g) nf4_step(c_work, g);
+      auto sub = [&](int g) { nf4_sub(c_work, g); };
+      unrolled<NSUB>(sub);
 #pragma unroll
       for (int j = 0; j < WPT; ++j) nf4_write(smem + (2 * s + 1) * P::SLOT_BYTES, j);
     }
@@ -1458,13 +1502,25 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
     // copies.
     constexpr bool DQ = NF4 && !EXT;
     const bool load_c = DQ && t + 3 < NS;
-    // the dequantization steps run one per bundle from the first bundle of k-step 0 on; word j
-    // is written at bundle LS j + LS / 2 of k-step 1, after its last step
-    static_assert(!NF4 || (4 + 4 * WPT <= 2 * NB && LS >= 4 && 4 + 3 < NB + LS / 2), "dequantization schedule");
-    // (one loop per k-step: one loop over both is past the compiler's full-unroll limit)
-    __builtin_amdgcn_sched_barrier(0);
+    // the dequantization sub-steps run SPB per bundle (one for the 256 x 256 tile's 128 bundles,
+    // two for the 128 x 128 tile's 32), ending two bundles before the stage does, so that few
+    // dequantized words wait in registers for the barrier; word j is written to the slot the
+    // barrier releases at the bundle after its last sub-step, at the earliest at bundle j + 1 of
+    // k-step 1 (bundles counted from the start of the stage)
+    constexpr int SPB = NB >= 64 ? 1 : 2;
+    constexpr int START = 2 * NB - 2 - ((NSUB - 1) / SPB + 1);
+    auto write_bundle = [](int j) {
+      const int done = START + (kNf4TableSteps + kNf4WordSteps * (j + 1) - 1) / SPB;
+      return done + 1 > NB + 1 + j ? done + 1 : NB + 1 + j;
+    };
+    static_assert(!NF4 || (START >= 1 && START + (NSUB - 1) / SPB + 1 < 2 * NB && NB + WPT < 2 * NB),
+                  "dequantization schedule");
+    auto sub_steps = [&](int b) {  // the sub-steps of bundle b of the stage
+      if (b < START) return;
 #pragma unroll
-    for (int m = 0; m < NB; ++m) {  // k-step 0
+      for (int q = 0; q < SPB; ++q) nf4_sub(c_work, SPB * (b - START) + q);
+    };
+    auto k0 = [&](int m) {  // bundle m of k-step 0
       const int i = m / P::NJ, j = m % P::NJ;
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[0].a[i], fr[0].b[j], acc[i][j], 0, 0, 0);
       if constexpr (DQ) __builtin_amdgcn_sched_barrier(0);  // (the bundle's VALU work after its MFMA)
@@ -1486,21 +1542,20 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
           }
           if (load_c) nfs.load(c_load, cr, ar, t + 3 - NE);
         }
-        if constexpr (DQ) nf4_step(c_work, m);
+        if constexpr (DQ) sub_steps(m);
       }
       if (m % LS == LS / 2) {
         if constexpr (EXT) issue_load(2 * t + 4, m / LS);
         else ox.load_one(m / LS, xdst, xr, kb2);
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int m = 0; m < NB; ++m) {  // k-step 1
+    };
+    auto k1 = [&](int m) {  // bundle m of k-step 1
       const int i = m / P::NJ, j = m % P::NJ;
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fr[1].a[i], fr[1].b[j], acc[i][j], 0, 0, 0);
       if constexpr (DQ) {
         __builtin_amdgcn_sched_barrier(0);
-        nf4_step(c_work, NB + m);
+        sub_steps(NB + m);
       }
       if (m == 0) {
         __builtin_amdgcn_sched_barrier(0);
@@ -1511,12 +1566,27 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
       } else if (m % RS == 1) {
         read_frag(fr[0], m / RS, xs2, ws2, 0);
       }
+      if constexpr (DQ) {
+#pragma unroll
+        for (int w = 0; w < WPT; ++w)
+          if (write_bundle(w) == NB + m) nf4_write(wdst, w);
+      }
       if (m % LS == LS / 2) {
         if constexpr (EXT) issue_load(2 * t + 5, m / LS);
-        else if constexpr (NF4) nf4_write(wdst, m / LS);
-        else ow.load_one(m / LS, wdst, wr, kb2);
+        else if constexpr (!NF4) ow.load_one(m / LS, wdst, wr, kb2);
       }
       __builtin_amdgcn_sched_barrier(0);
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NF4) {
+      unrolled<NB>(k0);
+      unrolled<NB>(k1);
+    } else {
+      // (one loop per k-step: one loop over both is past the compiler's full-unroll limit)
+#pragma unroll
+      for (int m = 0; m < NB; ++m) k0(m);
+#pragma unroll
+      for (int m = 0; m < NB; ++m) k1(m);
     }
   };
 
@@ -1619,15 +1689,7 @@ int max_groups_per_tile(const LinearProblem& p, int bn) {
 template __global__ void gemm_flow16_kernel<Flow16Cfg>(LinearProblem, int, int);
 template __global__ void gemm_flow16_kernel<Flow16SCfg>(LinearProblem, int, int);
 template __global__ void gemm_flow16_kernel<Flow16SCfg, true>(LinearProblem, int, int);
-
-// 4-bit weight dequantized inside the hot kernel (one adapter group at most, K a multiple of
-// 64): the 128 x 128 tile, whose two threads per weight row each dequantize 32 elements per
-// stage into registers the kernel has free at two workgroups per CU.
-hipError_t launch_nf4(const LinearProblem& p, hipStream_t s) {
-  const bool ranks_ok = p.n_groups == 0 || (p.n_groups == 1 && p.g[0].rank % 8 == 0);
-  if (!ranks_ok || p.act != Elt::BF16 || p.adapter != Elt::BF16 || p.K % 64 != 0) return hipErrorInvalidValue;
-  return launch_flow16<Flow16SCfg, true>(p, s);
-}
+template __global__ void gemm_flow16_kernel<Flow16Cfg, true>(LinearProblem, int, int);
 
 hipError_t launch(const LinearProblem& p, hipStream_t s) {
   if (max_groups_per_tile(p, Flow16Cfg::BN) <= 2) {
@@ -1646,8 +1708,10 @@ hipError_t launch(const LinearProblem& p, hipStream_t s) {
     const double est256 = 4.0 * static_cast<double>((t256 + cus - 1) / (cus > 0 ? cus : 1));
     const double est128 = 2.0 / 0.85 * static_cast<double>((t128 + 2 * cus - 1) / (cus > 0 ? 2 * cus : 1));
     const bool small = p.tile == 2 || (p.tile == 0 && cus > 0 && est128 < est256);
+    if (p.nf4) return small ? launch_flow16<Flow16SCfg, true>(p, s) : launch_flow16<Flow16Cfg, true>(p, s);
     return small ? launch_flow16<Flow16SCfg>(p, s) : launch_flow16<Flow16Cfg>(p, s);
   }
+  if (p.nf4) return hipErrorInvalidValue;  // (a 4-bit weight has one adapter group)
   using P = HotCfg;
   const int mt = static_cast<int>((p.T + P::BM - 1) / P::BM);
   const int nt = static_cast<int>((p.N + P::BN - 1) / P::BN);
@@ -2425,12 +2489,16 @@ hipError_t launch_lossless(const LinearProblem& p, hipStream_t s, int phase) {
   // few tokens: the rank-wide product runs inside the same launches (phase 1 has nothing to do)
   if (p.skinny != nullptr) return phase == 1 ? hipSuccess : launch_skinny(p, s);
   if (p.nf4 && p.panel == nullptr) {
-    // dequantized inside the hot GEMM (bf16 activations and adapter, ranks multiples of 8)
+    // dequantized inside the hot GEMM (bf16 activations and adapter, one group whose rank is a
+    // multiple of 8, K a multiple of 64)
+    const bool ok = p.act == Elt::BF16 && p.adapter == Elt::BF16 && p.K % 64 == 0 &&
+                    (p.n_groups == 0 || (p.n_groups == 1 && p.g[0].rank % 8 == 0));
+    if (!ok) return hipErrorInvalidValue;
     if (p.n_groups > 0 && phase != 2) {
       const hipError_t e = pipe::down::launch(p, s);
       if (e != hipSuccess) return e;
     }
-    return phase == 1 ? hipSuccess : pipe::launch_nf4(p, s);
+    return phase == 1 ? hipSuccess : pipe::launch(p, s);
   }
   if (p.nf4) {
     // the weight dequantized once into the panel, then the bf16 path over it

@@ -504,9 +504,13 @@ def test_nf4_one_hot_returns_dequantized_columns(T):
 # (<= 128); four (rank 200: the codes of the first main stage are loaded by the prologue ahead of
 # the extension stages); K of one and of two 64-element stages; ragged tiles both ways; a strided
 # input and a column view of a wider output; with and without bias.
+# The last two shapes have enough output tiles that the 256 x 256 tile is chosen on MI355X's 256
+# compute units (one row of weight per thread, eight code words per stage); the others take the
+# 128 x 128 tile.
 @pytest.mark.parametrize("T,K,N,r,bias", [
     (65, 256, 300, 16, True), (130, 256, 300, 0, False), (300, 64, 260, 8, True), (257, 128, 520, 128, True),
-    (600, 448, 1000, 200, False), (1000, 1024, 700, 64, True)])
+    (600, 448, 1000, 200, False), (1000, 1024, 700, 64, True), (1790, 128, 9100, 200, True),
+    (1000, 64, 16384, 16, False)])
 def test_nf4_in_gemm_equals_panel(T, K, N, r, bias):
     d = _nf4_small(T=T, K=K, N=N, r=max(r, 8), bias=bias, seed=60 + T)
     say(f"case nf4 in-GEMM vs panel T={T} K={K} N={N} r={r} bias={bias}")
