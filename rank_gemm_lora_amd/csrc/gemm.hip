@@ -1355,6 +1355,25 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
   const int NU = 2 * NS;
   const __amdgpu_buffer_rsrc_t tr =
       make_rsrc(static_cast<const char*>(p.work) + m0 * p.ldt * 2, static_cast<uint32_t>(rows_m) * ldt_b);
+  // K-extension stages after the prologue's (more than two): per-lane copy offsets of the t~ rows
+  // and of the B rows of each of the tile's two groups, computed once per tile, so that a copy
+  // takes a select and a K-tail mask instead of its whole offset arithmetic (a 4-bit weight, with
+  // its one adapter and the dequantization's registers, keeps the per-copy arithmetic)
+  TileOffsets<P, P::BM> oxe;
+  TileOffsets<P, P::BN> ob0, ob1;
+  if constexpr (!NF4) {
+    oxe.init(ldt_b, 0, rows_m, 0);
+    ob0.init(static_cast<uint32_t>(eg0.rkb), eg0.lo, eg0.hi, eg0.sh);
+    ob1.init(static_cast<uint32_t>(eg1.rkb), eg1.lo, eg1.hi, eg1.sh);
+  }
+  const __amdgpu_buffer_rsrc_t br0 =
+      make_rsrc(eg0.B, static_cast<uint32_t>(eg0.n_cols) * static_cast<uint32_t>(eg0.rkb));
+  const __amdgpu_buffer_rsrc_t br1 =
+      make_rsrc(eg1.B, static_cast<uint32_t>(eg1.n_cols) * static_cast<uint32_t>(eg1.rkb));
+  // this lane's 16-byte chunk of a B row, the same in every copy instruction of a unit (each
+  // instruction covers whole swizzle periods of rows)
+  static_assert((P::WAVES * 64 / P::CPR / P::RPL) % P::CPR == 0, "one chunk per lane across a unit");
+  const int c_ext = (lane % P::CPR) ^ (((wave * 64 + lane) / P::CPR / P::RPL) % P::CPR);
 
   auto slot = [&](int u) { return smem + (u % P::SLOTS) * P::SLOT_BYTES; };
   auto issue_load = [&](int u, int l) {
@@ -1497,6 +1516,19 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
     const int kb2 = (t + 2 - NE) * P::RB;
     char* const xdst = smem + a3 * P::SLOT_BYTES;
     char* const wdst = smem + a * P::SLOT_BYTES;
+    // K-extension stage: its copies belong to extension stage e2 of group 0 or 1 (t + 2 < NE)
+    const int s2 = t + 2;
+    const bool g2 = EXT && s2 >= eg0.ns;
+    const int e2 = g2 ? s2 - eg0.ns : s2;
+    const int kbx2 = (g2 ? eg1.tcb : eg0.tcb) + e2 * P::RB;  // t~ columns of the stage
+    const int kbw2 = e2 * P::RB;                              // B columns of the stage
+    const int rkb2 = g2 ? eg1.rkb : eg0.rkb;
+    auto ext_w_copy = [&](int it) {  // copy `it` of the B unit; chunks past the rank read zero
+      const int slot0 = (it * P::WAVES + wave) * 64;
+      uint32_t v = g2 ? ob1.v[it] : ob0.v[it];
+      if (kbw2 + c_ext * 16 >= rkb2) v = 0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g2 ? br1 : br0, (lds_void*)(wdst + slot0 * 16), 16, v, kbw2, 0, 0);
+    };
     // NF4: a main stage dequantizes the codes of stage t + 2 (loaded during stage t - 1, or by
     // the prologue for the first one) and loads those of stage t + 3 first thing, before its x
     // copies.
@@ -1545,7 +1577,8 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
         if constexpr (DQ) sub_steps(m);
       }
       if (m % LS == LS / 2) {
-        if constexpr (EXT) issue_load(2 * t + 4, m / LS);
+        if constexpr (EXT && NF4) issue_load(2 * t + 4, m / LS);
+        else if constexpr (EXT) oxe.load_one(m / LS, xdst, tr, kbx2);
         else ox.load_one(m / LS, xdst, xr, kb2);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -1572,7 +1605,8 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
           if (write_bundle(w) == NB + m) nf4_write(wdst, w);
       }
       if (m % LS == LS / 2) {
-        if constexpr (EXT) issue_load(2 * t + 5, m / LS);
+        if constexpr (EXT && NF4) issue_load(2 * t + 5, m / LS);
+        else if constexpr (EXT) ext_w_copy(m / LS);
         else if constexpr (!NF4) ow.load_one(m / LS, wdst, wr, kb2);
       }
       __builtin_amdgcn_sched_barrier(0);
