@@ -285,9 +285,10 @@ int lora_linear_multi_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
  *             quality) bytes. In the lossless tier with T > 64 it includes room for
  *             a bf16 copy of the dequantized weight ([N, K], rewritten by every
  *             call that uses it): above 256 tokens dequantizing once per call is
- *             cheaper than once per output tile. Up to 256 tokens (and in the
- *             exact tier) the weight is dequantized inside the kernel that reads
- *             it; lora_linear_nf4_fwd_ex names the choice.
+ *             cheaper than once per output tile. The weight is dequantized inside
+ *             the kernel that reads it up to 64 tokens, up to 256 tokens with a
+ *             bf16 adapter whose rank is a multiple of 8 (or no adapter), and in
+ *             the exact tier; lora_linear_nf4_fwd_ex names the choice.
  */
 int lora_linear_nf4_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
                         const uint8_t* codes, const float* absmax, const float* codebook,
@@ -310,7 +311,8 @@ int lora_linear_nf4_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
  *                     LDS; needs a bf16 adapter whose rank is a multiple of 8
  *                     (or no adapter), LORA_ERR_UNSUPPORTED otherwise
  *   LORA_NF4_AUTO     what lora_linear_nf4_fwd does: the GEMM form up to 256
- *                     tokens (where it measured faster on MI355X), the panel above
+ *                     tokens (where it measured faster on MI355X) when it applies,
+ *                     the panel otherwise
  * Both forms give the same weight, RN_bf16(RN_f32(codebook[code] * absmax)),
  * and the same output bits. Other values: LORA_ERR_UNSUPPORTED.
  * lora_linear_nf4_workspace_size covers every choice; the in-GEMM form needs only

@@ -95,9 +95,9 @@ size_t round_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 // Lossless fp32 adapters on bf16 activations: t~ [T, 3 sum r_pad] bf16, then the
 // split copies A2 of every group ([2 r_pad, K] bf16), then B2 ([n_cols, 3 r_pad]
 // bf16); assign_split() points the groups at them. A lossless 4-bit weight with
-// T > kSkinnyMaxT adds its bf16 panel [N, K] after all of that (256-byte
-// aligned); the GEMM then sees a bf16 weight, so an fp32 adapter takes the
-// split layout.
+// T > kSkinnyMaxT that is dequantized once per call (nf4_uses_panel) adds its bf16
+// panel [N, K] after all of that (256-byte aligned); the GEMM then sees a bf16
+// weight, so an fp32 adapter (which always takes the panel) takes the split layout.
 // The lossless bf16 producer splits K (fp32 partial sums after t~, 256-byte aligned).
 bool producer_split(const LinearProblem& p, bool lossless) {
   return lossless && p.act == Elt::BF16 && p.adapter == Elt::BF16 && p.n_groups > 0 &&

@@ -1255,11 +1255,11 @@ __device__ __forceinline__ void ext_stage_loads(const ExtPlan& g, int e, const T
 // bitwise-identical results.
 // NF4: the base weight is 4-bit codes with one fp32 scale per 64-element block (K a multiple
 // of 64). A main stage's weight unit is then written by the waves themselves instead of
-// copied: the codes of the weight unit of stage t + 2 are loaded into registers during stage
-// t - 1 (after the wait of that stage's code loads, before its x copies), dequantized into
-// registers over k-step 0 of stage t, and written into the slot that the barrier of stage t
-// releases, where the copies would have gone. The weight is the panel kernel's, bit for bit,
-// and so is the result.
+// copied: the codes of the weight unit of stage t + 2 are loaded into registers at the start
+// of stage t - 1 (after the wait for that stage's own codes, before its x copies), dequantized
+// during stage t in sub-steps of a few VALU instructions, one or two per MFMA bundle, and each
+// word written into the slot that the barrier of stage t releases, where the copies would have
+// gone. The weight is the panel kernel's, bit for bit, and so is the result.
 template <class P, bool NF4 = false>
 __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearProblem p, int mt, int nt) {
   static_assert(P::WAVES == 4, "schedule written for 4 waves");
@@ -1307,14 +1307,13 @@ __global__ __launch_bounds__(P::THREADS, P::OCC) void gemm_flow16_kernel(LinearP
   constexpr int NC = WPT / 4 + 1;  // code loads per stage
   Share nfs;
   Nf4Codes<WPT> c_load, c_work;     // codes of a later stage in flight; codes being dequantized
-  u32x4 dq[WPT];                    // dequantized weight words of stage t + 2
+  u32x4 dq[WPT];                    // dequantized weight words of stage t + 2, until written
   float cb[16];
   const __amdgpu_buffer_rsrc_t cr =
       make_rsrc(NF4 ? p.codes + n0 * (p.K / 2) : nullptr, NF4 ? static_cast<uint32_t>(rows_n * (p.K / 2)) : 0u);
   const __amdgpu_buffer_rsrc_t ar =
       make_rsrc(NF4 ? p.absmax + n0 * (p.K / 64) : nullptr, NF4 ? static_cast<uint32_t>(rows_n * (p.K / 64) * 4) : 0u);
   if constexpr (NF4) {
-    static_assert(WPT == TileOffsets<P, P::BN>::N, "one dequantized word per weight copy slot of the schedule");
     nfs.init(tid, rows_n, p.K);
 #pragma unroll
     for (int c = 0; c < 16; ++c) cb[c] = p.codebook[c];
