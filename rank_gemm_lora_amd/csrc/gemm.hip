@@ -2256,35 +2256,41 @@ __global__ __launch_bounds__(256) void skinny_kernel(LinearProblem p, int nbw, i
 // chunks' partial sums added in chunk order), then each thread takes one output
 // column: acc = the weight partial sums in chunk order, += t~ . B_g^T in fp32
 // (rank index ascending) for the group covering the column, + bias, one
-// rounding. Token rows past T repeat the last token (valid memory) and are
-// never stored; all partial sums of a thread are loaded before they are added.
+// rounding. Token rows past T repeat the last token and columns past N read
+// column N - 1 (valid memory); neither is stored. The chunk count S is a
+// template parameter, so a thread issues all its partial-sum loads before it
+// waits for any of them; each 8-rank piece of t~ is read from LDS as 16-byte
+// vectors before its FMAs. (Both measured on MI355X, with the same bits: a
+// 64-token FFN-up call went from 29.1 to 26.4 us, FFN down from 26.4 to 24.3.)
 constexpr int kMaxChunks = 8;  // skinny_plan never makes more
 
-template <bool AF32, int kFinishTokens>
-__global__ __launch_bounds__(256) void skinny_finish_kernel(LinearProblem p, int S, int64_t npad) {
+template <bool AF32, int kFinishTokens, int S>
+__global__ __launch_bounds__(256) void skinny_finish_kernel(LinearProblem p, int64_t npad) {
   extern __shared__ float tt[];  // [kFinishTokens, ldt]
   const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kFinishTokens;
   const int ldt = static_cast<int>(p.ldt);
   const float* pt = p.skinny + static_cast<int64_t>(S) * p.T * npad;
   const int64_t n = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  // this thread's weight partial sums, loaded first: their latency overlaps the t~ phase
-  float v[kFinishTokens][kMaxChunks];
+  // this thread's weight partial sums, loaded first: their latency overlaps the t~ phase.
+  // Every load is issued (a column past N reads column N - 1 and is never stored), with the chunk
+  // count fixed at compile time, so that none waits for another.
+  float v[kFinishTokens][S];
+  const float* pc = p.skinny + min<int64_t>(n, p.N - 1);
 #pragma unroll
   for (int i = 0; i < kFinishTokens; ++i) {
     const int64_t t = min<int64_t>(t0 + i, p.T - 1);
 #pragma unroll
-    for (int s = 0; s < kMaxChunks; ++s) v[i][s] = (s < S && n < p.N) ? p.skinny[(s * p.T + t) * npad + n] : 0.f;
+    for (int s = 0; s < S; ++s) v[i][s] = pc[(s * p.T + t) * npad];
   }
   for (int c = threadIdx.x; c < kFinishTokens * ldt; c += 256) {
     const int j = c / ldt, col = c - j * ldt;
     const int64_t t = min<int64_t>(t0 + j, p.T - 1);
-    float v[kMaxChunks];
+    float v[S];
 #pragma unroll
-    for (int s = 0; s < kMaxChunks; ++s) v[s] = s < S ? pt[(s * p.T + t) * ldt + col] : 0.f;
+    for (int s = 0; s < S; ++s) v[s] = pt[(s * p.T + t) * ldt + col];
     float sum = 0.f;
 #pragma unroll
-    for (int s = 0; s < kMaxChunks; ++s)
-      if (s < S) sum += v[s];
+    for (int s = 0; s < S; ++s) sum += v[s];
     int gi = 0;
     while (gi + 1 < p.n_groups && col >= p.g[gi + 1].t_col) ++gi;
     const float sc = p.g[gi].scale;
@@ -2298,8 +2304,7 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(LinearProblem p, int
   for (int i = 0; i < kFinishTokens; ++i) {
     acc[i] = 0.f;
 #pragma unroll
-    for (int s = 0; s < kMaxChunks; ++s)
-      if (s < S) acc[i] += v[i][s];
+    for (int s = 0; s < S; ++s) acc[i] += v[i][s];
   }
   for (int gi = 0; gi < p.n_groups; ++gi) {
     const GroupDev& g = p.g[gi];
@@ -2316,10 +2321,17 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(LinearProblem p, int
 #pragma unroll
         for (int e = 0; e < PE; ++e)
           bv[e] = AF32 ? __uint_as_float(w[e]) : __uint_as_float(e & 1 ? w[e >> 1] & 0xffff0000u : w[e >> 1] << 16);
+        // this piece's t~ of every token, read as 16-byte vectors before the FMAs (t_col and
+        // ldt are multiples of the rank padding and qq of PE: 16-byte aligned)
+        f32x4 tv[kFinishTokens][PE / 4];
+#pragma unroll
+        for (int i = 0; i < kFinishTokens; ++i)
+#pragma unroll
+          for (int h = 0; h < PE / 4; ++h) tv[i][h] = *reinterpret_cast<const f32x4*>(tg + i * ldt + qq + 4 * h);
 #pragma unroll
         for (int e = 0; e < PE; ++e)
 #pragma unroll
-          for (int i = 0; i < kFinishTokens; ++i) acc[i] = fmaf(tg[i * ldt + qq + e], bv[e], acc[i]);
+          for (int i = 0; i < kFinishTokens; ++i) acc[i] = fmaf(tv[i][e >> 2][e & 3], bv[e], acc[i]);
       }
     }
     for (; qq < g.rank; ++qq) {
@@ -2337,6 +2349,23 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(LinearProblem p, int
     if (t0 + i < p.T)
       static_cast<bf16_bits*>(p.y)[(t0 + i) * p.ldy + n] = f32_to_bf16_rne(has_bias ? acc[i] + bias : acc[i]);
   }
+}
+
+template <bool AF32, int TOK>
+hipError_t launch_finish(const LinearProblem& p, hipStream_t s, dim3 grid, size_t shmem, int S, int64_t npad) {
+  static_assert(kMaxChunks == 8, "one instance per chunk count 1 .. kMaxChunks");
+  switch (S) {
+    case 1: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 1>), grid, dim3(256), shmem, s, p, npad); break;
+    case 2: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 2>), grid, dim3(256), shmem, s, p, npad); break;
+    case 3: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 3>), grid, dim3(256), shmem, s, p, npad); break;
+    case 4: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 4>), grid, dim3(256), shmem, s, p, npad); break;
+    case 5: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 5>), grid, dim3(256), shmem, s, p, npad); break;
+    case 6: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 6>), grid, dim3(256), shmem, s, p, npad); break;
+    case 7: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 7>), grid, dim3(256), shmem, s, p, npad); break;
+    case 8: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 8>), grid, dim3(256), shmem, s, p, npad); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <bool NF4, bool AF32>
@@ -2377,9 +2406,8 @@ hipError_t launch_skinny(const LinearProblem& p, hipStream_t s) {
   constexpr int tok = 4;
   const dim3 fgrid(static_cast<unsigned>((p.N + 255) / 256), static_cast<unsigned>((p.T + tok - 1) / tok));
   const size_t shmem = static_cast<size_t>(tok) * static_cast<size_t>(p.ldt) * 4;
-  if (af32) hipLaunchKernelGGL((skinny_finish_kernel<true, tok>), fgrid, dim3(256), shmem, s, p, S, npad);
-  else hipLaunchKernelGGL((skinny_finish_kernel<false, tok>), fgrid, dim3(256), shmem, s, p, S, npad);
-  return hipGetLastError();
+  return af32 ? launch_finish<true, tok>(p, s, fgrid, shmem, S, npad)
+              : launch_finish<false, tok>(p, s, fgrid, shmem, S, npad);
 }
 
 }  // namespace
