@@ -59,7 +59,8 @@ def main():
     ap.add_argument("--layer-only", action="store_true",
                     help="only run the timed fused steps (for counter collection) and exit")
     ap.add_argument("--workload", choices=["attn_proj", "qkv_bf16", "qkv_f32", "nf4_layer", "nf4_layer_in_gemm",
-                                           "nf4_tokens256", "multi_ffn_up"],
+                                           "nf4_tokens256", "multi_ffn_up", "few_ffn_up", "backward_ffn_up",
+                                           "backward_ffn_down"],
                     help="only run this workload's fused call (--warmup + --steps times; for counter runs) and exit")
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="turn the four counter runs in DIR (f/, w/: FETCH_SIZE / WRITE_SIZE of --layer-only; "
@@ -320,6 +321,33 @@ def run_workload(torch, dev, name, warmup, steps):
                          dtype=torch.uint8, device=dev)
         fn = lambda: rg.lora_linear_nf4(x, codes, absmax, cb, sp.N, b, A, B, sp.alpha, sp.strength,
                                         sp.request_scale, out=y, workspace=ws, dequant=dq)
+    elif name == "few_ffn_up":  # 64 tokens: the few-token kernel and its finishing kernel
+        sp = lw.FEW_FFN_UP
+        h = lw.linear_inputs(sp)
+        x, W, b, A, B = (d2(h[k]) for k in ("x", "W", "b", "A", "B"))
+        y = torch.empty((sp.T, sp.N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(rg.lora_linear_workspace_size(sp.T, sp.K, sp.N, [sp.rank], rg.LORA_BF16), dtype=torch.uint8,
+                         device=dev)
+        fn = lambda: rg.lora_linear(x, W, b, A, B, sp.alpha, sp.strength, sp.request_scale, out=y, workspace=ws)
+    elif name in ("backward_ffn_up", "backward_ffn_down"):  # dx, dA, dB, db with t~ from the forward call
+        up_h, down_h = lw.ffn_pair_inputs()
+        sp, h = (lw.FFN_UP, up_h) if name == "backward_ffn_up" else (lw.FFN_DOWN, down_h)
+        del up_h, down_h
+        x, W, A, B = d2(h["x"]), d2(h["W"]), d2(h["A"]), d2(h["B"])
+        T, K, N, r = sp.T, sp.K, sp.N, sp.rank
+        dy = torch.randn((T, N), device=dev, generator=torch.Generator(device=dev).manual_seed(17)).to(torch.bfloat16)
+        ws = torch.empty(max(1, rg.lora_linear_bwd_workspace_size(T, K, N, r)), dtype=torch.uint8, device=dev)
+        outs = (torch.empty((T, K), dtype=torch.bfloat16, device=dev), torch.empty((r, K), device=dev),
+                torch.empty((N, r), device=dev), torch.empty((N,), device=dev))
+        fws = torch.empty(max(1, rg.lora_linear_workspace_size(T, K, N, [r], rg.LORA_BF16)), dtype=torch.uint8,
+                          device=dev)
+        rg.lora_linear(x, W, d2(h["b"]), A, B, sp.alpha, sp.strength, sp.request_scale, workspace=fws)
+        rp = -(-r // 64) * 64
+        sid = torch.cuda.current_stream().cuda_stream
+        fn = lambda: rg.lora_linear_bwd(x.data_ptr(), T, K, K, W.data_ptr(), N, A.data_ptr(), B.data_ptr(), r,
+                                        sp.alpha, sp.strength, sp.request_scale, dy.data_ptr(), N,
+                                        outs[0].data_ptr(), K, outs[1].data_ptr(), outs[2].data_ptr(),
+                                        outs[3].data_ptr(), fws.data_ptr(), rp, ws.data_ptr(), ws.numel(), sid)
     else:  # multi_ffn_up
         sp = lw.MULTI_FFN_UP
         h = lw.multi_inputs(sp)
