@@ -35,7 +35,8 @@
  *   A non-finite alpha, strength or request_scale is LORA_ERR_NONFINITE
  *   (FastVideo DenseLoRAPatch rejects a non-finite strength).
  * - Calls on distinct streams with distinct output and workspace buffers may
- *   run concurrently; the library holds no mutable global state.
+ *   run concurrently; the library holds no mutable global state apart from
+ *   the per-device scratch array of lora_linear_fwd_noalloc (see there).
  *
  * Quality tiers (SGLang PR #43501, Modifications):
  * - LORA_LOSSLESS (default): one fused pass. t~ = RN_adt(s . (x . A^T)) is
