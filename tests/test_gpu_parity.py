@@ -756,9 +756,17 @@ def test_backward_with_the_forward_t_is_the_same_bits(T, K, N, r):
     tt = ws[:T * rp * 2].view(torch.bfloat16).view(T, rp)
     got = rg.lora_linear_backward(x, W, A, B, dy, d["alpha"], 0.8, 0.7, t_tilde=tt)
     want = rg.lora_linear_backward(x, W, A, B, dy, d["alpha"], 0.8, 0.7)
+    # the same t~ at a row stride of rp + 3 elements from a start that is only 2-byte aligned
+    # (its transposed copy then takes the element-wise transpose instead of 16-byte pieces)
+    wide = torch.full((T, rp + 4), float("nan"), dtype=torch.bfloat16, device=DEV)
+    odd = wide.view(-1)[1:1 + (T - 1) * (rp + 3) + rp].as_strided((T, rp), (rp + 3, 1))
+    odd.copy_(tt)
+    assert odd.stride(0) == rp + 3 and odd.data_ptr() % 16 != 0
+    got_odd = rg.lora_linear_backward(x, W, A, B, dy, d["alpha"], 0.8, 0.7, t_tilde=odd)
     torch.cuda.synchronize()
-    for name, g, w in zip(("dx", "dA", "dB", "db"), got, want):
+    for name, g, g2, w in zip(("dx", "dA", "dB", "db"), got, got_odd, want):
         assert torch.equal(g, w), name
+        assert torch.equal(g2, w), name + " (t~ at an odd stride)"
 
 
 def test_backward_partial_outputs_and_empty_batch():
