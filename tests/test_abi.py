@@ -132,8 +132,8 @@ def test_workspace_size():
 @pytest.mark.parametrize("T,K,N,ranks", [(1, 4096, 14336, [16]), (16, 1536, 8960, [64]), (64, 8960, 1536, [64]),
                                          (10, 128, 96, []), (33, 3072, 9216, [128, 128, 128]), (64, 64, 96, [8])])
 def test_workspace_size_few_tokens(T, K, N, ranks):
-    """T <= 64 (lossless): S fp32 partial sums [S, T, round_up(N, 64) + R], 1 <= S <= ceil(K / 64),
-    or the intermediate's layout when that is larger (the activation dtype is not an argument)."""
+    """T <= 64 (lossless): S fp32 partial sums [S, T, round_up(N, 64) + R] with S the header's chunk
+    count, or the intermediate's layout when that is larger (the activation dtype is not an argument)."""
     R = sum(-(-r // 64) * 64 for r in ranks)
     row = T * (-(-N // 64) * 64 + R) * 4
     for adt in (BF16, F32):
@@ -146,6 +146,8 @@ def test_workspace_size_few_tokens(T, K, N, ranks):
         assert got >= plain
         if got != plain or got % row == 0:
             assert got % row == 0 and 1 <= got // row <= -(-K // 64), (got, row)
+        if got != plain:  # the partial sums' layout: S as the header defines it
+            assert got == _skinny_bytes(T, K, N, R), (got, _skinny_bytes(T, K, N, R))
     assert rg.lora_linear_workspace_size(T, K, N, ranks, BF16, EXACT) == T * R * 2
 
 
@@ -206,9 +208,9 @@ def test_multi_validation():
 
 def _skinny_bytes(T, K, N, ldt):
     """The few-token layout the header documents: S fp32 partial sums [S, T, round_up(N, 64) + ldt],
-    S = the number of K chunks (about 8, each a multiple of 128)."""
+    S = the number of K chunks (at most 8, each a multiple of 128 of at least 512 elements)."""
     c = -(-K // 8)
-    c = -(-c // 128) * 128
+    c = max(512, -(-c // 128) * 128)
     S = -(-K // c)
     return S * T * (-(-N // 64) * 64 + ldt) * 4
 
