@@ -416,7 +416,7 @@ size_t lora_linear_bwd_workspace_size(int64_t T, int64_t K, int64_t N, int32_t r
  * intermediate as [T, 3 R] bf16 plus the split copies of A ([2 R, K]) and B (at
  * most [N, 3 R]), each region 256-byte aligned. A lossless call with at most 64
  * tokens on bf16 activations splits K into S chunks (S = ceil(K / c), c =
- * max(512, round_up(ceil(K / 8), 128))) and needs S fp32 partial sums of the
+ * max(512, round_up(ceil(K / 32), 128))) and needs S fp32 partial sums of the
  * outputs and of x.A^T instead ([S, T, round_up(N, 64) + R] fp32);
  * for T <= 64 the larger of the layouts is returned. Returns 0 when T, K or
  * N <= 0, or when no rank is positive and T > 64.

@@ -2262,7 +2262,6 @@ __global__ __launch_bounds__(256) void skinny_kernel(LinearProblem p, int nbw, i
 // waits for any of them; each 8-rank piece of t~ is read from LDS as 16-byte
 // vectors before its FMAs. (Both measured on MI355X, with the same bits: a
 // 64-token FFN-up call went from 29.1 to 26.4 us, FFN down from 26.4 to 24.3.)
-constexpr int kMaxChunks = 8;  // skinny_plan never makes more
 
 template <bool AF32, int kFinishTokens, int S>
 __global__ __launch_bounds__(256) void skinny_finish_kernel(LinearProblem p, int64_t npad) {
@@ -2351,21 +2350,16 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(LinearProblem p, int
   }
 }
 
-template <bool AF32, int TOK>
-hipError_t launch_finish(const LinearProblem& p, hipStream_t s, dim3 grid, size_t shmem, int S, int64_t npad) {
-  static_assert(kMaxChunks == 8, "one instance per chunk count 1 .. kMaxChunks");
-  switch (S) {
-    case 1: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 1>), grid, dim3(256), shmem, s, p, npad); break;
-    case 2: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 2>), grid, dim3(256), shmem, s, p, npad); break;
-    case 3: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 3>), grid, dim3(256), shmem, s, p, npad); break;
-    case 4: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 4>), grid, dim3(256), shmem, s, p, npad); break;
-    case 5: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 5>), grid, dim3(256), shmem, s, p, npad); break;
-    case 6: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 6>), grid, dim3(256), shmem, s, p, npad); break;
-    case 7: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 7>), grid, dim3(256), shmem, s, p, npad); break;
-    case 8: hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, 8>), grid, dim3(256), shmem, s, p, npad); break;
-    default: return hipErrorInvalidValue;
+// One instance of the finishing kernel per chunk count 1 .. kSkinnyMaxChunks; n selects it.
+template <bool AF32, int TOK, int S = 1>
+hipError_t launch_finish(const LinearProblem& p, hipStream_t s, dim3 grid, size_t shmem, int n, int64_t npad) {
+  if constexpr (S > kSkinnyMaxChunks) {
+    return hipErrorInvalidValue;
+  } else {
+    if (n != S) return launch_finish<AF32, TOK, S + 1>(p, s, grid, shmem, n, npad);
+    hipLaunchKernelGGL((skinny_finish_kernel<AF32, TOK, S>), grid, dim3(256), shmem, s, p, npad);
+    return hipGetLastError();
   }
-  return hipGetLastError();
 }
 
 template <bool NF4, bool AF32>

@@ -49,15 +49,18 @@ constexpr int64_t kSkinnyMaxLdt = 4096;  // sum of the padded ranks (the finishi
 inline bool skinny_path(Elt act, bool lossless, int64_t T, int64_t ldt) {
   return lossless && act == Elt::BF16 && T > 0 && T <= kSkinnyMaxT && ldt <= kSkinnyMaxLdt;
 }
-// K chunk (a multiple of 128 elements, at least 512) and number of chunks S <= 8:
-// about 8 chunks for long K, fixed by K alone, so the summation order of an output
+// K chunk (a multiple of 128 elements, at least 512) and number of chunks S <= 32:
+// about 32 chunks for long K, fixed by K alone, so the summation order of an output
 // does not depend on N or on the adapters (a stacked call equals one call per
-// group, bit for bit). The 512 floor halves the fp32 partial sums where K is
-// short: measured on MI355X at 64 tokens, 1536 -> 8960, HIP-graph replay, chunks
-// of 256 / 512 / 768 / 1024 (6 / 3 / 2 / 2 chunks) took 26.2 / 23.2 / 25.0 / 26.2 us
-// with an adapter and 21.7 / 18.2 / 19.9 / 21.0 us without.
+// group, bit for bit). Measured on MI355X at 64 tokens (HIP-graph replay):
+// - the 512 floor halves the fp32 partial sums where K is short: 1536 -> 8960 with
+//   chunks of 256 / 512 / 768 / 1024 (6 / 3 / 2 / 2 chunks) took 26.2 / 23.2 / 25.0 /
+//   26.2 us with an adapter and 21.7 / 18.2 / 19.9 / 21.0 us without;
+// - more chunks give the long-K layer more workgroups: 8960 -> 1536 with 8 / 14 / 18
+//   chunks took 24.6 / 22.3 / 21.8 us with an adapter, 21.6 / 19.6 / 19.0 without.
+constexpr int kSkinnyMaxChunks = 32;
 inline void skinny_plan(int64_t K, int* S, int64_t* kchunk) {
-  int64_t c = (K + 7) / 8;
+  int64_t c = (K + kSkinnyMaxChunks - 1) / kSkinnyMaxChunks;
   c = (c + 127) / 128 * 128;
   c = c < 512 ? 512 : c;
   *kchunk = c;

@@ -208,8 +208,8 @@ def test_multi_validation():
 
 def _skinny_bytes(T, K, N, ldt):
     """The few-token layout the header documents: S fp32 partial sums [S, T, round_up(N, 64) + ldt],
-    S = the number of K chunks (at most 8, each a multiple of 128 of at least 512 elements)."""
-    c = -(-K // 8)
+    S = the number of K chunks (at most 32, each a multiple of 128 of at least 512 elements)."""
+    c = -(-K // 32)
     c = max(512, -(-c // 128) * 128)
     S = -(-K // c)
     return S * T * (-(-N // 64) * 64 + ldt) * 4
