@@ -1923,19 +1923,20 @@ __global__ __launch_bounds__(DP::THREADS) void down_kernel(LinearProblem p, int 
 }
 
 // t~ = RN_bf16(s . sum of the K splits' partial sums, in split order): 4 columns per thread.
-__global__ __launch_bounds__(256) void down_finish_kernel(LinearProblem p, int S) {
+// The split count S is a template parameter, so all S loads of a thread issue before the first
+// wait (with a run-time count each load sat behind a branch whose join waited for it).
+template <int S>
+__global__ __launch_bounds__(256) void down_finish_kernel(LinearProblem p) {
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
   if (i >= p.T * p.ldt) return;
   const int64_t m = i / p.ldt;
   const int col = static_cast<int>(i - m * p.ldt);
-  f32x4 v[kMaxProducerSplits];
+  f32x4 v[S];
 #pragma unroll
-  for (int z = 0; z < kMaxProducerSplits; ++z)
-    if (z < S) v[z] = *reinterpret_cast<const f32x4*>(p.tpart + (z * p.T + m) * p.ldt + col);
+  for (int z = 0; z < S; ++z) v[z] = *reinterpret_cast<const f32x4*>(p.tpart + (z * p.T + m) * p.ldt + col);
   f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int z = 0; z < kMaxProducerSplits; ++z)
-    if (z < S) sum += v[z];
+  for (int z = 0; z < S; ++z) sum += v[z];
   int gi = 0;
   while (gi + 1 < p.n_groups && col >= p.g[gi + 1].t_col) ++gi;
   const float sc = p.g[gi].scale;
@@ -1944,6 +1945,18 @@ __global__ __launch_bounds__(256) void down_finish_kernel(LinearProblem p, int S
   w.x = pack_bf16x2(sum[0], sum[1]);
   w.y = pack_bf16x2(sum[2], sum[3]);
   *reinterpret_cast<uint2*>(static_cast<bf16_bits*>(p.work) + i) = w;
+}
+
+// One instance of the finishing kernel per split count 2 .. kMaxProducerSplits; n selects it.
+template <int S = 2>
+hipError_t launch_down_finish(const LinearProblem& p, hipStream_t s, dim3 grid, int n) {
+  if constexpr (S > kMaxProducerSplits) {
+    return hipErrorInvalidValue;
+  } else {
+    if (n != S) return launch_down_finish<S + 1>(p, s, grid, n);
+    hipLaunchKernelGGL((down_finish_kernel<S>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
 }
 
 template <class DP, bool SPLIT>
@@ -1957,7 +1970,7 @@ hipError_t launch_cfg(const LinearProblem& p, hipStream_t s) {
   hipLaunchKernelGGL((down_kernel<DP, SPLIT>), grid, dim3(DP::THREADS), 0, s, p, ks);
   if (S > 1) {
     const int64_t quads = p.T * p.ldt / 4;
-    hipLaunchKernelGGL(down_finish_kernel, dim3(static_cast<unsigned>((quads + 255) / 256)), dim3(256), 0, s, p, S);
+    return launch_down_finish(p, s, dim3(static_cast<unsigned>((quads + 255) / 256)), S);
   }
   return hipGetLastError();
 }
