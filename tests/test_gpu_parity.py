@@ -330,7 +330,9 @@ def test_fp32_adapter_on_bf16(T, K, N, r):
 
 @pytest.mark.parametrize("T,K,N,r,bias", [(1, 328, 300, 16, True), (7, 1536, 300, 70, False),
                                           (16, 328, 1000, 8, True), (33, 64, 96, 128, True),
-                                          (64, 2056, 520, 24, False)])
+                                          (64, 2056, 520, 24, False),
+                                          # the most K chunks: 32 of 512, and 32 of 640 with a ragged last
+                                          (16, 16384, 300, 16, True), (5, 20000, 260, 24, False)])
 def test_few_tokens_linear(T, K, N, r, bias):
     d = lw.small_linear_inputs(T, K, N, r, 60 + T, bias=bias, alpha=2.0 * r, strength=0.8, request_scale=0.7)
     say(f"case few tokens T={T} K={K} N={N} r={r} bias={bias}")
@@ -358,7 +360,7 @@ def test_few_tokens_rows_do_not_depend_on_the_batch(adapter):
             assert torch.equal(yb[:ts], ys), (tb, ts)
 
 
-@pytest.mark.parametrize("T,K,N,r", [(40, 256, 520, 24), (3, 512, 300, 64)])
+@pytest.mark.parametrize("T,K,N,r", [(40, 256, 520, 24), (3, 512, 300, 64), (9, 16384, 260, 16)])
 def test_few_tokens_fp32_adapter(T, K, N, r):
     d = lw.small_linear_inputs(T, K, N, r, 70 + T, adapter="f32", bias=True, alpha=2.0 * r, strength=0.8,
                                request_scale=0.7)
