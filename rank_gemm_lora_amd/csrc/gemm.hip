@@ -2275,7 +2275,6 @@ __global__ __launch_bounds__(256) void skinny_kernel(LinearProblem p, int nbw, i
 // waits for any of them; each 8-rank piece of t~ is read from LDS as 16-byte
 // vectors before its FMAs. (Both measured on MI355X, with the same bits: a
 // 64-token FFN-up call went from 29.1 to 26.4 us, FFN down from 26.4 to 24.3.)
-
 template <bool AF32, int kFinishTokens, int S>
 __global__ __launch_bounds__(256) void skinny_finish_kernel(LinearProblem p, int64_t npad) {
   extern __shared__ float tt[];  // [kFinishTokens, ldt]
