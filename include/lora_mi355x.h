@@ -156,7 +156,7 @@ int lora_linear_fwd(const void* x, int64_t T, int64_t K, int64_t ldx,
  * stream are fine. No part of it needs to start at zero: each kernel writes
  * every scratch element it reads.
  */
-#define LORA_NOALLOC_SCRATCH_BYTES (32ull * 1024ull * 1024ull)
+#define LORA_NOALLOC_SCRATCH_BYTES (64ull * 1024ull * 1024ull)
 int lora_linear_fwd_noalloc(const void* x, int64_t T, int64_t K, int64_t ldx,
                             const void* W, int64_t N, const void* bias,
                             const void* A, const void* B, int32_t rank, int32_t adapter_dtype,

@@ -71,7 +71,7 @@ _lib.lora_linear_fwd.restype = ctypes.c_int
 _lib.lora_linear_fwd_noalloc.argtypes = [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _f64, _f64, _f64,
                                          _p, _i64, _i32, _i32, _p]
 _lib.lora_linear_fwd_noalloc.restype = ctypes.c_int
-LORA_NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
+LORA_NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 _lib.lora_mfma_probe.argtypes = [_i64, _i32, _p, _p, _p]
 _lib.lora_mfma_probe.restype = ctypes.c_int
 _lib.lora_linear_fwd_phase.argtypes = [_i32, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _p, _p, _i32, _i32, _f64,

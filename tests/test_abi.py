@@ -392,3 +392,13 @@ def test_backward_validation():
     sz = rg.lora_linear_bwd_workspace_size
     assert sz(32760, 1536, 8960, 64) > sz(32760, 1536, 8960, 64, False) > 0   # W^T only with dx
     assert sz(0, 1536, 8960, 64) == 0
+
+
+def test_noalloc_scratch_size_matches_the_header():
+    """The binding's copy of LORA_NOALLOC_SCRATCH_BYTES is the header's value."""
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "lora_mi355x.h")).read()
+    m = re.search(r"#define LORA_NOALLOC_SCRATCH_BYTES \((\d+)ull \* 1024ull \* 1024ull\)", hdr)
+    assert m is not None
+    assert rg.LORA_NOALLOC_SCRATCH_BYTES == int(m.group(1)) * 1024 * 1024
+    # the few-token layout of a 64-token call 8960 -> 8960 fits
+    assert rg.lora_linear_workspace_size(64, 8960, 8960, [64], BF16) <= rg.LORA_NOALLOC_SCRATCH_BYTES

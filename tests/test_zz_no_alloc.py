@@ -48,6 +48,7 @@ CASES = [  # (first call, second call smaller), options
     (((300, 512, 520, 24), (130, 256, 300, 24)), {}),
     (((4352, 1536, 1536, 32), (2000, 1536, 700, 32)), {}),                 # producer K split
     (((64, 8960, 1536, 64), (20, 1536, 520, 16)), {}),                     # few tokens
+    (((64, 8960, 8960, 64), (16, 4096, 3000, 32)), {}),                    # few tokens, 41.6 MB of scratch
     (((300, 512, 520, 24), (100, 256, 200, 8)), {"adapter": "f32"}),       # hi/lo split copies
     (((200, 256, 300, 24), (50, 128, 96, 8)), {"quality": "exact"}),
     (((64, 128, 96, 8), (33, 128, 40, 8)), {"act": "f32", "adapter": "f32"}),
