@@ -402,3 +402,15 @@ def test_noalloc_scratch_size_matches_the_header():
     assert rg.LORA_NOALLOC_SCRATCH_BYTES == int(m.group(1)) * 1024 * 1024
     # the few-token layout of a 64-token call 8960 -> 8960 fits
     assert rg.lora_linear_workspace_size(64, 8960, 8960, [64], BF16) <= rg.LORA_NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("T,K,S", [(129, 512, 2), (129, 768, 3), (129, 1024, 4), (6529, 2048, 5), (5377, 2048, 6),
+                                   (4609, 2048, 7), (129, 2048, 8), (16384, 2048, 1)])
+def test_producer_split_count_in_the_workspace(T, K, S):
+    """The lossless bf16 workspace holds t~ [T, 64] bf16 and, with a producer K split into S parts,
+    S fp32 partial sums [S, T, 64] after it (256-byte aligned): the split counts the GPU tests of
+    each count expect."""
+    r256 = lambda v: -(-v // 256) * 256
+    got = rg.lora_linear_workspace_size(T, K, 96, [16], BF16)
+    want = T * 64 * 2 if S == 1 else r256(T * 64 * 2) + S * T * 64 * 4
+    assert got == want, (got, want)

@@ -313,6 +313,19 @@ def test_gemm_tiles_bitwise_equal(case):
         assert torch.equal(y256, run_linear(d, "lossless")), f"{case}: the automatic choice differs"
 
 
+@pytest.mark.parametrize("T,K,S", [(129, 512, 2), (129, 768, 3), (129, 1024, 4), (6529, 2048, 5), (5377, 2048, 6),
+                                   (4609, 2048, 7), (129, 2048, 8)])
+def test_producer_k_split_counts(T, K, S):
+    """Fewer than 128 tiles of 128 tokens: the rank-wide producer splits K into S parts (chosen by T
+    and K alone) whose partial sums a finishing kernel adds, one kernel instance per S. Each S from
+    2 to 8 against the oracle."""
+    N, r = 96, 16
+    d = lw.small_linear_inputs(T, K, N, r, 500 + S, bias=True, alpha=2.0 * r, strength=0.8, request_scale=0.7)
+    say(f"case producer split S={S} T={T} K={K}")
+    y64, yc = oracle_pair(d)
+    assert_gate(run_linear(d, "lossless"), y64, yc, what=f"lossless, producer split {S}")
+
+
 @pytest.mark.parametrize("T,K,N,r", [(300, 200, 520, 24), (257, 512, 300, 64)])
 def test_fp32_adapter_on_bf16(T, K, N, r):
     d = lw.small_linear_inputs(T, K, N, r, 21, adapter="f32", bias=True, alpha=2.0 * r, strength=0.8,
