@@ -59,8 +59,8 @@ def main():
     ap.add_argument("--layer-only", action="store_true",
                     help="only run the timed fused steps (for counter collection) and exit")
     ap.add_argument("--workload", choices=["attn_proj", "qkv_bf16", "qkv_f32", "nf4_layer", "nf4_layer_in_gemm",
-                                           "nf4_tokens256", "multi_ffn_up", "few_ffn_up", "backward_ffn_up",
-                                           "backward_ffn_down"],
+                                           "nf4_tokens256", "multi_ffn_up", "few_ffn_up", "few_ffn_down", "nf4_vector",
+                                           "backward_ffn_up", "backward_ffn_down"],
                     help="only run this workload's fused call (--warmup + --steps times; for counter runs) and exit")
     ap.add_argument("--write-traffic", metavar="DIR",
                     help="turn the four counter runs in DIR (f/, w/: FETCH_SIZE / WRITE_SIZE of --layer-only; "
@@ -321,14 +321,23 @@ def run_workload(torch, dev, name, warmup, steps):
                          dtype=torch.uint8, device=dev)
         fn = lambda: rg.lora_linear_nf4(x, codes, absmax, cb, sp.N, b, A, B, sp.alpha, sp.strength,
                                         sp.request_scale, out=y, workspace=ws, dequant=dq)
-    elif name == "few_ffn_up":  # 64 tokens: the few-token kernel and its finishing kernel
-        sp = lw.FEW_FFN_UP
+    elif name in ("few_ffn_up", "few_ffn_down"):  # 64 tokens: the few-token kernel and its finishing kernel
+        sp = lw.FEW_FFN_UP if name == "few_ffn_up" else lw.FEW_FFN_DOWN
         h = lw.linear_inputs(sp)
         x, W, b, A, B = (d2(h[k]) for k in ("x", "W", "b", "A", "B"))
         y = torch.empty((sp.T, sp.N), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(rg.lora_linear_workspace_size(sp.T, sp.K, sp.N, [sp.rank], rg.LORA_BF16), dtype=torch.uint8,
                          device=dev)
         fn = lambda: rg.lora_linear(x, W, b, A, B, sp.alpha, sp.strength, sp.request_scale, out=y, workspace=ws)
+    elif name == "nf4_vector":  # one token through the 4-bit weight (dequantized in registers)
+        sp = lw.NF4_VECTOR
+        h = lw.nf4_inputs(sp)
+        x, codes, absmax, cb, A, B, b = (d2(h[k]) for k in ("x", "codes", "absmax", "codebook", "A", "B", "b"))
+        y = torch.empty((sp.T, sp.N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(1, rg.lora_linear_nf4_workspace_size(sp.T, sp.K, sp.N, sp.rank, rg.LORA_BF16)),
+                         dtype=torch.uint8, device=dev)
+        fn = lambda: rg.lora_linear_nf4(x, codes, absmax, cb, sp.N, b, A, B, sp.alpha, sp.strength,
+                                        sp.request_scale, out=y, workspace=ws)
     elif name in ("backward_ffn_up", "backward_ffn_down"):  # dx, dA, dB, db with t~ from the forward call
         up_h, down_h = lw.ffn_pair_inputs()
         sp, h = (lw.FFN_UP, up_h) if name == "backward_ffn_up" else (lw.FFN_DOWN, down_h)
